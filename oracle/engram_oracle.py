@@ -1,0 +1,255 @@
+"""CPU oracle for the DeepSeek-V4.1-Flash Engram forward (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or run this module.  The product path (the HIP library and its Python binding) never
+touches it and shares no code with it.
+
+What it computes is the plain definition of the Engram block, written from the pages:
+
+* "DeepSeek-V4.1 / blocks / engram-second" (atlas.klimoza.dev), code panel, ``Engram.forward``
+  and ``ParallelEngramEmbedding.forward``: gather fp8 rows and their block scales, multiply in
+  fp32, round to bf16, flatten the hash columns, project with ``wkv`` into four keys and one
+  value, gate each stream by a normalised dot product, add gate x value to every stream.
+* "DeepSeek's Other Modules" (monishver11.github.io), section "Engram", subsections "The lookup
+  pipeline" (context-aware gating, shared value and per-stream key) and "V4.1's two tables,
+  reconciled" (24 columns of 256 fp8 features, the 6,144 -> 25,600 projection).
+* "Engram in DeepSeek V4.1 Flash" (zhuai.tech), "Step 3: Inject memory at the correct layer
+  boundary": the same gate formula restated, per stream, with q and k weights used as a product.
+
+Precision: every floating-point step is carried out in IEEE double, except where the pages fix
+a narrower type, which is then applied as an explicit rounding:
+  * the dequantisation product is an fp32 multiply (fp8 value times fp32 scale);
+  * table rows are rounded to bf16 before the projection;
+  * the projection output (kv) is rounded to bf16 (reading: the Linear keeps the bf16
+    activation dtype; its accumulation is exact here, then rounded once via fp32);
+  * q_weight * k_weight is an fp32 product;
+  * the output streams are rounded to bf16 (through fp32).
+Reductions over ``dim`` start from +0 so that an all-zero sum is +0.
+
+All arrays are numpy; bf16 tensors are carried as uint16 bit patterns.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional, Tuple
+
+import numpy as np
+
+# ----------------------------------------------------------------------------------------
+# number formats
+# ----------------------------------------------------------------------------------------
+
+
+def e4m3fn_value(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 "fn" codes (torch.float8_e4m3fn; table dtype on the engram-second
+    page, ParallelEngramEmbedding): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits,
+    no infinities; exponent 15 with mantissa 7 is NaN; exponent 0 is subnormal (m * 2^-9)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = (c >> 7) & 1
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (8 + m) * np.exp2((e - 10).astype(np.float64)))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def round_fp32(x: np.ndarray) -> np.ndarray:
+    """Round doubles to the nearest fp32 (ties to even); returned as float64."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def bf16_bits_from_fp32(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (nearest, ties to even) and return the bit patterns.
+    NaN becomes the canonical quiet NaN 0x7FC0; overflow past the largest bf16 gives inf."""
+    with np.errstate(invalid="ignore", over="ignore"):
+        f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    b = f.view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)).astype(np.uint16)
+    return np.where(np.isnan(f), np.uint16(0x7FC0), r).astype(np.uint16)
+
+
+def bf16_value(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64 values (exact)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------------------
+# S1 + S2: row gather and dequantisation
+# ----------------------------------------------------------------------------------------
+
+RowFetch = Callable[[np.ndarray], Tuple[np.ndarray, np.ndarray]]
+
+
+def array_fetch(table: np.ndarray, scales: np.ndarray) -> RowFetch:
+    """Row provider over in-memory arrays: table uint8 [n_rows, hd], scales fp32 [n_rows, nb]."""
+
+    def fetch(rows: np.ndarray):
+        return table[rows], scales[rows]
+
+    return fetch
+
+
+def gather_dequant(hash_ids: np.ndarray, fetch: RowFetch, n_rows: int, head_dim: int,
+                   scale_block: int) -> np.ndarray:
+    """emb bf16 bits [M, C * head_dim] for hash_ids [M, C] (global row ids).
+
+    engram-second page, ParallelEngramEmbedding.forward with a single shard: rows outside
+    [0, n_rows) are replaced by row 0 for the lookup and then zeroed; the fp8 value of every
+    feature is multiplied in fp32 by the scale of its block (feature c uses scale c //
+    scale_block) and the product is rounded to bf16.  Engram.forward then flattens the
+    columns: feature c of column j lands at position j * head_dim + c.
+    """
+    ids = np.asarray(hash_ids, dtype=np.int64)
+    M, C = ids.shape
+    out_of_range = (ids < 0) | (ids >= n_rows)
+    local = np.where(out_of_range, 0, ids)
+    codes, scales = fetch(local.reshape(-1))
+    codes = np.asarray(codes, dtype=np.uint8).reshape(M, C, head_dim)
+    scales = np.asarray(scales, dtype=np.float32).reshape(M, C, head_dim // scale_block)
+    block_of_feature = np.arange(head_dim) // scale_block
+    with np.errstate(invalid="ignore", over="ignore"):
+        prod = e4m3fn_value(codes) * scales.astype(np.float64)[:, :, block_of_feature]
+    bits = bf16_bits_from_fp32(round_fp32(prod))
+    bits[out_of_range] = 0
+    return bits.reshape(M, C * head_dim)
+
+
+# ----------------------------------------------------------------------------------------
+# S3: wkv projection
+# ----------------------------------------------------------------------------------------
+
+
+def kv_proj(emb_bits: np.ndarray, wkv: np.ndarray, chunk: int = 4096) -> np.ndarray:
+    """kv bf16 bits [M, N] = bf16(emb @ wkv^T).
+
+    wkv is the Linear weight in [out, in] = [(hc + 1) * dim, C * head_dim] layout (the
+    engram-second page, ``self.wkv = Linear(n_hash_cols * head_dim, dim * (hc_mult + 1))``).
+    ``wkv`` is given either as bf16 bit patterns (uint16) or as float values that are exactly
+    bf16 numbers.  The products of two bf16 numbers are exact in double and 6,144-term sums
+    stay far inside double precision, so the accumulation is effectively exact; the result
+    is rounded to fp32 and then to bf16.
+    """
+    a = bf16_value(emb_bits)
+    M = a.shape[0]
+    N = wkv.shape[0]
+    out = np.empty((M, N), dtype=np.uint16)
+    for lo in range(0, N, chunk):
+        hi = min(N, lo + chunk)
+        w = wkv[lo:hi]
+        w = bf16_value(w) if w.dtype == np.uint16 else np.asarray(w, dtype=np.float64)
+        with np.errstate(invalid="ignore", over="ignore"):
+            out[:, lo:hi] = bf16_bits_from_fp32(round_fp32(a @ w.T))
+    return out
+
+
+# ----------------------------------------------------------------------------------------
+# S4 + S5: per-(token, stream) gate
+# ----------------------------------------------------------------------------------------
+
+
+def gate(x_bits: np.ndarray, kv_bits: np.ndarray, q_weight: np.ndarray, k_weight: np.ndarray,
+         token_mask: Optional[np.ndarray], eps: float, clamp: float) -> dict:
+    """Gate [M, hc] (float64) and its intermediate sums.
+
+    engram-second page, Engram.forward: keys are the first hc * dim columns of kv, one per
+    stream; with w = q_weight * k_weight (an fp32 product) and h = x as float,
+        rstd = rsqrt(mean_d h^2 + eps) * rsqrt(mean_d key^2 + eps)
+        dot  = (sum_d h * w * key) * rstd * dim^-1/2
+        gate = sigmoid(copysign(sqrt(max(|dot|, clamp)), dot))
+    normalised per (token, stream), not across streams; the gate is 0 where token_mask is
+    false.  The zhuai.tech page (Step 3) restates the same gate with q * k precomputed.
+    """
+    x = bf16_value(x_bits)
+    M, hc, dim = x.shape
+    key = bf16_value(kv_bits[:, :hc * dim]).reshape(M, hc, dim)
+    w = round_fp32(np.asarray(q_weight, np.float64) * np.asarray(k_weight, np.float64))
+    A = 0.0 + np.sum(x * x, axis=-1)
+    Kq = 0.0 + np.sum(key * key, axis=-1)
+    D = 0.0 + np.sum((x * w[None]) * key, axis=-1)
+    rstd = (1.0 / np.sqrt(A / dim + eps)) * (1.0 / np.sqrt(Kq / dim + eps))
+    dot = D * rstd * (dim ** -0.5)
+    z = np.copysign(np.sqrt(np.maximum(np.abs(dot), clamp)), dot)
+    g = 1.0 / (1.0 + np.exp(-z))
+    if token_mask is not None:
+        g = np.where(np.asarray(token_mask).reshape(M, 1).astype(bool), g, 0.0)
+    return {"gate": g, "A": A, "Kq": Kq, "D": D, "dot": dot}
+
+
+# ----------------------------------------------------------------------------------------
+# S6: residual add
+# ----------------------------------------------------------------------------------------
+
+
+def residual(x_bits: np.ndarray, kv_bits: np.ndarray, g: np.ndarray,
+             token_mask: Optional[np.ndarray]) -> dict:
+    """out = h + gate * value on every stream, value shared (engram-second page, last line of
+    Engram.forward; zhuai.tech Step 3: hidden += gate x value).  Returns the unrounded result
+    (float64) and its bf16 rounding; tokens whose mask is false keep x bit for bit, as the
+    Engram.forward docstring says they pass through untouched."""
+    x = bf16_value(x_bits)
+    M, hc, dim = x.shape
+    value = bf16_value(kv_bits[:, hc * dim:(hc + 1) * dim])
+    out_f = x + g[:, :, None] * value[:, None, :]
+    out_bits = bf16_bits_from_fp32(round_fp32(out_f))
+    if token_mask is not None:
+        keep = ~np.asarray(token_mask).reshape(M).astype(bool)
+        out_bits[keep] = x_bits[keep]
+        out_f[keep] = x[keep]
+    return {"out_f": out_f, "out_bits": out_bits}
+
+
+def gate_apply(x_bits, kv_bits, q_weight, k_weight, token_mask, eps, clamp) -> dict:
+    """S4-S6 from a given kv (the split the zhuai.tech page makes between projection and
+    gating)."""
+    g = gate(x_bits, kv_bits, q_weight, k_weight, token_mask, eps, clamp)
+    r = residual(x_bits, kv_bits, g["gate"], token_mask)
+    return {**g, **r}
+
+
+# ----------------------------------------------------------------------------------------
+# whole forward
+# ----------------------------------------------------------------------------------------
+
+
+def forward(x_bits: np.ndarray, hash_ids: np.ndarray, token_mask: Optional[np.ndarray],
+            fetch: RowFetch, n_rows: int, head_dim: int, scale_block: int, wkv: np.ndarray,
+            q_weight: np.ndarray, k_weight: np.ndarray, eps: float = 1e-20,
+            clamp: float = 1e-6) -> dict:
+    """Engram.forward for tokens x_bits [M, hc, dim] with hash_ids [M, C] and token_mask [M]
+    (None = all true).  Tokens are independent, so any subset of a batch can be evaluated
+    alone."""
+    emb = gather_dequant(hash_ids, fetch, n_rows, head_dim, scale_block)
+    kv = kv_proj(emb, wkv)
+    res = gate_apply(x_bits, kv, q_weight, k_weight, token_mask, eps, clamp)
+    return {"emb": emb, "kv": kv, **res}
+
+
+# ----------------------------------------------------------------------------------------
+# layout accounting
+# ----------------------------------------------------------------------------------------
+
+
+def param_counts(n_rows: int, head_dim: int, n_cols: int, hc: int, dim: int) -> dict:
+    """Learned element counts of one Engram instance (engram-second page, parameter table):
+    table rows x features, the wkv projection, and the q/k gate weights."""
+    table = n_rows * head_dim
+    wkv = (n_cols * head_dim) * (dim * (hc + 1))
+    gate_w = 2 * hc * dim
+    return {"table": table, "wkv": wkv, "gate": gate_w, "total": table + wkv + gate_w}
+
+
+def bytes_per_token(n_cols: int, head_dim: int, scale_block: int, scale_bytes: int) -> dict:
+    """Table traffic of one token in one module: one fp8 byte per feature of each gathered row
+    plus one scale per block ("DeepSeek's Other Modules", Serving cost)."""
+    codes = n_cols * head_dim
+    scales = n_cols * (head_dim // scale_block) * scale_bytes
+    return {"codes": codes, "scales": scales}
+
+
+__all__ = [
+    "e4m3fn_value", "round_fp32", "bf16_bits_from_fp32", "bf16_value", "array_fetch",
+    "gather_dequant", "kv_proj", "gate", "residual", "gate_apply", "forward", "param_counts",
+    "bytes_per_token",
+]

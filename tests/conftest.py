@@ -1,0 +1,20 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (runs the HIP path)")
+    config.addinivalue_line("markers", "slow: large-size GPU parity case")
+
+
+def pytest_collection_modifyitems(config, items):
+    # GPU tests print which case runs before they touch the device
+    for it in items:
+        if it.get_closest_marker("gpu") is not None:
+            it.user_properties.append(("gpu", True))
