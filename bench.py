@@ -1,0 +1,151 @@
+"""Engram forward benchmark on one MI355X.
+
+One step = one engram_forward call (row gather + dequantisation, wkv projection, per-stream
+gate, residual add) over one batch of seeded synthetic inputs already resident in HBM.
+Prints one JSON line.  `value` is tokens per second of the whole job (one GPU).
+
+  python bench.py [--steps K] [--warmup W] [--workload decode_b64|prefill_t8192|...]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+
+
+def algorithmic_bytes(w) -> int:
+    """Bytes one launch must move at least: every input read once, every output written once."""
+    per_token = (w.n_cols * 8 + w.n_cols * w.head_dim + w.n_cols * w.n_blocks * 4 +
+                 2 * w.hc * w.dim * 2 + 1)
+    per_call = w.N * w.K * 2 + 2 * w.hc * w.dim * 4
+    return per_call + w.M * per_token
+
+
+def algorithmic_flops(w) -> int:
+    return 2 * w.M * w.N * w.K
+
+
+def cpu_baseline(w, n_tokens: int):
+    """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sel = np.arange(n_tokens)
+    wkv = w.wkv_f32()
+    ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
+    mask = w.token_mask().reshape(-1)[sel]
+    x = w.x_tokens(sel)
+    q, k = w.qk()
+    fetch = synth.host_fetch(w)
+    t0 = time.perf_counter()
+    oracle.forward(x, ids, mask, fetch, w.n_rows, w.head_dim, w.scale_block, wkv, q, k,
+                   eps=w.eps, clamp=w.clamp)
+    dt = time.perf_counter() - t0
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} tokens of {w.name} (full layer dims, fp64 numpy), "
+                      f"{dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_b64")
+    ap.add_argument("--cpu-tokens", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the Engram forward is data parallel over tokens and "
+              "this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import hashed_gram_engram_amd as eg
+    import synth
+
+    w = synth.get(args.workload)
+    torch.cuda.set_device(0)
+    d = synth.device_inputs(w)
+    lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
+    ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty_like(d["x"])
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        eg.engram_forward(lay, d["x"], d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                          d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws, err_count=err)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per_launch_ms))
+    assert int(err.item()) == 0, "hash ids out of range"
+    assert int(ws[:4].view(torch.int32).item()) == 0, "a cross-workgroup wait timed out"
+
+    mode = "hbm" if w.M <= 512 else "mfma"
+    if mode == "hbm":
+        ach = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        ach = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+    roof["kernel"] = "engram_forward (k_stream fused)"
+    roof["per_launch_bytes"] = algorithmic_bytes(w)
+    roof["per_launch_flops"] = algorithmic_flops(w)
+    roof["ms_per_launch"] = round(ms, 5)
+
+    res = {
+        "metric": "Engram forward tokens/sec",
+        "value": round(w.M / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based generator; no trained weights)",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
+                   "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
+                   "table_rows": w.n_rows, "hash_ids": w.hash_dist,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_tokens or min(w.M, 64)
+        res["cpu_baseline"] = cpu_baseline(w, n)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

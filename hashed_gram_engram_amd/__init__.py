@@ -1,0 +1,202 @@
+"""Python binding of libengram.so, the MI355X (gfx950) Engram forward library.
+
+The functions here carry the C ABI's names (include/engram.h) and only marshal arguments:
+torch tensors provide device memory, the current torch stream provides the HIP stream, and
+every step of the computation runs in the library's HIP kernels.  If the shared library is
+missing, importing the binding raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                      "(hipcc --offload-arch=gfx950)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+ENGRAM_OK = 0
+STATUS = {0: "ok", -1: "null pointer", -2: "layout", -3: "shape", -4: "alignment",
+          -5: "workspace", -6: "hip", -7: "device"}
+
+
+class EngramLayout(ctypes.Structure):
+    _fields_ = [("hc", ctypes.c_int32), ("dim", ctypes.c_int32), ("n_cols", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("scale_block", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("clamp", ctypes.c_float)]
+
+
+class EngramError(RuntimeError):
+    def __init__(self, where: str, status: int):
+        msg = _lib.engram_status_str(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_LP = ctypes.POINTER(EngramLayout)
+_lib.engram_status_str.restype = ctypes.c_char_p
+_lib.engram_status_str.argtypes = [ctypes.c_int]
+_lib.engram_layout_check.argtypes = [_LP]
+_lib.engram_param_counts.argtypes = [_LP, ctypes.POINTER(ctypes.c_int64)]
+_lib.engram_forward_workspace_bytes.argtypes = [_LP, _i64, _i64]
+_lib.engram_forward_workspace_bytes.restype = _sz
+_lib.engram_gather_dequant.argtypes = [_LP, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.engram_kv_proj.argtypes = [_LP, _vp, _vp, _i64, _i64, _vp, _vp]
+_lib.engram_gate_apply.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.engram_forward.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp,
+                                _sz, _vp, _vp]
+for _f in (_lib.engram_layout_check, _lib.engram_param_counts, _lib.engram_gather_dequant,
+           _lib.engram_kv_proj, _lib.engram_gate_apply, _lib.engram_forward):
+    _f.restype = ctypes.c_int
+
+EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_workspace_bytes",
+            "engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
+            "engram_status_str"]
+
+
+def make_layout(hc: int, dim: int, n_cols: int, head_dim: int, scale_block: int, n_rows: int,
+                eps: float = 1e-20, clamp: float = 1e-6) -> EngramLayout:
+    return EngramLayout(hc, dim, n_cols, head_dim, scale_block, 0, n_rows, eps, clamp)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(where: str, st: int):
+    if st != ENGRAM_OK:
+        raise EngramError(where, st)
+
+
+def _contig(name: str, t: torch.Tensor, dtype=None) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t
+
+
+_BF16 = (torch.bfloat16, torch.int16)
+
+
+def engram_layout_check(layout: EngramLayout) -> int:
+    return _lib.engram_layout_check(ctypes.byref(layout))
+
+
+def engram_param_counts(layout: EngramLayout):
+    out = (ctypes.c_int64 * 3)()
+    _check("engram_param_counts", _lib.engram_param_counts(ctypes.byref(layout), out))
+    return int(out[0]), int(out[1]), int(out[2])
+
+
+def engram_forward_workspace_bytes(layout: EngramLayout, B: int, T: int) -> int:
+    return int(_lib.engram_forward_workspace_bytes(ctypes.byref(layout), B, T))
+
+
+def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: torch.Tensor,
+                          hash_ids: torch.Tensor, emb: Optional[torch.Tensor] = None,
+                          err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """emb [B, T, n_cols * head_dim] bf16 from hash_ids [B, T, n_cols] int64."""
+    B, T, C = hash_ids.shape
+    _contig("hash_ids", hash_ids, torch.int64)
+    _contig("table", table, torch.uint8)
+    _contig("scales", scales, torch.float32)
+    if emb is None:
+        emb = torch.empty((B, T, C * layout.head_dim), dtype=torch.bfloat16, device=hash_ids.device)
+    _check("engram_gather_dequant", _lib.engram_gather_dequant(
+        ctypes.byref(layout), _ptr(table), _ptr(scales), _ptr(hash_ids), B, T, _ptr(emb),
+        _ptr(err_count), _stream()))
+    return emb
+
+
+def engram_kv_proj(layout: EngramLayout, emb: torch.Tensor, wkv: torch.Tensor,
+                   kv: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """kv [B, T, (hc + 1) * dim] bf16 = emb @ wkv^T."""
+    B, T, _ = emb.shape
+    _contig("emb", emb, _BF16)
+    _contig("wkv", wkv, _BF16)
+    if kv is None:
+        kv = torch.empty((B, T, (layout.hc + 1) * layout.dim), dtype=torch.bfloat16,
+                         device=emb.device)
+    _check("engram_kv_proj", _lib.engram_kv_proj(ctypes.byref(layout), _ptr(emb), _ptr(wkv), B, T,
+                                                 _ptr(kv), _stream()))
+    return kv
+
+
+def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
+                      q_weight: torch.Tensor, k_weight: torch.Tensor,
+                      token_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                      gate: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out [B, T, hc, dim] bf16 = x + gate * value (gate per token and stream)."""
+    B, T = x.shape[0], x.shape[1]
+    _contig("x", x, _BF16)
+    _contig("kv", kv, _BF16)
+    _contig("q_weight", q_weight, torch.float32)
+    _contig("k_weight", k_weight, torch.float32)
+    if token_mask is not None:
+        _contig("token_mask", token_mask, (torch.uint8, torch.bool))
+    if out is None:
+        out = torch.empty_like(x)
+    _check("engram_gate_apply", _lib.engram_gate_apply(
+        ctypes.byref(layout), _ptr(x), _ptr(kv), _ptr(q_weight), _ptr(k_weight), _ptr(token_mask),
+        B, T, _ptr(out), _ptr(gate), _stream()))
+    return out
+
+
+class Workspace:
+    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves it
+    zero-filled after every call)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, layout: EngramLayout, B: int, T: int) -> torch.Tensor:
+        need = max(256, engram_forward_workspace_bytes(layout, B, T))
+        if self.buf is None or self.buf.numel() < need:
+            self.buf = torch.zeros(need, dtype=torch.uint8, device=self.device or "cuda")
+        return self.buf
+
+
+_default_ws: dict = {}
+
+
+def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
+                   token_mask: Optional[torch.Tensor], table: torch.Tensor, scales: torch.Tensor,
+                   wkv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole Engram forward: out [B, T, hc, dim] bf16 (may be x itself)."""
+    B, T = x.shape[0], x.shape[1]
+    _contig("x", x, _BF16)
+    _contig("hash_ids", hash_ids, torch.int64)
+    _contig("table", table, torch.uint8)
+    _contig("scales", scales, torch.float32)
+    _contig("wkv", wkv, _BF16)
+    _contig("q_weight", q_weight, torch.float32)
+    _contig("k_weight", k_weight, torch.float32)
+    if token_mask is not None:
+        _contig("token_mask", token_mask, (torch.uint8, torch.bool))
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
+        workspace = _default_ws.setdefault(dev, Workspace(x.device)).get(layout, B, T)
+    _check("engram_forward", _lib.engram_forward(
+        ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
+        _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(err_count), _stream()))
+    return out

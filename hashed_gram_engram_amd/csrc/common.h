@@ -1,0 +1,119 @@
+// Device helpers shared by the Engram kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace engram {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kFltMax = 3.40282347e38f;
+
+// ------------------------------------------------------------------ bf16 packing
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 p = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_round(float v) {
+  return bf16_lo(pack_bf16x2(v, 0.0f));
+}
+
+// Any NaN half of a packed bf16 pair becomes the canonical quiet NaN 0x7FC0 (the hardware
+// convert keeps the NaN's sign; the table dequantisation contract writes 0x7FC0).
+__device__ __forceinline__ uint32_t canon_nan2(uint32_t w) {
+  uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+  lo = ((lo & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : lo;
+  hi = ((hi & 0x7FFFu) > 0x7F80u) ? 0x7FC0u : hi;
+  return lo | (hi << 16);
+}
+
+// ------------------------------------------------------------------ fp8 dequantisation
+
+// Non-zero iff one of the four e4m3fn codes in `c` is a NaN code (low seven bits all ones).
+__device__ __forceinline__ uint32_t nan_code_bits(uint32_t c) {
+  return ((c & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+}
+
+// Four codes times one fp32 scale -> four bf16 in two dwords.  The fp8 decode is exact
+// (v_cvt_pk_f32_fp8, OCP e4m3), the product is one IEEE fp32 multiply and the bf16 rounding is
+// nearest-even; NaN results are not canonicalised here.
+__device__ __forceinline__ u32x2 dequant4_raw(uint32_t c, float s) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
+  u32x2 r;
+  r.x = pack_bf16x2(lo.x * s, lo.y * s);
+  r.y = pack_bf16x2(hi.x * s, hi.y * s);
+  return r;
+}
+
+// Sixteen codes with one scale -> sixteen bf16 (o0 = features 0..7, o1 = 8..15).  A NaN result
+// can only come from a NaN code or a non-finite scale; both are rare, so the canonicalisation
+// runs behind a branch that the whole wave normally skips.
+__device__ __forceinline__ void dequant16(u32x4 c, float s, u32x4& o0, u32x4& o1) {
+  u32x2 a = dequant4_raw(c.x, s), b = dequant4_raw(c.y, s);
+  u32x2 d = dequant4_raw(c.z, s), e = dequant4_raw(c.w, s);
+  o0 = u32x4{a.x, a.y, b.x, b.y};
+  o1 = u32x4{d.x, d.y, e.x, e.y};
+  uint32_t bad = nan_code_bits(c.x) | nan_code_bits(c.y) | nan_code_bits(c.z) | nan_code_bits(c.w);
+  if (__builtin_expect(bad != 0u || !(__builtin_fabsf(s) <= kFltMax), 0)) {
+    o0 = u32x4{canon_nan2(o0.x), canon_nan2(o0.y), canon_nan2(o0.z), canon_nan2(o0.w)};
+    o1 = u32x4{canon_nan2(o1.x), canon_nan2(o1.y), canon_nan2(o1.z), canon_nan2(o1.w)};
+  }
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// D = A * B + C for a 16x16 output block, K = 32 (v_mfma_f32_16x16x32_bf16).  Lane l supplies
+// A[l % 16][8 * (l / 16) + e] and B[8 * (l / 16) + e][l % 16], e = 0..7, and receives
+// D[4 * (l / 16) + r][l % 16], r = 0..3.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------ reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ------------------------------------------------------------------ cross-workgroup signalling
+
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin (with sleeps) until *p >= target or the spin budget is spent; returns false on time-out.
+// Every wait in these kernels is bounded so that a grid always drains.
+__device__ __forceinline__ bool wait_at_least(const uint32_t* p, uint32_t target, uint32_t budget) {
+  uint32_t it = 0;
+  while (load_relaxed(p) < target) {
+    __builtin_amdgcn_s_sleep(8);
+    if (++it > budget) return false;
+  }
+  return true;
+}
+
+}  // namespace engram

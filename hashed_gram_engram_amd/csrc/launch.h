@@ -1,0 +1,78 @@
+// Kernel argument blocks and launchers (host side of the HIP kernels).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace engram {
+
+struct GatherArgs {
+  const uint8_t* table;
+  const float* scales;
+  const int64_t* hash_ids;
+  int64_t n_pairs;  // tokens * n_cols
+  int head_dim;
+  int scale_block;
+  int64_t n_rows;
+  uint16_t* emb;
+  int32_t* err_count;
+};
+
+struct GateArgs {
+  const uint16_t* x;
+  const uint16_t* kv;
+  const float* q_weight;
+  const float* k_weight;
+  const uint8_t* token_mask;
+  int64_t M;
+  int dim;
+  float eps, clamp, inv_sqrt_dim;
+  uint16_t* out;
+  float* gate;
+};
+
+// Arguments of the weight-streaming projection kernels (projection alone, or the whole
+// Engram forward).  Token blocks are 64 tokens; the grid is persistent.
+struct StreamArgs {
+  const uint16_t* wkv;  // [N, K] bf16
+  int64_t M;
+  int K, N, dim;
+  // projection alone
+  const uint16_t* emb;  // [M, K] bf16
+  uint16_t* kv;         // [M, N] bf16
+  // whole forward
+  const uint16_t* x;
+  const int64_t* hash_ids;
+  const uint8_t* token_mask;
+  const uint8_t* table;
+  const float* scales;
+  const float* q_weight;
+  const float* k_weight;
+  uint16_t* out;
+  int32_t* err_count;
+  int n_cols, head_dim, scale_block;
+  int64_t n_rows;
+  float eps, clamp, inv_sqrt_dim;
+  // workspace views
+  uint32_t* ws_hdr;    // [0] wait time-outs, [1] exit counter
+  uint32_t* counters;  // [n_tb][4]
+  uint32_t* flags;     // [n_tb][4]
+  float* gates;        // [n_tb][4][64]
+  float* partials;     // [n_tb][grid][2][64][3]
+  uint32_t spin_budget;
+};
+
+hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream);
+hipError_t launch_gate_apply(const GateArgs& a, hipStream_t stream);
+
+// Projection alone: kv = bf16(emb @ wkv^T).
+hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream);
+
+// Whole forward, weight-streaming schedule.  Needs a zero-filled workspace of
+// stream_workspace_bytes(); all workgroups must be co-resident (cooperative launch).
+size_t stream_workspace_bytes(int64_t M, int N, int grid);
+int stream_grid(int N, int num_cus);
+hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
+
+}  // namespace engram

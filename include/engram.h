@@ -1,0 +1,138 @@
+/* engram.h: C ABI of the MI355X (gfx950) Engram forward library, libengram.so.
+ *
+ * The operation is the Engram block of DeepSeek-V4.1-Flash as given on the
+ * "DeepSeek-V4.1 / blocks / engram-second" page (code panel: Engram.forward and
+ * ParallelEngramEmbedding.forward), with the tensor statement of that page:
+ * x [B, T, hc, dim] in, the same shape out, hash_ids [B, T, n_cols] global row ids.
+ *
+ * Conventions shared by every entry point:
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Every tensor pointer is a DEVICE pointer to a contiguous row-major tensor, 16-byte
+ *    aligned.  The caller owns every buffer; the library allocates no device memory and
+ *    keeps no state between calls (beyond the caller-owned workspace of engram_forward).
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  Arguments are
+ *    checked synchronously on the host first; on any error nothing is enqueued and a
+ *    negative status is returned.  B * T == 0 is a no-op returning ENGRAM_OK.
+ *  - hc must be 4; dim a multiple of 64; head_dim a multiple of 64 and of scale_block;
+ *    scale_block a multiple of 16; n_cols * head_dim a multiple of 128.
+ *  - Hash ids outside [0, n_rows) read as an all-zero row (a single-shard
+ *    ParallelEngramEmbedding zero-fills rows it does not hold); when err_count is not NULL
+ *    each such (token, column) pair adds 1 to *err_count (device int32), so a caller can
+ *    check after synchronising.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* engram_stream_t; /* a hipStream_t */
+
+typedef enum {
+  ENGRAM_OK = 0,
+  ENGRAM_E_NULL = -1,      /* a required pointer is NULL                        */
+  ENGRAM_E_LAYOUT = -2,    /* the layout violates a constraint listed above      */
+  ENGRAM_E_SHAPE = -3,     /* negative B or T, or a size that overflows          */
+  ENGRAM_E_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned            */
+  ENGRAM_E_WORKSPACE = -5, /* workspace missing or smaller than required         */
+  ENGRAM_E_HIP = -6,       /* the HIP runtime refused a launch or query          */
+  ENGRAM_E_DEVICE = -7     /* the current device is not gfx950                   */
+} engram_status;
+
+/* Sizes of one Engram instance (engram-second page, Engram.__init__ and config.json:
+ * hc_mult = 4, dim = 5120, n_hash_cols = (engram_max_ngram_size - 1) * engram_n_heads = 24,
+ * engram_head_dim = 256, norm_eps = 1e-20, clamp value 1e-6).  scale_block is the number of
+ * features sharing one fp32 dequantisation scale (32 on the pages, 128 in the large
+ * synthetic workloads). */
+typedef struct {
+  int32_t hc;
+  int32_t dim;
+  int32_t n_cols;
+  int32_t head_dim;
+  int32_t scale_block;
+  int32_t reserved; /* must be 0 */
+  int64_t n_rows;   /* rows of the table: the sum of the prime range lengths */
+  float eps;
+  float clamp;
+} engram_layout;
+
+/* Host-only checks of a layout; no device work. */
+engram_status engram_layout_check(const engram_layout* layout);
+
+/* Learned element counts of one instance (engram-second page, Parameters table):
+ * out[0] = table entries n_rows * head_dim, out[1] = wkv entries
+ * (n_cols * head_dim) * ((hc + 1) * dim), out[2] = gate weights 2 * hc * dim. */
+engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
+
+/* Bytes of workspace engram_forward needs for B x T tokens on the current device (0 on an
+ * invalid layout).  The workspace must be zero-filled before its first use.  Its leading
+ * control words (counters and flags) are back at zero when engram_forward completes; the rest
+ * holds per-call partial sums that are always overwritten before they are read.  So one
+ * workspace serves any number of calls on one stream without clearing; calls that overlap in
+ * time must use different workspaces. */
+size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, int64_t T);
+
+/* S1 + S2: row gather and dequantisation (engram-second page,
+ * ParallelEngramEmbedding.forward, single shard; flatten as in Engram.forward).
+ *   table    [n_rows, head_dim]   uint8  fp8 e4m3fn codes
+ *   scales   [n_rows, head_dim / scale_block] fp32
+ *   hash_ids [B, T, n_cols]       int64  global row ids
+ *   emb      [B, T, n_cols * head_dim] bf16 out:
+ *            emb[m, j * head_dim + c] = bf16(fp32(e4m3(table[r, c]) * scales[r, c / scale_block]))
+ *            with r = hash_ids[m, j]; rounding to nearest even; NaN is written as 0x7FC0. */
+engram_status engram_gather_dequant(const engram_layout* layout, const uint8_t* table,
+                                    const float* scales, const int64_t* hash_ids, int64_t B,
+                                    int64_t T, uint16_t* emb, int32_t* err_count,
+                                    engram_stream_t stream);
+
+/* S3: the wkv projection (engram-second page, self.wkv, a Linear from n_cols * head_dim to
+ * (hc + 1) * dim features):
+ *   emb [B, T, K] bf16 with K = n_cols * head_dim
+ *   wkv [(hc + 1) * dim, K] bf16 (Linear weight layout [out, in])
+ *   kv  [B, T, (hc + 1) * dim] bf16 out: kv[m, n] = bf16(sum_k emb[m, k] * wkv[n, k]),
+ *       fp32 accumulation, rounded to nearest even.  Columns [s * dim, (s + 1) * dim) are
+ *       the key of stream s; the last dim columns are the shared value. */
+engram_status engram_kv_proj(const engram_layout* layout, const uint16_t* emb,
+                             const uint16_t* wkv, int64_t B, int64_t T, uint16_t* kv,
+                             engram_stream_t stream);
+
+/* S4 - S6: gate and residual add from a given kv (engram-second page, Engram.forward after
+ * the projection; zhuai.tech "Step 3: Inject memory at the correct layer boundary"):
+ *   x          [B, T, hc, dim] bf16
+ *   kv         [B, T, (hc + 1) * dim] bf16
+ *   q_weight, k_weight [hc, dim] fp32 (used only as their fp32 product)
+ *   token_mask [B, T] uint8, 0 = closed (the token passes through bit for bit), NULL = all open
+ *   out        [B, T, hc, dim] bf16; may be the same pointer as x (in place)
+ *   gate       [B, T, hc] fp32 out, may be NULL
+ * Per (token, stream s): rstd = rsqrt(mean(h^2) + eps) * rsqrt(mean(key_s^2) + eps),
+ * dot = sum(h * q * k * key_s) * rstd / sqrt(dim),
+ * g = sigmoid(copysign(sqrt(max(|dot|, clamp)), dot)), out = bf16(h + g * value). */
+engram_status engram_gate_apply(const engram_layout* layout, const uint16_t* x,
+                                const uint16_t* kv, const float* q_weight,
+                                const float* k_weight, const uint8_t* token_mask, int64_t B,
+                                int64_t T, uint16_t* out, float* gate, engram_stream_t stream);
+
+/* The whole Engram forward in one call (engram-second page, Engram.forward): S1 - S6 with
+ * the arguments above.  Key and value stay on chip; only small per-tile partial sums pass
+ * through `workspace` (engram_forward_workspace_bytes).  out may equal x.  Results equal
+ * engram_gate_apply(engram_kv_proj(engram_gather_dequant(...))) up to the summation order of
+ * the gate reductions. */
+engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
+                             const int64_t* hash_ids, const uint8_t* token_mask,
+                             const uint8_t* table, const float* scales, const uint16_t* wkv,
+                             const float* q_weight, const float* k_weight, int64_t B, int64_t T,
+                             uint16_t* out, void* workspace, size_t workspace_bytes,
+                             int32_t* err_count, engram_stream_t stream);
+
+/* Static description of a status code. */
+const char* engram_status_str(engram_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

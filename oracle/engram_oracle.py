@@ -121,7 +121,8 @@ def gather_dequant(hash_ids: np.ndarray, fetch: RowFetch, n_rows: int, head_dim:
 # ----------------------------------------------------------------------------------------
 
 
-def kv_proj(emb_bits: np.ndarray, wkv: np.ndarray, chunk: int = 4096) -> np.ndarray:
+def kv_proj(emb_bits: np.ndarray, wkv: np.ndarray, chunk: int = 4096,
+            with_exact: bool = False):
     """kv bf16 bits [M, N] = bf16(emb @ wkv^T).
 
     wkv is the Linear weight in [out, in] = [(hc + 1) * dim, C * head_dim] layout (the
@@ -129,19 +130,24 @@ def kv_proj(emb_bits: np.ndarray, wkv: np.ndarray, chunk: int = 4096) -> np.ndar
     ``wkv`` is given either as bf16 bit patterns (uint16) or as float values that are exactly
     bf16 numbers.  The products of two bf16 numbers are exact in double and 6,144-term sums
     stay far inside double precision, so the accumulation is effectively exact; the result
-    is rounded to fp32 and then to bf16.
+    is rounded to fp32 and then to bf16.  With ``with_exact`` the unrounded sums are returned
+    as well (for error bounds).
     """
     a = bf16_value(emb_bits)
     M = a.shape[0]
     N = wkv.shape[0]
     out = np.empty((M, N), dtype=np.uint16)
+    exact = np.empty((M, N), dtype=np.float64) if with_exact else None
     for lo in range(0, N, chunk):
         hi = min(N, lo + chunk)
         w = wkv[lo:hi]
         w = bf16_value(w) if w.dtype == np.uint16 else np.asarray(w, dtype=np.float64)
         with np.errstate(invalid="ignore", over="ignore"):
-            out[:, lo:hi] = bf16_bits_from_fp32(round_fp32(a @ w.T))
-    return out
+            acc = a @ w.T
+            out[:, lo:hi] = bf16_bits_from_fp32(round_fp32(acc))
+        if with_exact:
+            exact[:, lo:hi] = acc
+    return (out, exact) if with_exact else out
 
 
 # ----------------------------------------------------------------------------------------

@@ -440,3 +440,47 @@ class DeviceFill:
     def x(self, ptr, tok0, ntok, per_tok, key_x, key_outlier, thr, std, outlier_std, stream):
         self._chk(self.lib.synth_fill_x(ptr, tok0, ntok, per_tok, key_x, key_outlier, thr, std,
                                         outlier_std, stream), "fill x")
+
+
+def device_inputs(w: Workload, inst: int = 0, device: str = "cuda", with_table: bool = True) -> dict:
+    """Allocate and fill the inputs of one Engram call on the device (torch tensors).
+
+    Large tensors (table, scales, wkv, x) are written by the device fill from the same
+    definitions as the host generator; hash ids and the token mask are drawn on the host and
+    copied.  Returns x, hash_ids, token_mask, table, scales, wkv, q_weight, k_weight."""
+    import torch
+
+    fill = DeviceFill()
+    dev = torch.device(device)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    out = {}
+    x = torch.empty((w.B, w.T, w.hc, w.dim), dtype=torch.bfloat16, device=dev)
+    fill.x(x.data_ptr(), 0, w.M, w.hc * w.dim, w.key(S_X), w.key(S_OUTLIER),
+           w.outlier_threshold(), w.x_std, w.x_std * w.outlier_scale, stream)
+    out["x"] = x
+    out["hash_ids"] = torch.from_numpy(w.hash_ids(inst)).to(dev)
+    out["token_mask"] = torch.from_numpy(w.token_mask()).to(dev)
+    if with_table:
+        table = torch.empty((w.n_rows, w.head_dim), dtype=torch.uint8, device=dev)
+        fill.codes(table.data_ptr(), 0, w.n_rows, w.head_dim, w.key(S_CODES, inst), stream)
+        scales = torch.empty((w.n_rows, w.n_blocks), dtype=torch.float32, device=dev)
+        fill.scales(scales.data_ptr(), 0, w.n_rows, w.n_blocks, w.key(S_SCALES, inst),
+                    w.scale_lo, w.scale_hi, stream)
+        out["table"], out["scales"] = table, scales
+    wkv = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev)
+    fill.normal_bf16(wkv.data_ptr(), 0, w.N * w.K, w.key(S_WKV, inst), 0.0, w.wkv_std, stream)
+    out["wkv"] = wkv
+    q, k = w.qk(inst)
+    out["q_weight"] = torch.from_numpy(q).to(dev)
+    out["k_weight"] = torch.from_numpy(k).to(dev)
+    return out
+
+
+def host_fetch(w: Workload, inst: int = 0):
+    """Row provider for the oracle: regenerates table rows and their scales on the host."""
+
+    def fetch(rows):
+        rows = np.asarray(rows, dtype=np.int64)
+        return w.codes_rows(rows, inst), w.scales_rows(rows, inst)
+
+    return fetch

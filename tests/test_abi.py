@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports every declared entry point, and validates arguments on
+the host before touching a device (CPU only; no compute call reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+
+eg = pytest.importorskip("hashed_gram_engram_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
+                 "engram_forward_workspace_bytes", "engram_layout_check", "engram_param_counts",
+                 "engram_status_str"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(eg.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(eg.EXPORTED) == declared_functions()
+
+
+def good():
+    return eg.make_layout(4, 5120, 24, 256, 128, 384016682)
+
+
+def test_layout_checks():
+    assert eg.engram_layout_check(good()) == 0
+    assert eg.engram_layout_check(eg.make_layout(4, 256, 6, 64, 32, 6126)) == 0
+    bad = [dict(hc=3), dict(dim=5000), dict(head_dim=96), dict(scale_block=24),
+           dict(scale_block=512), dict(n_rows=0), dict(eps=float("nan")), dict(n_cols=0),
+           dict(reserved=1)]
+    for change in bad:
+        lay = good()
+        for k, v in change.items():
+            setattr(lay, k, v)
+        assert eg.engram_layout_check(lay) == -2, change
+
+
+def test_param_counts_on_host():
+    assert eg.engram_param_counts(good()) == (98308270592, 157286400, 40960)
+
+
+def test_entry_points_reject_bad_arguments_before_any_device_work():
+    lib = eg._lib
+    lay = good()
+    L = ctypes.byref(lay)
+    bad = eg.make_layout(4, 5120, 24, 256, 100, 10)
+    Lb = ctypes.byref(bad)
+    p = ctypes.c_void_p(16)
+    assert lib.engram_forward(Lb, p, p, None, p, p, p, p, p, 1, 1, p, p, 1 << 20, None, None) == -2
+    assert lib.engram_forward(L, None, p, None, p, p, p, p, p, 1, 1, p, p, 1 << 20, None, None) == -1
+    assert lib.engram_forward(L, p, p, None, p, p, p, p, p, -1, 1, p, p, 1 << 20, None, None) == -3
+    assert lib.engram_gather_dequant(L, p, p, None, 2, 3, p, None, None) == -1
+    assert lib.engram_kv_proj(L, p, None, 2, 3, p, None) == -1
+    assert lib.engram_gate_apply(L, p, p, p, None, None, 1, 1, p, None, None) == -1
+    # empty batches are a no-op
+    assert lib.engram_forward(L, None, None, None, None, None, None, None, None, 0, 7, None, None, 0,
+                              None, None) == 0
+    assert lib.engram_kv_proj(L, None, None, 5, 0, None, None) == 0
+    odd = ctypes.c_void_p(24)
+    assert lib.engram_kv_proj(L, odd, p, 1, 1, p, None) == -4
+    assert eg.engram_forward_workspace_bytes(bad, 1, 1) == 0
+
+
+def test_status_strings():
+    for st in range(-7, 1):
+        assert eg._lib.engram_status_str(st)

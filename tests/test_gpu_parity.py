@@ -1,0 +1,361 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
+
+Every GPU call goes through the C ABI (the ctypes binding).  Integer, byte and dequantisation
+results must be bit-exact; floating-point outputs are held to the tolerance stated for the
+forward: max |out - oracle| <= 2e-2 and mean <= 2e-3 against the unrounded oracle, except that
+tokens drawn with the x50 outlier scale get 2e-2 plus one bf16 ulp of the reference (bf16 output
+rounding alone exceeds 2e-2 there).  Tokens whose mask is false must come back bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+
+if torch.cuda.is_available():
+    import hashed_gram_engram_amd as eg  # noqa: E402
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def u16(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def layout(w):
+    return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
+
+
+_WKV = {}
+
+
+def host_wkv(w):
+    key = (w.name, w.seed, w.N, w.K)
+    if key not in _WKV:
+        _WKV.clear()
+        _WKV[key] = w.wkv_f32()
+    return _WKV[key]
+
+
+def oracle_for(w, sel):
+    sel = np.asarray(sel, dtype=np.int64)
+    ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
+    mask = w.token_mask().reshape(-1)[sel]
+    q, k = w.qk()
+    return oracle.forward(w.x_tokens(sel), ids, mask, synth.host_fetch(w), w.n_rows, w.head_dim,
+                          w.scale_block, host_wkv(w), q, k, eps=w.eps, clamp=w.clamp)
+
+
+def check_out(w, sel, got_bits, ref):
+    """Tolerance check of output streams for tokens `sel` (got_bits [len, hc, dim])."""
+    sel = np.asarray(sel)
+    got = oracle.bf16_value(got_bits)
+    err = np.abs(got - ref["out_f"])
+    mask = w.token_mask().reshape(-1)[sel].astype(bool)
+    outl = w.outlier_tokens()[sel]
+    x_bits = w.x_tokens(sel)
+    assert np.array_equal(got_bits[~mask], x_bits[~mask]), "closed tokens must pass through"
+    normal = ~outl
+    if normal.any():
+        assert err[normal].max() <= 2e-2, err[normal].max()
+        assert err[normal].mean() <= 2e-3, err[normal].mean()
+    if outl.any():
+        r = np.abs(ref["out_f"][outl])
+        ulp = np.exp2(np.floor(np.log2(np.maximum(r, 2.0 ** -126))) - 7)
+        assert np.all(err[outl] <= 2e-2 + ulp)
+    # against the oracle's own bf16 rounding nearly everything is exact or one ulp off (larger
+    # ulp counts only where h + g * v nearly cancels)
+    d = np.abs(got_bits.astype(np.int32) - ref["out_bits"].astype(np.int32))
+    assert (d > 1).mean() <= 1e-3, (d > 1).mean()
+    return err.max(), err.mean(), float((d > 0).mean())
+
+
+def forward(w, d, out=None, ws=None, err=None):
+    return eg.engram_forward(layout(w), d["x"], d["hash_ids"], d["token_mask"], d["table"],
+                             d["scales"], d["wkv"], d["q_weight"], d["k_weight"], out=out,
+                             workspace=ws, err_count=err)
+
+
+# ---------------------------------------------------------------------------- fixtures
+
+WORKLOADS = synth.workloads()
+TINY = WORKLOADS["tiny"]
+DECODE = WORKLOADS["decode_b64"]
+# decode layout, three sequences of 37 tokens: two token blocks and a ragged tail, skewed ids,
+# closed tokens and outlier streams
+RAGGED = synth.small_variant(DECODE, name="decode_dims_b3_t37", B=3, T=37, hash_dist="zipf",
+                             mask_false_frac=0.2, outlier_frac=0.05, seed=DECODE.seed + 100)
+
+
+@pytest.fixture(scope="module")
+def dev_tiny():
+    say("[gpu] inputs: tiny")
+    return synth.device_inputs(TINY)
+
+
+@pytest.fixture(scope="module")
+def dev_decode():
+    say("[gpu] inputs: decode_b64 (4.3 GB table)")
+    d = synth.device_inputs(DECODE)
+    torch.cuda.synchronize()
+    yield d
+    del d
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------- generator
+
+
+def test_device_fill_matches_host_generator(dev_tiny, dev_decode):
+    say("[gpu] device fill vs host generator")
+    w, d = TINY, dev_tiny
+    assert np.array_equal(u16(d["x"]).reshape(w.M, w.hc, w.dim), w.x_tokens(np.arange(w.M)))
+    assert np.array_equal(d["table"].cpu().numpy(), w.codes_rows(np.arange(w.n_rows)))
+    assert np.array_equal(d["scales"].cpu().numpy(), w.scales_rows(np.arange(w.n_rows)))
+    assert np.array_equal(u16(d["wkv"]), w.wkv_rows(0, w.N))
+    w, d = DECODE, dev_decode
+    rng = np.random.default_rng(0)
+    rows = np.concatenate([[0, w.n_rows - 1], rng.integers(0, w.n_rows, 300)])
+    assert np.array_equal(d["table"][torch.from_numpy(rows).cuda()].cpu().numpy(), w.codes_rows(rows))
+    assert np.array_equal(d["scales"][torch.from_numpy(rows).cuda()].cpu().numpy(), w.scales_rows(rows))
+    assert np.array_equal(u16(d["wkv"][:7]), w.wkv_rows(0, 7))
+    assert np.array_equal(u16(d["wkv"][-5:]), w.wkv_rows(w.N - 5, w.N))
+    toks = np.array([0, 17, 63])
+    assert np.array_equal(u16(d["x"]).reshape(w.M, w.hc, w.dim)[toks], w.x_tokens(toks))
+
+
+# ---------------------------------------------------------------------------- S1 + S2
+
+
+def _gather_case(w, d, sel_tokens=None):
+    emb = eg.engram_gather_dequant(layout(w), d["table"], d["scales"], d["hash_ids"])
+    torch.cuda.synchronize()
+    got = u16(emb).reshape(w.M, -1)
+    ids = w.hash_ids().reshape(w.M, w.n_cols)
+    sel = np.arange(w.M) if sel_tokens is None else sel_tokens
+    ref = oracle.gather_dequant(ids[sel], synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    assert np.array_equal(got[sel], ref)
+
+
+def test_gather_dequant_bit_exact_tiny(dev_tiny):
+    say("[gpu] gather tiny")
+    _gather_case(TINY, dev_tiny)
+
+
+def test_gather_dequant_bit_exact_decode(dev_decode):
+    say("[gpu] gather decode_b64")
+    _gather_case(DECODE, dev_decode)
+
+
+def test_gather_all_codes_special_scales_and_bad_ids():
+    say("[gpu] gather: all 256 codes, special scales, out-of-range ids")
+    hd, sb, n = 64, 32, 40
+    rng = np.random.default_rng(12)
+    table = np.tile(np.arange(256, dtype=np.uint8), n * hd // 256 + 1)[: n * hd].reshape(n, hd)
+    rng.shuffle(table.reshape(-1))
+    scales = rng.uniform(0.01, 0.1, (n, hd // sb)).astype(np.float32)
+    scales[0] = [1e-40, 2.0 ** -126]
+    scales[1] = [3e38, -1.5]
+    scales[2] = [np.inf, np.nan]
+    scales[3] = [0.0, -0.0]
+    C = 6
+    ids = rng.integers(0, n, (3, 5, C)).astype(np.int64)
+    ids.reshape(-1)[:n] = np.arange(n)  # every row at least once
+    ids[0, 0, 0] = -1
+    ids[1, 2, 3] = n
+    ids[2, 4, 5] = 1 << 40
+    lay = eg.make_layout(4, 256, C, hd, sb, n)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    emb = eg.engram_gather_dequant(lay, torch.from_numpy(table).cuda(), torch.from_numpy(scales).cuda(),
+                                   torch.from_numpy(ids).cuda(), err_count=err)
+    torch.cuda.synchronize()
+    ref = oracle.gather_dequant(ids.reshape(-1, C), oracle.array_fetch(table, scales), n, hd, sb)
+    assert np.array_equal(u16(emb).reshape(15, -1), ref)
+    bad = int(((ids < 0) | (ids >= n)).sum())
+    assert int(err.item()) == bad == 3
+
+
+# ---------------------------------------------------------------------------- S3
+
+
+def _kv_case(w, d, sel=None):
+    emb = eg.engram_gather_dequant(layout(w), d["table"], d["scales"], d["hash_ids"])
+    kv = eg.engram_kv_proj(layout(w), emb, d["wkv"])
+    torch.cuda.synchronize()
+    got = u16(kv).reshape(w.M, -1)
+    sel = np.arange(w.M) if sel is None else sel
+    ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
+    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    ref, exact = oracle.kv_proj(emb_ref, host_wkv(w), with_exact=True)
+    # fp32 accumulation (any order) then one bf16 rounding: |got - exact| <= ulp(exact) plus the
+    # classical sum-of-products bound K * 2^-24 * sum |a| |b|
+    abs_sum = np.abs(oracle.bf16_value(emb_ref)) @ np.abs(host_wkv(w)).astype(np.float64).T
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
+    err = np.abs(oracle.bf16_value(got[sel]) - exact)
+    bound = ulp + w.K * 2.0 ** -24 * abs_sum
+    worst = np.unravel_index(np.argmax(err / bound), err.shape)
+    say(f"    kv: worst err/bound {float((err / bound)[worst]):.3f} at {worst}: exact "
+        f"{exact[worst]:.6e} sum|ab| {abs_sum[worst]:.4e} err {err[worst]:.3e}; "
+        f"bf16 bits differ on {float((got[sel] != ref).mean()):.2e} of entries")
+    assert np.all(err <= bound)
+    assert (got[sel] != ref).mean() < 0.01
+    return emb, kv
+
+
+def test_kv_proj_tiny(dev_tiny):
+    say("[gpu] kv_proj tiny")
+    _kv_case(TINY, dev_tiny)
+
+
+def test_kv_proj_decode(dev_decode):
+    say("[gpu] kv_proj decode_b64")
+    _kv_case(DECODE, dev_decode)
+
+
+# ---------------------------------------------------------------------------- S4 - S6
+
+
+def _gate_case(w, d, in_place=False):
+    ids = w.hash_ids().reshape(w.M, w.n_cols)
+    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    kv_ref = oracle.kv_proj(emb_ref, host_wkv(w))
+    x_bits = w.x_tokens(np.arange(w.M))
+    q, k = w.qk()
+    mask = w.token_mask().reshape(-1)
+    ref = oracle.gate_apply(x_bits, kv_ref, q, k, mask, w.eps, w.clamp)
+    kv = torch.from_numpy(kv_ref.view(np.int16)).cuda().view(torch.bfloat16)
+    gate = torch.empty((w.M, w.hc), dtype=torch.float32, device="cuda")
+    x = d["x"].clone()
+    out = eg.engram_gate_apply(layout(w), x, kv, d["q_weight"], d["k_weight"], d["token_mask"],
+                               out=x if in_place else None, gate=gate)
+    torch.cuda.synchronize()
+    g = gate.cpu().numpy().astype(np.float64)
+    assert np.abs(g - ref["gate"]).max() <= 1e-4
+    got = u16(out).reshape(w.M, w.hc, w.dim)
+    d_ulp = np.abs(got.astype(np.int32) - ref["out_bits"].astype(np.int32))
+    assert (d_ulp > 1).mean() <= 1e-4, (d_ulp > 1).mean()
+    err = np.abs(oracle.bf16_value(got) - ref["out_f"])
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    assert np.array_equal(got[~mask.astype(bool)], x_bits[~mask.astype(bool)])
+
+
+def test_gate_apply_tiny(dev_tiny):
+    say("[gpu] gate_apply tiny")
+    _gate_case(TINY, dev_tiny)
+    _gate_case(TINY, dev_tiny, in_place=True)
+
+
+def test_gate_apply_decode(dev_decode):
+    say("[gpu] gate_apply decode_b64")
+    _gate_case(DECODE, dev_decode)
+
+
+# ---------------------------------------------------------------------------- whole forward
+
+
+def test_forward_tiny(dev_tiny):
+    say("[gpu] forward tiny")
+    w = TINY
+    out = forward(w, dev_tiny)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+
+
+def test_forward_decode(dev_decode):
+    say("[gpu] forward decode_b64")
+    w = DECODE
+    out = forward(w, dev_decode)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+
+
+def test_forward_ragged_multi_block():
+    say("[gpu] forward decode dims, B=3 T=37 (ragged, closed tokens, outliers)")
+    w = RAGGED
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_forward_equals_composition_in_place_and_deterministic(dev_decode):
+    say("[gpu] forward: composed path, in place, reruns")
+    w, d = DECODE, dev_decode
+    lay = layout(w)
+    ws = torch.zeros(eg.engram_forward_workspace_bytes(lay, w.B, w.T), dtype=torch.uint8, device="cuda")
+    a = forward(w, d, ws=ws)
+    b = forward(w, d, ws=ws)
+    x2 = d["x"].clone()
+    c = forward(w, d | {"x": x2}, out=x2, ws=ws)
+    emb = eg.engram_gather_dequant(lay, d["table"], d["scales"], d["hash_ids"])
+    kv = eg.engram_kv_proj(lay, emb, d["wkv"])
+    e = eg.engram_gate_apply(lay, d["x"], kv, d["q_weight"], d["k_weight"], d["token_mask"])
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)
+    # control words (256-byte header, then per-64-token-block counters and flags) are zero again
+    n_tb = (w.M + 63) // 64
+    control = (256 + n_tb * 32 + 255) // 256 * 256
+    assert int(ws[:control].count_nonzero().item()) == 0, "control words must be left zeroed"
+    diff = np.abs(u16(a).astype(np.int32) - u16(e).astype(np.int32))
+    assert (diff > 1).mean() <= 1e-4
+    assert np.abs(oracle.bf16_value(u16(a)) - oracle.bf16_value(u16(e))).max() <= 2e-2
+
+
+def test_forward_bad_ids_read_zero_rows():
+    say("[gpu] forward with out-of-range hash ids")
+    w = synth.small_variant(TINY, name="tiny_bad_ids", seed=TINY.seed + 7)
+    d = synth.device_inputs(w)
+    ids = w.hash_ids()
+    ids[0, 2, 1] = -5
+    ids[0, 7, 4] = w.n_rows
+    d["hash_ids"] = torch.from_numpy(ids).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = forward(w, d, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 2
+    q, k = w.qk()
+    ref = oracle.forward(w.x_tokens(np.arange(w.M)), ids.reshape(w.M, -1), w.token_mask().reshape(-1),
+                         synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block, host_wkv(w), q, k)
+    check_out(w, np.arange(w.M), u16(out).reshape(w.M, w.hc, w.dim), ref)
+
+
+@pytest.mark.parametrize("B,T", [(1, 1), (1, 65), (0, 5)])
+def test_forward_edge_token_counts(B, T):
+    say(f"[gpu] forward tiny dims B={B} T={T}")
+    w = synth.small_variant(TINY, name=f"tiny_{B}x{T}", B=B, T=T, masked_positions=())
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    if w.M == 0:
+        return
+    sel = np.arange(w.M)
+    check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel))
+
+
+@pytest.mark.slow
+def test_forward_prefill_sampled():
+    say("[gpu] forward prefill_t8192 (25.6 GB table), sampled tokens")
+    w = WORKLOADS["prefill_t8192"]
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    mask = w.token_mask().reshape(-1)
+    closed = np.nonzero(mask == 0)[0][:4]
+    sel = np.unique(np.concatenate([[0, 63, 64, w.M - 1], closed, rng.integers(0, w.M, 40)]))
+    got = u16(out).reshape(w.M, w.hc, w.dim)[sel]
+    say("   ", check_out(w, sel, got, oracle_for(w, sel)))
+    del d, out
+    torch.cuda.empty_cache()
