@@ -5,13 +5,22 @@
 // wkv matrix ([N, K], K contiguous).  A persistent grid of G workgroups (one per CU) gives
 // workgroup w the contiguous row blocks [w * nrb / G, (w + 1) * nrb / G), so every byte of wkv
 // is read exactly once per 64-token block and the load is balanced to within one row block.
-// Each of the four waves of a workgroup owns one 32-feature slice of every 128-feature chunk
-// of K (a split of K inside the workgroup), streams its weight fragments straight from HBM into
-// registers (no LDS, no reuse needed) with a ring of PF chunks in flight, and multiplies them
-// against the token tile held in LDS.  The token tile (64 tokens x 128 features, bf16) is
-// double buffered; in the fused kernel it is produced by gathering the fp8 rows of the hash
-// ids and dequantising them on the way into LDS.  At the end the four K-partials are summed in
-// a fixed order through LDS.
+// The four waves of a workgroup split K into four contiguous quarters; each wave multiplies its
+// quarter of the workgroup's rows against its quarter of the 64 token rows, and the four
+// K-partials are summed in a fixed order through LDS at the end.
+//
+// Two K loops feed the same reduction and epilogue:
+//  * wide (each K quarter a multiple of 128 features, head_dim a multiple of 128): weights are
+//    read 4 rows x 256 contiguous bytes per wave instruction -- HBM streams at close to its
+//    peak only with runs of this length -- and each 16-row x 128-feature unit is transposed
+//    through a small wave-private LDS tile into the MFMA fragment layout.  A whole chunk
+//    (all row blocks x 128 features) of loads stays in flight; the row-block count is a
+//    template constant so no load sits behind a branch.
+//  * narrow (any shape the library accepts): fragments are loaded in MFMA layout directly
+//    (16 rows x 64 bytes per instruction) with a ring of U steps in flight.
+// In the fused kernel the token operand is gathered: each lane loads the 8 fp8 codes and the
+// scale it needs straight from the table rows named by the hash ids (staged once per token
+// block in LDS) and dequantises them in registers, one chunk ahead of use.
 //
 // MFMA roles: the weight rows are the A operand (16 rows), the tokens the B operand (16 tokens),
 // so every lane ends up holding four consecutive output columns of one token.
@@ -31,9 +40,11 @@ namespace engram {
 
 namespace {
 
-constexpr int kTB = 64;        // tokens per token block
-constexpr int kKC = 128;       // features per K chunk (4 waves x 32)
-constexpr int kLdsRow = kKC + 8;  // padded LDS row (bf16 elements) against bank conflicts
+constexpr int kTB = 64;                          // tokens per token block
+constexpr int kRedBytes = 4 * 2 * 4 * 64 * 16;   // K-partial reduction buffer (two row blocks)
+constexpr int kTileRow = 272;                    // bytes per row of a transpose tile (256 + pad)
+constexpr int kTileBytes = 16 * kTileRow;        // one 16-row x 128-feature transpose tile
+constexpr int kTilesBytes = 4 * 2 * kTileBytes;  // two tiles per wave
 
 __device__ __forceinline__ int rb_begin(int w, int nrb, int G) { return int(int64_t(w) * nrb / G); }
 // workgroup that owns row block rb
@@ -41,338 +52,467 @@ __device__ __forceinline__ int owner_of_rb(int rb, int nrb, int G) {
   return int((int64_t(rb + 1) * G - 1) / nrb);
 }
 
-template <bool FUSED>
-struct TileLoader {
-  // two 16-feature groups per thread per chunk
-  u32x4 c[2];
-  u32x4 c2[2];
-  float s[2];
-  bool ok[2];
+// Eight fp8 codes (two dwords) times one fp32 scale -> eight bf16 (an MFMA operand).  NaN
+// payloads are not canonicalised here: a NaN operand makes the products NaN either way.
+__device__ __forceinline__ u32x4 dequant8(u32x2 c, float s) {
+  const u32x2 lo = dequant4_raw(c.x, s), hi = dequant4_raw(c.y, s);
+  return u32x4{lo.x, lo.y, hi.x, hi.y};
+}
 
-  __device__ __forceinline__ void load(const StreamArgs& a, int64_t m0, int chunk, int tid) {
-    const int grp = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = (tid >> 3) + 32 * i;
-      const int64_t m = m0 + tok;
-      const int f = chunk * kKC + 16 * grp;
-      ok[i] = false;
-      c[i] = u32x4{0u, 0u, 0u, 0u};
-      c2[i] = u32x4{0u, 0u, 0u, 0u};
-      s[i] = 0.0f;
-      if (m < a.M) {
-        if constexpr (FUSED) {
-          const int j = f / a.head_dim;
-          const int cc = f - j * a.head_dim;
-          const int64_t r = a.hash_ids[m * a.n_cols + j];
-          if (r >= 0 && r < a.n_rows) {
-            ok[i] = true;
-            c[i] = *reinterpret_cast<const u32x4*>(a.table + r * a.head_dim + cc);
-            s[i] = a.scales[r * (a.head_dim / a.scale_block) + cc / a.scale_block];
-          } else if (cc == 0 && blockIdx.x == 0 && a.err_count != nullptr) {
-            atomicAdd(a.err_count, 1);
-          }
-        } else {
-          const u32x4* src = reinterpret_cast<const u32x4*>(a.emb + m * a.K + f);
-          c[i] = src[0];
-          c2[i] = src[1];
-          ok[i] = true;
-        }
-      }
-    }
-  }
+__device__ __forceinline__ u32x4 masked(u32x4 v, uint32_t k) { return u32x4{v.x & k, v.y & k, v.z & k, v.w & k}; }
 
-  __device__ __forceinline__ void store(uint16_t* buf, int tid) {
-    const int grp = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int tok = (tid >> 3) + 32 * i;
-      u32x4 o0 = c[i], o1 = c2[i];
-      if constexpr (FUSED) {
-        if (ok[i]) {
-          dequant16(c[i], s[i], o0, o1);
-        } else {
-          o0 = u32x4{0u, 0u, 0u, 0u};
-          o1 = o0;
-        }
-      }
-      u32x4* dst = reinterpret_cast<u32x4*>(buf + tok * kLdsRow + 16 * grp);
-      dst[0] = o0;
-      dst[1] = o1;
-    }
-  }
+// Token fragment source of one lane for one 32-feature step: gathered codes + scale, or a row
+// slice of emb, and an all-ones / zero mask for rows that must read as zeros.
+struct TokFrag {
+  u32x2 code;
+  float scale;
+  u32x4 emb;
+  uint32_t keep;
 };
 
-template <int NRB>
-__device__ __forceinline__ void load_weights(u32x4 (&wb)[NRB], const StreamArgs& a, int rb0, int cnt,
-                                             int chunk, int lane, int wv) {
-  const size_t col = size_t(chunk) * kKC + 32 * wv + 8 * (lane >> 4);
+// Loads the token fragment of sub-block t for features [f, f + 8) of this lane (branch-free:
+// invalid ids read row 0 and out-of-range tokens read the last token, both masked at use).
+template <bool FUSED>
+__device__ __forceinline__ void load_tok(TokFrag& tf, const StreamArgs& a, const int64_t* s_ids, int64_t m0,
+                                         int t, int f, int lane) {
+  if constexpr (FUSED) {
+    const int j = f / a.head_dim;
+    const int cc = f - j * a.head_dim;
+    const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
+    const int64_t rr = r >= 0 ? r : 0;
+    tf.keep = r >= 0 ? 0xFFFFFFFFu : 0u;
+    tf.code = *reinterpret_cast<const u32x2*>(a.table + rr * a.head_dim + cc);
+    tf.scale = a.scales[rr * (a.head_dim / a.scale_block) + cc / a.scale_block];
+  } else {
+    const int64_t m = m0 + 16 * t + (lane & 15);
+    tf.keep = m < a.M ? 0xFFFFFFFFu : 0u;
+    const int64_t mm = m < a.M ? m : a.M - 1;
+    tf.emb = *reinterpret_cast<const u32x4*>(a.emb + mm * a.K + f);
+  }
+}
+
+template <bool FUSED>
+__device__ __forceinline__ u32x4 tok_operand(const TokFrag& tf) {
+  if constexpr (FUSED) return masked(dequant8(tf.code, tf.scale), tf.keep);
+  else return masked(tf.emb, tf.keep);
+}
+
+// ------------------------------------------------------------------------------ narrow K loop
+template <int NRB, int U, bool FUSED>
+struct NarrowSlot {
+  u32x4 w[NRB];
+  TokFrag tok[4];
+};
+
+template <int NRB, int U, bool FUSED>
+__device__ __forceinline__ void narrow_issue(NarrowSlot<NRB, U, FUSED>& sl, const StreamArgs& a, const int64_t* s_ids,
+                                             int64_t m0, int rb0, int cnt, int step, int lane, int wv) {
+  const int f = wv * (a.K >> 2) + 32 * step + 8 * (lane >> 4);  // first of this lane's 8 features
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    if (i < cnt) {
-      const size_t row = size_t(rb0 + i) * 16 + (lane & 15);
-      wb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.wkv + row * a.K + col));
+    const int ii = i < cnt ? i : cnt - 1;  // past the workgroup's count: re-read (cache hit)
+    const size_t row = size_t(rb0 + ii) * 16 + (lane & 15);
+    sl.w[i] = *reinterpret_cast<const u32x4*>(a.wkv + row * a.K + f);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t) load_tok<FUSED>(sl.tok[t], a, s_ids, m0, t, f, lane);
+}
+
+template <int NRB, int U, bool FUSED>
+__device__ __forceinline__ void narrow_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
+                                            int64_t m0, int rb0, int cnt, int lane, int wv) {
+  const int nstep = (a.K >> 2) / 32;  // 32-feature steps per wave; a multiple of U
+  NarrowSlot<NRB, U, FUSED> ring[U];
+#pragma unroll
+  for (int p = 0; p < U; ++p) {
+    narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rb0, cnt, p, lane, wv);
+    // pin the issue order: the compiler otherwise sinks ring loads into the next iteration
+    asm volatile("" ::: "memory");
+  }
+  for (int c0 = 0; c0 < nstep; c0 += U) {
+#pragma unroll
+    for (int p = 0; p < U; ++p) {
+      u32x4 bt[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bt[t] = tok_operand<FUSED>(ring[p].tok[t]);
+#pragma unroll
+      for (int i = 0; i < NRB; ++i)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(ring[p].w[i], bt[t], acc[i][t]);
+      const int nxt = c0 + p + U < nstep ? c0 + p + U : nstep - 1;
+      narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rb0, cnt, nxt, lane, wv);
+      asm volatile("" ::: "memory");
     }
   }
 }
 
-template <int NRB, int PF, bool FUSED>
-__global__ __launch_bounds__(256, 1) void k_stream(StreamArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ float s_red[4][kTB][3];
-  __shared__ int s_last[2];
+// ------------------------------------------------------------------------------ wide K loop
+// Chunk c of a wave covers features [q0 + 128 c, q0 + 128 c + 128) of its quarter q0.  Weight
+// unit (row block i, chunk c): instruction k in 0..3 loads rows 4k + lane/16 of the block, 16
+// bytes at feature 8 * (lane % 16) -- four rows of 256 contiguous bytes.  Through the tile each
+// lane then reads, for step s in 0..3, row lane % 16 at features 32 * (lane / 16) + 8 s: the
+// pairing of A and B rows along K is free, and this order gives every lane 32 contiguous token
+// features per chunk (two 16-byte code loads and one scale in the fused kernel).
+//
+// When `live` is false (the refill after the last chunk) the same instructions read the first
+// 256 bytes of rows 0..15 instead: a 4 KB cache-resident region, so no extra HBM traffic.
+__device__ __forceinline__ void wide_issue_w(u32x4 (&w)[4], const StreamArgs& a, int rb0, int i, int f_chunk,
+                                             bool live, int lane) {
+  const size_t rbase = live ? size_t(rb0 + i) * 16 : 0;
+  const size_t fbase = live ? size_t(f_chunk) : 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const size_t row = rbase + 4 * k + (lane >> 4);
+    w[k] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(a.wkv + row * a.K + fbase + 8 * (lane & 15)));
+  }
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+// Token operands of one chunk for one lane: sub-block t, features f_chunk + 32 * (lane / 16)
+// + [0, 32).  Gathered: 32 fp8 codes (two dwordx4) and one scale (scale_block is a multiple of
+// 32); dense: 32 bf16 (four dwordx4).
+template <bool FUSED>
+struct WideTok {
+  u32x4 v[4][FUSED ? 2 : 4];
+  float scale[4];
+  uint32_t keep[4];
+};
+
+template <bool FUSED>
+__device__ __forceinline__ void wide_issue_tok(WideTok<FUSED>& tk, const StreamArgs& a, const int64_t* s_ids,
+                                               int64_t m0, int f_chunk, int lane) {
+  const int f = f_chunk + 32 * (lane >> 4);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (FUSED) {
+      const int j = f / a.head_dim;
+      const int cc = f - j * a.head_dim;
+      const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
+      const int64_t rr = r >= 0 ? r : 0;
+      tk.keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.table + rr * a.head_dim + cc);
+      tk.v[t][0] = src[0];
+      tk.v[t][1] = src[1];
+      tk.scale[t] = a.scales[rr * (a.head_dim / a.scale_block) + cc / a.scale_block];
+    } else {
+      const int64_t m = m0 + 16 * t + (lane & 15);
+      tk.keep[t] = m < a.M ? 0xFFFFFFFFu : 0u;
+      const int64_t mm = m < a.M ? m : a.M - 1;
+      const u32x4* src = reinterpret_cast<const u32x4*>(a.emb + mm * a.K + f);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tk.v[t][q] = src[q];
+    }
+  }
+}
+
+// Operand of step s (features 8 s .. 8 s + 7 of the lane's 32) for sub-block t.
+template <bool FUSED>
+__device__ __forceinline__ u32x4 wide_operand(const WideTok<FUSED>& tk, int t, int s) {
+  if constexpr (FUSED) {
+    const u32x4 c = tk.v[t][s >> 1];
+    const u32x2 pair = (s & 1) ? u32x2{c.z, c.w} : u32x2{c.x, c.y};
+    return masked(dequant8(pair, tk.scale[t]), tk.keep[t]);
+  } else {
+    return masked(tk.v[t][s], tk.keep[t]);
+  }
+}
+
+template <int NRB, bool FUSED>
+__device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
+                                          char* tiles, int64_t m0, int rb0, int lane, int wv) {
+  const int q0 = wv * (a.K >> 2);
+  const int nch = (a.K >> 2) / 128;
+  u32x4 W[NRB][4];
+  WideTok<FUSED> tk;
+  // prologue in the loop's issue order (tokens, then row blocks): the wait counts at the loop
+  // head are the smaller of the prologue's and the loop's
+  wide_issue_tok<FUSED>(tk, a, s_ids, m0, q0, lane);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+    wide_issue_w(W[i], a, rb0, i, q0, true, lane);
+    asm volatile("" ::: "memory");
+  }
+  char* my_tiles = tiles + wv * 2 * kTileBytes;
+  for (int c = 0; c < nch; ++c) {
+    const bool live = c + 1 < nch;
+    const int fn = q0 + 128 * (live ? c + 1 : c);  // next chunk (tokens re-read the last one)
+    u32x4 bt[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) bt[s][t] = wide_operand<FUSED>(tk, t, s);
+    wide_issue_tok<FUSED>(tk, a, s_ids, m0, fn, lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      char* tile = my_tiles + (i & 1) * kTileBytes;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<u32x4*>(tile + (4 * k + (lane >> 4)) * kTileRow + 16 * (lane & 15)) = W[i][k];
+      wide_issue_w(W[i], a, rb0, i, fn, live, lane);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const u32x4 wf = *reinterpret_cast<const u32x4*>(tile + (lane & 15) * kTileRow + 16 * (4 * (lane >> 4) + s));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf, bt[s][t], acc[i][t]);
+      }
+      asm volatile("" ::: "memory");
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ per token block
+// Sums the four K-partials in wave order; afterwards wave wv holds token sub-block wv.
+template <int NRB>
+__device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4], f32x4* X, int cnt, int lane,
+                                         int wv) {
+#pragma unroll
+  for (int r0 = 0; r0 < NRB; r0 += 2) {
+    if (r0 < cnt) {
+      __syncthreads();
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+        if (r0 + ii < NRB && r0 + ii < cnt)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) X[((wv * 2 + ii) * 4 + t) * 64 + lane] = acc[r0 + ii][t];
+      __syncthreads();
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+        if (r0 + ii < NRB && r0 + ii < cnt) {
+          f32x4 s = X[((0 * 2 + ii) * 4 + wv) * 64 + lane];
+          s += X[((1 * 2 + ii) * 4 + wv) * 64 + lane];
+          s += X[((2 * 2 + ii) * 4 + wv) * 64 + lane];
+          s += X[((3 * 2 + ii) * 4 + wv) * 64 + lane];
+          red[r0 + ii] = s;
+        }
+    }
+  }
+}
+
+struct Shared {
+  float red[4][kTB][3];
+  int last[2];
+};
+
+template <int NRB, bool FUSED>
+__device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], Shared& sh, int64_t tb, int rb0,
+                                         int cnt, int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x, w = blockIdx.x;
   const int nrb = a.N >> 4;
-  const int rb0 = rb_begin(w, nrb, G);
-  const int cnt = rb_begin(w + 1, nrb, G) - rb0;
-  const int nchunk = a.K / kKC;
-  const int64_t n_tb = (a.M + kTB - 1) / kTB;
   const int R = a.dim >> 4;  // row blocks per stream segment
   const int seg_lo = rb0 / R;
   const int seg_hi = (rb0 + cnt - 1) / R;
+  const int64_t m0 = tb * kTB;
+  const int tok = 16 * wv + (lane & 15);
+  const int64_t m = m0 + tok;
+  const bool mvalid = m < a.M;
 
-  uint16_t* const lds_tiles = reinterpret_cast<uint16_t*>(smem);  // two token tiles
-
-  for (int64_t tb = 0; tb < n_tb; ++tb) {
-    const int64_t m0 = tb * kTB;
-    f32x4 acc[NRB][4];
+  if constexpr (!FUSED) {
+    if (mvalid) {
 #pragma unroll
-    for (int i = 0; i < NRB; ++i)
+      for (int i = 0; i < NRB; ++i)
+        if (i < cnt) {
+          const int n = (rb0 + i) * 16 + 4 * (lane >> 4);
+          *reinterpret_cast<u32x2*>(a.kv + m * a.N + n) =
+              u32x2{pack_bf16x2(red[i].x, red[i].y), pack_bf16x2(red[i].z, red[i].w)};
+        }
+    }
+    return;
+  } else {
+    // ---- key columns: per-token partial sums for up to two streams
+    float pa[2] = {0.f, 0.f}, pk[2] = {0.f, 0.f}, pd[2] = {0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    u32x4 wb[PF][NRB];
+    for (int i = 0; i < NRB; ++i) {
+      if (i < cnt) {
+        const int rb = rb0 + i;
+        const int s = rb / R;
+        if (s < 4) {
+          const int d = (rb - s * R) * 16 + 4 * (lane >> 4);
+          const float key[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
+                                bf16_round(red[i].w)};
+          u32x2 xw = {0u, 0u};
+          if (mvalid) xw = *reinterpret_cast<const u32x2*>(a.x + (m * 4 + s) * a.dim + d);
+          const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
+          const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
+          const float h[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
+          const float wq[4] = {q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
+          float sa = 0.f, sk = 0.f, sd = 0.f;
 #pragma unroll
-    for (int p = 0; p < PF; ++p)
-      if (p < nchunk) load_weights<NRB>(wb[p], a, rb0, cnt, p, lane, wv);
-
-    TileLoader<FUSED> tl;
-    tl.load(a, m0, 0, tid);
-    tl.store(lds_tiles, tid);
-    __syncthreads();
-
-    for (int c0 = 0; c0 < nchunk; c0 += PF) {
+          for (int r = 0; r < 4; ++r) {
+            sa += h[r] * h[r];
+            sk += key[r] * key[r];
+            sd += (h[r] * wq[r]) * key[r];
+          }
+          if (s == seg_lo) {
+            pa[0] += sa; pk[0] += sk; pd[0] += sd;
+          } else {
+            pa[1] += sa; pk[1] += sk; pd[1] += sd;
+          }
+        }
+      }
+    }
+    if (seg_lo < 4) {
 #pragma unroll
-      for (int p = 0; p < PF; ++p) {
-        const int c = c0 + p;
-        if (c < nchunk) {
-          if (c + 1 < nchunk) tl.load(a, m0, c + 1, tid);
-          const uint16_t* buf = lds_tiles + (c & 1) * (kTB * kLdsRow);
-          u32x4 bt[4];
+      for (int sl = 0; sl < 2; ++sl) {
+        pa[sl] += __shfl_xor(pa[sl], 16, 64); pa[sl] += __shfl_xor(pa[sl], 32, 64);
+        pk[sl] += __shfl_xor(pk[sl], 16, 64); pk[sl] += __shfl_xor(pk[sl], 32, 64);
+        pd[sl] += __shfl_xor(pd[sl], 16, 64); pd[sl] += __shfl_xor(pd[sl], 32, 64);
+      }
+      if (lane < 16) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            bt[t] = *reinterpret_cast<const u32x4*>(buf + (16 * t + (lane & 15)) * kLdsRow + 32 * wv +
-                                                    8 * (lane >> 4));
+        for (int sl = 0; sl < 2; ++sl) {
+          if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
+            float* P = a.partials + ((size_t(tb) * G + w) * 2 + sl) * (kTB * 3) + tok * 3;
+            P[0] = pa[sl];
+            P[1] = pk[sl];
+            P[2] = pd[sl];
+          }
+        }
+      }
+      fence_release_agent();
+      __syncthreads();
+      if (tid == 0) {
 #pragma unroll
-          for (int i = 0; i < NRB; ++i)
-            if (i < cnt)
+        for (int sl = 0; sl < 2; ++sl) {
+          const int s = seg_lo + sl;
+          sh.last[sl] = 0;
+          if (s <= seg_hi && s < 4) {
+            const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
+            const uint32_t old = atomic_add_relaxed(&a.counters[tb * 4 + s], 1u);
+            sh.last[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
+          }
+        }
+      }
+      __syncthreads();
 #pragma unroll
-              for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wb[p][i], bt[t], acc[i][t]);
-          if (c + PF < nchunk) load_weights<NRB>(wb[p], a, rb0, cnt, c + PF, lane, wv);
-          if (c + 1 < nchunk) tl.store(lds_tiles + ((c + 1) & 1) * (kTB * kLdsRow), tid);
+      for (int sl = 0; sl < 2; ++sl) {
+        if (sh.last[sl]) {
+          fence_acquire_agent();
+          const int s = seg_lo + sl;
+          const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
+          const int nW = wl - wf + 1;
+          const int t = tid & 63, q = tid >> 6;
+          const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
+          float ra = 0.f, rk = 0.f, rd = 0.f;
+          for (int w2 = wb0; w2 < wb1; ++w2) {
+            const int sl2 = s - rb_begin(w2, nrb, G) / R;
+            const float* P = a.partials + ((size_t(tb) * G + w2) * 2 + sl2) * (kTB * 3) + t * 3;
+            ra += P[0];
+            rk += P[1];
+            rd += P[2];
+          }
+          sh.red[q][t][0] = ra;
+          sh.red[q][t][1] = rk;
+          sh.red[q][t][2] = rd;
           __syncthreads();
+          if (q == 0) {
+            const float A = ((sh.red[0][t][0] + sh.red[1][t][0]) + sh.red[2][t][0]) + sh.red[3][t][0];
+            const float Kq = ((sh.red[0][t][1] + sh.red[1][t][1]) + sh.red[2][t][1]) + sh.red[3][t][1];
+            const float D = ((sh.red[0][t][2] + sh.red[1][t][2]) + sh.red[2][t][2]) + sh.red[3][t][2];
+            const float fd = float(a.dim);
+            const float rstd = __frsqrt_rn(A / fd + a.eps) * __frsqrt_rn(Kq / fd + a.eps);
+            const float dot = D * rstd * a.inv_sqrt_dim;
+            const float z = copysignf(sqrtf(fmaxf(fabsf(dot), a.clamp)), dot);
+            const float g = 1.0f / (1.0f + expf(-z));
+            const int64_t mt = m0 + t;
+            const bool open = mt < a.M && (a.token_mask == nullptr || a.token_mask[mt] != 0);
+            a.gates[(size_t(tb) * 4 + s) * kTB + t] = open ? g : 0.0f;
+            fence_release_agent();
+          }
+          __syncthreads();
+          if (tid == 0)
+            __hip_atomic_store(&a.flags[tb * 4 + s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
     }
 
-    // ---- sum the four K-partials in wave order; wave wv keeps token sub-block wv
-    f32x4 red[NRB];
-    f32x4* X = reinterpret_cast<f32x4*>(smem);  // [4 waves][2][4 sub-blocks][64 lanes]
+    // ---- value columns: wait for the four gates, then out = h + g * value on every stream
+    if (seg_hi == 4) {
+      if (tid == 0) {
+        bool ok = true;
 #pragma unroll
-    for (int r0 = 0; r0 < NRB; r0 += 2) {
-      if (r0 < cnt) {
-        __syncthreads();
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-          if (r0 + ii < NRB && r0 + ii < cnt)
-#pragma unroll
-            for (int t = 0; t < 4; ++t) X[((wv * 2 + ii) * 4 + t) * 64 + lane] = acc[r0 + ii][t];
-        __syncthreads();
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii)
-          if (r0 + ii < NRB && r0 + ii < cnt) {
-            f32x4 s = X[((0 * 2 + ii) * 4 + wv) * 64 + lane];
-            s += X[((1 * 2 + ii) * 4 + wv) * 64 + lane];
-            s += X[((2 * 2 + ii) * 4 + wv) * 64 + lane];
-            s += X[((3 * 2 + ii) * 4 + wv) * 64 + lane];
-            red[r0 + ii] = s;
-          }
+        for (int s = 0; s < 4; ++s) ok = ok && wait_at_least(&a.flags[tb * 4 + s], 1u, a.spin_budget);
+        if (!ok) atomic_add_relaxed(&a.ws_hdr[0], 1u);
       }
-    }
-
-    const int tok = 16 * wv + (lane & 15);
-    const int64_t m = m0 + tok;
-    const bool mvalid = m < a.M;
-
-    if constexpr (!FUSED) {
+      __syncthreads();
+      fence_acquire_agent();
+      float g[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) g[s] = a.gates[(size_t(tb) * 4 + s) * kTB + tok];
+      const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
       if (mvalid) {
 #pragma unroll
-        for (int i = 0; i < NRB; ++i)
-          if (i < cnt) {
-            const int n = (rb0 + i) * 16 + 4 * (lane >> 4);
-            *reinterpret_cast<u32x2*>(a.kv + m * a.N + n) =
-                u32x2{pack_bf16x2(red[i].x, red[i].y), pack_bf16x2(red[i].z, red[i].w)};
-          }
-      }
-      __syncthreads();
-    } else {
-      // ---- key columns: per-token partial sums for up to two streams
-      float pa[2] = {0.f, 0.f}, pk[2] = {0.f, 0.f}, pd[2] = {0.f, 0.f};
+        for (int i = 0; i < NRB; ++i) {
+          if (i < cnt && (rb0 + i) / R == 4) {
+            const int d = (rb0 + i - 4 * R) * 16 + 4 * (lane >> 4);
+            const float v[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
+                                bf16_round(red[i].w)};
 #pragma unroll
-      for (int i = 0; i < NRB; ++i) {
-        if (i < cnt) {
-          const int rb = rb0 + i;
-          const int s = rb / R;
-          if (s < 4) {
-            const int d = (rb - s * R) * 16 + 4 * (lane >> 4);
-            const float key[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
-                                  bf16_round(red[i].w)};
-            u32x2 xw = {0u, 0u};
-            if (mvalid) xw = *reinterpret_cast<const u32x2*>(a.x + (m * 4 + s) * a.dim + d);
-            const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
-            const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
-            const float h[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
-            const float wq[4] = {q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
-            float sa = 0.f, sk = 0.f, sd = 0.f;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              sa += h[r] * h[r];
-              sk += key[r] * key[r];
-              sd += (h[r] * wq[r]) * key[r];
-            }
-            const int slot = s - seg_lo;
-            if (slot == 0) {
-              pa[0] += sa; pk[0] += sk; pd[0] += sd;
-            } else {
-              pa[1] += sa; pk[1] += sk; pd[1] += sd;
-            }
-          }
-        }
-      }
-      if (seg_lo < 4) {
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          pa[sl] += __shfl_xor(pa[sl], 16, 64); pa[sl] += __shfl_xor(pa[sl], 32, 64);
-          pk[sl] += __shfl_xor(pk[sl], 16, 64); pk[sl] += __shfl_xor(pk[sl], 32, 64);
-          pd[sl] += __shfl_xor(pd[sl], 16, 64); pd[sl] += __shfl_xor(pd[sl], 32, 64);
-        }
-        if (lane < 16) {
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl) {
-            if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
-              float* P = a.partials + ((size_t(tb) * G + w) * 2 + sl) * (kTB * 3) + tok * 3;
-              P[0] = pa[sl];
-              P[1] = pk[sl];
-              P[2] = pd[sl];
-            }
-          }
-        }
-        fence_release_agent();
-        __syncthreads();
-        if (tid == 0) {
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl) {
-            const int s = seg_lo + sl;
-            s_last[sl] = 0;
-            if (s <= seg_hi && s < 4) {
-              const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
-              const uint32_t old = atomic_add_relaxed(&a.counters[tb * 4 + s], 1u);
-              s_last[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
-            }
-          }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          if (s_last[sl]) {
-            fence_acquire_agent();
-            const int s = seg_lo + sl;
-            const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
-            const int nW = wl - wf + 1;
-            const int t = tid & 63, q = tid >> 6;
-            const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
-            float ra = 0.f, rk = 0.f, rd = 0.f;
-            for (int w2 = wb0; w2 < wb1; ++w2) {
-              const int sl2 = s - rb_begin(w2, nrb, G) / R;
-              const float* P = a.partials + ((size_t(tb) * G + w2) * 2 + sl2) * (kTB * 3) + t * 3;
-              ra += P[0];
-              rk += P[1];
-              rd += P[2];
-            }
-            s_red[q][t][0] = ra;
-            s_red[q][t][1] = rk;
-            s_red[q][t][2] = rd;
-            __syncthreads();
-            if (q == 0) {
-              const float A = ((s_red[0][t][0] + s_red[1][t][0]) + s_red[2][t][0]) + s_red[3][t][0];
-              const float Kq = ((s_red[0][t][1] + s_red[1][t][1]) + s_red[2][t][1]) + s_red[3][t][1];
-              const float D = ((s_red[0][t][2] + s_red[1][t][2]) + s_red[2][t][2]) + s_red[3][t][2];
-              const float fd = float(a.dim);
-              const float rstd = __frsqrt_rn(A / fd + a.eps) * __frsqrt_rn(Kq / fd + a.eps);
-              const float dot = D * rstd * a.inv_sqrt_dim;
-              const float z = copysignf(sqrtf(fmaxf(fabsf(dot), a.clamp)), dot);
-              float g = 1.0f / (1.0f + expf(-z));
-              const int64_t mt = m0 + t;
-              const bool open = mt < a.M && (a.token_mask == nullptr || a.token_mask[mt] != 0);
-              a.gates[(size_t(tb) * 4 + s) * kTB + t] = open ? g : 0.0f;
-              fence_release_agent();
-            }
-            __syncthreads();
-            if (tid == 0)
-              __hip_atomic_store(&a.flags[tb * 4 + s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-      }
-
-      // ---- value columns: wait for the four gates, then out = h + g * value on every stream
-      if (seg_hi == 4) {
-        if (tid == 0) {
-          bool ok = true;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) ok = ok && wait_at_least(&a.flags[tb * 4 + s], 1u, a.spin_budget);
-          if (!ok) atomic_add_relaxed(&a.ws_hdr[0], 1u);
-        }
-        __syncthreads();
-        fence_acquire_agent();
-        float g[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) g[s] = a.gates[(size_t(tb) * 4 + s) * kTB + tok];
-        const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
-        if (mvalid) {
-#pragma unroll
-          for (int i = 0; i < NRB; ++i) {
-            if (i < cnt && (rb0 + i) / R == 4) {
-              const int d = (rb0 + i - 4 * R) * 16 + 4 * (lane >> 4);
-              const float v[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
-                                  bf16_round(red[i].w)};
-#pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                const size_t off = size_t(m * 4 + s) * a.dim + d;
-                const u32x2 xw = *reinterpret_cast<const u32x2*>(a.x + off);
-                u32x2 o = xw;
-                if (open) {
-                  o.x = pack_bf16x2(bf16_lo(xw.x) + g[s] * v[0], bf16_hi(xw.x) + g[s] * v[1]);
-                  o.y = pack_bf16x2(bf16_lo(xw.y) + g[s] * v[2], bf16_hi(xw.y) + g[s] * v[3]);
-                }
-                if (open || a.out != a.x) *reinterpret_cast<u32x2*>(a.out + off) = o;
+            for (int s = 0; s < 4; ++s) {
+              const size_t off = size_t(m * 4 + s) * a.dim + d;
+              const u32x2 xw = *reinterpret_cast<const u32x2*>(a.x + off);
+              u32x2 o = xw;
+              if (open) {
+                o.x = pack_bf16x2(bf16_lo(xw.x) + g[s] * v[0], bf16_hi(xw.x) + g[s] * v[1]);
+                o.y = pack_bf16x2(bf16_lo(xw.y) + g[s] * v[2], bf16_hi(xw.y) + g[s] * v[3]);
               }
+              if (open || a.out != a.x) *reinterpret_cast<u32x2*>(a.out + off) = o;
             }
           }
         }
       }
-      __syncthreads();
     }
   }
+}
 
+// One 64-token block: stage the hash ids, run the K loop, reduce, finish.
+template <int NRB, bool WIDE, int U, bool FUSED>
+__device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int rb0,
+                                            int cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t m0 = tb * kTB;
+  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + kTilesBytes);
+  if constexpr (FUSED) {
+    // hash ids of the token block, checked once: -1 marks a row that reads as zeros
+    for (int i = tid; i < kTB * a.n_cols; i += 256) {
+      const int64_t m = m0 + i / a.n_cols;
+      int64_t r = -1;
+      if (m < a.M) {
+        r = a.hash_ids[m0 * a.n_cols + i];
+        if (r < 0 || r >= a.n_rows) {
+          if (blockIdx.x == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+          r = -1;
+        }
+      }
+      s_ids[i] = r;
+    }
+    __syncthreads();
+  }
+  f32x4 acc[NRB][4];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (WIDE) wide_loop<NRB, FUSED>(acc, a, s_ids, smem, m0, rb0, lane, wv);
+  else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rb0, cnt, lane, wv);
+  f32x4 red[NRB];
+  reduce_k<NRB>(red, acc, reinterpret_cast<f32x4*>(smem), cnt, lane, wv);
+  epilogue<NRB, FUSED>(a, red, sh, tb, rb0, cnt, tid);
+  __syncthreads();
+}
+
+template <bool FUSED>
+__device__ __forceinline__ void finish_call(const StreamArgs& a, Shared& sh, int64_t n_tb) {
   if constexpr (FUSED) {
     // last workgroup out leaves the counters and flags zeroed for the next call
+    const int tid = threadIdx.x;
     fence_release_agent();
     __syncthreads();
-    if (tid == 0) s_last[0] = (atomic_add_relaxed(&a.ws_hdr[1], 1u) == uint32_t(G - 1)) ? 1 : 0;
+    if (tid == 0) sh.last[0] = (atomic_add_relaxed(&a.ws_hdr[1], 1u) == gridDim.x - 1u) ? 1 : 0;
     __syncthreads();
-    if (s_last[0]) {
+    if (sh.last[0]) {
       fence_acquire_agent();
       for (int64_t i = tid; i < n_tb * 4; i += 256) {
         store_relaxed(&a.counters[i], 0u);
@@ -383,24 +523,83 @@ __global__ __launch_bounds__(256, 1) void k_stream(StreamArgs a) {
   }
 }
 
-constexpr size_t kDynLds = size_t(2) * kTB * kLdsRow * 2;  // two bf16 token tiles (also holds
-                                                          // the 32 KB reduction buffer)
-static_assert(size_t(4) * 2 * 4 * 64 * 16 <= kDynLds, "reduction buffer must fit");
+// Narrow kernel: NRB is the maximum row-block count per workgroup.
+template <int NRB, int U, bool FUSED>
+__global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ Shared sh;
+  const int G = gridDim.x, w = blockIdx.x, nrb = a.N >> 4;
+  const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
+  const int64_t n_tb = (a.M + kTB - 1) / kTB;
+  for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, rb0, cnt);
+  finish_call<FUSED>(a, sh, n_tb);
+}
+
+// Wide kernel: every workgroup has NLO or NLO + 1 row blocks, each compiled exactly.
+template <int NLO, bool FUSED>
+__global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ Shared sh;
+  const int G = gridDim.x, w = blockIdx.x, nrb = a.N >> 4;
+  const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
+  const int64_t n_tb = (a.M + kTB - 1) / kTB;
+  for (int64_t tb = 0; tb < n_tb; ++tb) {
+    if (cnt == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, rb0, cnt);
+    else token_block<NLO + 1, true, 1, FUSED>(a, smem, sh, tb, rb0, cnt);
+  }
+  finish_call<FUSED>(a, sh, n_tb);
+}
+
+template <bool FUSED, int NRB>
+void* pick_narrow(int nstep) {
+  if (nstep % 3 == 0) return reinterpret_cast<void*>(&k_stream_narrow<NRB, 3, FUSED>);
+  if (nstep % 2 == 0) return reinterpret_cast<void*>(&k_stream_narrow<NRB, 2, FUSED>);
+  return reinterpret_cast<void*>(&k_stream_narrow<NRB, 1, FUSED>);
+}
 
 template <bool FUSED>
-hipError_t launch_stream_impl(const StreamArgs& a, int G, int per_wg, hipStream_t stream, bool coop) {
+void* pick_wide(int nlo) {
+  switch (nlo) {
+    case 1: return reinterpret_cast<void*>(&k_stream_wide<1, FUSED>);
+    case 2: return reinterpret_cast<void*>(&k_stream_wide<2, FUSED>);
+    case 3: return reinterpret_cast<void*>(&k_stream_wide<3, FUSED>);
+    case 4: return reinterpret_cast<void*>(&k_stream_wide<4, FUSED>);
+    case 5: return reinterpret_cast<void*>(&k_stream_wide<5, FUSED>);
+    case 6: return reinterpret_cast<void*>(&k_stream_wide<6, FUSED>);
+    default: return nullptr;
+  }
+}
+
+bool use_wide(const StreamArgs& a, int G, bool fused) {
+  const int nrb = a.N / 16;
+  // a 128-feature chunk stays in one column and a lane's 32 features share one scale
+  const bool hd_ok = !fused || (a.head_dim % 128 == 0 && a.scale_block % 32 == 0);
+  return (a.K / 4) % 128 == 0 && hd_ok && nrb / G >= 1 && nrb / G <= 6;
+}
+
+template <bool FUSED>
+hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream, bool coop) {
+  const int nrb = a.N / 16;
   void* fn = nullptr;
-  if (per_wg <= 1) fn = reinterpret_cast<void*>(&k_stream<1, 3, FUSED>);
-  else if (per_wg <= 2) fn = reinterpret_cast<void*>(&k_stream<2, 3, FUSED>);
-  else if (per_wg <= 4) fn = reinterpret_cast<void*>(&k_stream<4, 3, FUSED>);
-  else if (per_wg <= 8) fn = reinterpret_cast<void*>(&k_stream<8, 2, FUSED>);
-  else return hipErrorInvalidValue;
+  if (use_wide(a, G, FUSED)) {
+    fn = pick_wide<FUSED>(nrb / G);
+  } else {
+    const int per_wg = (nrb + G - 1) / G;
+    const int nstep = (a.K / 4) / 32;
+    if (per_wg <= 1) fn = pick_narrow<FUSED, 1>(nstep);
+    else if (per_wg <= 2) fn = pick_narrow<FUSED, 2>(nstep);
+    else if (per_wg <= 4) fn = pick_narrow<FUSED, 4>(nstep);
+    else if (per_wg <= 8) fn = pick_narrow<FUSED, 8>(nstep);
+  }
+  if (fn == nullptr) return hipErrorInvalidValue;
   StreamArgs arg = a;
   void* params[] = {&arg};
-  if (coop)
-    return hipLaunchCooperativeKernel(fn, dim3(G), dim3(256), params, unsigned(kDynLds), stream);
-  return hipLaunchKernel(fn, dim3(G), dim3(256), params, kDynLds, stream);
+  const size_t lds = size_t(kTilesBytes) + (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
+  if (coop) return hipLaunchCooperativeKernel(fn, dim3(G), dim3(256), params, unsigned(lds), stream);
+  return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
 }
+
+static_assert(kRedBytes <= kTilesBytes, "the reduction buffer reuses the transpose tiles");
 
 }  // namespace
 
@@ -424,14 +623,11 @@ size_t stream_workspace_bytes(int64_t M, int N, int grid) {
 }
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
-  const int G = stream_grid(a.N, num_cus);
-  const int nrb = a.N / 16;
-  return launch_stream_impl<false>(a, G, (nrb + G - 1) / G, stream, false);
+  return launch_stream_impl<false>(a, stream_grid(a.N, num_cus), stream, false);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
   const int G = stream_grid(a.N, num_cus);
-  const int nrb = a.N / 16;
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   char* ws = static_cast<char*>(workspace);
   a.ws_hdr = reinterpret_cast<uint32_t*>(ws);
@@ -442,7 +638,7 @@ hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hip
   a.gates = reinterpret_cast<float*>(ws + off);
   off += size_t(n_tb) * 4 * kTB * 4;
   a.partials = reinterpret_cast<float*>(ws + off);
-  return launch_stream_impl<true>(a, G, (nrb + G - 1) / G, stream, true);
+  return launch_stream_impl<true>(a, G, stream, true);
 }
 
 }  // namespace engram
