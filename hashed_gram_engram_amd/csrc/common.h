@@ -92,9 +92,6 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // ------------------------------------------------------------------ cross-workgroup signalling
 
-__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
 __device__ __forceinline__ uint32_t atomic_add_relaxed(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -104,6 +101,22 @@ __device__ __forceinline__ uint32_t load_relaxed(const uint32_t* p) {
 __device__ __forceinline__ void store_relaxed(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Device-coherent relaxed accesses (agent scope).  Each one reaches the device coherence point
+// instead of a possibly stale per-XCD L2 copy, so small blocks of data handed from one
+// workgroup to another need no cache-wide writeback or invalidate (which agent-scope fences
+// perform and which cost tens of microseconds per kernel).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every memory operation this wave has issued is complete (stores acknowledged by
+// their destination).  Followed by a workgroup barrier, it orders all coherent stores of the
+// workgroup before any access that one thread issues after the barrier.
+__device__ __forceinline__ void drain_memory_ops() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory"); }
 
 // Spin (with sleeps) until *p >= target or the spin budget is spent; returns false on time-out.
 // Every wait in these kernels is bounded so that a grid always drains.

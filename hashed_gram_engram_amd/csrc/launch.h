@@ -70,7 +70,7 @@ hipError_t launch_gate_apply(const GateArgs& a, hipStream_t stream);
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream);
 
 // Whole forward, weight-streaming schedule.  Needs a zero-filled workspace of
-// stream_workspace_bytes(); all workgroups must be co-resident (cooperative launch).
+// stream_workspace_bytes() whose control words are zero (the kernel leaves them zero).
 size_t stream_workspace_bytes(int64_t M, int N, int grid);
 int stream_grid(int N, int num_cus);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);

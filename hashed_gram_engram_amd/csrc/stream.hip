@@ -31,8 +31,13 @@
 // the partials of all contributing workgroups in workgroup order (deterministic), evaluates
 // the gate of the 64 tokens and raises a flag.  Workgroups holding value columns wait for the
 // four flags, then write out = bf16(h + g * value) for their features on all four streams.
-// Only value workgroups ever wait and they wait on work that never waits, so the grid cannot
-// deadlock once all workgroups are resident (cooperative launch); every wait is bounded.
+// Value columns belong to the highest workgroup ids and only value workgroups wait, on key
+// work of lower ids that never waits.  Workgroups are dispatched in id order and the grid is at
+// most one workgroup per CU, so every key workgroup is running or done before a value
+// workgroup can wait on it; each wait is bounded as well, and a time-out is recorded in the
+// workspace header instead of hanging.  Partial sums, gates and flags pass between workgroups
+// through device-coherent atomic loads and stores ordered by store completion and barriers;
+// control words are reset by their last user, so a call leaves them zero.
 #include "common.h"
 #include "launch.h"
 
@@ -295,11 +300,21 @@ struct Shared {
   int last[2];
 };
 
+// Cross-workgroup control words: one counter per (token block, stream) on its own 256-byte
+// line (contended atomics on one line serialise), one flag per (token block, stream, value
+// workgroup) with a single writer and a single reader.
+__device__ __forceinline__ uint32_t* counter_of(const StreamArgs& a, int64_t tb, int s) {
+  return a.counters + (size_t(tb) * 4 + s) * 64;
+}
+__device__ __forceinline__ uint32_t* flag_of(const StreamArgs& a, int64_t tb, int s, int w) {
+  return a.flags + (size_t(tb) * 4 + s) * gridDim.x + w;
+}
+
 template <int NRB, bool FUSED>
-__device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], Shared& sh, int64_t tb, int rb0,
-                                         int cnt, int tid) {
+__device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], Shared& sh, int64_t tb, int w,
+                                         int rb0, int cnt, int tid) {
   const int lane = tid & 63, wv = tid >> 6;
-  const int G = gridDim.x, w = blockIdx.x;
+  const int G = gridDim.x;
   const int nrb = a.N >> 4;
   const int R = a.dim >> 4;  // row blocks per stream segment
   const int seg_lo = rb0 / R;
@@ -365,13 +380,13 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
         for (int sl = 0; sl < 2; ++sl) {
           if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
             float* P = a.partials + ((size_t(tb) * G + w) * 2 + sl) * (kTB * 3) + tok * 3;
-            P[0] = pa[sl];
-            P[1] = pk[sl];
-            P[2] = pd[sl];
+            store_coherent(P + 0, pa[sl]);
+            store_coherent(P + 1, pk[sl]);
+            store_coherent(P + 2, pd[sl]);
           }
         }
       }
-      fence_release_agent();
+      drain_memory_ops();
       __syncthreads();
       if (tid == 0) {
 #pragma unroll
@@ -380,7 +395,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           sh.last[sl] = 0;
           if (s <= seg_hi && s < 4) {
             const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
-            const uint32_t old = atomic_add_relaxed(&a.counters[tb * 4 + s], 1u);
+            const uint32_t old = atomic_add_relaxed(counter_of(a, tb, s), 1u);
             sh.last[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
           }
         }
@@ -389,7 +404,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         if (sh.last[sl]) {
-          fence_acquire_agent();
+          // every contributor has posted: sum the partials in workgroup order
           const int s = seg_lo + sl;
           const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
           const int nW = wl - wf + 1;
@@ -399,9 +414,9 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           for (int w2 = wb0; w2 < wb1; ++w2) {
             const int sl2 = s - rb_begin(w2, nrb, G) / R;
             const float* P = a.partials + ((size_t(tb) * G + w2) * 2 + sl2) * (kTB * 3) + t * 3;
-            ra += P[0];
-            rk += P[1];
-            rd += P[2];
+            ra += load_coherent(P + 0);
+            rk += load_coherent(P + 1);
+            rd += load_coherent(P + 2);
           }
           sh.red[q][t][0] = ra;
           sh.red[q][t][1] = rk;
@@ -418,12 +433,14 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             const float g = 1.0f / (1.0f + expf(-z));
             const int64_t mt = m0 + t;
             const bool open = mt < a.M && (a.token_mask == nullptr || a.token_mask[mt] != 0);
-            a.gates[(size_t(tb) * 4 + s) * kTB + t] = open ? g : 0.0f;
-            fence_release_agent();
+            store_coherent(a.gates + (size_t(tb) * 4 + s) * kTB + t, open ? g : 0.0f);
           }
+          drain_memory_ops();
           __syncthreads();
-          if (tid == 0)
-            __hip_atomic_store(&a.flags[tb * 4 + s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          // this call is done with the counter; raise one flag per value workgroup
+          if (tid == 0) store_relaxed(counter_of(a, tb, s), 0u);
+          const int v0 = owner_of_rb(4 * R, nrb, G);
+          for (int v = v0 + tid; v < G; v += 256) store_relaxed(flag_of(a, tb, s, v), 1u);
         }
       }
     }
@@ -433,14 +450,15 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       if (tid == 0) {
         bool ok = true;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) ok = ok && wait_at_least(&a.flags[tb * 4 + s], 1u, a.spin_budget);
+        for (int s = 0; s < 4; ++s) ok = ok && wait_at_least(flag_of(a, tb, s, w), 1u, a.spin_budget);
         if (!ok) atomic_add_relaxed(&a.ws_hdr[0], 1u);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) store_relaxed(flag_of(a, tb, s, w), 0u);  // sole reader resets
       }
       __syncthreads();
-      fence_acquire_agent();
       float g[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) g[s] = a.gates[(size_t(tb) * 4 + s) * kTB + tok];
+      for (int s = 0; s < 4; ++s) g[s] = load_coherent(a.gates + (size_t(tb) * 4 + s) * kTB + tok);
       const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
       if (mvalid) {
 #pragma unroll
@@ -469,7 +487,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 
 // One 64-token block: stage the hash ids, run the K loop, reduce, finish.
 template <int NRB, bool WIDE, int U, bool FUSED>
-__device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int rb0,
+__device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w, int rb0,
                                             int cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t m0 = tb * kTB;
@@ -482,7 +500,7 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
       if (m < a.M) {
         r = a.hash_ids[m0 * a.n_cols + i];
         if (r < 0 || r >= a.n_rows) {
-          if (blockIdx.x == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+          if (w == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
           r = -1;
         }
       }
@@ -499,28 +517,8 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rb0, cnt, lane, wv);
   f32x4 red[NRB];
   reduce_k<NRB>(red, acc, reinterpret_cast<f32x4*>(smem), cnt, lane, wv);
-  epilogue<NRB, FUSED>(a, red, sh, tb, rb0, cnt, tid);
+  epilogue<NRB, FUSED>(a, red, sh, tb, w, rb0, cnt, tid);
   __syncthreads();
-}
-
-template <bool FUSED>
-__device__ __forceinline__ void finish_call(const StreamArgs& a, Shared& sh, int64_t n_tb) {
-  if constexpr (FUSED) {
-    // last workgroup out leaves the counters and flags zeroed for the next call
-    const int tid = threadIdx.x;
-    fence_release_agent();
-    __syncthreads();
-    if (tid == 0) sh.last[0] = (atomic_add_relaxed(&a.ws_hdr[1], 1u) == gridDim.x - 1u) ? 1 : 0;
-    __syncthreads();
-    if (sh.last[0]) {
-      fence_acquire_agent();
-      for (int64_t i = tid; i < n_tb * 4; i += 256) {
-        store_relaxed(&a.counters[i], 0u);
-        store_relaxed(&a.flags[i], 0u);
-      }
-      if (tid == 0) store_relaxed(&a.ws_hdr[1], 0u);
-    }
-  }
 }
 
 // Narrow kernel: NRB is the maximum row-block count per workgroup.
@@ -531,8 +529,7 @@ __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
   const int G = gridDim.x, w = blockIdx.x, nrb = a.N >> 4;
   const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
-  for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, rb0, cnt);
-  finish_call<FUSED>(a, sh, n_tb);
+  for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, w, rb0, cnt);
 }
 
 // Wide kernel: every workgroup has NLO or NLO + 1 row blocks, each compiled exactly.
@@ -544,10 +541,9 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   for (int64_t tb = 0; tb < n_tb; ++tb) {
-    if (cnt == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, rb0, cnt);
-    else token_block<NLO + 1, true, 1, FUSED>(a, smem, sh, tb, rb0, cnt);
+    if (cnt == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rb0, cnt);
+    else token_block<NLO + 1, true, 1, FUSED>(a, smem, sh, tb, w, rb0, cnt);
   }
-  finish_call<FUSED>(a, sh, n_tb);
 }
 
 template <bool FUSED, int NRB>
@@ -578,7 +574,7 @@ bool use_wide(const StreamArgs& a, int G, bool fused) {
 }
 
 template <bool FUSED>
-hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream, bool coop) {
+hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   const int nrb = a.N / 16;
   void* fn = nullptr;
   if (use_wide(a, G, FUSED)) {
@@ -595,7 +591,6 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream, bo
   StreamArgs arg = a;
   void* params[] = {&arg};
   const size_t lds = size_t(kTilesBytes) + (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
-  if (coop) return hipLaunchCooperativeKernel(fn, dim3(G), dim3(256), params, unsigned(lds), stream);
   return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
 }
 
@@ -611,19 +606,22 @@ int stream_grid(int N, int num_cus) {
   return G;
 }
 
+// Workspace: [256 B header][counters: n_tb * 4 lines of 256 B][flags: n_tb * 4 * grid words]
+// [gates: n_tb * 4 * 64 floats][partials: n_tb * grid * 2 * 64 * 3 floats].
+size_t stream_control_bytes(int64_t M, int grid) {
+  const int64_t n_tb = (M + kTB - 1) / kTB;
+  size_t b = 256 + size_t(n_tb) * 4 * 256 + size_t(n_tb) * 4 * grid * 4;
+  return (b + 255) & ~size_t(255);
+}
+
 size_t stream_workspace_bytes(int64_t M, int N, int grid) {
   const int64_t n_tb = (M + kTB - 1) / kTB;
-  size_t b = 256;                              // header
-  b += size_t(n_tb) * 4 * 4 * 2;               // counters + flags
-  b = (b + 255) & ~size_t(255);
-  b += size_t(n_tb) * 4 * kTB * 4;             // gates
-  b += size_t(n_tb) * grid * 2 * kTB * 3 * 4;  // partials
   (void)N;
-  return b;
+  return stream_control_bytes(M, grid) + size_t(n_tb) * 4 * kTB * 4 + size_t(n_tb) * grid * 2 * kTB * 3 * 4;
 }
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
-  return launch_stream_impl<false>(a, stream_grid(a.N, num_cus), stream, false);
+  return launch_stream_impl<false>(a, stream_grid(a.N, num_cus), stream);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
@@ -632,13 +630,11 @@ hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hip
   char* ws = static_cast<char*>(workspace);
   a.ws_hdr = reinterpret_cast<uint32_t*>(ws);
   a.counters = reinterpret_cast<uint32_t*>(ws + 256);
-  a.flags = a.counters + n_tb * 4;
-  size_t off = 256 + size_t(n_tb) * 4 * 4 * 2;
-  off = (off + 255) & ~size_t(255);
+  a.flags = reinterpret_cast<uint32_t*>(ws + 256 + size_t(n_tb) * 4 * 256);
+  const size_t off = stream_control_bytes(a.M, G);
   a.gates = reinterpret_cast<float*>(ws + off);
-  off += size_t(n_tb) * 4 * kTB * 4;
-  a.partials = reinterpret_cast<float*>(ws + off);
-  return launch_stream_impl<true>(a, G, stream, true);
+  a.partials = reinterpret_cast<float*>(ws + off + size_t(n_tb) * 4 * kTB * 4);
+  return launch_stream_impl<true>(a, G, stream);
 }
 
 }  // namespace engram
