@@ -157,8 +157,8 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
 
 
 class Workspace:
-    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves it
-    zero-filled after every call)."""
+    """Zero-filled device workspace for engram_forward with one layout, grown on demand (the
+    library leaves its control words zero after every call)."""
 
     def __init__(self, device=None):
         self.device = device
@@ -167,8 +167,15 @@ class Workspace:
     def get(self, layout: EngramLayout, B: int, T: int) -> torch.Tensor:
         need = max(256, engram_forward_workspace_bytes(layout, B, T))
         if self.buf is None or self.buf.numel() < need:
+            old = self.buf
             self.buf = torch.zeros(need, dtype=torch.uint8, device=self.device or "cuda")
+            if old is not None:  # keep the time-out counter across growth
+                self.buf[:4].copy_(old[:4])
         return self.buf
+
+
+def _layout_key(layout: EngramLayout):
+    return (layout.hc, layout.dim, layout.n_cols, layout.head_dim, layout.scale_block)
 
 
 _default_ws: dict = {}
@@ -194,7 +201,8 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
         out = torch.empty_like(x)
     if workspace is None:
         dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
-        workspace = _default_ws.setdefault(dev, Workspace(x.device)).get(layout, B, T)
+        key = (dev,) + _layout_key(layout)
+        workspace = _default_ws.setdefault(key, Workspace(x.device)).get(layout, B, T)
     _check("engram_forward", _lib.engram_forward(
         ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
         _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),

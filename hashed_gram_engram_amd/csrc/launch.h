@@ -55,11 +55,8 @@ struct StreamArgs {
   int64_t n_rows;
   float eps, clamp, inv_sqrt_dim;
   // workspace views
-  uint32_t* ws_hdr;    // [0] wait time-outs, [1] exit counter
-  uint32_t* counters;  // [n_tb][4]
-  uint32_t* flags;     // [n_tb][4]
-  float* gates;        // [n_tb][4][64]
-  float* partials;     // [n_tb][grid][2][64][3]
+  uint32_t* ws_hdr;    // workspace start: [0] wait time-outs, then per-token-block blocks
+  size_t tb_stride;    // bytes per token-block block
   uint32_t spin_budget;
 };
 

@@ -29,15 +29,16 @@
 // and h * q * k * key over their features; each workgroup posts one partial per (token,
 // stream) and bumps a per-stream counter.  The workgroup that arrives last for a stream sums
 // the partials of all contributing workgroups in workgroup order (deterministic), evaluates
-// the gate of the 64 tokens and raises a flag.  Workgroups holding value columns wait for the
-// four flags, then write out = bf16(h + g * value) for their features on all four streams.
+// the gate of the 64 tokens and writes it into a slot of every value workgroup.  Workgroups
+// holding value columns wait for their four slots, then write out = bf16(h + g * value) for
+// their features on all four streams.
 // Value columns belong to the highest workgroup ids and only value workgroups wait, on key
 // work of lower ids that never waits.  Workgroups are dispatched in id order and the grid is at
 // most one workgroup per CU, so every key workgroup is running or done before a value
 // workgroup can wait on it; each wait is bounded as well, and a time-out is recorded in the
-// workspace header instead of hanging.  Partial sums, gates and flags pass between workgroups
-// through device-coherent atomic loads and stores ordered by store completion and barriers;
-// control words are reset by their last user, so a call leaves them zero.
+// workspace header instead of hanging.  Partial sums and gates pass between workgroups through
+// device-coherent atomic loads and stores ordered by store completion and barriers; counters
+// and gate slots are reset by their last user, so a call leaves them zero.
 #include "common.h"
 #include "launch.h"
 
@@ -301,13 +302,24 @@ struct Shared {
 };
 
 // Cross-workgroup control words: one counter per (token block, stream) on its own 256-byte
-// line (contended atomics on one line serialise), one flag per (token block, stream, value
-// workgroup) with a single writer and a single reader.
-__device__ __forceinline__ uint32_t* counter_of(const StreamArgs& a, int64_t tb, int s) {
-  return a.counters + (size_t(tb) * 4 + s) * 64;
+// line (contended atomics on one line serialise).
+// The workspace holds one block per token block at a fixed stride (so, for one layout, every
+// control word sits at the same offset whatever the token count):
+//   [4 counters, 256 B apart][gate slots: grid x 4 x 64 words][partials: grid x 2 x 64 x 3]
+__device__ __forceinline__ uint32_t* tb_block(const StreamArgs& a, int64_t tb) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.ws_hdr) + 256 + size_t(tb) * a.tb_stride);
 }
-__device__ __forceinline__ uint32_t* flag_of(const StreamArgs& a, int64_t tb, int s, int w) {
-  return a.flags + (size_t(tb) * 4 + s) * gridDim.x + w;
+__device__ __forceinline__ uint32_t* counter_of(const StreamArgs& a, int64_t tb, int s) {
+  return tb_block(a, tb) + s * 64;
+}
+__device__ __forceinline__ float* partial_of(const StreamArgs& a, int64_t tb, int w, int sl) {
+  return reinterpret_cast<float*>(tb_block(a, tb) + 256 + size_t(gridDim.x) * 4 * kTB) +
+         (size_t(w) * 2 + sl) * (kTB * 3);
+}
+// Gate slot of value workgroup w for stream s: 64 words, written once by the stream's last
+// arriver (value bits with the sign bit set), read and cleared by w alone.
+__device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, int w, int s) {
+  return tb_block(a, tb) + 256 + (size_t(w) * 4 + s) * kTB;
 }
 
 template <int NRB, bool FUSED>
@@ -379,7 +391,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
           if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
-            float* P = a.partials + ((size_t(tb) * G + w) * 2 + sl) * (kTB * 3) + tok * 3;
+            float* P = partial_of(a, tb, w, sl) + tok * 3;
             store_coherent(P + 0, pa[sl]);
             store_coherent(P + 1, pk[sl]);
             store_coherent(P + 2, pd[sl]);
@@ -404,19 +416,35 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl) {
         if (sh.last[sl]) {
+          __syncthreads();  // sh.red may still be read for the other stream
           // every contributor has posted: sum the partials in workgroup order
           const int s = seg_lo + sl;
           const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
           const int nW = wl - wf + 1;
           const int t = tid & 63, q = tid >> 6;
           const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
+          // all loads of a group of 16 contributors are issued before any is used (one
+          // memory round trip per group, not one per contributor); sums stay in order
           float ra = 0.f, rk = 0.f, rd = 0.f;
-          for (int w2 = wb0; w2 < wb1; ++w2) {
-            const int sl2 = s - rb_begin(w2, nrb, G) / R;
-            const float* P = a.partials + ((size_t(tb) * G + w2) * 2 + sl2) * (kTB * 3) + t * 3;
-            ra += load_coherent(P + 0);
-            rk += load_coherent(P + 1);
-            rd += load_coherent(P + 2);
+          for (int base = wb0; base < wb1; base += 16) {
+            float v[16][3];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              const int w2 = base + k < wb1 ? base + k : wb0;
+              const int sl2 = s - rb_begin(w2, nrb, G) / R;
+              const float* P = partial_of(a, tb, w2, sl2) + t * 3;
+              v[k][0] = load_coherent(P + 0);
+              v[k][1] = load_coherent(P + 1);
+              v[k][2] = load_coherent(P + 2);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              if (base + k < wb1) {
+                ra += v[k][0];
+                rk += v[k][1];
+                rd += v[k][2];
+              }
+            }
           }
           sh.red[q][t][0] = ra;
           sh.red[q][t][1] = rk;
@@ -433,32 +461,54 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             const float g = 1.0f / (1.0f + expf(-z));
             const int64_t mt = m0 + t;
             const bool open = mt < a.M && (a.token_mask == nullptr || a.token_mask[mt] != 0);
-            store_coherent(a.gates + (size_t(tb) * 4 + s) * kTB + t, open ? g : 0.0f);
+            sh.red[0][t][0] = open ? g : 0.0f;
           }
-          drain_memory_ops();
           __syncthreads();
-          // this call is done with the counter; raise one flag per value workgroup
+          // this call is done with the counter; hand the 64 gates to every value workgroup in
+          // its own slot, sign bit set as the ready mark (gates are >= 0)
           if (tid == 0) store_relaxed(counter_of(a, tb, s), 0u);
           const int v0 = owner_of_rb(4 * R, nrb, G);
-          for (int v = v0 + tid; v < G; v += 256) store_relaxed(flag_of(a, tb, s, v), 1u);
+          for (int i = tid; i < (G - v0) * kTB; i += 256) {
+            const int v = v0 + i / kTB, tt = i % kTB;
+            store_relaxed(gate_slot(a, tb, v, s) + tt, __float_as_uint(sh.red[0][tt][0]) | 0x80000000u);
+          }
         }
       }
     }
 
     // ---- value columns: wait for the four gates, then out = h + g * value on every stream
     if (seg_hi == 4) {
-      if (tid == 0) {
-        bool ok = true;
+      // the streams of this workgroup's features are read before waiting
+      u32x2 xs[NRB][4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) ok = ok && wait_at_least(flag_of(a, tb, s, w), 1u, a.spin_budget);
-        if (!ok) atomic_add_relaxed(&a.ws_hdr[0], 1u);
+      for (int i = 0; i < NRB; ++i) {
+        if (i < cnt && (rb0 + i) / R == 4 && mvalid) {
+          const int d = (rb0 + i - 4 * R) * 16 + 4 * (lane >> 4);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) store_relaxed(flag_of(a, tb, s, w), 0u);  // sole reader resets
+          for (int s = 0; s < 4; ++s) xs[i][s] = *reinterpret_cast<const u32x2*>(a.x + size_t(m * 4 + s) * a.dim + d);
+        }
+      }
+      __syncthreads();  // sh.red may still be read by a last-arriver hand-off above
+      {
+        // thread (s, t) waits for gate t of stream s in this workgroup's slot, then clears it
+        const int s = tid >> 6, t = tid & 63;
+        uint32_t* slot = gate_slot(a, tb, w, s) + t;
+        uint32_t bits = 0u;
+        uint32_t it = 0;
+        while ((bits = load_relaxed(slot)) == 0u) {
+          __builtin_amdgcn_s_sleep(2);
+          if (++it > a.spin_budget) {
+            atomic_add_relaxed(&a.ws_hdr[0], 1u);
+            break;
+          }
+        }
+        store_relaxed(slot, 0u);
+        sh.red[s][t][0] = __uint_as_float(bits & 0x7FFFFFFFu);
       }
       __syncthreads();
       float g[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) g[s] = load_coherent(a.gates + (size_t(tb) * 4 + s) * kTB + tok);
+      for (int s = 0; s < 4; ++s) g[s] = sh.red[s][tok][0];
       const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
       if (mvalid) {
 #pragma unroll
@@ -470,7 +520,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const size_t off = size_t(m * 4 + s) * a.dim + d;
-              const u32x2 xw = *reinterpret_cast<const u32x2*>(a.x + off);
+              const u32x2 xw = xs[i][s];
               u32x2 o = xw;
               if (open) {
                 o.x = pack_bf16x2(bf16_lo(xw.x) + g[s] * v[0], bf16_hi(xw.x) + g[s] * v[1]);
@@ -606,18 +656,16 @@ int stream_grid(int N, int num_cus) {
   return G;
 }
 
-// Workspace: [256 B header][counters: n_tb * 4 lines of 256 B][flags: n_tb * 4 * grid words]
-// [gates: n_tb * 4 * 64 floats][partials: n_tb * grid * 2 * 64 * 3 floats].
-size_t stream_control_bytes(int64_t M, int grid) {
-  const int64_t n_tb = (M + kTB - 1) / kTB;
-  size_t b = 256 + size_t(n_tb) * 4 * 256 + size_t(n_tb) * 4 * grid * 4;
-  return (b + 255) & ~size_t(255);
+// Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
+// block at a fixed stride that depends only on the grid.
+size_t stream_tb_stride(int grid) {
+  return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 3 * 4;
 }
 
 size_t stream_workspace_bytes(int64_t M, int N, int grid) {
   const int64_t n_tb = (M + kTB - 1) / kTB;
   (void)N;
-  return stream_control_bytes(M, grid) + size_t(n_tb) * 4 * kTB * 4 + size_t(n_tb) * grid * 2 * kTB * 3 * 4;
+  return 256 + size_t(n_tb) * stream_tb_stride(grid);
 }
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
@@ -626,14 +674,8 @@ hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t s
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
   const int G = stream_grid(a.N, num_cus);
-  const int64_t n_tb = (a.M + kTB - 1) / kTB;
-  char* ws = static_cast<char*>(workspace);
-  a.ws_hdr = reinterpret_cast<uint32_t*>(ws);
-  a.counters = reinterpret_cast<uint32_t*>(ws + 256);
-  a.flags = reinterpret_cast<uint32_t*>(ws + 256 + size_t(n_tb) * 4 * 256);
-  const size_t off = stream_control_bytes(a.M, G);
-  a.gates = reinterpret_cast<float*>(ws + off);
-  a.partials = reinterpret_cast<float*>(ws + off + size_t(n_tb) * 4 * kTB * 4);
+  a.ws_hdr = static_cast<uint32_t*>(workspace);
+  a.tb_stride = stream_tb_stride(G);
   return launch_stream_impl<true>(a, G, stream);
 }
 
