@@ -34,6 +34,26 @@ def algorithmic_flops(w) -> int:
     return 2 * w.M * w.N * w.K
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed PMC summary of this kernel and workload, or None
+    when there is none or the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"k_stream_wide_fused_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith(("#", "|", " ")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = os.path.join(ROOT, "hashed_gram_engram_amd", "csrc")
+    now = " ".join(hashlib.sha256(open(os.path.join(src, f), "rb").read()).hexdigest()
+                   for f in ("stream.hip", "common.h"))
+    if fields.get("kernel_sources_sha256") != now or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
 def cpu_baseline(w, n_tokens: int):
     """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload."""
     import oracle
@@ -67,6 +87,8 @@ def main():
     ap.add_argument("--workload", default="decode_b64")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the Engram forward is data parallel over tokens and "
@@ -75,6 +97,15 @@ def main():
 
     import hashed_gram_engram_amd as eg
     import synth
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20)
+        src = torch.ones(n // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     w = synth.get(args.workload)
     torch.cuda.set_device(0)
@@ -111,11 +142,12 @@ def main():
     if mode == "hbm":
         ach = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name)}
     else:
         ach = algorithmic_flops(w) / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(w.name)}
     roof["kernel"] = "engram_forward (k_stream fused)"
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
