@@ -34,11 +34,22 @@ def algorithmic_flops(w) -> int:
     return 2 * w.M * w.N * w.K
 
 
-def measured_traffic(workload: str):
+TILED_MIN_TOKENS = 256  # the library's switch from weight streaming to 256 x 256 tiles
+
+
+def kernel_of(w):
+    """(profile name, sources) of the kernel that engram_forward runs for this workload."""
+    if w.M >= TILED_MIN_TOKENS:
+        return "k_tiled_fused", ("tiled.hip", "common.h")
+    return "k_stream_wide_fused", ("stream.hip", "common.h")
+
+
+def measured_traffic(w):
     """HBM bytes per launch from the committed PMC summary of this kernel and workload, or None
     when there is none or the kernel sources changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"k_stream_wide_fused_{workload}.md")
+    kname, sources = kernel_of(w)
+    path = os.path.join(ROOT, "profiles", f"{kname}_{w.name}.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -48,7 +59,7 @@ def measured_traffic(workload: str):
             fields[k.strip()] = v.strip()
     src = os.path.join(ROOT, "hashed_gram_engram_amd", "csrc")
     now = " ".join(hashlib.sha256(open(os.path.join(src, f), "rb").read()).hexdigest()
-                   for f in ("stream.hip", "common.h"))
+                   for f in sources)
     if fields.get("kernel_sources_sha256") != now or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -142,13 +153,13 @@ def main():
     if mode == "hbm":
         ach = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name)}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w)}
     else:
         ach = algorithmic_flops(w) / (ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(w.name)}
-    roof["kernel"] = "engram_forward (k_stream fused)"
+                "traffic": measured_traffic(w)}
+    roof["kernel"] = kernel_of(w)[0]
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
     roof["ms_per_launch"] = round(ms, 5)

@@ -157,8 +157,8 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
 
 
 class Workspace:
-    """Zero-filled device workspace for engram_forward with one layout, grown on demand (the
-    library leaves its control words zero after every call)."""
+    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves it
+    all zero after every call, except the time-out counter in word 0)."""
 
     def __init__(self, device=None):
         self.device = device
@@ -174,11 +174,7 @@ class Workspace:
         return self.buf
 
 
-def _layout_key(layout: EngramLayout):
-    return (layout.hc, layout.dim, layout.n_cols, layout.head_dim, layout.scale_block)
-
-
-_default_ws: dict = {}
+_default_ws: dict = {}  # one per device
 
 
 def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
@@ -201,8 +197,7 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
         out = torch.empty_like(x)
     if workspace is None:
         dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
-        key = (dev,) + _layout_key(layout)
-        workspace = _default_ws.setdefault(key, Workspace(x.device)).get(layout, B, T)
+        workspace = _default_ws.setdefault(dev, Workspace(x.device)).get(layout, B, T)
     _check("engram_forward", _lib.engram_forward(
         ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
         _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),

@@ -13,6 +13,10 @@ namespace {
 
 constexpr uint32_t kSpinBudget = 1u << 22;  // ~1 s of sleeping polls before a wait gives up
 
+// From this many tokens on, the tiled schedule (256 x 256 MFMA tiles, each weight panel read
+// once per 256 tokens) replaces weight streaming (all of wkv read once per 64 tokens).
+constexpr int64_t kTiledMinTokens = 256;
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct DeviceInfo {
@@ -46,6 +50,16 @@ engram_status check_tokens(int64_t B, int64_t T, int64_t* M) {
 
 int64_t K_of(const engram_layout* l) { return int64_t(l->n_cols) * l->head_dim; }
 int64_t N_of(const engram_layout* l) { return int64_t(l->hc + 1) * l->dim; }
+
+bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
+  return M >= kTiledMinTokens &&
+         tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, l->head_dim, l->scale_block, fused);
+}
+
+size_t forward_workspace(const engram_layout* l, int64_t M, int cus) {
+  if (use_tiled(l, M, true)) return tiled_workspace_bytes(M, l->dim);
+  return stream_workspace_bytes(M, int(N_of(l)), stream_grid(int(N_of(l)), cus));
+}
 
 }  // namespace
 
@@ -96,8 +110,7 @@ size_t engram_forward_workspace_bytes(const engram_layout* l, int64_t B, int64_t
   if (check_tokens(B, T, &M) != ENGRAM_OK) return 0;
   DeviceInfo di;
   int cus = (device_info(&di) == ENGRAM_OK) ? di.cus : 256;
-  const int G = stream_grid(int(N_of(l)), cus);
-  return stream_workspace_bytes(M, int(N_of(l)), G);
+  return forward_workspace(l, M, cus);
 }
 
 engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table, const float* scales,
@@ -130,6 +143,19 @@ engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const 
   if (!aligned16(emb) || !aligned16(wkv) || !aligned16(kv)) return ENGRAM_E_ALIGN;
   DeviceInfo di;
   if ((st = device_info(&di)) != ENGRAM_OK) return st;
+  if (use_tiled(l, M, false)) {
+    TiledArgs a;
+    memset(&a, 0, sizeof(a));
+    a.wkv = wkv;
+    a.M = M;
+    a.K = int(K_of(l));
+    a.N = int(N_of(l));
+    a.dim = l->dim;
+    a.emb = emb;
+    a.kv = kv;
+    return launch_kv_proj_tiled(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ENGRAM_OK
+                                                                                         : ENGRAM_E_HIP;
+  }
   StreamArgs a;
   memset(&a, 0, sizeof(a));
   a.wkv = wkv;
@@ -181,9 +207,38 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   DeviceInfo di;
   if ((st = device_info(&di)) != ENGRAM_OK) return st;
   const int N = int(N_of(l));
-  const int G = stream_grid(N, di.cus);
-  const size_t need = stream_workspace_bytes(M, N, G);
+  const size_t need = forward_workspace(l, M, di.cus);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  if (use_tiled(l, M, true)) {
+    TiledArgs a;
+    memset(&a, 0, sizeof(a));
+    a.wkv = wkv;
+    a.M = M;
+    a.K = int(K_of(l));
+    a.N = N;
+    a.dim = l->dim;
+    a.x = x;
+    a.hash_ids = hash_ids;
+    a.token_mask = token_mask;
+    a.table = table;
+    a.scales = scales;
+    a.q_weight = q_weight;
+    a.k_weight = k_weight;
+    a.out = out;
+    a.err_count = err_count;
+    a.n_cols = l->n_cols;
+    a.head_dim = l->head_dim;
+    a.scale_block = l->scale_block;
+    a.n_rows = l->n_rows;
+    a.eps = l->eps;
+    a.clamp = l->clamp;
+    a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
+    a.spin_budget = kSpinBudget;
+    return launch_forward_tiled(a, workspace, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? ENGRAM_OK
+               : ENGRAM_E_HIP;
+  }
+  const int G = stream_grid(N, di.cus);
   if ((N / 16 + G - 1) / G > l->dim / 16) return ENGRAM_E_LAYOUT;
   StreamArgs a;
   memset(&a, 0, sizeof(a));

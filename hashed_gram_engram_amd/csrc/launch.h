@@ -72,4 +72,41 @@ size_t stream_workspace_bytes(int64_t M, int N, int grid);
 int stream_grid(int N, int num_cus);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 
+// Arguments of the tiled kernels (256-token x 256-column tiles, for large token counts).
+struct TiledArgs {
+  const uint16_t* wkv;  // [N, K] bf16
+  int64_t M;
+  int K, N, dim;
+  // projection alone
+  const uint16_t* emb;  // [M, K] bf16
+  uint16_t* kv;         // [M, N] bf16
+  // whole forward
+  const uint16_t* x;
+  const int64_t* hash_ids;
+  const uint8_t* token_mask;
+  const uint8_t* table;
+  const float* scales;
+  const float* q_weight;
+  const float* k_weight;
+  uint16_t* out;
+  int32_t* err_count;
+  int n_cols, head_dim, scale_block;
+  int64_t n_rows;
+  float eps, clamp, inv_sqrt_dim;
+  uint32_t spin_budget;
+  // workspace views (set by the launcher)
+  void* ws;
+  int n_vcb;
+  size_t slot_off, part_off;
+};
+
+// Shapes the tiled kernels take: N and dim multiples of 256, K a multiple of 64 (fused: also
+// head_dim a multiple of 64 and scale_block of 16).
+bool tiled_shape_ok(int N, int K, int dim, int head_dim, int scale_block, bool fused);
+size_t tiled_workspace_bytes(int64_t M, int dim);
+hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream);
+// Whole forward, tiled schedule.  Same workspace contract as launch_forward_stream, with
+// tiled_workspace_bytes() bytes.
+hipError_t launch_forward_tiled(TiledArgs a, void* workspace, hipStream_t stream);
+
 }  // namespace engram

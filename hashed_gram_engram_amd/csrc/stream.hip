@@ -472,6 +472,14 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             const int v = v0 + i / kTB, tt = i % kTB;
             store_relaxed(gate_slot(a, tb, v, s) + tt, __float_as_uint(sh.red[0][tt][0]) | 0x80000000u);
           }
+          // the partials are consumed: leave them zero, so that the whole workspace is zero
+          // again after the call (any schedule may use it next)
+          for (int w2 = wb0; w2 < wb1; ++w2) {
+            float* P = partial_of(a, tb, w2, s - rb_begin(w2, nrb, G) / R) + t * 3;
+            store_coherent(P + 0, 0.0f);
+            store_coherent(P + 1, 0.0f);
+            store_coherent(P + 2, 0.0f);
+          }
         }
       }
     }

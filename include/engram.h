@@ -69,12 +69,12 @@ engram_status engram_layout_check(const engram_layout* layout);
 engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
 
 /* Bytes of workspace engram_forward needs for B x T tokens on the current device (0 on an
- * invalid layout).  The workspace must be zero-filled before its first use with a layout.  Its
- * control words (counters and gate slots) are back at zero when engram_forward completes and
- * sit at offsets that depend only on the layout and the device, so one workspace serves any
- * number of calls with that layout, for any B x T it is large enough for, on one stream without
- * clearing.  Word 0 counts cross-workgroup waits that timed out (0 in correct operation).
- * Calls that overlap in time must use different workspaces. */
+ * invalid layout).  The workspace must be zero-filled before its first use.  Every call leaves
+ * all of it zero again (counters, gate slots and partial sums), so one workspace serves any
+ * number of calls, with any layout and any B x T it is large enough for, on one stream without
+ * clearing.  The exception is word 0, which counts cross-workgroup waits that timed out (0 in
+ * correct operation); after a time-out the workspace must be zero-filled again.  Calls that
+ * overlap in time must use different workspaces. */
 size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
 /* S1 + S2: row gather and dequantisation (engram-second page,

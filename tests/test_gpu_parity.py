@@ -92,6 +92,14 @@ DECODE = WORKLOADS["decode_b64"]
 # closed tokens and outlier streams
 RAGGED = synth.small_variant(DECODE, name="decode_dims_b3_t37", B=3, T=37, hash_dist="zipf",
                              mask_false_frac=0.2, outlier_frac=0.05, seed=DECODE.seed + 100)
+# token counts that take the tiled (256 x 256) schedule: tiny dims with three token blocks (the
+# last one ragged), and the decode layout with one full and one ragged token block
+TILED_TINY = synth.small_variant(TINY, name="tiny_dims_b2_t300", B=2, T=300, hash_dist="zipf",
+                                 mask_false_frac=0.15, outlier_frac=0.05, masked_positions=(),
+                                 seed=TINY.seed + 200)
+TILED_DECODE = synth.small_variant(DECODE, name="decode_dims_b1_t300", B=1, T=300,
+                                   hash_dist="zipf", mask_false_frac=0.1, outlier_frac=0.02,
+                                   seed=DECODE.seed + 200)
 
 
 @pytest.fixture(scope="module")
@@ -304,9 +312,9 @@ def test_forward_equals_composition_in_place_and_deterministic(dev_decode):
     e = eg.engram_gate_apply(lay, d["x"], kv, d["q_weight"], d["k_weight"], d["token_mask"])
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
-    # no cross-workgroup wait timed out (first header word), and a fresh zero-filled workspace
-    # gives the same result as the reused one (so the control words were left zeroed)
-    assert int(ws[:4].view(torch.int32).item()) == 0
+    # no cross-workgroup wait timed out (word 0), every call left the workspace all zero, and a
+    # fresh zero-filled workspace gives the same result as the reused one
+    assert int(torch.count_nonzero(ws).item()) == 0
     fresh = forward(w, d, ws=torch.zeros_like(ws))
     torch.cuda.synchronize()
     assert torch.equal(a, fresh)
@@ -356,8 +364,85 @@ def test_forward_prefill_sampled():
     rng = np.random.default_rng(5)
     mask = w.token_mask().reshape(-1)
     closed = np.nonzero(mask == 0)[0][:4]
-    sel = np.unique(np.concatenate([[0, 63, 64, w.M - 1], closed, rng.integers(0, w.M, 40)]))
+    sel = np.unique(np.concatenate([[0, 63, 64, 255, 256, w.M - 1], closed, rng.integers(0, w.M, 40)]))
     got = u16(out).reshape(w.M, w.hc, w.dim)[sel]
     say("   ", check_out(w, sel, got, oracle_for(w, sel)))
     del d, out
     torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------- tiled schedule
+
+
+def test_kv_proj_tiled_tiny_dims():
+    say("[gpu] kv_proj tiled: tiny dims, B=2 T=300")
+    w = TILED_TINY
+    d = synth.device_inputs(w)
+    _kv_case(w, d)
+
+
+def test_forward_tiled_tiny_dims_bad_ids_in_place():
+    say("[gpu] forward tiled: tiny dims, B=2 T=300 (ragged block, closed tokens, outliers, bad ids)")
+    w = TILED_TINY
+    d = synth.device_inputs(w)
+    ids = w.hash_ids()
+    ids[0, 5, 1] = -3
+    ids[1, 299, 5] = w.n_rows
+    ids[1, 40, 0] = 1 << 40
+    d["hash_ids"] = torch.from_numpy(ids).cuda()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = forward(w, d, err=err)
+    x2 = d["x"].clone()
+    out2 = forward(w, d | {"x": x2}, out=x2)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 3
+    assert torch.equal(out, out2)
+    q, k = w.qk()
+    sel = np.arange(w.M)
+    ref = oracle.forward(w.x_tokens(sel), ids.reshape(w.M, -1), w.token_mask().reshape(-1),
+                         synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block, host_wkv(w), q, k)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), ref))
+
+
+def test_workspace_all_zero_and_shared_across_schedules():
+    say("[gpu] workspace: all zero after calls, shared by the streaming and tiled schedules")
+    w_big, w_small = TILED_TINY, synth.small_variant(TILED_TINY, name="tiny_dims_b1_t40", B=1, T=40)
+    lay = layout(w_big)
+    n = max(eg.engram_forward_workspace_bytes(lay, w_big.B, w_big.T),
+            eg.engram_forward_workspace_bytes(lay, w_small.B, w_small.T))
+    ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    d_big, d_small = synth.device_inputs(w_big), synth.device_inputs(w_small)
+    outs = []
+    for w, d in ((w_big, d_big), (w_small, d_small), (w_big, d_big), (w_small, d_small)):
+        outs.append(forward(w, d, ws=ws))
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws).item()) == 0, w.name
+    fresh_big = forward(w_big, d_big, ws=torch.zeros_like(ws))
+    fresh_small = forward(w_small, d_small, ws=torch.zeros_like(ws))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], fresh_big) and torch.equal(outs[2], fresh_big)
+    assert torch.equal(outs[1], fresh_small) and torch.equal(outs[3], fresh_small)
+
+
+@pytest.fixture(scope="module")
+def dev_tiled_decode():
+    say("[gpu] inputs: decode layout, B=1 T=300")
+    d = synth.device_inputs(TILED_DECODE)
+    torch.cuda.synchronize()
+    yield d
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_kv_proj_tiled_decode_dims(dev_tiled_decode):
+    say("[gpu] kv_proj tiled: decode layout, B=1 T=300")
+    _kv_case(TILED_DECODE, dev_tiled_decode)
+
+
+def test_forward_tiled_decode_dims(dev_tiled_decode):
+    say("[gpu] forward tiled: decode layout, B=1 T=300")
+    w = TILED_DECODE
+    out = forward(w, dev_tiled_decode)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
