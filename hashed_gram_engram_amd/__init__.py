@@ -49,6 +49,8 @@ _lib.engram_layout_check.argtypes = [_LP]
 _lib.engram_param_counts.argtypes = [_LP, ctypes.POINTER(ctypes.c_int64)]
 _lib.engram_forward_workspace_bytes.argtypes = [_LP, _i64, _i64]
 _lib.engram_forward_workspace_bytes.restype = _sz
+_lib.engram_forward_staging_bytes.argtypes = [_LP, _i64, _i64]
+_lib.engram_forward_staging_bytes.restype = _sz
 _lib.engram_gather_dequant.argtypes = [_LP, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.engram_kv_proj.argtypes = [_LP, _vp, _vp, _i64, _i64, _vp, _vp]
 _lib.engram_gate_apply.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
@@ -59,6 +61,7 @@ for _f in (_lib.engram_layout_check, _lib.engram_param_counts, _lib.engram_gathe
     _f.restype = ctypes.c_int
 
 EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_workspace_bytes",
+            "engram_forward_staging_bytes",
             "engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
             "engram_status_str"]
 
@@ -104,6 +107,10 @@ def engram_param_counts(layout: EngramLayout):
 
 def engram_forward_workspace_bytes(layout: EngramLayout, B: int, T: int) -> int:
     return int(_lib.engram_forward_workspace_bytes(ctypes.byref(layout), B, T))
+
+
+def engram_forward_staging_bytes(layout: EngramLayout, B: int, T: int) -> int:
+    return int(_lib.engram_forward_staging_bytes(ctypes.byref(layout), B, T))
 
 
 def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: torch.Tensor,
@@ -157,8 +164,9 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
 
 
 class Workspace:
-    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves it
-    all zero after every call, except the time-out counter in word 0)."""
+    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves its
+    control words zero after every call, except the time-out counter in word 0; the staging
+    area at its end holds scratch rows)."""
 
     def __init__(self, device=None):
         self.device = device

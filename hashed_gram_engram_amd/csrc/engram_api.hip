@@ -52,13 +52,33 @@ int64_t K_of(const engram_layout* l) { return int64_t(l->n_cols) * l->head_dim; 
 int64_t N_of(const engram_layout* l) { return int64_t(l->hc + 1) * l->dim; }
 
 bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
-  return M >= kTiledMinTokens &&
-         tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, l->head_dim, l->scale_block, fused);
+  return M >= kTiledMinTokens && tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, fused);
+}
+
+// Workspace of engram_forward for M tokens: control words at the start (the schedule in use
+// leaves them zero), then room for the staging area of the tiled schedule, which sits at the
+// END of the caller's buffer.  control(M) is the larger of the two schedules' control sizes for
+// every token count up to M, so it never decreases with M; neither does staging(M).  Hence for
+// any two calls on one buffer (same workspace_bytes W, each with W >= control + staging), the
+// control words of one never overlap the staging area of the other: the dequantised rows a
+// call leaves behind never sit where a later call expects zeros.
+size_t forward_control(const engram_layout* l, int64_t M, int cus) {
+  const int N = int(N_of(l));
+  const int64_t Ms = M < kTiledMinTokens ? M : kTiledMinTokens - 1;
+  size_t c = stream_workspace_bytes(Ms, N, stream_grid(N, cus));
+  if (use_tiled(l, M, true)) {
+    const size_t t = tiled_control_bytes(M, l->dim);
+    c = t > c ? t : c;
+  }
+  return (c + 255) & ~size_t(255);
+}
+
+size_t forward_staging(const engram_layout* l, int64_t M) {
+  return use_tiled(l, M, true) ? tiled_staging_bytes(M, int(K_of(l))) + 256 : 0;
 }
 
 size_t forward_workspace(const engram_layout* l, int64_t M, int cus) {
-  if (use_tiled(l, M, true)) return tiled_workspace_bytes(M, l->dim);
-  return stream_workspace_bytes(M, int(N_of(l)), stream_grid(int(N_of(l)), cus));
+  return forward_control(l, M, cus) + forward_staging(l, M);
 }
 
 }  // namespace
@@ -111,6 +131,13 @@ size_t engram_forward_workspace_bytes(const engram_layout* l, int64_t B, int64_t
   DeviceInfo di;
   int cus = (device_info(&di) == ENGRAM_OK) ? di.cus : 256;
   return forward_workspace(l, M, cus);
+}
+
+size_t engram_forward_staging_bytes(const engram_layout* l, int64_t B, int64_t T) {
+  if (engram_layout_check(l) != ENGRAM_OK) return 0;
+  int64_t M = 0;
+  if (check_tokens(B, T, &M) != ENGRAM_OK) return 0;
+  return forward_staging(l, M);
 }
 
 engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table, const float* scales,
@@ -234,7 +261,12 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     a.clamp = l->clamp;
     a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
     a.spin_budget = kSpinBudget;
-    return launch_forward_tiled(a, workspace, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+    GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block, l->n_rows, nullptr, err_count};
+    // the staging area: the last forward_staging() bytes of the buffer, 256-byte aligned
+    const size_t stg = forward_staging(l, M);
+    const uintptr_t start = (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes - stg + 255) & ~uintptr_t(255);
+    return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(start),
+                                reinterpret_cast<hipStream_t>(stream)) == hipSuccess
                ? ENGRAM_OK
                : ENGRAM_E_HIP;
   }

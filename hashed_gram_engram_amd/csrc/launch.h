@@ -100,13 +100,17 @@ struct TiledArgs {
   size_t slot_off, part_off;
 };
 
-// Shapes the tiled kernels take: N and dim multiples of 256, K a multiple of 64 (fused: also
-// head_dim a multiple of 64 and scale_block of 16).
-bool tiled_shape_ok(int N, int K, int dim, int head_dim, int scale_block, bool fused);
-size_t tiled_workspace_bytes(int64_t M, int dim);
+// Shapes the tiled kernels take: N a multiple of 256, K of 32 (fused: also dim of 256).
+bool tiled_shape_ok(int N, int K, int dim, bool fused);
+// Control words of the fused tiled schedule (zero before and after every call) and the staging
+// area of its dequantised rows (M x K bf16, contents unspecified after a call).
+size_t tiled_control_bytes(int64_t M, int dim);
+size_t tiled_staging_bytes(int64_t M, int K);
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream);
-// Whole forward, tiled schedule.  Same workspace contract as launch_forward_stream, with
-// tiled_workspace_bytes() bytes.
-hipError_t launch_forward_tiled(TiledArgs a, void* workspace, hipStream_t stream);
+// Whole forward, tiled schedule: the gather pass `g` writes the dequantised rows into `staging`
+// (tiled_staging_bytes, 256-byte aligned), then the tiled kernel runs with `workspace` as its
+// control words (tiled_control_bytes, zero on entry, left zero).
+hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging,
+                                hipStream_t stream);
 
 }  // namespace engram

@@ -1,26 +1,35 @@
-// Tiled wkv projection for large token counts (prefill), alone or fused with the row gather,
-// the per-stream gate and the residual add.
+// Tiled wkv projection for large token counts (prefill), alone or fused with the per-stream
+// gate and the residual add.  The dequantised rows come from a gather pass that writes them, as
+// bf16, into a staging area (k_gather_dequant): at these token counts every row feeds all
+// (hc + 1) * dim / 256 column tiles of its token block, and one bf16 write per row costs less
+// than re-gathering the fp8 row for every tile.
 //
 // A workgroup computes one tile of 256 tokens x 256 wkv rows (output columns) over all of K, in
-// steps of 64 features.  Each step's two operands sit in LDS as 256 rows of 128 bytes with an
-// XOR swizzle of 16-byte chunks (double buffered, 128 KB); while step k is multiplied, step
-// k + 1 is loaded.  Eight waves (two per SIMD, so one can issue MFMAs while the other waits
-// at a barrier or on LDS) each own 128 columns x 64 tokens: 8 x 4 blocks of
-// v_mfma_f32_16x16x32_bf16, 128 accumulator registers.  The wkv rows are the A operand and the
-// tokens the B operand, so a lane ends up holding four consecutive output columns of one token.
+// stages of 32 features.  A stage holds both operands in LDS, 256 rows of 64 bytes each, with
+// 16-byte chunk c of row r at position c ^ ((r >> 1) & 3) (measured conflict-free for the
+// fragment reads below).  Stages live in a ring of five (160 KB); global -> LDS copies
+// (global_load_lds_dwordx4, one instruction fills 16 rows) run four stages ahead.
 //
-// Operand loads: wkv rows (and, for the projection alone, the dense bf16 tokens) are copied
-// from global memory straight into LDS (global_load_lds_dwordx4, 8 rows of 128 bytes per wave
-// instruction), so they take no registers.  In the fused kernel a step's 64 features of a token
-// lie in one hash column (head_dim is a multiple of 64): 4 lanes per token gather 16 fp8 codes
-// each from the token's table row, dequantise them with the row's block scale and write bf16 to
-// LDS.  The hash ids of step k + 2 are loaded during step k, so no gather address waits on a
-// load issued in the same step.
+// Eight waves, two per SIMD.  Waves 0-3 (group 0) own wkv rows 0-127 of the tile, waves 4-7
+// (group 1) rows 128-255; within a group, wave w & 3 owns tokens 64 (w & 3) .. + 63.  Each wave
+// computes 128 columns x 64 tokens as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128 accumulator
+// registers).  The groups alternate ("ping-pong"): while the group-0 wave of a SIMD issues the
+// 32 MFMAs of one stage, the group-1 wave issues its copies and fragment reads for the same
+// stage, then the roles swap; a workgroup barrier separates phases.  So each SIMD's matrix unit
+// is fed by one wave at a time whose operands are already in registers, and the LDS and memory
+// latency of one wave hides under the other's MFMAs.
+//
+// Phase p (p = 0, 1, ...): group 0 multiplies stage p / 2 when p is even and loads stage
+// p / 2 + 1 when p is odd; group 1 loads stage p / 2 when p is even and multiplies it when p is
+// odd.  The load phase of stage j copies this wave's share of stage j + 4 into ring slot
+// (j + 4) % 5, whose previous stage (j - 1) both groups finished reading before the barrier
+// ending phase 2 j - 2; before the barrier ending phase 2 j - 2 each wave waits until its share of
+// stage j has landed, so stage j is complete before its first reader (group 0, phase 2 j - 1).
 //
 // Tile order: workgroup b takes token block b % n_tb and column block b / n_tb, so the tiles
 // resident at one time share weight panels across token blocks, and (workgroups being dealt
 // to the 8 XCDs round robin) all tiles of a token block run on one XCD when n_tb is a multiple
-// of 8, keeping its gathered rows and its x in that XCD's L2.  In the fused kernel every key
+// of 8, keeping its staged rows and its x in that XCD's L2.  In the fused kernel every key
 // column block comes before every value column block.  Key tiles post per-(token, stream)
 // partial sums of the gate's three reductions; the last key tile of each (token block, stream)
 // sums them in column-block order, evaluates the gates and hands them to the value tiles of the
@@ -33,169 +42,203 @@ namespace engram {
 
 namespace {
 
-constexpr int kThreads = 512;           // 8 waves
-constexpr int kTM = 256;                // tokens per tile
-constexpr int kTN = 256;                // wkv rows per tile
-constexpr int kTK = 64;                 // features per K step
-constexpr int kRowB = kTK * 2;          // bytes per LDS row: 8 chunks of 16 bytes
-constexpr int kOp = 256 * kRowB;        // one operand of one stage (32 KB)
-constexpr int kStage = 2 * kOp;         // wkv rows + tokens
-constexpr int kLds = 2 * kStage;        // double buffer: 128 KB
-constexpr int kBI = 8;                  // 16-column blocks per wave
-constexpr int kBJ = 4;                  // 16-token blocks per wave
+constexpr int kThreads = 512;               // 8 waves
+constexpr int kTM = 256;                    // tokens per tile
+constexpr int kTN = 256;                    // wkv rows per tile
+constexpr int kTK = 32;                     // features per stage
+constexpr int kRowB = kTK * 2;              // bytes per LDS row: 4 chunks of 16 bytes
+constexpr int kOpB = 256 * kRowB;           // one operand of one stage (16 KB)
+constexpr int kStageB = 2 * kOpB;           // wkv rows, then tokens (32 KB)
+constexpr int kRing = 5;                    // stages in the ring
+constexpr int kAhead = kRing - 1;           // copies run this many stages ahead
+constexpr int kLds = kRing * kStageB;       // 160 KB, all of a CU's LDS
+constexpr int kCopies = 4;                  // copy instructions per wave per stage
+constexpr int kBI = 8;                      // 16-column blocks per wave
+constexpr int kBJ = 4;                      // 16-token blocks per wave
 
 typedef f32x4 TileAcc[kBI][kBJ];
-
-// LDS rows are stored with 16-byte chunk c of row r at position c ^ (r & 7): the eight rows that
-// one 8-lane phase of a 16-byte LDS read touches then hit eight distinct bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kRowB + 16 * (chunk ^ (row & 7)); }
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Direct global -> LDS copy of 256 rows x 128 bytes (features k0 .. k0 + 63 of rows
-// row0 .. row0 + 255 of a row-major bf16 matrix with ld elements per row; rows past row_last
-// repeat row_last).  Each wave instruction fills 1024 contiguous LDS bytes (lane l at 16 l),
-// i.e. 8 rows: lane l supplies chunk (l & 7) ^ (l >> 3) of row l >> 3 of its group, which is
-// the swizzled position (l & 7).  Wave w fills the row groups 4 w .. 4 w + 3.
-__device__ __forceinline__ void dma_rows(const uint16_t* src, int64_t ld, int64_t row0, int64_t row_last, int k0,
-                                         char* dst, int wv_u, int lane) {
-  const int r = lane >> 3, c = (lane & 7) ^ r;
+// Everything a wave needs to copy and read stages.
+struct Pipe {
+  const char* src[kCopies];  // per-lane global source of each copy at feature 0 (2 wkv, 2 token)
+  uint32_t frag_off;         // per-lane byte offset of a fragment read inside a 16-row block
+  int wv_u;                  // wave index (wave-uniform)
+  int a_off, b_off;          // byte offsets of this wave's first wkv row and first token row
+};
+
+// Copies of this wave for stage t into ring slot `slot`: wkv row groups 2 w, 2 w + 1 and token
+// row groups 2 w, 2 w + 1 (16 rows each).  Instruction g fills LDS bytes [1024 g, 1024 g + 1024)
+// of its operand, lane l at 16 l: row g * 16 + (l >> 2), position l & 3, which holds chunk
+// (l & 3) ^ (((l >> 2) >> 1) & 3).
+__device__ __forceinline__ void copy_stage(const Pipe& p, char* lds, int slot, int t) {
+  char* st = lds + slot * kStageB;
+  const size_t k_bytes = size_t(t) * (kTK * 2);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int g = wv_u * 4 + i;  // 8-row group 0..31 (wave-uniform)
-    int64_t row = row0 + 8 * g + r;
-    row = row < row_last ? row : row_last;
-    __builtin_amdgcn_global_load_lds((const void*)(src + row * ld + k0 + 8 * c), (lds_ptr_t)(dst + g * 1024), 16,
+  for (int i = 0; i < kCopies; ++i) {
+    const int op = i >> 1, g = 2 * p.wv_u + (i & 1);
+    __builtin_amdgcn_global_load_lds((const void*)(p.src[i] + k_bytes), (lds_ptr_t)(st + op * kOpB + g * 1024), 16,
                                      0, 0);
   }
 }
 
-struct TiledIds {
-  int64_t r[2];    // hash id of token (tid >> 2) + 128 i for one column (of the last token for
-                   // positions past it: validity is decided where the ids are used)
-};
-
-struct TiledCodes {
-  u32x4 c[2];      // 16 fp8 codes of token (tid >> 2) + 128 i at features 16 (tid & 3) of the step
-  float scale[2];  // their block scale
-  uint32_t keep[2];
-};
-
-__device__ __forceinline__ void issue_ids(TiledIds& ids, const TiledArgs& a, int64_t m0, int k0, int tid) {
-  const int j = k0 / a.head_dim;
+// The 12 fragments of one stage for this wave: F[i] = wkv rows 16 i .. 16 i + 15 of the wave's
+// 128, F[8 + j] = tokens 16 j .. 16 j + 15 of its 64.  Lane l gets row l & 15, features
+// 8 (l >> 4) .. + 7 of the stage (the MFMA operand layout).
+__device__ __forceinline__ void read_frags(u32x4 (&F)[12], const Pipe& p, const char* lds, int slot) {
+  const char* st = lds + slot * kStageB + p.frag_off;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t m = m0 + (tid >> 2) + 128 * i;
-    const int64_t mm = m < a.M ? m : a.M - 1;
-    ids.r[i] = a.hash_ids[mm * a.n_cols + j];
+  for (int i = 0; i < kBI; ++i) F[i] = *reinterpret_cast<const u32x4*>(st + p.a_off + i * 1024);
+#pragma unroll
+  for (int j = 0; j < kBJ; ++j) F[kBI + j] = *reinterpret_cast<const u32x4*>(st + kOpB + p.b_off + j * 1024);
+}
+
+__device__ __forceinline__ void stage_mma(TileAcc& acc, const u32x4 (&F)[12]) {
+#pragma unroll
+  for (int i = 0; i < kBI; ++i)
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) acc[i][j] = mfma16x16x32(F[i], F[kBI + j], acc[i][j]);
+}
+
+// A phase boundary: nothing is scheduled across it, then the workgroup barrier.
+__device__ __forceinline__ void phase_end() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int N>
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_frags() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ int next_slot(int s) { return s + 1 == kRing ? 0 : s + 1; }
+
+// The K loop of group G.  Copies past the last stage repeat the last stage (into a slot no
+// stage in use occupies), so that every wave issues the same number of copies per phase and the
+// wait counts above stay exact; the same holds for group 0's fragment reads after the last
+// stage.
+template <int G>
+__device__ __forceinline__ void k_loop(TileAcc& acc, const Pipe& p, char* lds, int S) {
+  u32x4 F[12];
+  // prologue: group 0 copies stages 0 .. 4, group 1 stages 0 .. 3; stage 0 lands
+  constexpr int kPro = G == 0 ? kAhead + 1 : kAhead;
+#pragma unroll
+  for (int t = 0; t < kPro; ++t) copy_stage(p, lds, t, t < S ? t : S - 1);
+  wait_copies<(kPro - 1) * kCopies>();
+  phase_end();
+  if constexpr (G == 0) {
+    read_frags(F, p, lds, 0);
+    wait_frags();
   }
-}
-
-__device__ __forceinline__ void issue_codes(TiledCodes& st, const TiledIds& ids, const TiledArgs& a, int64_t m0,
-                                            int k0, int tid) {
-  const int j = k0 / a.head_dim;
-  const int cc = k0 - j * a.head_dim + 16 * (tid & 3);
-  const int nb = a.head_dim / a.scale_block;
-  const int sb = cc / a.scale_block;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int64_t r = ids.r[i];
-    const bool ok = m0 + (tid >> 2) + 128 * i < a.M && r >= 0 && r < a.n_rows;
-    const int64_t rr = ok ? r : 0;
-    st.keep[i] = ok ? 0xFFFFFFFFu : 0u;
-    st.c[i] = *reinterpret_cast<const u32x4*>(a.table + rr * a.head_dim + cc);
-    st.scale[i] = a.scales[rr * nb + sb];
+  phase_end();
+  int rd = G == 0 ? 1 : 0;        // ring slot of the next stage to read
+  int cp = G == 0 ? 0 : kAhead;   // ring slot of the next stage to copy
+  for (int s = 0; s < S; ++s) {
+    if constexpr (G == 0) {
+      stage_mma(acc, F);                    // phase 2 s: stage s
+      __builtin_amdgcn_sched_barrier(0);    // (the wait goes after every MFMA is issued)
+      wait_copies<3 * kCopies>();           // this wave's share of stage s + 1 has landed
+      phase_end();
+      const int tc = s + kAhead + 1;        // phase 2 s + 1: load stage s + 1 (after the last
+      copy_stage(p, lds, cp, tc < S ? tc : S - 1);  // stage, fragments nobody uses)
+      read_frags(F, p, lds, rd);
+      wait_frags();
+      phase_end();
+    } else {
+      const int tc = s + kAhead;            // phase 2 s: load stage s
+      copy_stage(p, lds, cp, tc < S ? tc : S - 1);
+      read_frags(F, p, lds, rd);
+      wait_frags();
+      wait_copies<3 * kCopies>();           // this wave's share of stage s + 1 has landed
+      phase_end();
+      stage_mma(acc, F);                    // phase 2 s + 1: stage s
+      phase_end();
+    }
+    rd = next_slot(rd);
+    cp = next_slot(cp);
   }
+  // the repeated copies may still be landing: every copy done before LDS is reused
+  wait_copies<0>();
+  phase_end();
 }
 
-// Dequantised tokens of one step into the token operand of a stage (bf16, swizzled rows).
-__device__ __forceinline__ void store_codes(const TiledCodes& st, char* T, int tid) {
+__device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char* lds, int64_t m0, int n0,
+                                          int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  Pipe p;
+  p.wv_u = __builtin_amdgcn_readfirstlane(wv);
+  {
+    const int rr = lane >> 2, chunk = (lane & 3) ^ ((rr >> 1) & 3);
+    const size_t row_bytes = size_t(a.K) * 2;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const u32x4 c = st.c[i];
-    const uint32_t k = st.keep[i];
-    const float s = st.scale[i];
-    const u32x2 p0 = dequant4_raw(c.x, s), p1 = dequant4_raw(c.y, s);
-    const u32x2 p2 = dequant4_raw(c.z, s), p3 = dequant4_raw(c.w, s);
-    const int row = (tid >> 2) + 128 * i, ch = 2 * (tid & 3);
-    *reinterpret_cast<u32x4*>(T + swz(row, ch)) = u32x4{p0.x & k, p0.y & k, p1.x & k, p1.y & k};
-    *reinterpret_cast<u32x4*>(T + swz(row, ch + 1)) = u32x4{p2.x & k, p2.y & k, p3.x & k, p3.y & k};
+    for (int i = 0; i < 2; ++i) {
+      const int r = (2 * p.wv_u + i) * 16 + rr;  // row of the tile
+      p.src[i] = reinterpret_cast<const char*>(a.wkv) + size_t(n0 + r) * row_bytes + 16 * chunk;
+      int64_t m = m0 + r;
+      m = m < a.M ? m : a.M - 1;  // rows past the last token repeat it (their results are dropped)
+      p.src[2 + i] = reinterpret_cast<const char*>(a.emb) + size_t(m) * row_bytes + 16 * chunk;
+    }
   }
-}
-
-// The 64 features of one stage: two k32 steps of 8 x 4 MFMA blocks per wave.
-__device__ __forceinline__ void stage_mma(TileAcc& acc, const char* stage, int lane, int wr, int wt) {
-  const char* W = stage + (128 * wr) * kRowB;
-  const char* T = stage + kOp + (64 * wt) * kRowB;
-  const int r = lane & 15;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int ch = 4 * s + (lane >> 4);
-    u32x4 af[kBI], bf[kBJ];
-#pragma unroll
-    for (int i = 0; i < kBI; ++i) af[i] = *reinterpret_cast<const u32x4*>(W + swz(16 * i + r, ch));
-#pragma unroll
-    for (int j = 0; j < kBJ; ++j) bf[j] = *reinterpret_cast<const u32x4*>(T + swz(16 * j + r, ch));
-#pragma unroll
-    for (int i = 0; i < kBI; ++i)
-#pragma unroll
-      for (int j = 0; j < kBJ; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+  {
+    const int r = lane & 15;
+    p.frag_off = uint32_t(r * kRowB + 16 * ((lane >> 4) ^ ((r >> 1) & 3)));
   }
-}
-
-// Every load of this wave has landed (registers and LDS) and every LDS access is done; then the
-// workgroup barrier.  (A plain barrier: LDS needs no cache maintenance.)
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Operand loads of the step at feature k0 into stage buffer `stage`.  The fused kernel's token
-// operand goes through registers: the codes are gathered here (with the hash ids loaded one
-// step earlier), the ids of the step after are loaded, and store_codes writes the tokens later.
-// The gathers come first, so that the wait for the ids they use is a wait for loads issued
-// before the previous barrier, never for the copies issued here.
-template <bool FUSED>
-__device__ __forceinline__ void issue_step(TiledCodes& codes, TiledIds& ids, const TiledArgs& a, char* stage,
-                                           int64_t m0, int n0, int k0, int k0_ids, int wv_u, int lane, int tid) {
-  if constexpr (FUSED) {
-    issue_codes(codes, ids, a, m0, k0, tid);
-    issue_ids(ids, a, m0, k0_ids, tid);
-  }
-  dma_rows(a.wkv, a.K, n0, int64_t(n0) + kTN - 1, k0, stage, wv_u, lane);
-  if constexpr (!FUSED) dma_rows(a.emb, a.K, m0, a.M - 1, k0, stage + kOp, wv_u, lane);
-}
-
-template <bool FUSED>
-__device__ __forceinline__ void tiled_gemm(TileAcc& acc, const TiledArgs& a, char* lds, int64_t m0, int n0,
-                                           int tid) {
-  const int lane = tid & 63, wv = tid >> 6, wr = wv >> 2, wt = wv & 3;
-  const int wv_u = __builtin_amdgcn_readfirstlane(wv);
-  const int nsteps = a.K / kTK;
+  p.a_off = (wv >> 2) * 128 * kRowB;
+  p.b_off = (wv & 3) * 64 * kRowB;
 #pragma unroll
   for (int i = 0; i < kBI; ++i)
 #pragma unroll
     for (int j = 0; j < kBJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  TiledCodes codes;
-  TiledIds ids;
-  // step 0 into buffer 0; the hash ids of step 1 in registers
-  if constexpr (FUSED) issue_ids(ids, a, m0, 0, tid);
-  issue_step<FUSED>(codes, ids, a, lds, m0, n0, 0, nsteps > 1 ? kTK : 0, wv_u, lane, tid);
-  if constexpr (FUSED) store_codes(codes, lds + kOp, tid);
-  stage_barrier();
-  // step k: loads of step k + 1 into the other buffer (read during step k - 1, which every
-  // wave has finished at the barrier), the hash ids of step k + 2, then the MFMAs of step k
-  // The loop has no branches around loads (a load under a branch makes the compiler wait for
-  // it at the join): in the last step the loads repeat that step into the free buffer.
-  for (int k = 0; k < nsteps; ++k) {
-    char* cur = lds + (k & 1) * kStage;
-    char* nxt = lds + ((k + 1) & 1) * kStage;
-    const int k1 = k + 1 < nsteps ? k + 1 : k;
-    const int k2 = k + 2 < nsteps ? k + 2 : k1;
-    issue_step<FUSED>(codes, ids, a, nxt, m0, n0, k1 * kTK, k2 * kTK, wv_u, lane, tid);
-    asm volatile("" ::: "memory");
-    stage_mma(acc, cur, lane, wr, wt);
-    if constexpr (FUSED) store_codes(codes, nxt + kOp, tid);
-    stage_barrier();
+  const int S = a.K / kTK;
+  if (__builtin_amdgcn_readfirstlane(wv) < 4)
+    k_loop<0>(acc, p, lds, S);
+  else
+    k_loop<1>(acc, p, lds, S);
+}
+
+// ---------------------------------------------------------------- epilogues
+// After the K loop the accumulator tile goes to LDS as bf16 (the rounding the projection output
+// has): 256 token rows of 512 bytes, 16-byte chunk c of row t at position c ^ (t & 31).  The
+// epilogues then walk token rows with half a wave per row (32 lanes x 8 features), so every
+// global access of x, out and kv is 16 bytes per lane and 512 contiguous bytes per row.
+constexpr int kVRow = kTN * 2;                     // bytes per token row
+constexpr int kVBytes = kTM * kVRow;               // 128 KB
+constexpr int kGateOff = kVBytes;                  // value tiles: gates [4][256] fp32
+constexpr int kFlagOff = kGateOff + 4 * kTM * 4;   // key tiles: last-arriver flag
+static_assert(kFlagOff + 4 <= kLds, "epilogue LDS");
+
+__device__ __forceinline__ int vswz(int t, int c) { return t * kVRow + 16 * (c ^ (t & 31)); }
+
+// Accumulator block (i, j) of wave (wr, wt) holds columns 128 wr + 16 i + 4 (l >> 4) + 0..3 of
+// token 64 wt + 16 j + (l & 15).
+__device__ __forceinline__ void acc_to_lds(const TileAcc& acc, char* V, int lane, int wr, int wt) {
+#pragma unroll
+  for (int j = 0; j < kBJ; ++j) {
+    const int t = 64 * wt + 16 * j + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < kBI; ++i) {
+      const int f = 128 * wr + 16 * i + 4 * (lane >> 4);
+      *reinterpret_cast<u32x2*>(V + vswz(t, f >> 3) + 2 * (f & 7)) =
+          u32x2{pack_bf16x2(acc[i][j].x, acc[i][j].y), pack_bf16x2(acc[i][j].z, acc[i][j].w)};
+    }
+  }
+}
+
+__device__ __forceinline__ void unpack8(u32x4 w, float (&v)[8]) {
+  v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+  v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+}
+
+// Projection alone: the tile's kv rows, 512 contiguous bytes per token.
+__device__ __forceinline__ void kv_epilogue(const TiledArgs& a, const char* V, int64_t m0, int n0, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+#pragma unroll 4
+  for (int p = 0; p < 16; ++p) {
+    const int t = p * 16 + wv * 2 + half;
+    const int64_t m = m0 + t;
+    if (m < a.M)
+      *reinterpret_cast<u32x4*>(a.kv + m * a.N + n0 + 8 * l32) = *reinterpret_cast<const u32x4*>(V + vswz(t, l32));
   }
 }
 
@@ -213,81 +256,68 @@ __device__ __forceinline__ float* tpartial(const TiledArgs& a, int64_t tb, int s
          ((size_t(tb) * 4 + s) * a.n_vcb + cbs) * (kTM * 3);
 }
 
-// Hash ids of the tile's tokens that name no table row (each (token, column) pair counts 1).
-__device__ __forceinline__ void count_bad_ids(const TiledArgs& a, int64_t m0, int tid) {
-  if (a.err_count == nullptr) return;
-  const int64_t m1 = m0 + kTM < a.M ? m0 + kTM : a.M;
-  const int64_t n = (m1 - m0) * a.n_cols;
-  const int64_t* ids = a.hash_ids + m0 * a.n_cols;
-  int bad = 0;
-  for (int64_t e = tid; e < n; e += kThreads) {
-    const int64_t r = ids[e];
-    bad += (r < 0 || r >= a.n_rows) ? 1 : 0;
+// Key tile (stream s, features dseg .. dseg + 255 of the stream): per token, this tile's share
+// of the gate's three sums (|h|^2, |key|^2 and sum h * q * k * key) is posted to the workspace;
+// the last of the stream's key tiles sums the shares in column-block order, evaluates the 256
+// gates and hands them to the value tiles of the token block.
+__device__ __forceinline__ void key_epilogue(const TiledArgs& a, char* lds, int64_t tb, int64_t m0, int s, int cbs,
+                                             int dseg, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const char* V = lds;
+  int* flag = reinterpret_cast<int*>(lds + kFlagOff);
+  const int d = dseg + 8 * l32;
+  float wq[8];
+  {
+    const f32x4 q0 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
+    const f32x4 q1 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d + 4);
+    const f32x4 k0 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
+    const f32x4 k1 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d + 4);
+    wq[0] = q0.x * k0.x; wq[1] = q0.y * k0.y; wq[2] = q0.z * k0.z; wq[3] = q0.w * k0.w;
+    wq[4] = q1.x * k1.x; wq[5] = q1.y * k1.y; wq[6] = q1.z * k1.z; wq[7] = q1.w * k1.w;
   }
-  if (bad) atomicAdd(a.err_count, bad);
-}
-
-// Key tile epilogue: this tile's share of the gate's three per-token sums (|h|^2, |k|^2 and
-// the weighted dot product over the tile's 256 features of stream s), posted to the workspace;
-// the last of the stream's key tiles evaluates the 256 gates and hands them to the value tiles.
-__device__ __forceinline__ void key_epilogue(const TileAcc& acc, const TiledArgs& a, char* lds, int* s_last,
-                                             int64_t tb, int64_t m0, int s, int cbs, int d0, int tid) {
-  const int lane = tid & 63, wv = tid >> 6, wr = wv >> 2, wt = wv & 3;
-  float (*red)[kTM][3] = reinterpret_cast<float (*)[kTM][3]>(lds);  // [2 column halves][256][3]
-  float pa[kBJ], pk[kBJ], pd[kBJ];
+  float* P = tpartial(a, tb, s, cbs);
+  // 16 passes of 16 rows (8 waves x 2 half-waves); the x loads of 8 passes are in flight at once
 #pragma unroll
-  for (int j = 0; j < kBJ; ++j) {
-    const int64_t m = m0 + 64 * wt + 16 * j + (lane & 15);
-    const int64_t mm = m < a.M ? m : a.M - 1;
-    float sa = 0.f, sk = 0.f, sd = 0.f;
+  for (int p0 = 0; p0 < 16; p0 += 8) {
+    u32x4 xv[8];
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) {
-      const int d = d0 + 16 * i + 4 * (lane >> 4);
-      const u32x2 xw = *reinterpret_cast<const u32x2*>(a.x + (mm * 4 + s) * a.dim + d);
-      const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
-      const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
-      const float h[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
-      const float key[4] = {bf16_round(acc[i][j].x), bf16_round(acc[i][j].y), bf16_round(acc[i][j].z),
-                            bf16_round(acc[i][j].w)};
-      const float wq[4] = {q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
+    for (int q = 0; q < 8; ++q) {
+      const int t = (p0 + q) * 16 + wv * 2 + half;
+      const int64_t m = m0 + t;
+      const int64_t mm = m < a.M ? m : a.M - 1;
+      xv[q] = *reinterpret_cast<const u32x4*>(a.x + (mm * 4 + s) * a.dim + d);
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        sa += h[r] * h[r];
-        sk += key[r] * key[r];
-        sd += (h[r] * wq[r]) * key[r];
+    for (int q = 0; q < 8; ++q) {
+      const int t = (p0 + q) * 16 + wv * 2 + half;
+      float h[8], key[8];
+      unpack8(xv[q], h);
+      unpack8(*reinterpret_cast<const u32x4*>(V + vswz(t, l32)), key);
+      float sa = 0.f, sk = 0.f, sd = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sa += h[e] * h[e];
+        sk += key[e] * key[e];
+        sd += (h[e] * wq[e]) * key[e];
+      }
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        sa += __shfl_xor(sa, o, 64);
+        sk += __shfl_xor(sk, o, 64);
+        sd += __shfl_xor(sd, o, 64);
+      }
+      if (l32 == 0) {
+        store_coherent(P + t * 3 + 0, sa);
+        store_coherent(P + t * 3 + 1, sk);
+        store_coherent(P + t * 3 + 2, sd);
       }
     }
-    sa += __shfl_xor(sa, 16, 64);
-    sa += __shfl_xor(sa, 32, 64);
-    sk += __shfl_xor(sk, 16, 64);
-    sk += __shfl_xor(sk, 32, 64);
-    sd += __shfl_xor(sd, 16, 64);
-    sd += __shfl_xor(sd, 32, 64);
-    pa[j] = sa;
-    pk[j] = sk;
-    pd[j] = sd;
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int j = 0; j < kBJ; ++j) {
-      const int t = 64 * wt + 16 * j + lane;
-      red[wr][t][0] = pa[j];
-      red[wr][t][1] = pk[j];
-      red[wr][t][2] = pd[j];
-    }
-  }
-  __syncthreads();
-  if (tid < kTM) {
-    float* P = tpartial(a, tb, s, cbs) + tid * 3;
-    store_coherent(P + 0, red[0][tid][0] + red[1][tid][0]);
-    store_coherent(P + 1, red[0][tid][1] + red[1][tid][1]);
-    store_coherent(P + 2, red[0][tid][2] + red[1][tid][2]);
   }
   drain_memory_ops();
   __syncthreads();
-  if (tid == 0) *s_last = (atomic_add_relaxed(tcounter(a, tb, s), 1u) == uint32_t(a.n_vcb - 1)) ? 1 : 0;
+  if (tid == 0) *flag = (atomic_add_relaxed(tcounter(a, tb, s), 1u) == uint32_t(a.n_vcb - 1)) ? 1 : 0;
   __syncthreads();
-  if (*s_last && tid < kTM) {
+  if (*flag && tid < kTM) {
     // every column block of this stream has posted: sum in column-block order
     float A = 0.f, Kq = 0.f, D = 0.f;
     for (int base = 0; base < a.n_vcb; base += 8) {
@@ -295,10 +325,10 @@ __device__ __forceinline__ void key_epilogue(const TileAcc& acc, const TiledArgs
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int c = base + q < a.n_vcb ? base + q : base;
-        const float* P = tpartial(a, tb, s, c) + tid * 3;
-        v[q][0] = load_coherent(P + 0);
-        v[q][1] = load_coherent(P + 1);
-        v[q][2] = load_coherent(P + 2);
+        const float* Pc = tpartial(a, tb, s, c) + tid * 3;
+        v[q][0] = load_coherent(Pc + 0);
+        v[q][1] = load_coherent(Pc + 1);
+        v[q][2] = load_coherent(Pc + 2);
       }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
@@ -320,23 +350,24 @@ __device__ __forceinline__ void key_epilogue(const TileAcc& acc, const TiledArgs
     const uint32_t bits = __float_as_uint(open ? g : 0.0f) | 0x80000000u;
     if (tid == 0) store_relaxed(tcounter(a, tb, s), 0u);
     for (int v = 0; v < a.n_vcb; ++v) store_relaxed(tslot(a, tb, v, s) + tid, bits);
-    // the partials are consumed: leave them zero, so that the whole workspace is zero again
-    // after the call (any schedule may use it next)
+    // the partials are consumed: leave them zero, so that the control words are all zero again
+    // after the call (any schedule may use them next)
     for (int c = 0; c < a.n_vcb; ++c) {
-      float* P = tpartial(a, tb, s, c) + tid * 3;
-      store_coherent(P + 0, 0.0f);
-      store_coherent(P + 1, 0.0f);
-      store_coherent(P + 2, 0.0f);
+      float* Pc = tpartial(a, tb, s, c) + tid * 3;
+      store_coherent(Pc + 0, 0.0f);
+      store_coherent(Pc + 1, 0.0f);
+      store_coherent(Pc + 2, 0.0f);
     }
   }
 }
 
-// Value tile epilogue: wait for the 4 x 256 gates of the token block, then
-// out = h + gate * value on every stream for the tile's 256 features.
-__device__ __forceinline__ void value_epilogue(const TileAcc& acc, const TiledArgs& a, char* lds, int64_t tb,
-                                               int64_t m0, int cbs, int d0, int tid) {
-  const int lane = tid & 63, wv = tid >> 6, wt = wv & 3;
-  float (*gates)[kTM] = reinterpret_cast<float (*)[kTM]>(lds);  // [4 streams][256]
+// Value tile (features dseg .. dseg + 255 of the value): wait for the 4 x 256 gates of the
+// token block, then out = h + gate * value on every stream.
+__device__ __forceinline__ void value_epilogue(const TiledArgs& a, char* lds, int64_t tb, int64_t m0, int cbs,
+                                               int dseg, int tid) {
+  const int lane = tid & 63, wv = tid >> 6, l32 = lane & 31, half = lane >> 5;
+  const char* V = lds;
+  float (*gates)[kTM] = reinterpret_cast<float (*)[kTM]>(lds + kGateOff);
   // each thread waits for two slot words (stream w >> 8, token w & 255) and clears them
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
@@ -355,29 +386,37 @@ __device__ __forceinline__ void value_epilogue(const TileAcc& acc, const TiledAr
     gates[s2][t] = __uint_as_float(bits & 0x7FFFFFFFu);
   }
   __syncthreads();
+  const int d = dseg + 8 * l32;
+  // 1024 rows (token r >> 2, stream r & 3) in 64 passes of 16; 8 passes of x loads in flight
+  for (int p0 = 0; p0 < 64; p0 += 8) {
+    u32x4 xv[8];
 #pragma unroll
-  for (int j = 0; j < kBJ; ++j) {
-    const int t = 64 * wt + 16 * j + (lane & 15);
-    const int64_t m = m0 + t;
-    if (m >= a.M) continue;
-    const bool open = a.token_mask == nullptr || a.token_mask[m] != 0;
+    for (int q = 0; q < 8; ++q) {
+      const int r = (p0 + q) * 16 + wv * 2 + half;
+      const int64_t m = m0 + (r >> 2);
+      const int64_t mm = m < a.M ? m : a.M - 1;
+      xv[q] = *reinterpret_cast<const u32x4*>(a.x + (mm * 4 + (r & 3)) * a.dim + d);
+    }
 #pragma unroll
-    for (int i = 0; i < kBI; ++i) {
-      const int d = d0 + 16 * i + 4 * (lane >> 4);
-      const float v[4] = {bf16_round(acc[i][j].x), bf16_round(acc[i][j].y), bf16_round(acc[i][j].z),
-                          bf16_round(acc[i][j].w)};
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const size_t off = size_t(m * 4 + s2) * a.dim + d;
-        const u32x2 xw = *reinterpret_cast<const u32x2*>(a.x + off);
-        const float g = gates[s2][t];
-        u32x2 o = xw;
-        if (open) {
-          o.x = pack_bf16x2(bf16_lo(xw.x) + g * v[0], bf16_hi(xw.x) + g * v[1]);
-          o.y = pack_bf16x2(bf16_lo(xw.y) + g * v[2], bf16_hi(xw.y) + g * v[3]);
-        }
-        if (open || a.out != a.x) *reinterpret_cast<u32x2*>(a.out + off) = o;
+    for (int q = 0; q < 8; ++q) {
+      const int r = (p0 + q) * 16 + wv * 2 + half;
+      const int t = r >> 2, s2 = r & 3;
+      const int64_t m = m0 + t;
+      if (m >= a.M) continue;
+      const bool open = a.token_mask == nullptr || a.token_mask[m] != 0;
+      uint16_t* dst = a.out + (m * 4 + s2) * a.dim + d;
+      if (!open) {
+        if (a.out != a.x) *reinterpret_cast<u32x4*>(dst) = xv[q];
+        continue;
       }
+      float h[8], v[8];
+      unpack8(xv[q], h);
+      unpack8(*reinterpret_cast<const u32x4*>(V + vswz(t, l32)), v);
+      const float g = gates[s2][t];
+      *reinterpret_cast<u32x4*>(dst) = u32x4{pack_bf16x2(h[0] + g * v[0], h[1] + g * v[1]),
+                                             pack_bf16x2(h[2] + g * v[2], h[3] + g * v[3]),
+                                             pack_bf16x2(h[4] + g * v[4], h[5] + g * v[5]),
+                                             pack_bf16x2(h[6] + g * v[6], h[7] + g * v[7])};
     }
   }
 }
@@ -385,8 +424,7 @@ __device__ __forceinline__ void value_epilogue(const TileAcc& acc, const TiledAr
 template <bool FUSED>
 __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, wr = wv >> 2, wt = wv & 3;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
   const int64_t b = blockIdx.x;
   const int64_t tb = b % n_tb;
@@ -395,31 +433,20 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   const int n0 = cb * kTN;
 
   TileAcc acc;
-  tiled_gemm<FUSED>(acc, a, lds, m0, n0, tid);
-  // the last K step ended with a barrier: the stage buffers are free for the epilogue
-
+  tile_gemm(acc, a, lds, m0, n0, tid);
+  // the K loop ended with a barrier after its last LDS access: the ring is free
+  acc_to_lds(acc, lds, lane, wv >> 2, wv & 3);
+  __syncthreads();
   if constexpr (!FUSED) {
-#pragma unroll
-    for (int j = 0; j < kBJ; ++j) {
-      const int64_t m = m0 + 64 * wt + 16 * j + (lane & 15);
-      if (m < a.M) {
-#pragma unroll
-        for (int i = 0; i < kBI; ++i) {
-          const int n = n0 + 128 * wr + 16 * i + 4 * (lane >> 4);
-          *reinterpret_cast<u32x2*>(a.kv + m * a.N + n) =
-              u32x2{pack_bf16x2(acc[i][j].x, acc[i][j].y), pack_bf16x2(acc[i][j].z, acc[i][j].w)};
-        }
-      }
-    }
+    kv_epilogue(a, lds, m0, n0, tid);
   } else {
     const int s = n0 / a.dim;  // a tile lies in one segment: dim is a multiple of 256
-    const int cbs = (n0 - s * a.dim) / kTN;
-    const int d0 = n0 - s * a.dim + 128 * wr;
-    if (cb == 0) count_bad_ids(a, m0, tid);
+    const int dseg = n0 - s * a.dim;
+    const int cbs = dseg / kTN;
     if (s < 4)
-      key_epilogue(acc, a, lds, &s_last, tb, m0, s, cbs, d0, tid);
+      key_epilogue(a, lds, tb, m0, s, cbs, dseg, tid);
     else
-      value_epilogue(acc, a, lds, tb, m0, cbs, d0, tid);
+      value_epilogue(a, lds, tb, m0, cbs, dseg, tid);
   }
 }
 
@@ -440,7 +467,9 @@ hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream)
   return hipLaunchKernel(fn, dim3(unsigned(tiles)), dim3(kThreads), params, kLds, stream);
 }
 
-size_t tiled_layout(TiledArgs* a, int64_t M, int dim) {
+// Control words of the fused schedule: header, per-(token block, stream) counters, gate slots,
+// partial sums.  All zero before and after every call.
+size_t tiled_control_layout(TiledArgs* a, int64_t M, int dim) {
   const int64_t n_tb = (M + kTM - 1) / kTM;
   const int n_vcb = dim / kTN;
   size_t off = 256 + size_t(n_tb) * 4 * 256;  // header, counters (one 256-byte line each)
@@ -459,19 +488,27 @@ size_t tiled_layout(TiledArgs* a, int64_t M, int dim) {
 
 }  // namespace
 
-bool tiled_shape_ok(int N, int K, int dim, int head_dim, int scale_block, bool fused) {
+bool tiled_shape_ok(int N, int K, int dim, bool fused) {
   if (N % kTN != 0 || K % kTK != 0) return false;
-  if (fused && (dim % kTN != 0 || head_dim % kTK != 0 || scale_block % 16 != 0)) return false;
+  if (fused && dim % kTN != 0) return false;
   return true;
 }
 
-size_t tiled_workspace_bytes(int64_t M, int dim) { return tiled_layout(nullptr, M, dim); }
+size_t tiled_control_bytes(int64_t M, int dim) { return tiled_control_layout(nullptr, M, dim); }
+
+size_t tiled_staging_bytes(int64_t M, int K) { return (size_t(M) * K * 2 + 255) & ~size_t(255); }
 
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream) { return launch_tiled_impl(a, false, stream); }
 
-hipError_t launch_forward_tiled(TiledArgs a, void* workspace, hipStream_t stream) {
+hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging,
+                                hipStream_t stream) {
+  GatherArgs ga = g;
+  ga.emb = reinterpret_cast<uint16_t*>(staging);
+  hipError_t e = launch_gather_dequant(ga, stream);
+  if (e != hipSuccess) return e;
   a.ws = workspace;
-  tiled_layout(&a, a.M, a.dim);
+  a.emb = reinterpret_cast<const uint16_t*>(staging);
+  tiled_control_layout(&a, a.M, a.dim);
   return launch_tiled_impl(a, true, stream);
 }
 

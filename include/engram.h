@@ -69,13 +69,23 @@ engram_status engram_layout_check(const engram_layout* layout);
 engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
 
 /* Bytes of workspace engram_forward needs for B x T tokens on the current device (0 on an
- * invalid layout).  The workspace must be zero-filled before its first use.  Every call leaves
- * all of it zero again (counters, gate slots and partial sums), so one workspace serves any
- * number of calls, with any layout and any B x T it is large enough for, on one stream without
- * clearing.  The exception is word 0, which counts cross-workgroup waits that timed out (0 in
- * correct operation); after a time-out the workspace must be zero-filled again.  Calls that
- * overlap in time must use different workspaces. */
+ * invalid layout).  The workspace holds control words at its start (counters, gate slots and
+ * partial sums) and, for token counts where the tiled schedule runs, a staging area for the
+ * dequantised rows in its last engram_forward_staging_bytes() bytes.  It must be zero-filled
+ * before its first use.  Every call leaves all control words zero again; the staging area's
+ * contents are unspecified after a call.  So one workspace serves any number of calls, with any
+ * layout and any B x T it is large enough for, on one stream without clearing, provided every
+ * call on it passes the same workspace_bytes (the control words of any call then lie below the
+ * staging area of every other).  The exception is word 0, which counts cross-workgroup waits
+ * that timed out (0 in correct operation); after a time-out the workspace must be zero-filled
+ * again.  Calls that overlap in time must use different workspaces. */
 size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, int64_t T);
+
+/* Bytes at the end of the workspace that engram_forward uses as a staging area for the
+ * dequantised rows (B x T x n_cols x head_dim bf16 plus alignment slack) for B x T tokens; 0
+ * where the fused weight-streaming schedule runs (small token counts), which keeps the rows on
+ * chip.  Included in engram_forward_workspace_bytes(). */
+size_t engram_forward_staging_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
 /* S1 + S2: row gather and dequantisation (engram-second page,
  * ParallelEngramEmbedding.forward, single shard; flatten as in Engram.forward).
@@ -119,7 +129,8 @@ engram_status engram_gate_apply(const engram_layout* layout, const uint16_t* x,
 
 /* The whole Engram forward in one call (engram-second page, Engram.forward): S1 - S6 with
  * the arguments above.  Key and value stay on chip; only small per-tile partial sums pass
- * through `workspace` (engram_forward_workspace_bytes).  out may equal x.  Results equal
+ * through `workspace` (engram_forward_workspace_bytes), and at large token counts the
+ * dequantised rows pass through its staging area.  out may equal x.  Results equal
  * engram_gate_apply(engram_kv_proj(engram_gather_dequant(...))) up to the summation order of
  * the gate reductions. */
 engram_status engram_forward(const engram_layout* layout, const uint16_t* x,

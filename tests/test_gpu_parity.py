@@ -404,24 +404,29 @@ def test_forward_tiled_tiny_dims_bad_ids_in_place():
     say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), ref))
 
 
-def test_workspace_all_zero_and_shared_across_schedules():
-    say("[gpu] workspace: all zero after calls, shared by the streaming and tiled schedules")
+def test_workspace_control_zero_and_shared_across_schedules():
+    say("[gpu] workspace: control words zero after calls, shared by the streaming and tiled "
+        "schedules and two tiled token counts")
     w_big, w_small = TILED_TINY, synth.small_variant(TILED_TINY, name="tiny_dims_b1_t40", B=1, T=40)
+    w_mid = synth.small_variant(TILED_TINY, name="tiny_dims_b1_t260", B=1, T=260)
     lay = layout(w_big)
-    n = max(eg.engram_forward_workspace_bytes(lay, w_big.B, w_big.T),
-            eg.engram_forward_workspace_bytes(lay, w_small.B, w_small.T))
+    cases = [w_big, w_small, w_mid]
+    n = max(eg.engram_forward_workspace_bytes(lay, w.B, w.T) for w in cases)
+    assert eg.engram_forward_staging_bytes(lay, w_small.B, w_small.T) == 0
+    assert eg.engram_forward_staging_bytes(lay, w_big.B, w_big.T) >= w_big.M * w_big.K * 2
     ws = torch.zeros(n, dtype=torch.uint8, device="cuda")
-    d_big, d_small = synth.device_inputs(w_big), synth.device_inputs(w_small)
+    devs = {w.name: synth.device_inputs(w) for w in cases}
     outs = []
-    for w, d in ((w_big, d_big), (w_small, d_small), (w_big, d_big), (w_small, d_small)):
-        outs.append(forward(w, d, ws=ws))
+    for w in (w_big, w_small, w_mid, w_big, w_small, w_mid):
+        outs.append(forward(w, devs[w.name], ws=ws))
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws).item()) == 0, w.name
-    fresh_big = forward(w_big, d_big, ws=torch.zeros_like(ws))
-    fresh_small = forward(w_small, d_small, ws=torch.zeros_like(ws))
+        # below the largest staging area, every byte is a control word of some call: all zero
+        ctrl = n - max(eg.engram_forward_staging_bytes(lay, v.B, v.T) for v in cases)
+        assert int(torch.count_nonzero(ws[:ctrl]).item()) == 0, w.name
+    fresh = [forward(w, devs[w.name], ws=torch.zeros_like(ws)) for w in cases]
     torch.cuda.synchronize()
-    assert torch.equal(outs[0], fresh_big) and torch.equal(outs[2], fresh_big)
-    assert torch.equal(outs[1], fresh_small) and torch.equal(outs[3], fresh_small)
+    for i in range(3):
+        assert torch.equal(outs[i], fresh[i]) and torch.equal(outs[i + 3], fresh[i]), cases[i].name
 
 
 @pytest.fixture(scope="module")
