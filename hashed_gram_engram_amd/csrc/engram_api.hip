@@ -271,7 +271,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
                : ENGRAM_E_HIP;
   }
   const int G = stream_grid(N, di.cus);
-  if ((N / 16 + G - 1) / G > l->dim / 16) return ENGRAM_E_LAYOUT;
+  if (stream_rows_per_group(N, G) > l->dim) return ENGRAM_E_LAYOUT;  // a workgroup spans <= 2 segments
   StreamArgs a;
   memset(&a, 0, sizeof(a));
   a.wkv = wkv;

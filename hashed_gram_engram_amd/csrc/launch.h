@@ -70,6 +70,8 @@ hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t s
 // stream_workspace_bytes() whose control words are zero (the kernel leaves them zero).
 size_t stream_workspace_bytes(int64_t M, int N, int grid);
 int stream_grid(int N, int num_cus);
+// Most rows of wkv one workgroup of the weight-streaming schedule owns.
+int stream_rows_per_group(int N, int G);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 
 // Arguments of the tiled kernels (256-token x 256-column tiles, for large token counts).

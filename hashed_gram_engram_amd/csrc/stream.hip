@@ -1,21 +1,25 @@
 // Weight-streaming wkv projection for small token counts (decode), alone or fused with the
 // row gather, the per-stream gate and the residual add.
 //
-// Schedule.  The N = (hc + 1) * dim output columns are cut into 16-column row blocks of the
-// wkv matrix ([N, K], K contiguous).  A persistent grid of G workgroups (one per CU) gives
-// workgroup w the contiguous row blocks [w * nrb / G, (w + 1) * nrb / G), so every byte of wkv
-// is read exactly once per 64-token block and the load is balanced to within one row block.
+// Schedule.  The N = (hc + 1) * dim output columns are the rows of the wkv matrix ([N, K], K
+// contiguous).  A persistent grid of G workgroups (one per CU) gives workgroup w the contiguous
+// rows [4 floor(w Q / G), 4 floor((w + 1) Q / G)) with Q = N / 4, so every byte of wkv is read
+// exactly once per 64-token block and the load is balanced to within four rows (25600 rows on
+// 256 CUs: exactly 100 each).  A workgroup's rows form 16-row blocks starting at its first row;
+// rows of a last, partial block past the workgroup's end are neither loaded from HBM (their
+// loads repeat the last row) nor written.
 // The four waves of a workgroup split K into four contiguous quarters; each wave multiplies its
 // quarter of the workgroup's rows against its quarter of the 64 token rows, and the four
 // K-partials are summed in a fixed order through LDS at the end.
 //
 // Two K loops feed the same reduction and epilogue:
 //  * wide (each K quarter a multiple of 128 features, head_dim a multiple of 128): weights are
-//    read 4 rows x 256 contiguous bytes per wave instruction -- HBM streams at close to its
-//    peak only with runs of this length -- and each 16-row x 128-feature unit is transposed
-//    through a small wave-private LDS tile into the MFMA fragment layout.  A whole chunk
-//    (all row blocks x 128 features) of loads stays in flight; the row-block count is a
-//    template constant so no load sits behind a branch.
+//    copied global -> LDS (global_load_lds_dwordx4) 4 rows x 256 contiguous bytes per wave
+//    instruction -- HBM streams at close to its peak only with runs of this length -- into a
+//    wave-private slot per row block, with the 16-byte chunks of each row permuted so that the
+//    MFMA fragment reads hit distinct banks.  A whole chunk (all row blocks x 128 features) of
+//    copies stays in flight without holding registers; the row-block count is a template
+//    constant so no load sits behind a branch.
 //  * narrow (any shape the library accepts): fragments are loaded in MFMA layout directly
 //    (16 rows x 64 bytes per instruction) with a ring of U steps in flight.
 // In the fused kernel the token operand is gathered: each lane loads the 8 fp8 codes and the
@@ -48,14 +52,33 @@ namespace {
 
 constexpr int kTB = 64;                          // tokens per token block
 constexpr int kRedBytes = 4 * 2 * 4 * 64 * 16;   // K-partial reduction buffer (two row blocks)
-constexpr int kTileRow = 272;                    // bytes per row of a transpose tile (256 + pad)
-constexpr int kTileBytes = 16 * kTileRow;        // one 16-row x 128-feature transpose tile
-constexpr int kTilesBytes = 4 * 2 * kTileBytes;  // two tiles per wave
+constexpr int kWBlk = 16 * 256;                  // LDS slot of one row block x 128 features
+constexpr int kTokBuf_ = 9 * 1024;               // fused wide loop: token buffer per wave
+// LDS in front of the staged hash ids: the weight slots of the wide loop (4 waves x nblk row
+// blocks), which the K-partial reduction reuses afterwards.
+// (The one-round K-partial reduction needs nblk x 16 KB: exactly the weight slots.)
+__host__ __device__ constexpr int wide_lds_bytes(int nblk, bool fused) {
+  return 4 * nblk * kWBlk + (fused ? 4 * kTokBuf_ : 0) > kRedBytes ? 4 * nblk * kWBlk + (fused ? 4 * kTokBuf_ : 0)
+                                                                  : kRedBytes;
+}
 
-__device__ __forceinline__ int rb_begin(int w, int nrb, int G) { return int(int64_t(w) * nrb / G); }
-// workgroup that owns row block rb
-__device__ __forceinline__ int owner_of_rb(int rb, int nrb, int G) {
-  return int((int64_t(rb + 1) * G - 1) / nrb);
+// First row of workgroup w (rows are dealt in groups of four: Q = N / 4 groups).
+__device__ __forceinline__ int row_begin(int w, int Q, int G) { return 4 * int(int64_t(w) * Q / G); }
+// workgroup that owns a row
+__device__ __forceinline__ int owner_of_row(int row, int Q, int G) {
+  return int((int64_t(row / 4 + 1) * G - 1) / Q);
+}
+
+// The rows of one workgroup: [r0, r1) in nblk blocks of 16 (the last one possibly partial).
+struct Rows {
+  int r0, r1, nblk;
+};
+__device__ __forceinline__ Rows rows_of(int w, int N, int G) {
+  Rows r;
+  r.r0 = row_begin(w, N / 4, G);
+  r.r1 = row_begin(w + 1, N / 4, G);
+  r.nblk = (r.r1 - r.r0 + 15) / 16;
+  return r;
 }
 
 // Eight fp8 codes (two dwords) times one fp32 scale -> eight bf16 (an MFMA operand).  NaN
@@ -112,13 +135,13 @@ struct NarrowSlot {
 
 template <int NRB, int U, bool FUSED>
 __device__ __forceinline__ void narrow_issue(NarrowSlot<NRB, U, FUSED>& sl, const StreamArgs& a, const int64_t* s_ids,
-                                             int64_t m0, int rb0, int cnt, int step, int lane, int wv) {
+                                             int64_t m0, const Rows& rw, int step, int lane, int wv) {
   const int f = wv * (a.K >> 2) + 32 * step + 8 * (lane >> 4);  // first of this lane's 8 features
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    const int ii = i < cnt ? i : cnt - 1;  // past the workgroup's count: re-read (cache hit)
-    const size_t row = size_t(rb0 + ii) * 16 + (lane & 15);
-    sl.w[i] = *reinterpret_cast<const u32x4*>(a.wkv + row * a.K + f);
+    int row = rw.r0 + 16 * i + (lane & 15);
+    row = row < rw.r1 ? row : rw.r1 - 1;  // past the workgroup's rows: re-read (cache hit)
+    sl.w[i] = *reinterpret_cast<const u32x4*>(a.wkv + size_t(row) * a.K + f);
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t) load_tok<FUSED>(sl.tok[t], a, s_ids, m0, t, f, lane);
@@ -126,12 +149,12 @@ __device__ __forceinline__ void narrow_issue(NarrowSlot<NRB, U, FUSED>& sl, cons
 
 template <int NRB, int U, bool FUSED>
 __device__ __forceinline__ void narrow_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
-                                            int64_t m0, int rb0, int cnt, int lane, int wv) {
+                                            int64_t m0, const Rows& rw, int lane, int wv) {
   const int nstep = (a.K >> 2) / 32;  // 32-feature steps per wave; a multiple of U
   NarrowSlot<NRB, U, FUSED> ring[U];
 #pragma unroll
   for (int p = 0; p < U; ++p) {
-    narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rb0, cnt, p, lane, wv);
+    narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rw, p, lane, wv);
     // pin the issue order: the compiler otherwise sinks ring loads into the next iteration
     asm volatile("" ::: "memory");
   }
@@ -146,7 +169,7 @@ __device__ __forceinline__ void narrow_loop(f32x4 (&acc)[NRB][4], const StreamAr
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(ring[p].w[i], bt[t], acc[i][t]);
       const int nxt = c0 + p + U < nstep ? c0 + p + U : nstep - 1;
-      narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rb0, cnt, nxt, lane, wv);
+      narrow_issue<NRB, U, FUSED>(ring[p], a, s_ids, m0, rw, nxt, lane, wv);
       asm volatile("" ::: "memory");
     }
   }
@@ -154,23 +177,32 @@ __device__ __forceinline__ void narrow_loop(f32x4 (&acc)[NRB][4], const StreamAr
 
 // ------------------------------------------------------------------------------ wide K loop
 // Chunk c of a wave covers features [q0 + 128 c, q0 + 128 c + 128) of its quarter q0.  Weight
-// unit (row block i, chunk c): instruction k in 0..3 loads rows 4k + lane/16 of the block, 16
-// bytes at feature 8 * (lane % 16) -- four rows of 256 contiguous bytes.  Through the tile each
-// lane then reads, for step s in 0..3, row lane % 16 at features 32 * (lane / 16) + 8 s: the
-// pairing of A and B rows along K is free, and this order gives every lane 32 contiguous token
-// features per chunk (two 16-byte code loads and one scale in the fused kernel).
+// unit (row block i, chunk c): copy instruction k in 0..3 fills LDS bytes [1024 k, 1024 k + 1024)
+// of the row block's slot, lane l at 16 l: row 4 k + l / 16 of the block, position l % 16, which
+// holds the 16-byte chunk (l % 16) ^ row -- four rows of 256 contiguous bytes from HBM.  Each
+// lane then reads, for step s in 0..3, row l % 16 at features 32 (l / 16) + 8 s (chunk
+// 4 (l / 16) + s, at position chunk ^ row): the pairing of A and B rows along K is free, and
+// this order gives every lane 32 contiguous token features per chunk (two 16-byte code loads
+// and one scale in the fused kernel).
 //
 // When `live` is false (the refill after the last chunk) the same instructions read the first
 // 256 bytes of rows 0..15 instead: a 4 KB cache-resident region, so no extra HBM traffic.
-__device__ __forceinline__ void wide_issue_w(u32x4 (&w)[4], const StreamArgs& a, int rb0, int i, int f_chunk,
-                                             bool live, int lane) {
-  const size_t rbase = live ? size_t(rb0 + i) * 16 : 0;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void wide_copy_w(char* slot, const StreamArgs& a, const Rows& rw, int i, int f_chunk,
+                                            bool live, int lane) {
+  const int rbase = live ? rw.r0 + 16 * i : 0;
+  const int rlast = live ? rw.r1 - 1 : 15;
   const size_t fbase = live ? size_t(f_chunk) : 0;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const size_t row = rbase + 4 * k + (lane >> 4);
-    w[k] = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(a.wkv + row * a.K + fbase + 8 * (lane & 15)));
+    const int rr = 4 * k + (lane >> 4);
+    const int r = rbase + rr;
+    const size_t row = size_t(r < rlast ? r : rlast);
+    const int chunk = (lane & 15) ^ rr;
+    // cache policy 2: non-temporal (each weight byte is read once)
+    __builtin_amdgcn_global_load_lds((const void*)(a.wkv + row * a.K + fbase + 8 * chunk),
+                                     (lds_ptr_t)(slot + k * 1024), 16, 0, 2);
   }
 }
 
@@ -223,56 +255,144 @@ __device__ __forceinline__ u32x4 wide_operand(const WideTok<FUSED>& tk, int t, i
   }
 }
 
+// Fused kernel: the gathered token codes and scales of one chunk are copied global -> LDS as
+// well, into a wave-private 9 KB buffer (copy 2 t + h: 16 codes of sub-block t per lane at
+// 1024 (2 t + h) + 16 lane; copy 8 + t: the lane's scale at 8192 + 256 t + 4 lane), so that the
+// K loop holds no register loads: the compiler would otherwise wait for every copy in flight
+// before each use of a token register.  `keep` marks lanes whose hash id names a table row.
+constexpr int kTokBuf = kTokBuf_;
+
+__device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], const StreamArgs& a,
+                                              const int64_t* s_ids, int f_chunk, int lane) {
+  const int f = f_chunk + 32 * (lane >> 4);
+  const int j = f / a.head_dim;
+  const int cc = f - j * a.head_dim;
+  const int nb = a.head_dim / a.scale_block;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
+    const int64_t rr = r >= 0 ? r : 0;
+    keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
+    const uint8_t* src = a.table + rr * a.head_dim + cc;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(tbuf + (2 * t) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src + 16), (lds_ptr_t)(tbuf + (2 * t + 1) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(a.scales + rr * nb + cc / a.scale_block),
+                                     (lds_ptr_t)(tbuf + 8192 + t * 256), 4, 0, 0);
+  }
+}
+
+// The 16 token operands of one chunk (steps s = 0..3 x sub-blocks t = 0..3) from the buffer.
+__device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char* tbuf, const uint32_t (&keep)[4],
+                                                  int lane) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const u32x4 c0 = *reinterpret_cast<const u32x4*>(tbuf + (2 * t) * 1024 + 16 * lane);
+    const u32x4 c1 = *reinterpret_cast<const u32x4*>(tbuf + (2 * t + 1) * 1024 + 16 * lane);
+    const float sc = *reinterpret_cast<const float*>(tbuf + 8192 + t * 256 + 4 * lane);
+    bt[0][t] = masked(dequant8(u32x2{c0.x, c0.y}, sc), keep[t]);
+    bt[1][t] = masked(dequant8(u32x2{c0.z, c0.w}, sc), keep[t]);
+    bt[2][t] = masked(dequant8(u32x2{c1.x, c1.y}, sc), keep[t]);
+    bt[3][t] = masked(dequant8(u32x2{c1.z, c1.w}, sc), keep[t]);
+  }
+}
+
+// Vector memory instructions of one chunk's token operands of a lane (fused: copies).
+template <bool FUSED>
+constexpr int kTokLoads = FUSED ? 12 : 16;
+
 template <int NRB, bool FUSED>
 __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
-                                          char* tiles, int64_t m0, int rb0, int lane, int wv) {
+                                          char* slots, int64_t m0, const Rows& rw, int lane, int wv) {
   const int q0 = wv * (a.K >> 2);
   const int nch = (a.K >> 2) / 128;
-  u32x4 W[NRB][4];
-  WideTok<FUSED> tk;
-  // prologue in the loop's issue order (tokens, then row blocks): the wait counts at the loop
-  // head are the smaller of the prologue's and the loop's
-  wide_issue_tok<FUSED>(tk, a, s_ids, m0, q0, lane);
+  char* my_slots = slots + wv * NRB * kWBlk;
+  char* my_tok = slots + 4 * NRB * kWBlk + wv * kTokBuf;  // fused only
+  WideTok<false> tk;       // dense only
+  uint32_t keep[4];        // fused only
+  // prologue in the loop's issue order (tokens, then row blocks)
+  if constexpr (FUSED) wide_copy_tok(my_tok, keep, a, s_ids, q0, lane);
+  else wide_issue_tok<false>(tk, a, s_ids, m0, q0, lane);
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    wide_issue_w(W[i], a, rb0, i, q0, true, lane);
+    wide_copy_w(my_slots + i * kWBlk, a, rw, i, q0, true, lane);
     asm volatile("" ::: "memory");
   }
-  char* my_tiles = tiles + wv * 2 * kTileBytes;
+  // Issue order per chunk c: the tokens of chunk c + 1, then (as row block i of chunk c is read)
+  // the copies of row block i of chunk c + 1.  So when row block i of chunk c is read, the
+  // copies of blocks i + 1 .. NRB - 1 of chunk c, the tokens of chunk c + 1 and the copies of
+  // blocks 0 .. i - 1 of chunk c + 1 -- always 4 (NRB - 1) + kTokLoads instructions -- may still
+  // be in flight.
+  constexpr int kInFlight = 4 * (NRB - 1) + kTokLoads<FUSED>;
+  static_assert(kInFlight <= 63, "vmcnt range");
+  const int fl = (lane & 15) * 256;  // this lane's fragment row in a slot
   for (int c = 0; c < nch; ++c) {
     const bool live = c + 1 < nch;
     const int fn = q0 + 128 * (live ? c + 1 : c);  // next chunk (tokens re-read the last one)
     u32x4 bt[4][4];
+    if constexpr (FUSED) {
+      // the token copies of chunk c have landed once only the weight copies of chunk c remain
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NRB) : "memory");
+      wide_tok_operands(bt, my_tok, keep, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
+      wide_copy_tok(my_tok, keep, a, s_ids, fn, lane);
+    } else {
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) bt[s][t] = wide_operand<FUSED>(tk, t, s);
-    wide_issue_tok<FUSED>(tk, a, s_ids, m0, fn, lane);
+        for (int t = 0; t < 4; ++t) bt[s][t] = wide_operand<false>(tk, t, s);
+      wide_issue_tok<false>(tk, a, s_ids, m0, fn, lane);
+    }
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-      char* tile = my_tiles + (i & 1) * kTileBytes;
+      char* slot = my_slots + i * kWBlk;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
+      u32x4 wf[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        *reinterpret_cast<u32x4*>(tile + (4 * k + (lane >> 4)) * kTileRow + 16 * (lane & 15)) = W[i][k];
-      wide_issue_w(W[i], a, rb0, i, fn, live, lane);
+      for (int s = 0; s < 4; ++s)
+        wf[s] = *reinterpret_cast<const u32x4*>(slot + fl + 16 * ((4 * (lane >> 4) + s) ^ (lane & 15)));
+      // the slot is read (into registers) before its next copy is issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wide_copy_w(slot, a, rw, i, fn, live, lane);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4 wf = *reinterpret_cast<const u32x4*>(tile + (lane & 15) * kTileRow + 16 * (4 * (lane >> 4) + s));
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf, bt[s][t], acc[i][t]);
-      }
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[s], bt[s][t], acc[i][t]);
       asm volatile("" ::: "memory");
     }
   }
+  // the refill copies after the last chunk land before the slots are reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------------------ per token block
-// Sums the four K-partials in wave order; afterwards wave wv holds token sub-block wv.
-template <int NRB>
+// Sums the four K-partials in wave order; afterwards wave wv holds token sub-block wv.  With
+// ONE_ROUND (X holds NRB x 16 KB: the wide loop's weight slots) all row blocks pass through LDS
+// at once, else two at a time.
+template <int NRB, bool ONE_ROUND>
 __device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4], f32x4* X, int cnt, int lane,
                                          int wv) {
+  if constexpr (ONE_ROUND) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+      if (i < cnt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) X[((i * 4 + wv) * 4 + t) * 64 + lane] = acc[i][t];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+      if (i < cnt) {
+        f32x4 s = X[((i * 4 + 0) * 4 + wv) * 64 + lane];
+        s += X[((i * 4 + 1) * 4 + wv) * 64 + lane];
+        s += X[((i * 4 + 2) * 4 + wv) * 64 + lane];
+        s += X[((i * 4 + 3) * 4 + wv) * 64 + lane];
+        red[i] = s;
+      }
+    __syncthreads();  // X overlaps the epilogue's shared words
+    return;
+  }
 #pragma unroll
   for (int r0 = 0; r0 < NRB; r0 += 2) {
     if (r0 < cnt) {
@@ -301,6 +421,35 @@ struct Shared {
   int last[2];
 };
 
+// Inputs of the key columns' partial sums, loaded before the K-partial reduction: per row block,
+// the lane's 4 features of x (token 16 wv + lane % 16, its stream) and the fp32 products q * k of
+// those features.
+template <int NRB>
+struct KeyPre {
+  u32x2 x[NRB];
+  f32x4 wq[NRB];
+};
+
+template <int NRB>
+__device__ __forceinline__ void prefetch_key(KeyPre<NRB>& kp, const StreamArgs& a, const Rows& rw, int64_t m0,
+                                             int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t m = m0 + 16 * wv + (lane & 15);
+  const int64_t mm = m < a.M ? m : a.M - 1;
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+    int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+    n = n < rw.r1 ? n : rw.r1 - 4;
+    int s = n / a.dim;
+    s = s < 4 ? s : 3;  // value columns: unused, any in-range address
+    const int d = n - (n / a.dim) * a.dim;
+    kp.x[i] = *reinterpret_cast<const u32x2*>(a.x + (mm * 4 + s) * a.dim + d);
+    const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
+    const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
+    kp.wq[i] = f32x4{q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
+  }
+}
+
 // Cross-workgroup control words: one counter per (token block, stream) on its own 256-byte
 // line (contended atomics on one line serialise).
 // The workspace holds one block per token block at a fixed stride (so, for one layout, every
@@ -323,14 +472,15 @@ __device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, 
 }
 
 template <int NRB, bool FUSED>
-__device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], Shared& sh, int64_t tb, int w,
-                                         int rb0, int cnt, int tid) {
+__device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], const KeyPre<NRB>& kp, Shared& sh,
+                                         int64_t tb, int w,
+                                         const Rows& rw, int tid) {
   const int lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x;
-  const int nrb = a.N >> 4;
-  const int R = a.dim >> 4;  // row blocks per stream segment
-  const int seg_lo = rb0 / R;
-  const int seg_hi = (rb0 + cnt - 1) / R;
+  const int Q = a.N >> 2;
+  const int cnt = rw.nblk;
+  const int seg_lo = rw.r0 / a.dim;
+  const int seg_hi = (rw.r1 - 1) / a.dim;
   const int64_t m0 = tb * kTB;
   const int tok = 16 * wv + (lane & 15);
   const int64_t m = m0 + tok;
@@ -339,12 +489,12 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
   if constexpr (!FUSED) {
     if (mvalid) {
 #pragma unroll
-      for (int i = 0; i < NRB; ++i)
-        if (i < cnt) {
-          const int n = (rb0 + i) * 16 + 4 * (lane >> 4);
+      for (int i = 0; i < NRB; ++i) {
+        const int n = rw.r0 + 16 * i + 4 * (lane >> 4);  // four columns, all in [r0, r1) or none
+        if (i < cnt && n < rw.r1)
           *reinterpret_cast<u32x2*>(a.kv + m * a.N + n) =
               u32x2{pack_bf16x2(red[i].x, red[i].y), pack_bf16x2(red[i].z, red[i].w)};
-        }
+      }
     }
     return;
   } else {
@@ -352,19 +502,17 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
     float pa[2] = {0.f, 0.f}, pk[2] = {0.f, 0.f}, pd[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-      if (i < cnt) {
-        const int rb = rb0 + i;
-        const int s = rb / R;
+      const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+      if (i < cnt && n < rw.r1) {
+        const int s = n / a.dim;  // dim is a multiple of 4: the lane's four columns share it
         if (s < 4) {
-          const int d = (rb - s * R) * 16 + 4 * (lane >> 4);
+          const int d = n - s * a.dim;
           const float key[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
                                 bf16_round(red[i].w)};
-          u32x2 xw = {0u, 0u};
-          if (mvalid) xw = *reinterpret_cast<const u32x2*>(a.x + (m * 4 + s) * a.dim + d);
-          const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
-          const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
+          (void)d;
+          const u32x2 xw = mvalid ? kp.x[i] : u32x2{0u, 0u};
           const float h[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
-          const float wq[4] = {q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
+          const float wq[4] = {kp.wq[i].x, kp.wq[i].y, kp.wq[i].z, kp.wq[i].w};
           float sa = 0.f, sk = 0.f, sd = 0.f;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -406,7 +554,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           const int s = seg_lo + sl;
           sh.last[sl] = 0;
           if (s <= seg_hi && s < 4) {
-            const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
+            const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
             const uint32_t old = atomic_add_relaxed(counter_of(a, tb, s), 1u);
             sh.last[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
           }
@@ -419,7 +567,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           __syncthreads();  // sh.red may still be read for the other stream
           // every contributor has posted: sum the partials in workgroup order
           const int s = seg_lo + sl;
-          const int wf = owner_of_rb(s * R, nrb, G), wl = owner_of_rb((s + 1) * R - 1, nrb, G);
+          const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
           const int nW = wl - wf + 1;
           const int t = tid & 63, q = tid >> 6;
           const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
@@ -431,7 +579,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
               const int w2 = base + k < wb1 ? base + k : wb0;
-              const int sl2 = s - rb_begin(w2, nrb, G) / R;
+              const int sl2 = s - row_begin(w2, Q, G) / a.dim;
               const float* P = partial_of(a, tb, w2, sl2) + t * 3;
               v[k][0] = load_coherent(P + 0);
               v[k][1] = load_coherent(P + 1);
@@ -467,7 +615,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           // this call is done with the counter; hand the 64 gates to every value workgroup in
           // its own slot, sign bit set as the ready mark (gates are >= 0)
           if (tid == 0) store_relaxed(counter_of(a, tb, s), 0u);
-          const int v0 = owner_of_rb(4 * R, nrb, G);
+          const int v0 = owner_of_row(4 * a.dim, Q, G);
           for (int i = tid; i < (G - v0) * kTB; i += 256) {
             const int v = v0 + i / kTB, tt = i % kTB;
             store_relaxed(gate_slot(a, tb, v, s) + tt, __float_as_uint(sh.red[0][tt][0]) | 0x80000000u);
@@ -475,7 +623,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           // the partials are consumed: leave them zero, so that the whole workspace is zero
           // again after the call (any schedule may use it next)
           for (int w2 = wb0; w2 < wb1; ++w2) {
-            float* P = partial_of(a, tb, w2, s - rb_begin(w2, nrb, G) / R) + t * 3;
+            float* P = partial_of(a, tb, w2, s - row_begin(w2, Q, G) / a.dim) + t * 3;
             store_coherent(P + 0, 0.0f);
             store_coherent(P + 1, 0.0f);
             store_coherent(P + 2, 0.0f);
@@ -490,8 +638,9 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       u32x2 xs[NRB][4];
 #pragma unroll
       for (int i = 0; i < NRB; ++i) {
-        if (i < cnt && (rb0 + i) / R == 4 && mvalid) {
-          const int d = (rb0 + i - 4 * R) * 16 + 4 * (lane >> 4);
+        const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+        if (i < cnt && n < rw.r1 && n / a.dim == 4 && mvalid) {
+          const int d = n - 4 * a.dim;
 #pragma unroll
           for (int s = 0; s < 4; ++s) xs[i][s] = *reinterpret_cast<const u32x2*>(a.x + size_t(m * 4 + s) * a.dim + d);
         }
@@ -521,8 +670,9 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       if (mvalid) {
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
-          if (i < cnt && (rb0 + i) / R == 4) {
-            const int d = (rb0 + i - 4 * R) * 16 + 4 * (lane >> 4);
+          const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+          if (i < cnt && n < rw.r1 && n / a.dim == 4) {
+            const int d = n - 4 * a.dim;
             const float v[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
                                 bf16_round(red[i].w)};
 #pragma unroll
@@ -545,24 +695,34 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 
 // One 64-token block: stage the hash ids, run the K loop, reduce, finish.
 template <int NRB, bool WIDE, int U, bool FUSED>
-__device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w, int rb0,
-                                            int cnt) {
+__device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w,
+                                            const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t m0 = tb * kTB;
-  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + kTilesBytes);
+  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + (WIDE ? wide_lds_bytes(NRB, FUSED) : kRedBytes));
+  KeyPre<NRB> kp;
   if constexpr (FUSED) {
-    // hash ids of the token block, checked once: -1 marks a row that reads as zeros
-    for (int i = tid; i < kTB * a.n_cols; i += 256) {
-      const int64_t m = m0 + i / a.n_cols;
-      int64_t r = -1;
-      if (m < a.M) {
-        r = a.hash_ids[m0 * a.n_cols + i];
-        if (r < 0 || r >= a.n_rows) {
+    // hash ids of the token block, checked once: -1 marks a row that reads as zeros.  Eight
+    // loads per thread are in flight at a time.
+    const int n_ids = kTB * a.n_cols;
+    const int64_t n_valid = (a.M - m0 < kTB ? a.M - m0 : kTB) * a.n_cols;
+    for (int base = 0; base < n_ids; base += 8 * 256) {
+      int64_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = base + q * 256 + tid;
+        v[q] = i < n_valid ? a.hash_ids[m0 * a.n_cols + i] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = base + q * 256 + tid;
+        int64_t r = v[q];
+        if (i < n_valid && (r < 0 || r >= a.n_rows)) {
           if (w == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
           r = -1;
         }
+        if (i < n_ids) s_ids[i] = r;
       }
-      s_ids[i] = r;
     }
     __syncthreads();
   }
@@ -571,11 +731,14 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WIDE) wide_loop<NRB, FUSED>(acc, a, s_ids, smem, m0, rb0, lane, wv);
-  else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rb0, cnt, lane, wv);
+  if constexpr (WIDE) wide_loop<NRB, FUSED>(acc, a, s_ids, smem, m0, rw, lane, wv);
+  else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rw, lane, wv);
+  // the key columns' epilogue inputs are loaded now, so that their latency hides under the
+  // K-partial reduction (loaded before the K loop they slow it down: registers)
+  if constexpr (FUSED) prefetch_key<NRB>(kp, a, rw, m0, tid);
   f32x4 red[NRB];
-  reduce_k<NRB>(red, acc, reinterpret_cast<f32x4*>(smem), cnt, lane, wv);
-  epilogue<NRB, FUSED>(a, red, sh, tb, w, rb0, cnt, tid);
+  reduce_k<NRB, WIDE>(red, acc, reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
+  epilogue<NRB, FUSED>(a, red, kp, sh, tb, w, rw, tid);
   __syncthreads();
 }
 
@@ -583,24 +746,31 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
 template <int NRB, int U, bool FUSED>
 __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ Shared sh;
-  const int G = gridDim.x, w = blockIdx.x, nrb = a.N >> 4;
-  const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
+  // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
+  Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
+  const int G = gridDim.x, w = blockIdx.x;
+  const Rows rw = rows_of(w, a.N, G);
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
-  for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, w, rb0, cnt);
+  for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, w, rw);
 }
 
-// Wide kernel: every workgroup has NLO or NLO + 1 row blocks, each compiled exactly.
-template <int NLO, bool FUSED>
+// Wide kernel: every workgroup has NLO or NHI = NLO + 1 row blocks, each compiled exactly (only
+// one path when every workgroup has the same count, so registers are sized for it alone).
+template <int NLO, int NHI, bool FUSED>
 __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ Shared sh;
-  const int G = gridDim.x, w = blockIdx.x, nrb = a.N >> 4;
-  const int rb0 = rb_begin(w, nrb, G), cnt = rb_begin(w + 1, nrb, G) - rb0;
+  // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
+  Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
+  const int G = gridDim.x, w = blockIdx.x;
+  const Rows rw = rows_of(w, a.N, G);
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   for (int64_t tb = 0; tb < n_tb; ++tb) {
-    if (cnt == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rb0, cnt);
-    else token_block<NLO + 1, true, 1, FUSED>(a, smem, sh, tb, w, rb0, cnt);
+    if constexpr (NLO == NHI) {
+      token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rw);
+    } else {
+      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rw);
+      else token_block<NHI, true, 1, FUSED>(a, smem, sh, tb, w, rw);
+    }
   }
 }
 
@@ -611,34 +781,47 @@ void* pick_narrow(int nstep) {
   return reinterpret_cast<void*>(&k_stream_narrow<NRB, 1, FUSED>);
 }
 
+template <int NLO, bool FUSED>
+void* pick_wide_n(bool same) {
+  return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED>)
+              : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED>);
+}
+
 template <bool FUSED>
-void* pick_wide(int nlo) {
+void* pick_wide(int nlo, int nhi) {
+  const bool same = nlo == nhi;
   switch (nlo) {
-    case 1: return reinterpret_cast<void*>(&k_stream_wide<1, FUSED>);
-    case 2: return reinterpret_cast<void*>(&k_stream_wide<2, FUSED>);
-    case 3: return reinterpret_cast<void*>(&k_stream_wide<3, FUSED>);
-    case 4: return reinterpret_cast<void*>(&k_stream_wide<4, FUSED>);
-    case 5: return reinterpret_cast<void*>(&k_stream_wide<5, FUSED>);
-    case 6: return reinterpret_cast<void*>(&k_stream_wide<6, FUSED>);
+    case 1: return pick_wide_n<1, FUSED>(same);
+    case 2: return pick_wide_n<2, FUSED>(same);
+    case 3: return pick_wide_n<3, FUSED>(same);
+    case 4: return pick_wide_n<4, FUSED>(same);
+    case 5: return pick_wide_n<5, FUSED>(same);
+    case 6: return pick_wide_n<6, FUSED>(same);
+    case 7: return pick_wide_n<7, FUSED>(same);
     default: return nullptr;
   }
 }
 
+// Fewest and most 16-row blocks of a workgroup (rows per workgroup: 4 floor(Q / G) or
+// 4 ceil(Q / G)).
+int min_blocks(int N, int G) { return (4 * ((N / 4) / G) + 15) / 16; }
+int max_blocks(int N, int G) { return (4 * ((N / 4 + G - 1) / G) + 15) / 16; }
+
 bool use_wide(const StreamArgs& a, int G, bool fused) {
-  const int nrb = a.N / 16;
   // a 128-feature chunk stays in one column and a lane's 32 features share one scale
   const bool hd_ok = !fused || (a.head_dim % 128 == 0 && a.scale_block % 32 == 0);
-  return (a.K / 4) % 128 == 0 && hd_ok && nrb / G >= 1 && nrb / G <= 6;
+  const int lo = min_blocks(a.N, G), hi = max_blocks(a.N, G);
+  return (a.K / 4) % 128 == 0 && hd_ok && lo >= 1 && lo <= 7 && hi <= lo + 1;
 }
 
 template <bool FUSED>
 hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
-  const int nrb = a.N / 16;
   void* fn = nullptr;
-  if (use_wide(a, G, FUSED)) {
-    fn = pick_wide<FUSED>(nrb / G);
+  const bool wide = use_wide(a, G, FUSED);
+  if (wide) {
+    fn = pick_wide<FUSED>(min_blocks(a.N, G), max_blocks(a.N, G));
   } else {
-    const int per_wg = (nrb + G - 1) / G;
+    const int per_wg = max_blocks(a.N, G);
     const int nstep = (a.K / 4) / 32;
     if (per_wg <= 1) fn = pick_narrow<FUSED, 1>(nstep);
     else if (per_wg <= 2) fn = pick_narrow<FUSED, 2>(nstep);
@@ -648,21 +831,44 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   if (fn == nullptr) return hipErrorInvalidValue;
   StreamArgs arg = a;
   void* params[] = {&arg};
-  const size_t lds = size_t(kTilesBytes) + (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
+  size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(a.N, G), FUSED) : kRedBytes) +
+               (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
+  if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
+  if (lds > 163840) return hipErrorInvalidValue;
+  if (lds > 65536) {
+    // above the default limit: raise it once per kernel (a kernel's need is fixed by its shape
+    // class, and the largest value set so far stays in force)
+    static void* raised[64];
+    static int raised_lds[64];
+    static int n_raised = 0;
+    int k = 0;
+    while (k < n_raised && raised[k] != fn) ++k;
+    if (k == n_raised || raised_lds[k] < int(lds)) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+      if (e != hipSuccess) return e;
+      if (k == n_raised && n_raised < 64) {
+        raised[n_raised] = fn;
+        raised_lds[n_raised++] = int(lds);
+      } else if (k < n_raised) {
+        raised_lds[k] = int(lds);
+      }
+    }
+  }
   return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
 }
 
-static_assert(kRedBytes <= kTilesBytes, "the reduction buffer reuses the transpose tiles");
 
 }  // namespace
 
 int stream_grid(int N, int num_cus) {
-  const int nrb = N / 16;
+  const int Q = N / 4;
   int G = num_cus;
-  if (G > nrb) G = nrb;
-  while ((nrb + G - 1) / G > 8) ++G;  // at most 8 row blocks per workgroup
+  if (G > Q) G = Q;
+  while (max_blocks(N, G) > 8) ++G;  // at most 8 row blocks per workgroup
   return G;
 }
+
+int stream_rows_per_group(int N, int G) { return 4 * ((N / 4 + G - 1) / G); }
 
 // Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
 // block at a fixed stride that depends only on the grid.

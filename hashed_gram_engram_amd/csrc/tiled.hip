@@ -45,14 +45,14 @@ namespace {
 constexpr int kThreads = 512;               // 8 waves
 constexpr int kTM = 256;                    // tokens per tile
 constexpr int kTN = 256;                    // wkv rows per tile
-constexpr int kTK = 32;                     // features per stage
-constexpr int kRowB = kTK * 2;              // bytes per LDS row: 4 chunks of 16 bytes
-constexpr int kOpB = 256 * kRowB;           // one operand of one stage (16 KB)
-constexpr int kStageB = 2 * kOpB;           // wkv rows, then tokens (32 KB)
-constexpr int kRing = 5;                    // stages in the ring
-constexpr int kAhead = kRing - 1;           // copies run this many stages ahead
-constexpr int kLds = kRing * kStageB;       // 160 KB, all of a CU's LDS
-constexpr int kCopies = 4;                  // copy instructions per wave per stage
+constexpr int kTK = 64;                     // features per stage
+constexpr int kRowB = kTK * 2;              // bytes per LDS row: 8 chunks of 16 bytes
+constexpr int kOpB = 256 * kRowB;           // one operand of one stage (32 KB)
+constexpr int kARing = 3;                   // wkv stages in LDS
+constexpr int kBRing = 2;                   // token stages in LDS
+constexpr int kBOff = kARing * kOpB;        // token ring offset
+constexpr int kLds = (kARing + kBRing) * kOpB;  // 160 KB, all of a CU's LDS
+constexpr int kCopies = 4;                  // copy instructions per wave per operand and stage
 constexpr int kBI = 8;                      // 16-column blocks per wave
 constexpr int kBJ = 4;                      // 16-token blocks per wave
 
@@ -61,39 +61,38 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Everything a wave needs to copy and read stages.
 struct Pipe {
-  const char* src[kCopies];  // per-lane global source of each copy at feature 0 (2 wkv, 2 token)
-  uint32_t frag_off;         // per-lane byte offset of a fragment read inside a 16-row block
-  int wv_u;                  // wave index (wave-uniform)
-  int a_off, b_off;          // byte offsets of this wave's first wkv row and first token row
+  const char* a_src[kCopies];  // per-lane global source of each wkv copy at feature 0
+  const char* b_src[kCopies];  // the same for the token copies
+  uint32_t frag_off[2];        // per-lane byte offset of a fragment read (stage half 0, 1)
+  int wv_u;                    // wave index (wave-uniform)
+  int a_off, b_off;            // byte offsets of this wave's first wkv row and first token row
 };
 
-// Copies of this wave for stage t into ring slot `slot`: wkv row groups 2 w, 2 w + 1 and token
-// row groups 2 w, 2 w + 1 (16 rows each).  Instruction g fills LDS bytes [1024 g, 1024 g + 1024)
-// of its operand, lane l at 16 l: row g * 16 + (l >> 2), position l & 3, which holds chunk
-// (l & 3) ^ (((l >> 2) >> 1) & 3).
-__device__ __forceinline__ void copy_stage(const Pipe& p, char* lds, int slot, int t) {
-  char* st = lds + slot * kStageB;
+// This wave's copies of one operand of stage t into `dst` (one ring slot): row groups
+// 4 w .. 4 w + 3 of 8 rows.  Instruction g fills LDS bytes [1024 g, 1024 g + 1024) of the
+// slot, lane l at 16 l: row 8 g + (l >> 3), position l & 7, which holds chunk
+// (l & 7) ^ (l >> 3), i.e. row r keeps chunk c at position c ^ (r & 7).
+__device__ __forceinline__ void copy_op(const char* const (&src)[kCopies], char* dst, int wv_u, int t) {
   const size_t k_bytes = size_t(t) * (kTK * 2);
 #pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
-    const int op = i >> 1, g = 2 * p.wv_u + (i & 1);
-    __builtin_amdgcn_global_load_lds((const void*)(p.src[i] + k_bytes), (lds_ptr_t)(st + op * kOpB + g * 1024), 16,
+  for (int i = 0; i < kCopies; ++i)
+    __builtin_amdgcn_global_load_lds((const void*)(src[i] + k_bytes), (lds_ptr_t)(dst + (4 * wv_u + i) * 1024), 16,
                                      0, 0);
-  }
 }
 
-// The 12 fragments of one stage for this wave: F[i] = wkv rows 16 i .. 16 i + 15 of the wave's
-// 128, F[8 + j] = tokens 16 j .. 16 j + 15 of its 64.  Lane l gets row l & 15, features
-// 8 (l >> 4) .. + 7 of the stage (the MFMA operand layout).
-__device__ __forceinline__ void read_frags(u32x4 (&F)[12], const Pipe& p, const char* lds, int slot) {
-  const char* st = lds + slot * kStageB + p.frag_off;
+// The 12 fragments of one half (32 features) of a stage for this wave: F[i] = wkv rows
+// 16 i .. 16 i + 15 of the wave's 128, F[8 + j] = tokens 16 j .. 16 j + 15 of its 64.  Lane l
+// gets row l & 15, features 32 hh + 8 (l >> 4) .. + 7 of the stage (the MFMA operand layout).
+__device__ __forceinline__ void read_frags(u32x4 (&F)[12], const Pipe& p, const char* A, const char* B, int hh) {
+  const char* a = A + p.a_off + p.frag_off[hh];
+  const char* b = B + p.b_off + p.frag_off[hh];
 #pragma unroll
-  for (int i = 0; i < kBI; ++i) F[i] = *reinterpret_cast<const u32x4*>(st + p.a_off + i * 1024);
+  for (int i = 0; i < kBI; ++i) F[i] = *reinterpret_cast<const u32x4*>(a + i * 16 * kRowB);
 #pragma unroll
-  for (int j = 0; j < kBJ; ++j) F[kBI + j] = *reinterpret_cast<const u32x4*>(st + kOpB + p.b_off + j * 1024);
+  for (int j = 0; j < kBJ; ++j) F[kBI + j] = *reinterpret_cast<const u32x4*>(b + j * 16 * kRowB);
 }
 
-__device__ __forceinline__ void stage_mma(TileAcc& acc, const u32x4 (&F)[12]) {
+__device__ __forceinline__ void half_mma(TileAcc& acc, const u32x4 (&F)[12]) {
 #pragma unroll
   for (int i = 0; i < kBI; ++i)
 #pragma unroll
@@ -108,55 +107,86 @@ __device__ __forceinline__ void phase_end() {
 }
 template <int N>
 __device__ __forceinline__ void wait_copies() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_frags() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ int next_slot(int s) { return s + 1 == kRing ? 0 : s + 1; }
+// Copy batch J: the operand with two ring slots for stage J + 1, then the one with three for
+// stage J + 2 (stages past the last repeat the last).
+__device__ __forceinline__ void copy_batch(const Pipe& p, char* lds, int J, int S) {
+  const int t1 = J + 1 < S ? J + 1 : S - 1, t2 = J + 2 < S ? J + 2 : S - 1;
+  if constexpr (kARing == 2) {
+    copy_op(p.a_src, lds + ((J + 1) % kARing) * kOpB, p.wv_u, t1);
+    copy_op(p.b_src, lds + kBOff + ((J + 2) % kBRing) * kOpB, p.wv_u, t2);
+  } else {
+    copy_op(p.b_src, lds + kBOff + ((J + 1) % kBRing) * kOpB, p.wv_u, t1);
+    copy_op(p.a_src, lds + ((J + 2) % kARing) * kOpB, p.wv_u, t2);
+  }
+}
 
-// The K loop of group G.  Copies past the last stage repeat the last stage (into a slot no
-// stage in use occupies), so that every wave issues the same number of copies per phase and the
-// wait counts above stay exact; the same holds for group 0's fragment reads after the last
-// stage.
+// The K loop of group G over S stages of 64 features (halves h = 0 .. 2 S - 1 of 32).
+//   group 0: phase 2 h multiplies half h, phase 2 h + 1 reads the fragments of half h + 1;
+//   group 1: phase 2 h reads the fragments of half h, phase 2 h + 1 multiplies it.
+// Copy batch J (tokens of stage J + 1 into token slot (J + 1) % 2, wkv of stage J + 2 into wkv
+// slot (J + 2) % 3) is issued by every wave in phase 4 J - 1: both slots held stage J - 1,
+// whose last fragments were read in phase 4 J - 2.  At the end of phase 4 J + 2 every wave
+// waits until only its wkv copies of batch J are in flight, so the tokens of stage J + 1 and
+// the wkv rows of stage J + 1 (batch J - 1) have landed before their first reader (group 0,
+// phase 4 J + 3).  Copies past the last stage repeat the last stage into a free slot, so the
+// wait counts hold in every phase.
 template <int G>
 __device__ __forceinline__ void k_loop(TileAcc& acc, const Pipe& p, char* lds, int S) {
   u32x4 F[12];
-  // prologue: group 0 copies stages 0 .. 4, group 1 stages 0 .. 3; stage 0 lands
-  constexpr int kPro = G == 0 ? kAhead + 1 : kAhead;
-#pragma unroll
-  for (int t = 0; t < kPro; ++t) copy_stage(p, lds, t, t < S ? t : S - 1);
-  wait_copies<(kPro - 1) * kCopies>();
+  // prologue (phase -1): stage 0, wkv stage 1, batch 0; stage 0 lands
+  copy_op(p.a_src, lds, p.wv_u, 0);
+  copy_op(p.b_src, lds + kBOff, p.wv_u, 0);
+  if constexpr (kARing == 3)
+    copy_op(p.a_src, lds + kOpB, p.wv_u, S > 1 ? 1 : 0);
+  else
+    copy_op(p.b_src, lds + kBOff + kOpB, p.wv_u, S > 1 ? 1 : 0);
+  copy_batch(p, lds, 0, S);
+  wait_copies<3 * kCopies>();
   phase_end();
   if constexpr (G == 0) {
-    read_frags(F, p, lds, 0);
+    read_frags(F, p, lds, lds + kBOff, 0);
     wait_frags();
   }
   phase_end();
-  int rd = G == 0 ? 1 : 0;        // ring slot of the next stage to read
-  int cp = G == 0 ? 0 : kAhead;   // ring slot of the next stage to copy
-  for (int s = 0; s < S; ++s) {
+  int sa = 0, sb = 0;  // ring slots of stage J
+  for (int J = 0; J < S; ++J) {
+    const char* A = lds + sa * kOpB;
+    const char* B = lds + kBOff + sb * kOpB;
+    const int na = sa + 1 == kARing ? 0 : sa + 1, nb = sb + 1 == kBRing ? 0 : sb + 1;  // stage J + 1
     if constexpr (G == 0) {
-      stage_mma(acc, F);                    // phase 2 s: stage s
-      __builtin_amdgcn_sched_barrier(0);    // (the wait goes after every MFMA is issued)
-      wait_copies<3 * kCopies>();           // this wave's share of stage s + 1 has landed
+      half_mma(acc, F);                                           // 4 J: half 2 J
       phase_end();
-      const int tc = s + kAhead + 1;        // phase 2 s + 1: load stage s + 1 (after the last
-      copy_stage(p, lds, cp, tc < S ? tc : S - 1);  // stage, fragments nobody uses)
-      read_frags(F, p, lds, rd);
+      read_frags(F, p, A, B, 1);                                  // 4 J + 1: read half 2 J + 1
+      wait_frags();
+      phase_end();
+      half_mma(acc, F);                                           // 4 J + 2: half 2 J + 1
+      wait_copies<kCopies>();
+      phase_end();
+      copy_batch(p, lds, J + 1, S);                               // 4 J + 3: read half 2 J + 2
+      read_frags(F, p, lds + na * kOpB, lds + kBOff + nb * kOpB, 0);
       wait_frags();
       phase_end();
     } else {
-      const int tc = s + kAhead;            // phase 2 s: load stage s
-      copy_stage(p, lds, cp, tc < S ? tc : S - 1);
-      read_frags(F, p, lds, rd);
+      read_frags(F, p, A, B, 0);                                  // 4 J: read half 2 J
       wait_frags();
-      wait_copies<3 * kCopies>();           // this wave's share of stage s + 1 has landed
       phase_end();
-      stage_mma(acc, F);                    // phase 2 s + 1: stage s
+      half_mma(acc, F);                                           // 4 J + 1: half 2 J
+      phase_end();
+      read_frags(F, p, A, B, 1);                                  // 4 J + 2: read half 2 J + 1
+      wait_frags();
+      wait_copies<kCopies>();
+      phase_end();
+      copy_batch(p, lds, J + 1, S);                               // 4 J + 3: half 2 J + 1
+      half_mma(acc, F);
       phase_end();
     }
-    rd = next_slot(rd);
-    cp = next_slot(cp);
+    sa = na;
+    sb = nb;
   }
   // the repeated copies may still be landing: every copy done before LDS is reused
   wait_copies<0>();
@@ -169,20 +199,21 @@ __device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char
   Pipe p;
   p.wv_u = __builtin_amdgcn_readfirstlane(wv);
   {
-    const int rr = lane >> 2, chunk = (lane & 3) ^ ((rr >> 1) & 3);
+    const int rr = lane >> 3, chunk = (lane & 7) ^ rr;
     const size_t row_bytes = size_t(a.K) * 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int r = (2 * p.wv_u + i) * 16 + rr;  // row of the tile
-      p.src[i] = reinterpret_cast<const char*>(a.wkv) + size_t(n0 + r) * row_bytes + 16 * chunk;
+    for (int i = 0; i < kCopies; ++i) {
+      const int r = (4 * p.wv_u + i) * 8 + rr;  // row of the tile
+      p.a_src[i] = reinterpret_cast<const char*>(a.wkv) + size_t(n0 + r) * row_bytes + 16 * chunk;
       int64_t m = m0 + r;
       m = m < a.M ? m : a.M - 1;  // rows past the last token repeat it (their results are dropped)
-      p.src[2 + i] = reinterpret_cast<const char*>(a.emb) + size_t(m) * row_bytes + 16 * chunk;
+      p.b_src[i] = reinterpret_cast<const char*>(a.emb) + size_t(m) * row_bytes + 16 * chunk;
     }
   }
   {
     const int r = lane & 15;
-    p.frag_off = uint32_t(r * kRowB + 16 * ((lane >> 4) ^ ((r >> 1) & 3)));
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) p.frag_off[hh] = uint32_t(r * kRowB + 16 * ((4 * hh + (lane >> 4)) ^ (r & 7)));
   }
   p.a_off = (wv >> 2) * 128 * kRowB;
   p.b_off = (wv & 3) * 64 * kRowB;
@@ -488,7 +519,7 @@ size_t tiled_control_layout(TiledArgs* a, int64_t M, int dim) {
 
 }  // namespace
 
-bool tiled_shape_ok(int N, int K, int dim, bool fused) {
+bool tiled_shape_ok(int N, int K, int dim, bool fused) {  // K: stages of 64 features
   if (N % kTN != 0 || K % kTK != 0) return false;
   if (fused && dim % kTN != 0) return false;
   return true;
