@@ -38,10 +38,16 @@ TILED_MIN_TOKENS = 256  # the library's switch from weight streaming to 256 x 25
 
 
 def kernel_of(w):
-    """(profile name, sources) of the kernel that engram_forward runs for this workload."""
+    """(profile name, sources) of the kernels that engram_forward runs for this workload: the
+    fused weight-streaming kernel for small token counts; for large ones the row gather into the
+    staging area followed by the fused tiled kernel (timed together: one forward)."""
     if w.M >= TILED_MIN_TOKENS:
-        return "k_tiled_fused", ("tiled.hip", "common.h")
+        return "k_tiled_fused", ("tiled.hip", "gather_gate.hip", "common.h")
     return "k_stream_wide_fused", ("stream.hip", "common.h")
+
+
+KERNEL_LABEL = {"k_tiled_fused": "k_gather_dequant + k_tiled<true> (one forward)",
+                "k_stream_wide_fused": "k_stream_wide<.., true>"}
 
 
 def measured_traffic(w):
@@ -159,7 +165,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(w)}
-    roof["kernel"] = kernel_of(w)[0]
+    roof["kernel"] = KERNEL_LABEL[kernel_of(w)[0]]
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
     roof["ms_per_launch"] = round(ms, 5)
