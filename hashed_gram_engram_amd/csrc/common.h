@@ -113,6 +113,21 @@ __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same for 16-byte records at byte offset `off` from a wave-uniform base (one
+// buffer_store / buffer_load_dwordx4 with the agent-coherent cache policy, sc1): one memory
+// transaction per lane instead of four.  Readers only read records whose writers have
+// finished (ordered by a counter), so the 16 bytes need no atomicity.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(0x7FFFFFFF), 0x00020000);
+}
+constexpr int kCpolSc1 = 16;  // cache policy bit: coherent at agent scope
+__device__ __forceinline__ void store_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolSc1);
+}
+__device__ __forceinline__ f32x4 load_coherent4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolSc1));
+}
+
 // Waits until every memory operation this wave has issued is complete (stores acknowledged by
 // their destination).  Followed by a workgroup barrier, it orders all coherent stores of the
 // workgroup before any access that one thread issues after the barrier.

@@ -102,7 +102,7 @@ const char* engram_status_str(engram_status s) {
 engram_status engram_layout_check(const engram_layout* l) {
   if (l == nullptr) return ENGRAM_E_NULL;
   if (l->hc != 4) return ENGRAM_E_LAYOUT;
-  if (l->dim <= 0 || l->dim % 64 != 0) return ENGRAM_E_LAYOUT;
+  if (l->dim <= 0 || l->dim % 64 != 0 || l->dim > (1 << 22)) return ENGRAM_E_LAYOUT;
   if (l->n_cols <= 0 || l->head_dim <= 0 || l->head_dim % 64 != 0) return ENGRAM_E_LAYOUT;
   if (l->scale_block <= 0 || l->scale_block % 16 != 0 || l->head_dim % l->scale_block != 0)
     return ENGRAM_E_LAYOUT;

@@ -63,10 +63,11 @@ __host__ __device__ constexpr int wide_lds_bytes(int nblk, bool fused) {
 }
 
 // First row of workgroup w (rows are dealt in groups of four: Q = N / 4 groups).
-__device__ __forceinline__ int row_begin(int w, int Q, int G) { return 4 * int(int64_t(w) * Q / G); }
+// (32-bit arithmetic: the host keeps G * Q below 2^32.)
+__device__ __forceinline__ int row_begin(int w, int Q, int G) { return 4 * int(uint32_t(w) * uint32_t(Q) / uint32_t(G)); }
 // workgroup that owns a row
 __device__ __forceinline__ int owner_of_row(int row, int Q, int G) {
-  return int((int64_t(row / 4 + 1) * G - 1) / Q);
+  return int((uint32_t(row / 4 + 1) * uint32_t(G) - 1u) / uint32_t(Q));
 }
 
 // The rows of one workgroup: [r0, r1) in nblk blocks of 16 (the last one possibly partial).
@@ -454,16 +455,19 @@ __device__ __forceinline__ void prefetch_key(KeyPre<NRB>& kp, const StreamArgs& 
 // line (contended atomics on one line serialise).
 // The workspace holds one block per token block at a fixed stride (so, for one layout, every
 // control word sits at the same offset whatever the token count):
-//   [4 counters, 256 B apart][gate slots: grid x 4 x 64 words][partials: grid x 2 x 64 x 3]
+//   [4 counters, 256 B apart][gate slots: grid x 4 x 64 words][partials: grid x 2 x 64 x 16 B]
 __device__ __forceinline__ uint32_t* tb_block(const StreamArgs& a, int64_t tb) {
   return reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.ws_hdr) + 256 + size_t(tb) * a.tb_stride);
 }
 __device__ __forceinline__ uint32_t* counter_of(const StreamArgs& a, int64_t tb, int s) {
   return tb_block(a, tb) + s * 64;
 }
-__device__ __forceinline__ float* partial_of(const StreamArgs& a, int64_t tb, int w, int sl) {
-  return reinterpret_cast<float*>(tb_block(a, tb) + 256 + size_t(gridDim.x) * 4 * kTB) +
-         (size_t(w) * 2 + sl) * (kTB * 3);
+// Partial sums of workgroup w for its stream slot sl: 64 records of 16 bytes (|h|^2, |key|^2,
+// h q k key, 0), as a byte offset from the workspace start (they are accessed through a buffer
+// resource on it).
+__device__ __forceinline__ uint32_t partial_off(const StreamArgs& a, int64_t tb, int w, int sl) {
+  return uint32_t(256 + size_t(tb) * a.tb_stride + (256 + size_t(gridDim.x) * 4 * kTB) * 4 +
+                  (size_t(w) * 2 + sl) * (kTB * 16));
 }
 // Gate slot of value workgroup w for stream s: 64 words, written once by the stream's last
 // arriver (value bits with the sign bit set), read and cleared by w alone.
@@ -478,6 +482,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
   const int lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x;
   const int Q = a.N >> 2;
+  const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
   const int cnt = rw.nblk;
   const int seg_lo = rw.r0 / a.dim;
   const int seg_hi = (rw.r1 - 1) / a.dim;
@@ -539,10 +544,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
         for (int sl = 0; sl < 2; ++sl) {
           if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
-            float* P = partial_of(a, tb, w, sl) + tok * 3;
-            store_coherent(P + 0, pa[sl]);
-            store_coherent(P + 1, pk[sl]);
-            store_coherent(P + 2, pd[sl]);
+            store_coherent4(wsr, partial_off(a, tb, w, sl) + tok * 16, f32x4{pa[sl], pk[sl], pd[sl], 0.f});
           }
         }
       }
@@ -575,22 +577,19 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           // memory round trip per group, not one per contributor); sums stay in order
           float ra = 0.f, rk = 0.f, rd = 0.f;
           for (int base = wb0; base < wb1; base += 16) {
-            float v[16][3];
+            f32x4 v[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
               const int w2 = base + k < wb1 ? base + k : wb0;
               const int sl2 = s - row_begin(w2, Q, G) / a.dim;
-              const float* P = partial_of(a, tb, w2, sl2) + t * 3;
-              v[k][0] = load_coherent(P + 0);
-              v[k][1] = load_coherent(P + 1);
-              v[k][2] = load_coherent(P + 2);
+              v[k] = load_coherent4(wsr, partial_off(a, tb, w2, sl2) + t * 16);
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
               if (base + k < wb1) {
-                ra += v[k][0];
-                rk += v[k][1];
-                rd += v[k][2];
+                ra += v[k].x;
+                rk += v[k].y;
+                rd += v[k].z;
               }
             }
           }
@@ -623,10 +622,8 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           // the partials are consumed: leave them zero, so that the whole workspace is zero
           // again after the call (any schedule may use it next)
           for (int w2 = wb0; w2 < wb1; ++w2) {
-            float* P = partial_of(a, tb, w2, s - row_begin(w2, Q, G) / a.dim) + t * 3;
-            store_coherent(P + 0, 0.0f);
-            store_coherent(P + 1, 0.0f);
-            store_coherent(P + 2, 0.0f);
+            store_coherent4(wsr, partial_off(a, tb, w2, s - row_begin(w2, Q, G) / a.dim) + t * 16,
+                            f32x4{0.f, 0.f, 0.f, 0.f});
           }
         }
       }
@@ -647,11 +644,21 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       }
       __syncthreads();  // sh.red may still be read by a last-arriver hand-off above
       {
-        // thread (s, t) waits for gate t of stream s in this workgroup's slot, then clears it
+        // thread (s, t) waits for gate t of stream s in this workgroup's slot, then clears it.
+        // Only lane 0 of the stream's wave polls until the first word arrives (the stream's last
+        // arriver writes all 64 words together): a whole workgroup polling device-coherent
+        // words would load the memory path the hand-off itself takes.
         const int s = tid >> 6, t = tid & 63;
         uint32_t* slot = gate_slot(a, tb, w, s) + t;
         uint32_t bits = 0u;
         uint32_t it = 0;
+        if (t == 0) {
+          while (load_relaxed(slot) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (++it > a.spin_budget) break;
+          }
+          it = 0;
+        }
         while ((bits = load_relaxed(slot)) == 0u) {
           __builtin_amdgcn_s_sleep(2);
           if (++it > a.spin_budget) {
@@ -873,7 +880,7 @@ int stream_rows_per_group(int N, int G) { return 4 * ((N / 4 + G - 1) / G); }
 // Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
 // block at a fixed stride that depends only on the grid.
 size_t stream_tb_stride(int grid) {
-  return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 3 * 4;
+  return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 16;
 }
 
 size_t stream_workspace_bytes(int64_t M, int N, int grid) {

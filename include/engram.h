@@ -13,7 +13,7 @@
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream).  Arguments are
  *    checked synchronously on the host first; on any error nothing is enqueued and a
  *    negative status is returned.  B * T == 0 is a no-op returning ENGRAM_OK.
- *  - hc must be 4; dim a multiple of 64; head_dim a multiple of 64 and of scale_block;
+ *  - hc must be 4; dim a multiple of 64 and at most 2^22; head_dim a multiple of 64 and of scale_block;
  *    scale_block a multiple of 16; n_cols * head_dim a multiple of 128.
  *  - Hash ids outside [0, n_rows) read as an all-zero row (a single-shard
  *    ParallelEngramEmbedding zero-fills rows it does not hold); when err_count is not NULL
