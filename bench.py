@@ -1,10 +1,15 @@
 """Engram forward benchmark on one MI355X.
 
 One step = one engram_forward call (row gather + dequantisation, wkv projection, per-stream
-gate, residual add) over one batch of seeded synthetic inputs already resident in HBM.
+gate, residual add) over one batch of seeded synthetic inputs already resident in HBM; for the
+two-instance workloads, two calls, the second consuming the first one's output.
 Prints one JSON line.  `value` is tokens per second of the whole job (one GPU).
 
   python bench.py [--steps K] [--warmup W] [--workload decode_b64|prefill_t8192|...]
+                  [--flush-mib F]
+
+With --flush-mib, F MiB are written between steps (evicting the L2s and the Infinity Cache) and
+each step is timed by its own event pair.
 """
 import argparse
 import json
@@ -72,7 +77,8 @@ def measured_traffic(w):
 
 
 def cpu_baseline(w, n_tokens: int):
-    """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload."""
+    """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload (every
+    instance of it in turn, each consuming the previous one's output)."""
     import oracle
     import synth
     try:
@@ -81,16 +87,19 @@ def cpu_baseline(w, n_tokens: int):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     sel = np.arange(n_tokens)
-    wkv = w.wkv_f32()
-    ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
     mask = w.token_mask().reshape(-1)[sel]
     x = w.x_tokens(sel)
-    q, k = w.qk()
-    fetch = synth.host_fetch(w)
-    t0 = time.perf_counter()
-    oracle.forward(x, ids, mask, fetch, w.n_rows, w.head_dim, w.scale_block, wkv, q, k,
-                   eps=w.eps, clamp=w.clamp)
-    dt = time.perf_counter() - t0
+    dt = 0.0
+    for inst in range(w.n_instances):
+        wkv = w.wkv_f32(inst)
+        ids = w.hash_ids(inst).reshape(w.M, w.n_cols)[sel]
+        q, k = w.qk(inst)
+        fetch = synth.host_fetch(w, inst)
+        t0 = time.perf_counter()
+        x = oracle.forward(x, ids, mask, fetch, w.n_rows, w.head_dim, w.scale_block, wkv, q, k,
+                           eps=w.eps, clamp=w.clamp)["out_bits"]
+        dt += time.perf_counter() - t0
+        del wkv
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {n_tokens} tokens of {w.name} (full layer dims, fp64 numpy), "
                       f"{dt:.2f} s"}
@@ -104,6 +113,8 @@ def main():
     ap.add_argument("--workload", default="decode_b64")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write this many MiB between steps and time each step alone")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (scales HBM byte counters)")
     args = ap.parse_args()
@@ -126,49 +137,67 @@ def main():
 
     w = synth.get(args.workload)
     torch.cuda.set_device(0)
-    d = synth.device_inputs(w)
+    insts = []
+    for inst in range(w.n_instances):
+        d = synth.device_inputs(w, inst=inst)
+        if inst:
+            del d["x"]  # a later instance reads the previous one's output
+        insts.append(d)
+    x0 = insts[0]["x"]
     lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
     ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
                      device="cuda")
-    out = torch.empty_like(d["x"])
+    outs = [torch.empty_like(x0) for _ in insts]
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda")
+             if args.flush_mib else None)
 
     def step():
-        eg.engram_forward(lay, d["x"], d["hash_ids"], d["token_mask"], d["table"], d["scales"],
-                          d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws, err_count=err)
+        x = x0
+        for d, out in zip(insts, outs):
+            eg.engram_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                              d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws,
+                              err_count=err)
+            x = out
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
+            ev[2 * i].record(stream)
         step()
-        ev[i + 1].record(stream)
+        ev[2 * i + 1].record(stream)
+        if flush is None:
+            ev[2 * i + 2] = ev[2 * i + 1]
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per_launch_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    ms = float(np.mean(per_launch_ms))
+    per_step_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    ms = float(np.mean(per_step_ms))
+    ms_launch = ms / w.n_instances
     assert int(err.item()) == 0, "hash ids out of range"
     assert int(ws[:4].view(torch.int32).item()) == 0, "a cross-workgroup wait timed out"
 
     mode = "hbm" if w.M <= 512 else "mfma"
     if mode == "hbm":
-        ach = algorithmic_bytes(w) / (ms * 1e-3) / 1e9
+        ach = algorithmic_bytes(w) / (ms_launch * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w)}
     else:
-        ach = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+        ach = algorithmic_flops(w) / (ms_launch * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(w)}
     roof["kernel"] = KERNEL_LABEL[kernel_of(w)[0]]
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
-    roof["ms_per_launch"] = round(ms, 5)
+    roof["ms_per_launch"] = round(ms_launch, 5)
 
     res = {
         "metric": "Engram forward tokens/sec",
@@ -187,6 +216,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
                    "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
                    "table_rows": w.n_rows, "hash_ids": w.hash_dist,
+                   "instances": w.n_instances, "flush_mib": args.flush_mib,
                    "parallelism": "single GPU"},
         "roofline": roof,
     }

@@ -30,6 +30,7 @@ Generator definition (the same on the host, in numpy, and on the device, in
 """
 from __future__ import annotations
 
+import concurrent.futures
 import ctypes
 import dataclasses
 import math
@@ -253,11 +254,18 @@ class Workload:
         return normal_bf16(self.key(S_WKV, inst), n_lo * self.K, n, 0.0, self.wkv_std).reshape(
             n_hi - n_lo, self.K)
 
-    def wkv_f32(self, inst: int = 0, chunk_rows: int = 512) -> np.ndarray:
+    def wkv_f32(self, inst: int = 0, chunk_rows: int = 512, threads: int = 0) -> np.ndarray:
+        """All of wkv as fp32 values; chunks of rows are generated on a thread pool (numpy
+        releases the GIL inside its array operations)."""
         out = np.empty((self.N, self.K), dtype=np.float32)
-        for lo in range(0, self.N, chunk_rows):
+
+        def fill(lo):
             hi = min(self.N, lo + chunk_rows)
             out[lo:hi] = bf16_bits_to_f32(self.wkv_rows(lo, hi, inst))
+
+        n = threads or min(16, os.cpu_count() or 1)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as pool:
+            list(pool.map(fill, range(0, self.N, chunk_rows)))
         return out
 
     def outlier_tokens(self) -> np.ndarray:

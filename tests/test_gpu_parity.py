@@ -1,13 +1,8 @@
 """HIP path vs the CPU oracle on the same seeded inputs (needs an MI355X).
 
-Every GPU call goes through the C ABI (the ctypes binding).  Integer, byte and dequantisation
-results must be bit-exact; floating-point outputs are held to the tolerance stated for the
-forward: max |out - oracle| <= 2e-2 and mean <= 2e-3 against the unrounded oracle, except that
-tokens drawn with the x50 outlier scale get 2e-2 plus one bf16 ulp of the reference (bf16 output
-rounding alone exceeds 2e-2 there).  Tokens whose mask is false must come back bit for bit.
+Every GPU call goes through the C ABI (the ctypes binding); the tolerances are those stated in
+gpu_common.py.
 """
-import sys
-
 import numpy as np
 import pytest
 
@@ -16,71 +11,7 @@ pytestmark = pytest.mark.gpu
 
 import oracle  # noqa: E402
 import synth  # noqa: E402
-
-if torch.cuda.is_available():
-    import hashed_gram_engram_amd as eg  # noqa: E402
-
-
-def say(*a):
-    print(*a, file=sys.stderr, flush=True)
-
-
-def u16(t):
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def layout(w):
-    return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
-
-
-_WKV = {}
-
-
-def host_wkv(w):
-    key = (w.name, w.seed, w.N, w.K)
-    if key not in _WKV:
-        _WKV.clear()
-        _WKV[key] = w.wkv_f32()
-    return _WKV[key]
-
-
-def oracle_for(w, sel):
-    sel = np.asarray(sel, dtype=np.int64)
-    ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
-    mask = w.token_mask().reshape(-1)[sel]
-    q, k = w.qk()
-    return oracle.forward(w.x_tokens(sel), ids, mask, synth.host_fetch(w), w.n_rows, w.head_dim,
-                          w.scale_block, host_wkv(w), q, k, eps=w.eps, clamp=w.clamp)
-
-
-def check_out(w, sel, got_bits, ref):
-    """Tolerance check of output streams for tokens `sel` (got_bits [len, hc, dim])."""
-    sel = np.asarray(sel)
-    got = oracle.bf16_value(got_bits)
-    err = np.abs(got - ref["out_f"])
-    mask = w.token_mask().reshape(-1)[sel].astype(bool)
-    outl = w.outlier_tokens()[sel]
-    x_bits = w.x_tokens(sel)
-    assert np.array_equal(got_bits[~mask], x_bits[~mask]), "closed tokens must pass through"
-    normal = ~outl
-    if normal.any():
-        assert err[normal].max() <= 2e-2, err[normal].max()
-        assert err[normal].mean() <= 2e-3, err[normal].mean()
-    if outl.any():
-        r = np.abs(ref["out_f"][outl])
-        ulp = np.exp2(np.floor(np.log2(np.maximum(r, 2.0 ** -126))) - 7)
-        assert np.all(err[outl] <= 2e-2 + ulp)
-    # against the oracle's own bf16 rounding nearly everything is exact or one ulp off (larger
-    # ulp counts only where h + g * v nearly cancels)
-    d = np.abs(got_bits.astype(np.int32) - ref["out_bits"].astype(np.int32))
-    assert (d > 1).mean() <= 1e-3, (d > 1).mean()
-    return err.max(), err.mean(), float((d > 0).mean())
-
-
-def forward(w, d, out=None, ws=None, err=None):
-    return eg.engram_forward(layout(w), d["x"], d["hash_ids"], d["token_mask"], d["table"],
-                             d["scales"], d["wkv"], d["q_weight"], d["k_weight"], out=out,
-                             workspace=ws, err_count=err)
+from gpu_common import check_out, eg, forward, host_wkv, layout, oracle_for, say, u16  # noqa: E402
 
 
 # ---------------------------------------------------------------------------- fixtures
