@@ -257,38 +257,54 @@ __device__ __forceinline__ u32x4 wide_operand(const WideTok<FUSED>& tk, int t, i
 }
 
 // Fused kernel: the gathered token codes and scales of one chunk are copied global -> LDS as
-// well, into a wave-private 9 KB buffer (copy 2 t + h: 16 codes of sub-block t per lane at
-// 1024 (2 t + h) + 16 lane; copy 8 + t: the lane's scale at 8192 + 256 t + 4 lane), so that the
-// K loop holds no register loads: the compiler would otherwise wait for every copy in flight
-// before each use of a token register.  `keep` marks lanes whose hash id names a table row.
+// well, into a wave-private 9 KB buffer, so that the K loop holds no register loads: the
+// compiler would otherwise wait for every copy in flight before each use of a token register.
+// Codes: the chunk's 128 features are one 128-byte piece of each token's table row (a chunk
+// stays inside one column), and copy k (0..7) fills buffer bytes [1024 k, 1024 k + 1024) with
+// the pieces of tokens 8 k .. 8 k + 7, eight lanes per token, so every cache line the gather
+// touches is read whole.  Row `tok` of the buffer keeps its 16-byte part p at position
+// p ^ ((tok >> 1) & 7), which spreads the reads of 16 consecutive tokens over all banks.
+// Scales: copy 8 + t puts the scale a lane needs for sub-block t (token 16 t + lane % 16,
+// features 32 (lane / 16) ..) at 8192 + 256 t + 4 lane.  `keep` marks lanes whose hash id
+// names a table row.
 constexpr int kTokBuf = kTokBuf_;
 
 __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], const StreamArgs& a,
                                               const int64_t* s_ids, int f_chunk, int lane) {
-  const int f = f_chunk + 32 * (lane >> 4);
-  const int j = f / a.head_dim;
-  const int cc = f - j * a.head_dim;
+  const int j = f_chunk / a.head_dim;
+  const int cc0 = f_chunk - j * a.head_dim;
   const int nb = a.head_dim / a.scale_block;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int tok = 8 * k + (lane >> 3);
+    const int64_t r = s_ids[tok * a.n_cols + j];
+    const int64_t rr = r >= 0 ? r : 0;
+    const int part = (lane & 7) ^ ((tok >> 1) & 7);
+    __builtin_amdgcn_global_load_lds((const void*)(a.table + rr * a.head_dim + cc0 + 16 * part),
+                                     (lds_ptr_t)(tbuf + k * 1024), 16, 0, 0);
+  }
+  const int cc = cc0 + 32 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
     const int64_t rr = r >= 0 ? r : 0;
     keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
-    const uint8_t* src = a.table + rr * a.head_dim + cc;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(tbuf + (2 * t) * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((const void*)(src + 16), (lds_ptr_t)(tbuf + (2 * t + 1) * 1024), 16, 0, 0);
     __builtin_amdgcn_global_load_lds((const void*)(a.scales + rr * nb + cc / a.scale_block),
                                      (lds_ptr_t)(tbuf + 8192 + t * 256), 4, 0, 0);
   }
 }
 
-// The 16 token operands of one chunk (steps s = 0..3 x sub-blocks t = 0..3) from the buffer.
+// The 16 token operands of one chunk (steps s = 0..3 x sub-blocks t = 0..3) from the buffer:
+// the lane's 32 features are the 16-byte parts 2 (lane / 16) and 2 (lane / 16) + 1 of its token.
 __device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char* tbuf, const uint32_t (&keep)[4],
                                                   int lane) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const u32x4 c0 = *reinterpret_cast<const u32x4*>(tbuf + (2 * t) * 1024 + 16 * lane);
-    const u32x4 c1 = *reinterpret_cast<const u32x4*>(tbuf + (2 * t + 1) * 1024 + 16 * lane);
+    const int tok = 16 * t + (lane & 15);
+    const int sw = (tok >> 1) & 7;
+    const int p0 = 2 * (lane >> 4);
+    const u32x4 c0 = *reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * (p0 ^ sw));
+    const u32x4 c1 = *reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * ((p0 + 1) ^ sw));
     const float sc = *reinterpret_cast<const float*>(tbuf + 8192 + t * 256 + 4 * lane);
     bt[0][t] = masked(dequant8(u32x2{c0.x, c0.y}, sc), keep[t]);
     bt[1][t] = masked(dequant8(u32x2{c0.z, c0.w}, sc), keep[t]);
@@ -606,9 +622,8 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             const float dot = D * rstd * a.inv_sqrt_dim;
             const float z = copysignf(sqrtf(fmaxf(fabsf(dot), a.clamp)), dot);
             const float g = 1.0f / (1.0f + expf(-z));
-            const int64_t mt = m0 + t;
-            const bool open = mt < a.M && (a.token_mask == nullptr || a.token_mask[mt] != 0);
-            sh.red[0][t][0] = open ? g : 0.0f;
+            // (closed tokens keep x: the value workgroups apply the mask)
+            sh.red[0][t][0] = m0 + t < a.M ? g : 0.0f;
           }
           __syncthreads();
           // this call is done with the counter; hand the 64 gates to every value workgroup in
@@ -642,6 +657,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           for (int s = 0; s < 4; ++s) xs[i][s] = *reinterpret_cast<const u32x2*>(a.x + size_t(m * 4 + s) * a.dim + d);
         }
       }
+      const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
       __syncthreads();  // sh.red may still be read by a last-arriver hand-off above
       {
         // thread (s, t) waits for gate t of stream s in this workgroup's slot, then clears it.
@@ -673,7 +689,6 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       float g[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) g[s] = sh.red[s][tok][0];
-      const bool open = mvalid && (a.token_mask == nullptr || a.token_mask[m] != 0);
       if (mvalid) {
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {

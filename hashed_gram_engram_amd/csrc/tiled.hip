@@ -26,11 +26,14 @@
 // ending phase 2 j - 2; before the barrier ending phase 2 j - 2 each wave waits until its share of
 // stage j has landed, so stage j is complete before its first reader (group 0, phase 2 j - 1).
 //
-// Tile order: workgroup b takes token block b % n_tb and column block b / n_tb, so the tiles
-// resident at one time share weight panels across token blocks, and (workgroups being dealt
-// to the 8 XCDs round robin) all tiles of a token block run on one XCD when n_tb is a multiple
-// of 8, keeping its staged rows and its x in that XCD's L2.  In the fused kernel every key
-// column block comes before every value column block.  Key tiles post per-(token, stream)
+// Tile order: token blocks are taken in groups of 32; inside a group, workgroup b takes token
+// block b % 32 and column block b / 32 (a last, smaller group likewise with its own size), so
+// the 256 tiles resident at one time cover 32 token panels and 8 weight panels, each XCD
+// holding 4 of the one and 8 of the other (the fewest panels per XCD for 32 tiles), and
+// (workgroups being dealt to the 8 XCDs round robin) all tiles of a token block run on one
+// XCD when its group size is a multiple of 8, keeping its staged rows and its x in that XCD's
+// L2.  In the fused kernel every key column block of a token block comes before every value
+// column block.  Key tiles post per-(token, stream)
 // partial sums of the gate's three reductions; the last key tile of each (token block, stream)
 // sums them in column-block order, evaluates the gates and hands them to the value tiles of the
 // token block through per-tile slots.  A value tile waits only on key tiles with lower ids,
@@ -43,6 +46,7 @@ namespace engram {
 namespace {
 
 constexpr int kThreads = 512;               // 8 waves
+constexpr int kGroupTb = 32;                // token blocks per tile group
 constexpr int kTM = 256;                    // tokens per tile
 constexpr int kTN = 256;                    // wkv rows per tile
 constexpr int kTK = 64;                     // features per stage
@@ -458,8 +462,12 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
   const int64_t b = blockIdx.x;
-  const int64_t tb = b % n_tb;
-  const int cb = int(b / n_tb);
+  const int64_t per_group = int64_t(kGroupTb) * (a.N / kTN);
+  const int64_t g = b / per_group;
+  const int64_t g_size = n_tb - g * kGroupTb < kGroupTb ? n_tb - g * kGroupTb : kGroupTb;
+  const int64_t local = b - g * per_group;
+  const int64_t tb = g * kGroupTb + local % g_size;
+  const int cb = int(local / g_size);
   const int64_t m0 = tb * kTM;
   const int n0 = cb * kTN;
 
