@@ -778,13 +778,25 @@ __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
 
 // Wide kernel: every workgroup has NLO or NHI = NLO + 1 row blocks, each compiled exactly (only
 // one path when every workgroup has the same count, so registers are sized for it alone).
-template <int NLO, int NHI, bool FUSED>
+// ONE_TB: the call has a single token block.  Without a loop over token blocks the compiler
+// has nothing to hoist above the hash-id loads; with one it computes every loop-invariant
+// address of the K loop and the epilogue first, about 3 us before the first memory access.
+template <int NLO, int NHI, bool FUSED, bool ONE_TB>
 __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
   const int G = gridDim.x, w = blockIdx.x;
   const Rows rw = rows_of(w, a.N, G);
+  if constexpr (ONE_TB) {
+    if constexpr (NLO == NHI) {
+      token_block<NLO, true, 1, FUSED>(a, smem, sh, 0, w, rw);
+    } else {
+      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, 0, w, rw);
+      else token_block<NHI, true, 1, FUSED>(a, smem, sh, 0, w, rw);
+    }
+    return;
+  }
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   for (int64_t tb = 0; tb < n_tb; ++tb) {
     if constexpr (NLO == NHI) {
@@ -804,22 +816,25 @@ void* pick_narrow(int nstep) {
 }
 
 template <int NLO, bool FUSED>
-void* pick_wide_n(bool same) {
-  return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED>)
-              : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED>);
+void* pick_wide_n(bool same, bool one_tb) {
+  if (one_tb)
+    return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, true>)
+                : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, true>);
+  return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, false>)
+              : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, false>);
 }
 
 template <bool FUSED>
-void* pick_wide(int nlo, int nhi) {
+void* pick_wide(int nlo, int nhi, bool one_tb) {
   const bool same = nlo == nhi;
   switch (nlo) {
-    case 1: return pick_wide_n<1, FUSED>(same);
-    case 2: return pick_wide_n<2, FUSED>(same);
-    case 3: return pick_wide_n<3, FUSED>(same);
-    case 4: return pick_wide_n<4, FUSED>(same);
-    case 5: return pick_wide_n<5, FUSED>(same);
-    case 6: return pick_wide_n<6, FUSED>(same);
-    case 7: return pick_wide_n<7, FUSED>(same);
+    case 1: return pick_wide_n<1, FUSED>(same, one_tb);
+    case 2: return pick_wide_n<2, FUSED>(same, one_tb);
+    case 3: return pick_wide_n<3, FUSED>(same, one_tb);
+    case 4: return pick_wide_n<4, FUSED>(same, one_tb);
+    case 5: return pick_wide_n<5, FUSED>(same, one_tb);
+    case 6: return pick_wide_n<6, FUSED>(same, one_tb);
+    case 7: return pick_wide_n<7, FUSED>(same, one_tb);
     default: return nullptr;
   }
 }
@@ -841,7 +856,7 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   void* fn = nullptr;
   const bool wide = use_wide(a, G, FUSED);
   if (wide) {
-    fn = pick_wide<FUSED>(min_blocks(a.N, G), max_blocks(a.N, G));
+    fn = pick_wide<FUSED>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
   } else {
     const int per_wg = max_blocks(a.N, G);
     const int nstep = (a.K / 4) / 32;
