@@ -5,26 +5,21 @@
 // than re-gathering the fp8 row for every tile.
 //
 // A workgroup computes one tile of 256 tokens x 256 wkv rows (output columns) over all of K, in
-// stages of 32 features.  A stage holds both operands in LDS, 256 rows of 64 bytes each, with
-// 16-byte chunk c of row r at position c ^ ((r >> 1) & 3) (measured conflict-free for the
-// fragment reads below).  Stages live in a ring of five (160 KB); global -> LDS copies
-// (global_load_lds_dwordx4, one instruction fills 16 rows) run four stages ahead.
+// stages of 64 features.  A stage of one operand is 256 rows of 128 bytes in LDS, 16-byte chunk c
+// of row r at position c ^ (r & 7) (conflict-free for the fragment reads below).  wkv stages
+// live in a ring of three slots and are copied two stages ahead, token stages in a ring of two,
+// copied one stage ahead (5 x 32 KB = 160 KB); every copy is a global -> LDS
+// global_load_lds_dwordx4 filling 8 rows x 128 bytes.
 //
 // Eight waves, two per SIMD.  Waves 0-3 (group 0) own wkv rows 0-127 of the tile, waves 4-7
 // (group 1) rows 128-255; within a group, wave w & 3 owns tokens 64 (w & 3) .. + 63.  Each wave
 // computes 128 columns x 64 tokens as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (128 accumulator
 // registers).  The groups alternate ("ping-pong"): while the group-0 wave of a SIMD issues the
-// 32 MFMAs of one stage, the group-1 wave issues its copies and fragment reads for the same
-// stage, then the roles swap; a workgroup barrier separates phases.  So each SIMD's matrix unit
-// is fed by one wave at a time whose operands are already in registers, and the LDS and memory
-// latency of one wave hides under the other's MFMAs.
-//
-// Phase p (p = 0, 1, ...): group 0 multiplies stage p / 2 when p is even and loads stage
-// p / 2 + 1 when p is odd; group 1 loads stage p / 2 when p is even and multiplies it when p is
-// odd.  The load phase of stage j copies this wave's share of stage j + 4 into ring slot
-// (j + 4) % 5, whose previous stage (j - 1) both groups finished reading before the barrier
-// ending phase 2 j - 2; before the barrier ending phase 2 j - 2 each wave waits until its share of
-// stage j has landed, so stage j is complete before its first reader (group 0, phase 2 j - 1).
+// 32 MFMAs of one half stage, the group-1 wave reads its fragments (and issues copies), then the
+// roles swap; a workgroup barrier separates phases.  So each SIMD's matrix unit is fed by one
+// wave at a time whose operands are already in registers, and the LDS and memory latency of one
+// wave hides under the other's MFMAs.  The phase-by-phase schedule and its wait counts are
+// spelled out at k_loop.
 //
 // Tile order: token blocks are taken in groups of 32; inside a group, workgroup b takes token
 // block b % 32 and column block b / 32 (a last, smaller group likewise with its own size), so
