@@ -39,7 +39,7 @@ def algorithmic_flops(w) -> int:
     return 2 * w.M * w.N * w.K
 
 
-TILED_MIN_TOKENS = 256  # the library's switch from weight streaming to 256 x 256 tiles
+TILED_MIN_TOKENS = 65  # the whole forward switches from weight streaming to 256 x 256 tiles here
 
 
 def kernel_of(w):

@@ -14,8 +14,13 @@ namespace {
 constexpr uint32_t kSpinBudget = 1u << 22;  // ~1 s of sleeping polls before a wait gives up
 
 // From this many tokens on, the tiled schedule (256 x 256 MFMA tiles, each weight panel read
-// once per 256 tokens) replaces weight streaming (all of wkv read once per 64 tokens).
+// once per 256 tokens) replaces weight streaming (all of wkv read once per 64-token block).
+// The whole forward switches after one token block: with at most 128 tiles its K loop is split
+// over two workgroups per tile (measured at the decode layout: 133-155 us for 96-256 tokens,
+// against 139-266 us streaming two to four token blocks).  The projection alone has no
+// workspace for split partials and switches at 256 tokens.
 constexpr int64_t kTiledMinTokens = 256;
+constexpr int64_t kTiledMinTokensFused = 65;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -52,7 +57,8 @@ int64_t K_of(const engram_layout* l) { return int64_t(l->n_cols) * l->head_dim; 
 int64_t N_of(const engram_layout* l) { return int64_t(l->hc + 1) * l->dim; }
 
 bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
-  return M >= kTiledMinTokens && tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, fused);
+  return M >= (fused ? kTiledMinTokensFused : kTiledMinTokens) &&
+         tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, fused);
 }
 
 // Workspace of engram_forward for M tokens: control words at the start (the schedule in use
@@ -64,7 +70,10 @@ bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
 // call leaves behind never sit where a later call expects zeros.
 size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   const int N = int(N_of(l));
-  const int64_t Ms = M < kTiledMinTokens ? M : kTiledMinTokens - 1;
+  // token counts the streaming schedule takes: up to the tiled threshold, or all of them when
+  // the layout has no tiled schedule
+  const bool tiled_layout = tiled_shape_ok(N, int(K_of(l)), l->dim, true);
+  const int64_t Ms = tiled_layout && M >= kTiledMinTokensFused ? kTiledMinTokensFused - 1 : M;
   size_t c = stream_workspace_bytes(Ms, N, stream_grid(N, cus));
   if (use_tiled(l, M, true)) {
     const size_t t = tiled_control_bytes(M, l->dim);
@@ -74,7 +83,7 @@ size_t forward_control(const engram_layout* l, int64_t M, int cus) {
 }
 
 size_t forward_staging(const engram_layout* l, int64_t M) {
-  return use_tiled(l, M, true) ? tiled_staging_bytes(M, int(K_of(l))) + 256 : 0;
+  return use_tiled(l, M, true) ? tiled_staging_bytes(M, int(K_of(l)), int(N_of(l))) + 256 : 0;
 }
 
 size_t forward_workspace(const engram_layout* l, int64_t M, int cus) {

@@ -100,14 +100,20 @@ struct TiledArgs {
   void* ws;
   int n_vcb;
   size_t slot_off, part_off;
+  // split K (fused schedule, at most 128 tiles): each tile is computed by two workgroups over
+  // the two halves of K; the first to finish leaves its fp32 partial tile in kpart
+  int ksplit;
+  size_t split_off;  // per-tile arrival and hand-off words (control words)
+  float* kpart;      // [tile][256 x 256] fp32 (staging area)
 };
 
-// Shapes the tiled kernels take: N a multiple of 256, K of 32 (fused: also dim of 256).
+// Shapes the tiled kernels take: N a multiple of 256, K of 64 (fused: also dim of 256).
 bool tiled_shape_ok(int N, int K, int dim, bool fused);
-// Control words of the fused tiled schedule (zero before and after every call) and the staging
-// area of its dequantised rows (M x K bf16, contents unspecified after a call).
+// Control words of the fused tiled schedule (zero before and after every call) and its staging
+// area: the dequantised rows (M x K bf16) and room for the split-K partial tiles (contents
+// unspecified after a call).  Neither size decreases with M.
 size_t tiled_control_bytes(int64_t M, int dim);
-size_t tiled_staging_bytes(int64_t M, int K);
+size_t tiled_staging_bytes(int64_t M, int K, int N);
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream);
 // Whole forward, tiled schedule: the gather pass `g` writes the dequantised rows into `staging`
 // (tiled_staging_bytes, 256-byte aligned), then the tiled kernel runs with `workspace` as its

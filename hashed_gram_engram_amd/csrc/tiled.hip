@@ -192,21 +192,23 @@ __device__ __forceinline__ void k_loop(TileAcc& acc, const Pipe& p, char* lds, i
   phase_end();
 }
 
-__device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char* lds, int64_t m0, int n0,
-                                          int tid) {
+// Stages [s0, s0 + ns) of the tile's K loop.
+__device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char* lds, int64_t m0, int n0, int s0,
+                                          int ns, int tid) {
   const int lane = tid & 63, wv = tid >> 6;
   Pipe p;
   p.wv_u = __builtin_amdgcn_readfirstlane(wv);
   {
     const int rr = lane >> 3, chunk = (lane & 7) ^ rr;
     const size_t row_bytes = size_t(a.K) * 2;
+    const size_t k0 = size_t(s0) * kRowB;
 #pragma unroll
     for (int i = 0; i < kCopies; ++i) {
       const int r = (4 * p.wv_u + i) * 8 + rr;  // row of the tile
-      p.a_src[i] = reinterpret_cast<const char*>(a.wkv) + size_t(n0 + r) * row_bytes + 16 * chunk;
+      p.a_src[i] = reinterpret_cast<const char*>(a.wkv) + size_t(n0 + r) * row_bytes + k0 + 16 * chunk;
       int64_t m = m0 + r;
       m = m < a.M ? m : a.M - 1;  // rows past the last token repeat it (their results are dropped)
-      p.b_src[i] = reinterpret_cast<const char*>(a.emb) + size_t(m) * row_bytes + 16 * chunk;
+      p.b_src[i] = reinterpret_cast<const char*>(a.emb) + size_t(m) * row_bytes + k0 + 16 * chunk;
     }
   }
   {
@@ -220,11 +222,65 @@ __device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char
   for (int i = 0; i < kBI; ++i)
 #pragma unroll
     for (int j = 0; j < kBJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int S = a.K / kTK;
   if (__builtin_amdgcn_readfirstlane(wv) < 4)
-    k_loop<0>(acc, p, lds, S);
+    k_loop<0>(acc, p, lds, ns);
   else
-    k_loop<1>(acc, p, lds, S);
+    k_loop<1>(acc, p, lds, ns);
+}
+
+// ---------------------------------------------------------------- split K
+// Tile t's two workgroups share two control words at split_off + 64 t: arrivals and "partial
+// written".  The first to arrive stores its fp32 partial tile (16-byte device-coherent stores,
+// one 1 KB run per wave instruction), waits for the stores to complete, sets the second word and
+// exits; the second waits for that word (its partner has already arrived and never waits), adds
+// the partial to its own accumulators, clears both words and finishes the tile.  The sum of two
+// fp32 values does not depend on their order, so the result does not depend on which half
+// arrives first.  (The partial's offsets are a per-lane part and a scalar part per block.)
+// Returns false in the workgroup that exits.
+__device__ __forceinline__ bool split_merge(TileAcc& acc, const TiledArgs& a, int64_t tile, char* lds, int tid) {
+  uint32_t* w = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(a.ws) + a.split_off + size_t(tile) * 64);
+  int* flag = reinterpret_cast<int*>(lds + kLds - 4);  // past every LDS user of the epilogue
+  if (tid == 0) *flag = int(atomic_add_relaxed(w, 1u));
+  __syncthreads();
+  const bool first = *flag == 0;
+  const __amdgpu_buffer_rsrc_t pr = coherent_rsrc(a.kpart + size_t(tile) * (kTM * kTN));
+  if (first) {
+#pragma unroll
+    for (int i = 0; i < kBI; ++i)
+#pragma unroll
+      for (int j = 0; j < kBJ; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i][j]), pr, uint32_t(tid * 16),
+                                               (i * kBJ + j) * kThreads * 16, kCpolSc1);
+    drain_memory_ops();
+    __syncthreads();
+    if (tid == 0) store_relaxed(w + 1, 1u);
+    return false;
+  }
+  if (tid == 0) {
+    uint32_t it = 0;
+    while (load_relaxed(w + 1) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it > a.spin_budget) {
+        atomic_add_relaxed(reinterpret_cast<uint32_t*>(a.ws), 1u);
+        break;
+      }
+    }
+    store_relaxed(w, 0u);
+    store_relaxed(w + 1, 0u);
+  }
+  __syncthreads();
+  // one row block (4 loads) at a time: the accumulators already fill most of the registers
+#pragma unroll
+  for (int i = 0; i < kBI; ++i) {
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j)
+      acc[i][j] += __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, uint32_t(tid * 16),
+                                                                                (i * kBJ + j) * kThreads * 16,
+                                                                                kCpolSc1));
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();  // the flag word is reused by the epilogue's LDS
+  return true;
 }
 
 // ---------------------------------------------------------------- epilogues
@@ -456,7 +512,8 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
-  const int64_t b = blockIdx.x;
+  const int64_t b = FUSED && a.ksplit == 2 ? int64_t(blockIdx.x) >> 1 : int64_t(blockIdx.x);  // the tile
+  const int half_k = FUSED && a.ksplit == 2 ? int(blockIdx.x & 1) : -1;
   const int64_t per_group = int64_t(kGroupTb) * (a.N / kTN);
   const int64_t g = b / per_group;
   const int64_t g_size = n_tb - g * kGroupTb < kGroupTb ? n_tb - g * kGroupTb : kGroupTb;
@@ -467,7 +524,11 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   const int n0 = cb * kTN;
 
   TileAcc acc;
-  tile_gemm(acc, a, lds, m0, n0, tid);
+  const int S = a.K / kTK, sh = S / 2;
+  const int s0 = half_k <= 0 ? 0 : sh;
+  const int ns = half_k < 0 ? S : (half_k == 0 ? sh : S - sh);
+  tile_gemm(acc, a, lds, m0, n0, s0, ns, tid);
+  if (half_k >= 0 && !split_merge(acc, a, b, lds, tid)) return;
   // the K loop ended with a barrier after its last LDS access: the ring is free
   acc_to_lds(acc, lds, lane, wv >> 2, wv & 3);
   __syncthreads();
@@ -486,7 +547,8 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
 
 hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream) {
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
-  const int64_t tiles = n_tb * (a.N / kTN);
+  int64_t tiles = n_tb * (a.N / kTN);
+  if (fused && a.ksplit == 2) tiles *= 2;
   if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   const void* fn = fused ? reinterpret_cast<const void*>(&k_tiled<true>)
                          : reinterpret_cast<const void*>(&k_tiled<false>);
@@ -501,12 +563,22 @@ hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream)
   return hipLaunchKernel(fn, dim3(unsigned(tiles)), dim3(kThreads), params, kLds, stream);
 }
 
-// Control words of the fused schedule: header, per-(token block, stream) counters, gate slots,
-// partial sums.  All zero before and after every call.
+// Split K pays while the tiles fill at most half of a 256-CU device: two workgroups per tile.
+constexpr int64_t kSplitMaxTiles = 128;
+int tiled_ksplit(int64_t M, int N, int K) {
+  const int64_t tiles = (M + kTM - 1) / kTM * (N / kTN);
+  return tiles <= kSplitMaxTiles && K / kTK >= 2 ? 2 : 1;
+}
+
+// Control words of the fused schedule: header, per-(token block, stream) counters, split-K
+// words (a fixed 64 bytes for each of up to kSplitMaxTiles tiles), gate slots, partial sums.
+// All zero before and after every call.
 size_t tiled_control_layout(TiledArgs* a, int64_t M, int dim) {
   const int64_t n_tb = (M + kTM - 1) / kTM;
   const int n_vcb = dim / kTN;
   size_t off = 256 + size_t(n_tb) * 4 * 256;  // header, counters (one 256-byte line each)
+  const size_t split_off = off;
+  off += size_t(kSplitMaxTiles) * 64;
   const size_t slot_off = off;
   off += size_t(n_tb) * n_vcb * 4 * kTM * 4;
   off = (off + 255) & ~size_t(255);
@@ -514,10 +586,19 @@ size_t tiled_control_layout(TiledArgs* a, int64_t M, int dim) {
   off += size_t(n_tb) * 4 * n_vcb * kTM * 3 * 4;
   if (a != nullptr) {
     a->n_vcb = n_vcb;
+    a->split_off = split_off;
     a->slot_off = slot_off;
     a->part_off = part_off;
   }
   return off;
+}
+
+// fp32 partial tiles of split K: as many tiles as any token count of this layout splits (the
+// largest multiple of N / 256 not above kSplitMaxTiles), so the staging size grows with M.
+size_t split_partial_bytes(int N) {
+  const int64_t per_tb = N / kTN;
+  if (per_tb <= 0 || per_tb > kSplitMaxTiles) return 0;
+  return size_t(kSplitMaxTiles / per_tb * per_tb) * kTM * kTN * 4;
 }
 
 }  // namespace
@@ -530,7 +611,9 @@ bool tiled_shape_ok(int N, int K, int dim, bool fused) {  // K: stages of 64 fea
 
 size_t tiled_control_bytes(int64_t M, int dim) { return tiled_control_layout(nullptr, M, dim); }
 
-size_t tiled_staging_bytes(int64_t M, int K) { return (size_t(M) * K * 2 + 255) & ~size_t(255); }
+size_t tiled_staging_bytes(int64_t M, int K, int N) {
+  return ((size_t(M) * K * 2 + 255) & ~size_t(255)) + split_partial_bytes(N);
+}
 
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream) { return launch_tiled_impl(a, false, stream); }
 
@@ -543,6 +626,8 @@ hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspac
   a.ws = workspace;
   a.emb = reinterpret_cast<const uint16_t*>(staging);
   tiled_control_layout(&a, a.M, a.dim);
+  a.ksplit = tiled_ksplit(a.M, a.N, a.K);
+  a.kpart = reinterpret_cast<float*>(static_cast<char*>(staging) + ((size_t(a.M) * a.K * 2 + 255) & ~size_t(255)));
   return launch_tiled_impl(a, true, stream);
 }
 

@@ -73,18 +73,20 @@ engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
  * partial sums) and, for token counts where the tiled schedule runs, a staging area for the
  * dequantised rows in its last engram_forward_staging_bytes() bytes.  It must be zero-filled
  * before its first use.  Every call leaves all control words zero again; the staging area's
- * contents are unspecified after a call.  So one workspace serves any number of calls, with any
+ * contents are unspecified after a call.  So one workspace serves any number of calls with one
  * layout and any B x T it is large enough for, on one stream without clearing, provided every
- * call on it passes the same workspace_bytes (the control words of any call then lie below the
- * staging area of every other).  The exception is word 0, which counts cross-workgroup waits
+ * call on it passes the same workspace_bytes (neither part shrinks as B x T grows, so the
+ * control words of any call then lie below the staging area of every other).  The exception is word 0, which counts cross-workgroup waits
  * that timed out (0 in correct operation); after a time-out the workspace must be zero-filled
  * again.  Calls that overlap in time must use different workspaces. */
 size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
-/* Bytes at the end of the workspace that engram_forward uses as a staging area for the
- * dequantised rows (B x T x n_cols x head_dim bf16 plus alignment slack) for B x T tokens; 0
- * where the fused weight-streaming schedule runs (small token counts), which keeps the rows on
- * chip.  Included in engram_forward_workspace_bytes(). */
+/* Bytes at the end of the workspace that engram_forward uses as a staging area for B x T
+ * tokens: the dequantised rows (B x T x n_cols x head_dim bf16), room for the fp32 partial
+ * tiles of a K loop split over two workgroups (taken when a call has few tiles; a fixed amount
+ * per layout, 25.6 MB at the decode layout), alignment slack; 0 where the fused
+ * weight-streaming schedule runs (up to 64 tokens), which keeps the rows on chip.  Included in
+ * engram_forward_workspace_bytes(). */
 size_t engram_forward_staging_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
 /* S1 + S2: row gather and dequantisation (engram-second page,

@@ -360,6 +360,53 @@ def test_workspace_control_zero_and_shared_across_schedules():
         assert torch.equal(outs[i], fresh[i]) and torch.equal(outs[i + 3], fresh[i]), cases[i].name
 
 
+# a layout without a tiled schedule (dim not a multiple of 256): the whole forward streams wkv
+# once per 64-token block at every token count; three blocks, the last one ragged
+STREAM_ONLY = synth.small_variant(TINY, name="dim320_b2_t75", B=2, T=75, dim=320, n_cols=4,
+                                  head_dim=128, scale_block=32, primes=synth.primes_from(1009, 4),
+                                  hash_dist="zipf", mask_false_frac=0.1, masked_positions=(),
+                                  outlier_frac=0.05, seed=TINY.seed + 300)
+
+
+def test_forward_streaming_token_blocks_exact_workspace_with_guard():
+    say("[gpu] forward, layout without a tiled schedule: three token blocks, workspace of exactly "
+        "the reported size followed by guard bytes")
+    w = STREAM_ONLY
+    lay = layout(w)
+    d = synth.device_inputs(w)
+    need = eg.engram_forward_workspace_bytes(lay, w.B, w.T)
+    assert eg.engram_forward_staging_bytes(lay, w.B, w.T) == 0
+    buf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    buf[need:] = 0xA5
+    out = forward(w, d, ws=buf[:need])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "a kernel wrote past the workspace"
+    assert int(torch.count_nonzero(buf[:need]).item()) == 0
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+
+
+def test_kv_proj_streaming_two_token_blocks():
+    say("[gpu] kv_proj decode dims, B=3 T=37 (weight streaming, two token blocks)")
+    w = RAGGED
+    d = synth.device_inputs(w)
+    _kv_case(w, d)
+    del d
+    torch.cuda.empty_cache()
+
+
+def test_workspace_sizes_never_decrease_with_token_count():
+    say("[gpu] workspace and staging sizes against the token count")
+    for w in (TINY, DECODE, STREAM_ONLY):
+        lay = layout(w)
+        last_ws = last_stg = last_ctrl = 0
+        for M in list(range(1, 300)) + [320, 511, 512, 513, 1000, 4096, 8192]:
+            ws = eg.engram_forward_workspace_bytes(lay, 1, M)
+            stg = eg.engram_forward_staging_bytes(lay, 1, M)
+            assert ws >= last_ws and stg >= last_stg and ws - stg >= last_ctrl, (w.name, M)
+            last_ws, last_stg, last_ctrl = ws, stg, ws - stg
+
+
 @pytest.fixture(scope="module")
 def dev_tiled_decode():
     say("[gpu] inputs: decode layout, B=1 T=300")
