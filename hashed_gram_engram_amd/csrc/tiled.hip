@@ -21,6 +21,10 @@
 // wave hides under the other's MFMAs.  The phase-by-phase schedule and its wait counts are
 // spelled out at k_loop.
 //
+// Split K: when a call has at most 128 tiles (up to 256 tokens at the decode layout), two
+// workgroups compute each tile, one over each half of K; the first to finish leaves its fp32
+// partial tile in the staging area and the second adds it and runs the epilogue (split_merge).
+//
 // Tile order: token blocks are taken in groups of 32; inside a group, workgroup b takes token
 // block b % 32 and column block b / 32 (a last, smaller group likewise with its own size), so
 // the 256 tiles resident at one time cover 32 token panels and 8 weight panels, each XCD
