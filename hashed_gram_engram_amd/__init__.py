@@ -30,7 +30,7 @@ STATUS = {0: "ok", -1: "null pointer", -2: "layout", -3: "shape", -4: "alignment
 class EngramLayout(ctypes.Structure):
     _fields_ = [("hc", ctypes.c_int32), ("dim", ctypes.c_int32), ("n_cols", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("scale_block", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("eps", ctypes.c_float),
+                ("scale_format", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("eps", ctypes.c_float),
                 ("clamp", ctypes.c_float)]
 
 
@@ -66,9 +66,12 @@ EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_worksp
             "engram_status_str"]
 
 
+SCALE_FP32, SCALE_E8M0 = 0, 1  # engram_scale_format
+
+
 def make_layout(hc: int, dim: int, n_cols: int, head_dim: int, scale_block: int, n_rows: int,
-                eps: float = 1e-20, clamp: float = 1e-6) -> EngramLayout:
-    return EngramLayout(hc, dim, n_cols, head_dim, scale_block, 0, n_rows, eps, clamp)
+                eps: float = 1e-20, clamp: float = 1e-6, scale_format: int = SCALE_FP32) -> EngramLayout:
+    return EngramLayout(hc, dim, n_cols, head_dim, scale_block, scale_format, n_rows, eps, clamp)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -120,7 +123,7 @@ def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: tor
     B, T, C = hash_ids.shape
     _contig("hash_ids", hash_ids, torch.int64)
     _contig("table", table, torch.uint8)
-    _contig("scales", scales, torch.float32)
+    _contig("scales", scales, torch.uint8 if layout.scale_format == SCALE_E8M0 else torch.float32)
     if emb is None:
         emb = torch.empty((B, T, C * layout.head_dim), dtype=torch.bfloat16, device=hash_ids.device)
     _check("engram_gather_dequant", _lib.engram_gather_dequant(
@@ -195,7 +198,7 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
     _contig("x", x, _BF16)
     _contig("hash_ids", hash_ids, torch.int64)
     _contig("table", table, torch.uint8)
-    _contig("scales", scales, torch.float32)
+    _contig("scales", scales, torch.uint8 if layout.scale_format == SCALE_E8M0 else torch.float32)
     _contig("wkv", wkv, _BF16)
     _contig("q_weight", q_weight, torch.float32)
     _contig("k_weight", k_weight, torch.float32)

@@ -45,6 +45,19 @@ __device__ __forceinline__ uint32_t nan_code_bits(uint32_t c) {
   return ((c & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
 }
 
+// E8M0 block scale (OCP MX v1.0, the scale of the MXFP8 tables): 2^(e - 127) for e = 0..254,
+// NaN for 255.  e = 0 is the fp32 subnormal 2^-127; every other value is a normal fp32 whose
+// exponent field is e.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  const uint32_t bits = e == 0u ? 0x00400000u : (e == 255u ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
+
+// Scale idx of a table's block scales: fp32, or E8M0 bytes.
+__device__ __forceinline__ float load_scale(const void* scales, int64_t idx, int e8m0) {
+  return e8m0 ? e8m0_to_f32(static_cast<const uint8_t*>(scales)[idx]) : static_cast<const float*>(scales)[idx];
+}
+
 // Four codes times one fp32 scale -> four bf16 in two dwords.  The fp8 decode is exact
 // (v_cvt_pk_f32_fp8, OCP e4m3), the product is one IEEE fp32 multiply and the bf16 rounding is
 // nearest-even; NaN results are not canonicalised here.

@@ -117,7 +117,10 @@ engram_status engram_layout_check(const engram_layout* l) {
     return ENGRAM_E_LAYOUT;
   if ((int64_t(l->n_cols) * l->head_dim) % 128 != 0) return ENGRAM_E_LAYOUT;
   if (int64_t(l->n_cols) * l->head_dim > (int64_t(1) << 20)) return ENGRAM_E_LAYOUT;
-  if (l->reserved != 0 || l->n_rows <= 0) return ENGRAM_E_LAYOUT;
+  if (l->n_rows <= 0) return ENGRAM_E_LAYOUT;
+  if (l->scale_format != ENGRAM_SCALE_FP32 && l->scale_format != ENGRAM_SCALE_E8M0) return ENGRAM_E_LAYOUT;
+  // E8M0 scales of a row are whole dwords (the streaming kernel copies them dword-wise)
+  if (l->scale_format == ENGRAM_SCALE_E8M0 && (l->head_dim / l->scale_block) % 4 != 0) return ENGRAM_E_LAYOUT;
   if (!(l->eps >= 0.0f) || !isfinite(l->eps) || !(l->clamp >= 0.0f) || !isfinite(l->clamp))
     return ENGRAM_E_LAYOUT;
   return ENGRAM_OK;
@@ -149,7 +152,7 @@ size_t engram_forward_staging_bytes(const engram_layout* l, int64_t B, int64_t T
   return forward_staging(l, M);
 }
 
-engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table, const float* scales,
+engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table, const void* scales,
                                     const int64_t* hash_ids, int64_t B, int64_t T, uint16_t* emb,
                                     int32_t* err_count, engram_stream_t stream) {
   engram_status st = engram_layout_check(l);
@@ -163,7 +166,8 @@ engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table
     return ENGRAM_E_ALIGN;
   DeviceInfo di;
   if ((st = device_info(&di)) != ENGRAM_OK) return st;
-  GatherArgs a{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block, l->n_rows, emb, err_count};
+  GatherArgs a{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
+               l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, emb, err_count};
   return launch_gather_dequant(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ENGRAM_OK
                                                                                         : ENGRAM_E_HIP;
 }
@@ -227,7 +231,7 @@ engram_status engram_gate_apply(const engram_layout* l, const uint16_t* x, const
 }
 
 engram_status engram_forward(const engram_layout* l, const uint16_t* x, const int64_t* hash_ids,
-                             const uint8_t* token_mask, const uint8_t* table, const float* scales,
+                             const uint8_t* token_mask, const uint8_t* table, const void* scales,
                              const uint16_t* wkv, const float* q_weight, const float* k_weight, int64_t B,
                              int64_t T, uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream) {
@@ -265,12 +269,14 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     a.n_cols = l->n_cols;
     a.head_dim = l->head_dim;
     a.scale_block = l->scale_block;
+    a.scale_e8m0 = l->scale_format == ENGRAM_SCALE_E8M0;
     a.n_rows = l->n_rows;
     a.eps = l->eps;
     a.clamp = l->clamp;
     a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
     a.spin_budget = kSpinBudget;
-    GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block, l->n_rows, nullptr, err_count};
+    GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
+                 l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, nullptr, err_count};
     // the staging area: the last forward_staging() bytes of the buffer, 256-byte aligned
     const size_t stg = forward_staging(l, M);
     const uintptr_t start = (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes - stg + 255) & ~uintptr_t(255);
@@ -300,6 +306,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   a.n_cols = l->n_cols;
   a.head_dim = l->head_dim;
   a.scale_block = l->scale_block;
+  a.scale_e8m0 = l->scale_format == ENGRAM_SCALE_E8M0;
   a.n_rows = l->n_rows;
   a.eps = l->eps;
   a.clamp = l->clamp;

@@ -7,7 +7,7 @@ namespace engram {
 // ----------------------------------------------------------------------------------------
 // Row gather and dequantisation (engram-second page, ParallelEngramEmbedding.forward with one
 // shard, flattened as in Engram.forward).  One thread per 16 codes of one gathered row:
-// a 16-byte load of codes, one fp32 scale, two 16-byte stores of bf16.
+// a 16-byte load of codes, one scale (fp32, or an E8M0 byte), two 16-byte stores of bf16.
 // ----------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gather_dequant(GatherArgs a) {
   const int chunks = a.head_dim >> 4;
@@ -20,7 +20,7 @@ __global__ __launch_bounds__(256) void k_gather_dequant(GatherArgs a) {
   u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
   if (r >= 0 && r < a.n_rows) {
     const u32x4 c = *reinterpret_cast<const u32x4*>(a.table + r * a.head_dim + ch * 16);
-    const float s = a.scales[r * nb + (ch * 16) / a.scale_block];
+    const float s = load_scale(a.scales, r * nb + (ch * 16) / a.scale_block, a.scale_e8m0);
     dequant16(c, s, o0, o1);
   } else if (ch == 0 && a.err_count != nullptr) {
     atomicAdd(a.err_count, 1);

@@ -9,11 +9,12 @@ namespace engram {
 
 struct GatherArgs {
   const uint8_t* table;
-  const float* scales;
+  const void* scales;  // fp32, or E8M0 bytes when scale_e8m0
   const int64_t* hash_ids;
   int64_t n_pairs;  // tokens * n_cols
   int head_dim;
   int scale_block;
+  int scale_e8m0;
   int64_t n_rows;
   uint16_t* emb;
   int32_t* err_count;
@@ -46,12 +47,12 @@ struct StreamArgs {
   const int64_t* hash_ids;
   const uint8_t* token_mask;
   const uint8_t* table;
-  const float* scales;
+  const void* scales;  // fp32, or E8M0 bytes when scale_e8m0
   const float* q_weight;
   const float* k_weight;
   uint16_t* out;
   int32_t* err_count;
-  int n_cols, head_dim, scale_block;
+  int n_cols, head_dim, scale_block, scale_e8m0;
   int64_t n_rows;
   float eps, clamp, inv_sqrt_dim;
   // workspace views
@@ -87,12 +88,12 @@ struct TiledArgs {
   const int64_t* hash_ids;
   const uint8_t* token_mask;
   const uint8_t* table;
-  const float* scales;
+  const void* scales;  // fp32, or E8M0 bytes when scale_e8m0
   const float* q_weight;
   const float* k_weight;
   uint16_t* out;
   int32_t* err_count;
-  int n_cols, head_dim, scale_block;
+  int n_cols, head_dim, scale_block, scale_e8m0;
   int64_t n_rows;
   float eps, clamp, inv_sqrt_dim;
   uint32_t spin_budget;

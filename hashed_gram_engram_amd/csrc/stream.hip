@@ -112,7 +112,7 @@ __device__ __forceinline__ void load_tok(TokFrag& tf, const StreamArgs& a, const
     const int64_t rr = r >= 0 ? r : 0;
     tf.keep = r >= 0 ? 0xFFFFFFFFu : 0u;
     tf.code = *reinterpret_cast<const u32x2*>(a.table + rr * a.head_dim + cc);
-    tf.scale = a.scales[rr * (a.head_dim / a.scale_block) + cc / a.scale_block];
+    tf.scale = load_scale(a.scales, rr * (a.head_dim / a.scale_block) + cc / a.scale_block, a.scale_e8m0);
   } else {
     const int64_t m = m0 + 16 * t + (lane & 15);
     tf.keep = m < a.M ? 0xFFFFFFFFu : 0u;
@@ -207,54 +207,30 @@ __device__ __forceinline__ void wide_copy_w(char* slot, const StreamArgs& a, con
   }
 }
 
-// Token operands of one chunk for one lane: sub-block t, features f_chunk + 32 * (lane / 16)
-// + [0, 32).  Gathered: 32 fp8 codes (two dwordx4) and one scale (scale_block is a multiple of
-// 32); dense: 32 bf16 (four dwordx4).
-template <bool FUSED>
+// Dense token operands (the projection alone) of one chunk for one lane: sub-block t, features
+// f_chunk + 32 * (lane / 16) + [0, 32) of emb, four dwordx4 per sub-block, loaded into
+// registers one chunk ahead.  (The fused kernel copies gathered codes into LDS instead.)
 struct WideTok {
-  u32x4 v[4][FUSED ? 2 : 4];
-  float scale[4];
+  u32x4 v[4][4];
   uint32_t keep[4];
 };
 
-template <bool FUSED>
-__device__ __forceinline__ void wide_issue_tok(WideTok<FUSED>& tk, const StreamArgs& a, const int64_t* s_ids,
-                                               int64_t m0, int f_chunk, int lane) {
+__device__ __forceinline__ void wide_issue_tok(WideTok& tk, const StreamArgs& a, int64_t m0, int f_chunk,
+                                               int lane) {
   const int f = f_chunk + 32 * (lane >> 4);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    if constexpr (FUSED) {
-      const int j = f / a.head_dim;
-      const int cc = f - j * a.head_dim;
-      const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
-      const int64_t rr = r >= 0 ? r : 0;
-      tk.keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.table + rr * a.head_dim + cc);
-      tk.v[t][0] = src[0];
-      tk.v[t][1] = src[1];
-      tk.scale[t] = a.scales[rr * (a.head_dim / a.scale_block) + cc / a.scale_block];
-    } else {
-      const int64_t m = m0 + 16 * t + (lane & 15);
-      tk.keep[t] = m < a.M ? 0xFFFFFFFFu : 0u;
-      const int64_t mm = m < a.M ? m : a.M - 1;
-      const u32x4* src = reinterpret_cast<const u32x4*>(a.emb + mm * a.K + f);
+    const int64_t m = m0 + 16 * t + (lane & 15);
+    tk.keep[t] = m < a.M ? 0xFFFFFFFFu : 0u;
+    const int64_t mm = m < a.M ? m : a.M - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.emb + mm * a.K + f);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) tk.v[t][q] = src[q];
-    }
+    for (int q = 0; q < 4; ++q) tk.v[t][q] = src[q];
   }
 }
 
 // Operand of step s (features 8 s .. 8 s + 7 of the lane's 32) for sub-block t.
-template <bool FUSED>
-__device__ __forceinline__ u32x4 wide_operand(const WideTok<FUSED>& tk, int t, int s) {
-  if constexpr (FUSED) {
-    const u32x4 c = tk.v[t][s >> 1];
-    const u32x2 pair = (s & 1) ? u32x2{c.z, c.w} : u32x2{c.x, c.y};
-    return masked(dequant8(pair, tk.scale[t]), tk.keep[t]);
-  } else {
-    return masked(tk.v[t][s], tk.keep[t]);
-  }
-}
+__device__ __forceinline__ u32x4 wide_operand(const WideTok& tk, int t, int s) { return masked(tk.v[t][s], tk.keep[t]); }
 
 // Fused kernel: the gathered token codes and scales of one chunk are copied global -> LDS as
 // well, into a wave-private 9 KB buffer, so that the K loop holds no register loads: the
@@ -265,8 +241,10 @@ __device__ __forceinline__ u32x4 wide_operand(const WideTok<FUSED>& tk, int t, i
 // touches is read whole.  Row `tok` of the buffer keeps its 16-byte part p at position
 // p ^ ((tok >> 1) & 7), which spreads the reads of 16 consecutive tokens over all banks.
 // Scales: copy 8 + t puts the scale a lane needs for sub-block t (token 16 t + lane % 16,
-// features 32 (lane / 16) ..) at 8192 + 256 t + 4 lane.  `keep` marks lanes whose hash id
-// names a table row.
+// features 32 (lane / 16) ..) at 8192 + 256 t + 4 lane: the fp32 scale, or for E8M0 scales the
+// aligned dword that holds the byte (a row's E8M0 scales are whole dwords: the layout check
+// asks for a multiple of 4 per row), which the read takes apart.  `keep` marks lanes whose
+// hash id names a table row.
 constexpr int kTokBuf = kTokBuf_;
 
 __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], const StreamArgs& a,
@@ -284,20 +262,23 @@ __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], c
                                      (lds_ptr_t)(tbuf + k * 1024), 16, 0, 0);
   }
   const int cc = cc0 + 32 * (lane >> 4);
+  const int sbyte = a.scale_e8m0 ? 1 : 4;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
     const int64_t rr = r >= 0 ? r : 0;
     keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
-    __builtin_amdgcn_global_load_lds((const void*)(a.scales + rr * nb + cc / a.scale_block),
+    const size_t off = size_t(rr * nb + cc / a.scale_block) * sbyte;
+    __builtin_amdgcn_global_load_lds((const void*)(static_cast<const char*>(a.scales) + (off & ~size_t(3))),
                                      (lds_ptr_t)(tbuf + 8192 + t * 256), 4, 0, 0);
   }
 }
 
 // The 16 token operands of one chunk (steps s = 0..3 x sub-blocks t = 0..3) from the buffer:
 // the lane's 32 features are the 16-byte parts 2 (lane / 16) and 2 (lane / 16) + 1 of its token.
+// e8m0_shift: 0 for fp32 scales, else 8 x (byte offset of the lane's E8M0 scale in its dword).
 __device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char* tbuf, const uint32_t (&keep)[4],
-                                                  int lane) {
+                                                  int lane, int e8m0, uint32_t e8m0_shift) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int tok = 16 * t + (lane & 15);
@@ -305,7 +286,8 @@ __device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char*
     const int p0 = 2 * (lane >> 4);
     const u32x4 c0 = *reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * (p0 ^ sw));
     const u32x4 c1 = *reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * ((p0 + 1) ^ sw));
-    const float sc = *reinterpret_cast<const float*>(tbuf + 8192 + t * 256 + 4 * lane);
+    const uint32_t sw32 = *reinterpret_cast<const uint32_t*>(tbuf + 8192 + t * 256 + 4 * lane);
+    const float sc = e8m0 ? e8m0_to_f32((sw32 >> e8m0_shift) & 0xFFu) : __uint_as_float(sw32);
     bt[0][t] = masked(dequant8(u32x2{c0.x, c0.y}, sc), keep[t]);
     bt[1][t] = masked(dequant8(u32x2{c0.z, c0.w}, sc), keep[t]);
     bt[2][t] = masked(dequant8(u32x2{c1.x, c1.y}, sc), keep[t]);
@@ -324,11 +306,11 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   const int nch = (a.K >> 2) / 128;
   char* my_slots = slots + wv * NRB * kWBlk;
   char* my_tok = slots + 4 * NRB * kWBlk + wv * kTokBuf;  // fused only
-  WideTok<false> tk;       // dense only
+  WideTok tk;              // dense only
   uint32_t keep[4];        // fused only
   // prologue in the loop's issue order (tokens, then row blocks)
   if constexpr (FUSED) wide_copy_tok(my_tok, keep, a, s_ids, q0, lane);
-  else wide_issue_tok<false>(tk, a, s_ids, m0, q0, lane);
+  else wide_issue_tok(tk, a, m0, q0, lane);
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
@@ -350,15 +332,18 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
     if constexpr (FUSED) {
       // the token copies of chunk c have landed once only the weight copies of chunk c remain
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NRB) : "memory");
-      wide_tok_operands(bt, my_tok, keep, lane);
+      // the lane's E8M0 scale byte within its dword (row scales are whole dwords)
+      const int cc_cur = (q0 + 128 * c) % a.head_dim + 32 * (lane >> 4);
+      const uint32_t e8m0_shift = uint32_t((cc_cur / a.scale_block) & 3) * 8u;
+      wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
       wide_copy_tok(my_tok, keep, a, s_ids, fn, lane);
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bt[s][t] = wide_operand<false>(tk, t, s);
-      wide_issue_tok<false>(tk, a, s_ids, m0, fn, lane);
+        for (int t = 0; t < 4; ++t) bt[s][t] = wide_operand(tk, t, s);
+      wide_issue_tok(tk, a, m0, fn, lane);
     }
     asm volatile("" ::: "memory");
 #pragma unroll

@@ -43,18 +43,24 @@ typedef enum {
   ENGRAM_E_DEVICE = -7     /* the current device is not gfx950                   */
 } engram_status;
 
+/* Block scales of the fp8 table: one fp32 value per block, or one E8M0 byte per block (the
+ * MXFP8 format of the official tables, "Engram in DeepSeek V4.1 Flash", Step 2: OCP MX v1.0
+ * scale, value 2^(e - 127), 0xFF = NaN). */
+typedef enum { ENGRAM_SCALE_FP32 = 0, ENGRAM_SCALE_E8M0 = 1 } engram_scale_format;
+
 /* Sizes of one Engram instance (engram-second page, Engram.__init__ and config.json:
  * hc_mult = 4, dim = 5120, n_hash_cols = (engram_max_ngram_size - 1) * engram_n_heads = 24,
  * engram_head_dim = 256, norm_eps = 1e-20, clamp value 1e-6).  scale_block is the number of
- * features sharing one fp32 dequantisation scale (32 on the pages, 128 in the large
- * synthetic workloads). */
+ * features sharing one dequantisation scale (32 on the pages, 128 in the large synthetic
+ * workloads); scale_format is an engram_scale_format (E8M0 needs head_dim / scale_block to be
+ * a multiple of 4, e.g. 256 / 32). */
 typedef struct {
   int32_t hc;
   int32_t dim;
   int32_t n_cols;
   int32_t head_dim;
   int32_t scale_block;
-  int32_t reserved; /* must be 0 */
+  int32_t scale_format; /* engram_scale_format */
   int64_t n_rows;   /* rows of the table: the sum of the prime range lengths */
   float eps;
   float clamp;
@@ -92,13 +98,14 @@ size_t engram_forward_staging_bytes(const engram_layout* layout, int64_t B, int6
 /* S1 + S2: row gather and dequantisation (engram-second page,
  * ParallelEngramEmbedding.forward, single shard; flatten as in Engram.forward).
  *   table    [n_rows, head_dim]   uint8  fp8 e4m3fn codes
- *   scales   [n_rows, head_dim / scale_block] fp32
+ *   scales   [n_rows, head_dim / scale_block] fp32, or uint8 E8M0 exponents (scale_format);
+ *            4-byte aligned
  *   hash_ids [B, T, n_cols]       int64  global row ids
  *   emb      [B, T, n_cols * head_dim] bf16 out:
- *            emb[m, j * head_dim + c] = bf16(fp32(e4m3(table[r, c]) * scales[r, c / scale_block]))
+ *            emb[m, j * head_dim + c] = bf16(fp32(e4m3(table[r, c]) * scale(r, c / scale_block)))
  *            with r = hash_ids[m, j]; rounding to nearest even; NaN is written as 0x7FC0. */
 engram_status engram_gather_dequant(const engram_layout* layout, const uint8_t* table,
-                                    const float* scales, const int64_t* hash_ids, int64_t B,
+                                    const void* scales, const int64_t* hash_ids, int64_t B,
                                     int64_t T, uint16_t* emb, int32_t* err_count,
                                     engram_stream_t stream);
 
@@ -137,7 +144,7 @@ engram_status engram_gate_apply(const engram_layout* layout, const uint16_t* x,
  * the gate reductions. */
 engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
                              const int64_t* hash_ids, const uint8_t* token_mask,
-                             const uint8_t* table, const float* scales, const uint16_t* wkv,
+                             const uint8_t* table, const void* scales, const uint16_t* wkv,
                              const float* q_weight, const float* k_weight, int64_t B, int64_t T,
                              uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream);

@@ -52,6 +52,16 @@ def e4m3fn_value(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
+def e8m0_value(exps: np.ndarray) -> np.ndarray:
+    """Value of E8M0 scale bytes, the block scale of the MXFP8 tables ("Engram in DeepSeek V4.1
+    Flash", Step 2; "DeepSeek's Other Modules", V4.1's two tables, reconciled: E4M3 codes with
+    one E8M0 scale per 32 values).  The format is the OCP Microscaling (MX) v1.0 scale: an 8-bit
+    unsigned biased exponent, value 2^(e - 127) for e = 0 .. 254; e = 255 is NaN."""
+    e = np.asarray(exps, dtype=np.uint8).astype(np.int64)
+    val = np.exp2((e - 127).astype(np.float64))
+    return np.where(e == 255, np.nan, val)
+
+
 def round_fp32(x: np.ndarray) -> np.ndarray:
     """Round doubles to the nearest fp32 (ties to even); returned as float64."""
     with np.errstate(over="ignore"):
@@ -83,7 +93,8 @@ RowFetch = Callable[[np.ndarray], Tuple[np.ndarray, np.ndarray]]
 
 
 def array_fetch(table: np.ndarray, scales: np.ndarray) -> RowFetch:
-    """Row provider over in-memory arrays: table uint8 [n_rows, hd], scales fp32 [n_rows, nb]."""
+    """Row provider over in-memory arrays: table uint8 [n_rows, hd], scales [n_rows, nb] (fp32,
+    or uint8 E8M0 exponents)."""
 
     def fetch(rows: np.ndarray):
         return table[rows], scales[rows]
@@ -91,15 +102,25 @@ def array_fetch(table: np.ndarray, scales: np.ndarray) -> RowFetch:
     return fetch
 
 
+def scale_value(scales: np.ndarray, scale_format: str) -> np.ndarray:
+    """Block scales as float64 values: fp32 scales as stored, or E8M0 exponent bytes."""
+    if scale_format == "fp32":
+        return np.asarray(scales, dtype=np.float32).astype(np.float64)
+    if scale_format == "e8m0":
+        return e8m0_value(scales)
+    raise ValueError(scale_format)
+
+
 def gather_dequant(hash_ids: np.ndarray, fetch: RowFetch, n_rows: int, head_dim: int,
-                   scale_block: int) -> np.ndarray:
+                   scale_block: int, scale_format: str = "fp32") -> np.ndarray:
     """emb bf16 bits [M, C * head_dim] for hash_ids [M, C] (global row ids).
 
     engram-second page, ParallelEngramEmbedding.forward with a single shard: rows outside
     [0, n_rows) are replaced by row 0 for the lookup and then zeroed; the fp8 value of every
     feature is multiplied in fp32 by the scale of its block (feature c uses scale c //
     scale_block) and the product is rounded to bf16.  Engram.forward then flattens the
-    columns: feature c of column j lands at position j * head_dim + c.
+    columns: feature c of column j lands at position j * head_dim + c.  Scales are fp32 (the
+    benchmark workloads' tables) or E8M0 (the official MXFP8 tables, ``scale_format="e8m0"``).
     """
     ids = np.asarray(hash_ids, dtype=np.int64)
     M, C = ids.shape
@@ -107,10 +128,10 @@ def gather_dequant(hash_ids: np.ndarray, fetch: RowFetch, n_rows: int, head_dim:
     local = np.where(out_of_range, 0, ids)
     codes, scales = fetch(local.reshape(-1))
     codes = np.asarray(codes, dtype=np.uint8).reshape(M, C, head_dim)
-    scales = np.asarray(scales, dtype=np.float32).reshape(M, C, head_dim // scale_block)
+    scales = scale_value(scales, scale_format).reshape(M, C, head_dim // scale_block)
     block_of_feature = np.arange(head_dim) // scale_block
     with np.errstate(invalid="ignore", over="ignore"):
-        prod = e4m3fn_value(codes) * scales.astype(np.float64)[:, :, block_of_feature]
+        prod = e4m3fn_value(codes) * scales[:, :, block_of_feature]
     bits = bf16_bits_from_fp32(round_fp32(prod))
     bits[out_of_range] = 0
     return bits.reshape(M, C * head_dim)
@@ -222,11 +243,11 @@ def gate_apply(x_bits, kv_bits, q_weight, k_weight, token_mask, eps, clamp) -> d
 def forward(x_bits: np.ndarray, hash_ids: np.ndarray, token_mask: Optional[np.ndarray],
             fetch: RowFetch, n_rows: int, head_dim: int, scale_block: int, wkv: np.ndarray,
             q_weight: np.ndarray, k_weight: np.ndarray, eps: float = 1e-20,
-            clamp: float = 1e-6) -> dict:
+            clamp: float = 1e-6, scale_format: str = "fp32") -> dict:
     """Engram.forward for tokens x_bits [M, hc, dim] with hash_ids [M, C] and token_mask [M]
     (None = all true).  Tokens are independent, so any subset of a batch can be evaluated
     alone."""
-    emb = gather_dequant(hash_ids, fetch, n_rows, head_dim, scale_block)
+    emb = gather_dequant(hash_ids, fetch, n_rows, head_dim, scale_block, scale_format)
     kv = kv_proj(emb, wkv)
     res = gate_apply(x_bits, kv, q_weight, k_weight, token_mask, eps, clamp)
     return {"emb": emb, "kv": kv, **res}
@@ -255,7 +276,8 @@ def bytes_per_token(n_cols: int, head_dim: int, scale_block: int, scale_bytes: i
 
 
 __all__ = [
-    "e4m3fn_value", "round_fp32", "bf16_bits_from_fp32", "bf16_value", "array_fetch",
+    "e4m3fn_value", "e8m0_value", "scale_value", "round_fp32", "bf16_bits_from_fp32", "bf16_value",
+    "array_fetch",
     "gather_dequant", "kv_proj", "gate", "residual", "gate_apply", "forward", "param_counts",
     "bytes_per_token",
 ]

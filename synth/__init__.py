@@ -125,6 +125,12 @@ def uniform_f32_from_draws(d: np.ndarray, lo: float, hi: float) -> np.ndarray:
     return (np.float64(lo) + w * u).astype(np.float32)
 
 
+def e8m0_from_draws(d: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """E8M0 exponent bytes, uniform integers in [lo, hi] (integer-only, as on the device)."""
+    span = np.uint64(hi - lo + 1)
+    return (np.uint64(lo) + (((d >> _U64(40)) * span) >> _U64(24))).astype(np.uint8)
+
+
 def normal_f32_from_draws(d3: np.ndarray, mean: float, std) -> np.ndarray:
     """d3: [..., 3] uint64 draws -> approximately N(mean, std) rounded to fp32."""
     s = np.zeros(d3.shape[:-1], dtype=np.int64)
@@ -204,6 +210,9 @@ class Workload:
     n_instances: int = 1
     scale_lo: float = 0.01
     scale_hi: float = 0.1
+    scale_format: str = "fp32"        # or "e8m0": one exponent byte per block (MXFP8 tables)
+    e8m0_lo: int = 120                # E8M0 exponents drawn uniformly in [lo, hi] (2^-7 .. 2^-3)
+    e8m0_hi: int = 124
     eps: float = 1e-20
     clamp: float = 1e-6
 
@@ -246,6 +255,8 @@ class Workload:
         rows = np.asarray(rows, dtype=np.int64)
         b = np.arange(self.n_blocks, dtype=np.int64)
         d = draw(self.key(S_SCALES, inst), rows[:, None] * self.n_blocks + b[None, :])
+        if self.scale_format == "e8m0":
+            return e8m0_from_draws(d, self.e8m0_lo, self.e8m0_hi)
         return uniform_f32_from_draws(d, self.scale_lo, self.scale_hi)
 
     def wkv_rows(self, n_lo: int, n_hi: int, inst: int = 0) -> np.ndarray:
@@ -424,8 +435,9 @@ class DeviceFill:
         lib.synth_fill_scales.argtypes = [vp, i64, i64, i32, u64, f64, f64, vp]
         lib.synth_fill_normal_bf16.argtypes = [vp, i64, i64, u64, f64, f64, vp]
         lib.synth_fill_x.argtypes = [vp, i64, i64, i64, u64, u64, u32, f64, f64, vp]
+        lib.synth_fill_e8m0.argtypes = [vp, i64, i64, i32, u64, u32, u32, vp]
         for f in (lib.synth_fill_codes, lib.synth_fill_scales, lib.synth_fill_normal_bf16,
-                  lib.synth_fill_x):
+                  lib.synth_fill_x, lib.synth_fill_e8m0):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -440,6 +452,10 @@ class DeviceFill:
     def scales(self, ptr, row0, nrows, n_blocks, key, lo, hi, stream):
         self._chk(self.lib.synth_fill_scales(ptr, row0, nrows, n_blocks, key, lo, hi, stream),
                   "fill scales")
+
+    def e8m0(self, ptr, row0, nrows, n_blocks, key, lo, hi, stream):
+        self._chk(self.lib.synth_fill_e8m0(ptr, row0, nrows, n_blocks, key, lo, hi, stream),
+                  "fill e8m0")
 
     def normal_bf16(self, ptr, i0, n, key, mean, std, stream):
         self._chk(self.lib.synth_fill_normal_bf16(ptr, i0, n, key, mean, std, stream),
@@ -471,9 +487,14 @@ def device_inputs(w: Workload, inst: int = 0, device: str = "cuda", with_table: 
     if with_table:
         table = torch.empty((w.n_rows, w.head_dim), dtype=torch.uint8, device=dev)
         fill.codes(table.data_ptr(), 0, w.n_rows, w.head_dim, w.key(S_CODES, inst), stream)
-        scales = torch.empty((w.n_rows, w.n_blocks), dtype=torch.float32, device=dev)
-        fill.scales(scales.data_ptr(), 0, w.n_rows, w.n_blocks, w.key(S_SCALES, inst),
-                    w.scale_lo, w.scale_hi, stream)
+        if w.scale_format == "e8m0":
+            scales = torch.empty((w.n_rows, w.n_blocks), dtype=torch.uint8, device=dev)
+            fill.e8m0(scales.data_ptr(), 0, w.n_rows, w.n_blocks, w.key(S_SCALES, inst),
+                      w.e8m0_lo, w.e8m0_hi, stream)
+        else:
+            scales = torch.empty((w.n_rows, w.n_blocks), dtype=torch.float32, device=dev)
+            fill.scales(scales.data_ptr(), 0, w.n_rows, w.n_blocks, w.key(S_SCALES, inst),
+                        w.scale_lo, w.scale_hi, stream)
         out["table"], out["scales"] = table, scales
     wkv = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev)
     fill.normal_bf16(wkv.data_ptr(), 0, w.N * w.K, w.key(S_WKV, inst), 0.0, w.wkv_std, stream)

@@ -90,6 +90,16 @@ __global__ void k_fill_uniform_f32(float* __restrict__ dst, int64_t first, int64
   }
 }
 
+// E8M0 exponent bytes, uniform integers in [lo, hi]: lo + ((draw >> 40) * (hi - lo + 1)) >> 24.
+__global__ void k_fill_e8m0(uint8_t* __restrict__ dst, int64_t first, int64_t n, uint64_t key,
+                            uint32_t lo, uint32_t span) {
+  int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
+    uint64_t d = draw(key, uint64_t(first + i));
+    dst[i] = uint8_t(lo + uint32_t(((d >> 40) * uint64_t(span)) >> 24));
+  }
+}
+
 __global__ void k_fill_normal_bf16(uint16_t* __restrict__ dst, int64_t first, int64_t n,
                                    uint64_t key, double mean, double stdv) {
   int64_t stride = int64_t(gridDim.x) * blockDim.x;
@@ -138,6 +148,17 @@ int synth_fill_scales(float* dst, int64_t row0, int64_t nrows, int32_t n_blocks,
   if (n <= 0) return 0;
   hipLaunchKernelGGL(k_fill_uniform_f32, dim3(grid_for(n, 256)), dim3(256), 0, stream, dst,
                      row0 * n_blocks, n, key, lo, hi);
+  return int(hipGetLastError());
+}
+
+// Fills nrows x n_blocks E8M0 scale bytes, uniform in [lo, hi]; dst points at row row0.
+int synth_fill_e8m0(uint8_t* dst, int64_t row0, int64_t nrows, int32_t n_blocks, uint64_t key,
+                    uint32_t lo, uint32_t hi, hipStream_t stream) {
+  int64_t n = nrows * n_blocks;
+  if (n <= 0) return 0;
+  if (hi < lo || hi > 255u) return int(hipErrorInvalidValue);
+  hipLaunchKernelGGL(k_fill_e8m0, dim3(grid_for(n, 256)), dim3(256), 0, stream, dst,
+                     row0 * n_blocks, n, key, lo, hi - lo + 1u);
   return int(hipGetLastError());
 }
 

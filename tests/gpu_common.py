@@ -30,7 +30,9 @@ def u16(t):
 
 
 def layout(w):
-    return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
+    fmt = eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32
+    return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
+                          scale_format=fmt)
 
 
 _WKV = {}
@@ -55,7 +57,8 @@ def oracle_for(w, sel, inst=0, x_bits=None, keep=1):
     q, k = w.qk(inst)
     x = w.x_tokens(sel) if x_bits is None else x_bits
     return oracle.forward(x, ids, mask, synth.host_fetch(w, inst), w.n_rows, w.head_dim,
-                          w.scale_block, host_wkv(w, inst, keep), q, k, eps=w.eps, clamp=w.clamp)
+                          w.scale_block, host_wkv(w, inst, keep), q, k, eps=w.eps, clamp=w.clamp,
+                          scale_format=w.scale_format)
 
 
 def check_out(w, sel, got_bits, ref, x_bits=None):

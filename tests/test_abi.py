@@ -40,9 +40,14 @@ def good():
 def test_layout_checks():
     assert eg.engram_layout_check(good()) == 0
     assert eg.engram_layout_check(eg.make_layout(4, 256, 6, 64, 32, 6126)) == 0
+    # MXFP8 tables: E8M0 scales, one per 32 features of a 256-feature row
+    assert eg.engram_layout_check(eg.make_layout(4, 5120, 24, 256, 32, 16803844,
+                                                 scale_format=eg.SCALE_E8M0)) == 0
     bad = [dict(hc=3), dict(dim=5000), dict(head_dim=96), dict(scale_block=24),
            dict(scale_block=512), dict(n_rows=0), dict(eps=float("nan")), dict(n_cols=0),
-           dict(reserved=1)]
+           dict(scale_format=2), dict(scale_format=-1),
+           # E8M0 with 2 scales per row (not whole dwords)
+           dict(scale_format=1, scale_block=128)]
     for change in bad:
         lay = good()
         for k, v in change.items():

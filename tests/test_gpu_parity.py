@@ -407,6 +407,74 @@ def test_workspace_sizes_never_decrease_with_token_count():
             last_ws, last_stg, last_ctrl = ws, stg, ws - stg
 
 
+# ---------------------------------------------------------------------------- E8M0 scales
+# MXFP8 tables (E8M0 block scales): the decode layout with one scale per 32 features (the
+# pages' format; weight streaming, and the tiled schedule at 100 tokens), one per 64 features
+# (a scale's byte position in its dword changes from chunk to chunk), and tiny dims with 16
+# features per scale (the narrow streaming loop).  Exponents 120..124 (scales 2^-7 .. 2^-3, the
+# magnitude of the fp32 workloads' scales); the gather test covers all 256 exponents.
+E8M0_DECODE = synth.small_variant(DECODE, name="decode_dims_e8m0_sb32", B=2, T=3, scale_block=32,
+                                  scale_format="e8m0", hash_dist="zipf", mask_false_frac=0.2,
+                                  seed=DECODE.seed + 400)
+E8M0_DECODE64 = synth.small_variant(E8M0_DECODE, name="decode_dims_e8m0_sb64", scale_block=64,
+                                    seed=DECODE.seed + 401)
+E8M0_TILED = synth.small_variant(E8M0_DECODE, name="decode_dims_e8m0_t100", B=1, T=100,
+                                 seed=DECODE.seed + 402)
+E8M0_TINY = synth.small_variant(TINY, name="tiny_e8m0_sb16", scale_block=16, scale_format="e8m0",
+                                seed=TINY.seed + 403)
+
+
+def test_gather_e8m0_all_codes_all_exponents_bad_ids():
+    say("[gpu] gather with E8M0 scales: all 256 codes x all 256 exponents, out-of-range ids")
+    hd, sb = 256, 32
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    exps = np.repeat(np.arange(256, dtype=np.uint8)[:, None], hd // sb, axis=1)
+    exps[7] = np.arange(8, dtype=np.uint8) + 120  # different exponents within one row
+    C = 4
+    rng = np.random.default_rng(13)
+    ids = rng.integers(0, 256, (2, 40, C)).astype(np.int64)
+    ids.reshape(-1)[:256] = np.arange(256)  # every row at least once
+    ids[0, 1, 2] = -1
+    ids[1, 39, 3] = 256
+    lay = eg.make_layout(4, 256, C, hd, sb, 256, scale_format=eg.SCALE_E8M0)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    emb = eg.engram_gather_dequant(lay, torch.from_numpy(codes).cuda(), torch.from_numpy(exps).cuda(),
+                                   torch.from_numpy(ids).cuda(), err_count=err)
+    torch.cuda.synchronize()
+    ref = oracle.gather_dequant(ids.reshape(-1, C), oracle.array_fetch(codes, exps), 256, hd, sb,
+                                scale_format="e8m0")
+    assert np.array_equal(u16(emb).reshape(80, -1), ref)
+    assert int(err.item()) == 2
+
+
+def test_device_fill_e8m0_matches_host_generator():
+    say("[gpu] device fill of E8M0 scales vs host generator")
+    w = E8M0_TINY
+    d = synth.device_inputs(w)
+    assert d["scales"].dtype == torch.uint8
+    assert np.array_equal(d["scales"].cpu().numpy(), w.scales_rows(np.arange(w.n_rows)))
+
+
+@pytest.mark.parametrize("w", [E8M0_DECODE, E8M0_DECODE64, E8M0_TILED, E8M0_TINY],
+                         ids=lambda w: w.name)
+def test_forward_e8m0(w):
+    say(f"[gpu] forward with E8M0 scales: {w.name} (B={w.B} T={w.T}, scale_block {w.scale_block})")
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+    # the rows themselves, bit for bit
+    emb = eg.engram_gather_dequant(layout(w), d["table"], d["scales"], d["hash_ids"])
+    torch.cuda.synchronize()
+    ids = w.hash_ids().reshape(w.M, w.n_cols)
+    ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block,
+                                scale_format="e8m0")
+    assert np.array_equal(u16(emb).reshape(w.M, -1), ref)
+    del d
+    torch.cuda.empty_cache()
+
+
 @pytest.fixture(scope="module")
 def dev_tiled_decode():
     say("[gpu] inputs: decode layout, B=1 T=300")

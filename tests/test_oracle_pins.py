@@ -106,6 +106,38 @@ def test_dequant_matches_torch_conversions_all_codes():
     assert np.array_equal(ours[~nan], ref[~nan])
 
 
+def test_e8m0_decode_matches_torch_float8_e8m0fnu():
+    # the library's E8M0 type (OCP MX scale: 2^(e - 127), 0xFF NaN) on all 256 bytes
+    e = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(e).view(torch.float8_e8m0fnu).float().double().numpy()
+    ours = oracle.e8m0_value(e)
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255])
+    # closed forms: 2^0 at the bias, the extremes
+    assert ours[127] == 1.0 and ours[0] == 2.0 ** -127 and ours[254] == 2.0 ** 127
+
+
+def test_dequant_e8m0_matches_torch_conversions_all_codes_and_exponents():
+    # every e4m3 code against every E8M0 exponent: fp8 value x 2^(e - 127) rounded to fp32 and
+    # then to bf16, as torch computes it (subnormal fp32 products, overflow to inf, NaN scales)
+    hd, sb = 256, 32
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))           # row e: all codes
+    exps = np.repeat(np.arange(256, dtype=np.uint8)[:, None], hd // sb, axis=1)
+    ids = np.arange(256, dtype=np.int64).reshape(-1, 1)
+    ours = oracle.gather_dequant(ids, oracle.array_fetch(codes, exps), 256, hd, sb,
+                                 scale_format="e8m0").reshape(256, hd)
+    v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()
+    sc = torch.from_numpy(exps).view(torch.float8_e8m0fnu).float()
+    ref = (v * sc[:, torch.arange(hd) // sb]).to(torch.bfloat16).view(torch.int16).numpy()
+    ref = ref.view(np.uint16)
+    nan = np.isnan(oracle.bf16_value(ref))
+    assert np.array_equal(nan, ours == 0x7FC0)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # with a power-of-two scale the product is exact wherever it stays a normal bf16 number:
+    # code 0x38 (1.0) at exponent e reproduces 2^(e - 127)
+    assert all(oracle.bf16_value(ours[e, 0x38]) == 2.0 ** (e - 127) for e in range(1, 255))
+
+
 def test_gather_brute_force_flatten_and_scale_blocks():
     """Scalar loops with struct rounding: feature c of column j at j*hd + c, scale c // sb."""
     rng = np.random.default_rng(5)
