@@ -29,7 +29,8 @@ BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 
 def algorithmic_bytes(w) -> int:
     """Bytes one launch must move at least: every input read once, every output written once."""
-    per_token = (w.n_cols * 8 + w.n_cols * w.head_dim + w.n_cols * w.n_blocks * 4 +
+    scale_bytes = 1 if w.scale_format == "e8m0" else 4
+    per_token = (w.n_cols * 8 + w.n_cols * w.head_dim + w.n_cols * w.n_blocks * scale_bytes +
                  2 * w.hc * w.dim * 2 + 1)
     per_call = w.N * w.K * 2 + 2 * w.hc * w.dim * 4
     return per_call + w.M * per_token
@@ -98,7 +99,7 @@ def cpu_baseline(w, n_tokens: int, min_seconds: float = 10.0):
         for wkv, ids, (q, k), fetch in inputs:
             t0 = time.perf_counter()
             x = oracle.forward(x, ids, mask, fetch, w.n_rows, w.head_dim, w.scale_block, wkv, q,
-                               k, eps=w.eps, clamp=w.clamp)["out_bits"]
+                               k, eps=w.eps, clamp=w.clamp, scale_format=w.scale_format)["out_bits"]
             dt += time.perf_counter() - t0
         reps += 1
     return {"value": n_tokens * reps / dt, "unit": "tokens/s", "cores": int(cores),
@@ -146,7 +147,8 @@ def main():
             del d["x"]  # a later instance reads the previous one's output
         insts.append(d)
     x0 = insts[0]["x"]
-    lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp)
+    lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
+                         scale_format=eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32)
     ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.empty_like(x0) for _ in insts]
@@ -217,6 +219,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; no trained weights)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
                    "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
+                   "scale_format": w.scale_format,
                    "table_rows": w.n_rows, "hash_ids": w.hash_dist,
                    "instances": w.n_instances, "flush_mib": args.flush_mib,
                    "parallelism": "single GPU"},

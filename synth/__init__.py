@@ -403,7 +403,10 @@ def workloads() -> dict:
                      head_dim=256, scale_block=128, primes=model_primes(1), seed=_SEED0 + 4,
                      qk_std=0.05, hash_dist="zipf", n_instances=2)
     two_d = dataclasses.replace(two_p, name="two_instance_decode_b256", B=256, T=1)
-    return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d)}
+    # the decode workload over a table in the pages' MXFP8 format (E8M0 scale per 32 features)
+    decode_mx = dataclasses.replace(decode, name="decode_b64_mxfp8", scale_block=32,
+                                    scale_format="e8m0")
+    return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d, decode_mx)}
 
 
 def get(name: str) -> Workload:
