@@ -254,6 +254,55 @@ def forward(x_bits: np.ndarray, hash_ids: np.ndarray, token_mask: Optional[np.nd
 
 
 # ----------------------------------------------------------------------------------------
+# The hash step in front of the path: token ids -> the 24 global row ids of each Engram layer
+# ----------------------------------------------------------------------------------------
+
+
+def hash_ids(input_ids: np.ndarray, token_map: np.ndarray, multipliers: np.ndarray,
+             primes: np.ndarray, offsets: np.ndarray, pad_id: int, history: np.ndarray,
+             start_pos: int = 0, token_mask: Optional[np.ndarray] = None,
+             dead: int = -1) -> np.ndarray:
+    """Hash ids [B, L, n_layers, (max_ngram - 1) * n_heads] of tokens input_ids [B, L] at
+    positions start_pos .. start_pos + L - 1 (engram-second page, code panel, the hash module's
+    forward; "DeepSeek's Other Modules", Engram, The lookup pipeline: compressed ids, one odd
+    multiplier per look-back, XOR, modulo a prime per head).
+
+    token_map [vocab] maps raw ids to compressed ids; tokens whose mask is false become ``dead``
+    (image spans).  ``history`` [B, S] holds the compressed ids of earlier positions of each
+    sequence and receives those of this call (in place).  For each look-back ``shift`` the
+    source id is the history at position - shift; once a source lies before the sequence start
+    or is dead, it and every longer look-back read ``pad_id``.  products = tokens * multipliers
+    [n_layers, max_ngram]; the running XOR over look-backs 0..i is the (i+1)-gram's hash, taken
+    modulo primes[layer, i - 1, head] (floor modulo) and offset by offsets[layer, column].
+
+    Integer dtype decides the arithmetic: int64 arrays wrap modulo 2^64 as the page's int64
+    tensors do; object arrays of Python ints give unbounded products."""
+    ids = np.asarray(input_ids)
+    B, L = ids.shape
+    n_layers, max_ngram = multipliers.shape
+    compressed = np.asarray(token_map)[ids.astype(np.int64)]
+    if token_mask is not None:
+        compressed = np.where(np.asarray(token_mask).astype(bool), compressed, dead)
+    history[:B, start_pos:start_pos + L] = compressed
+    positions = np.arange(start_pos, start_pos + L)
+    blocked = np.zeros((B, L), dtype=bool)
+    tokens = []
+    for shift in range(max_ngram):
+        source = history[:B, np.maximum(positions - shift, 0)]
+        blocked = blocked | (positions < shift)[None, :] | (source == dead)
+        tokens.append(np.where(blocked, pad_id, source))
+    tokens = np.stack(tokens, axis=-1)                          # [B, L, max_ngram]
+    with np.errstate(over="ignore"):
+        products = tokens[:, :, None, :] * multipliers[None, None]  # [B, L, n_layers, max_ngram]
+    rolling = products[..., 0]
+    hashes = []
+    for i in range(1, max_ngram):
+        rolling = rolling ^ products[..., i]
+        hashes.append(np.mod(rolling[..., None], primes[None, None, :, i - 1, :]))
+    return np.concatenate(hashes, axis=-1) + offsets[None, None]
+
+
+# ----------------------------------------------------------------------------------------
 # layout accounting
 # ----------------------------------------------------------------------------------------
 
@@ -278,6 +327,7 @@ def bytes_per_token(n_cols: int, head_dim: int, scale_block: int, scale_bytes: i
 __all__ = [
     "e4m3fn_value", "e8m0_value", "scale_value", "round_fp32", "bf16_bits_from_fp32", "bf16_value",
     "array_fetch",
-    "gather_dequant", "kv_proj", "gate", "residual", "gate_apply", "forward", "param_counts",
+    "gather_dequant", "kv_proj", "gate", "residual", "gate_apply", "forward", "hash_ids",
+    "param_counts",
     "bytes_per_token",
 ]

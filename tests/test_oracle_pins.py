@@ -420,3 +420,98 @@ def test_bytes_per_token_and_totals():
     rows = g("table_rows_first_module") + g("table_rows_second_module")
     assert round(rows * (256 + 8) / 2 ** 30, 1) == g("both_modules_gib")
     assert int(rows * 256 / 2 ** 30) == g("codes_both_layers_gib")
+
+
+# ---------------------------------------------------------------------------- hash step
+
+
+def _hash_case(rng, B, L, n_layers=2, max_ngram=4, n_heads=8, vocab=5000, cvocab=3000):
+    token_map = rng.integers(0, cvocab, vocab).astype(np.int64)
+    mult = (rng.integers(0, 2 ** 63 - 1, (n_layers, max_ngram), dtype=np.int64) * 2 + 1)  # odd, wraps
+    primes = np.array(synth.primes_from(16_000_001, n_layers * (max_ngram - 1) * n_heads),
+                      dtype=np.int64).reshape(n_layers, max_ngram - 1, n_heads)
+    offsets = np.concatenate([np.zeros((n_layers, 1), np.int64),
+                              np.cumsum(primes.reshape(n_layers, -1), axis=1)[:, :-1]], axis=1)
+    ids = rng.integers(0, vocab, (B, L)).astype(np.int64)
+    return ids, token_map, mult, primes, offsets
+
+
+def test_hash_big_int_reproduces_page_demo():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_hash_demo.json")))
+    mult = np.array([[int(m, 16) for m in g["multipliers"]]], dtype=object)      # 1 layer
+    n = g["ngram"]
+    primes = np.array([[g["primes"], g["primes"]]], dtype=object)                 # orders 2 and 3
+    offsets = np.zeros((1, 2 * len(g["primes"])), dtype=object)
+    ids = np.array([g["compressed_ids"]], dtype=object)
+    token_map = np.arange(max(g["compressed_ids"]) + 1, dtype=object)            # already compressed
+    history = np.zeros((1, len(g["compressed_ids"])), dtype=object)
+    out = oracle.hash_ids(ids, token_map, mult, primes, offsets, g["pad_id"], history)
+    assert mult.shape[1] == n
+    assert [int(v) for v in out[0, -1, 0, len(g["primes"]):]] == g["rows_at_last_token"]
+
+
+def _hash_brute_force_int64(ids, token_map, mult, primes, offsets, pad_id, mask=None, dead=-1):
+    """Scalar restatement with explicit two's-complement wrap, one token at a time, in the shape
+    of the page demo's loop (look back, multiply, XOR, modulo each head's prime)."""
+    B, L = ids.shape
+    n_layers, max_ngram = mult.shape
+    n_heads = primes.shape[2]
+    out = np.zeros((B, L, n_layers, (max_ngram - 1) * n_heads), dtype=np.int64)
+    for b in range(B):
+        comp = [int(token_map[i]) for i in ids[b]]
+        if mask is not None:
+            comp = [c if mask[b, t] else dead for t, c in enumerate(comp)]
+        for t in range(L):
+            toks, blocked = [], False
+            for sh in range(max_ngram):
+                src = comp[t - sh] if t - sh >= 0 else None
+                blocked = blocked or src is None or src == dead
+                toks.append(pad_id if blocked else src)
+            for layer in range(n_layers):
+                h = 0
+                for i in range(max_ngram):
+                    prod = (toks[i] * int(mult[layer, i])) % (1 << 64)
+                    h ^= prod
+                    if i >= 1:
+                        sh = h - (1 << 64) if h >= (1 << 63) else h   # as a signed 64-bit value
+                        for k in range(n_heads):
+                            p = int(primes[layer, i - 1, k])
+                            col = (i - 1) * n_heads + k
+                            out[b, t, layer, col] = sh % p + int(offsets[layer, col])
+    return out
+
+
+def test_hash_int64_matches_scalar_brute_force_with_masks():
+    rng = np.random.default_rng(21)
+    ids, tm, mult, primes, offsets = _hash_case(rng, 2, 11)
+    mask = np.ones(ids.shape, dtype=bool)
+    mask[0, 4] = mask[1, 0] = mask[1, 7] = False
+    hist = np.zeros((2, 11), dtype=np.int64)
+    got = oracle.hash_ids(ids, tm, mult, primes, offsets, 2, hist, token_mask=mask)
+    ref = _hash_brute_force_int64(ids, tm, mult, primes, offsets, 2, mask=mask)
+    assert np.array_equal(got, ref)
+    # every id lies in its column's prime range of the module's table
+    lo = offsets[None, None]
+    assert np.all(got >= lo) and np.all(got < lo + primes.reshape(2, -1)[None, None])
+
+
+def test_hash_chunked_calls_equal_one_call_and_dead_blocks_lookback():
+    rng = np.random.default_rng(22)
+    ids, tm, mult, primes, offsets = _hash_case(rng, 3, 40)
+    mask = rng.random(ids.shape) > 0.1
+    h1 = np.zeros((3, 40), dtype=np.int64)
+    whole = oracle.hash_ids(ids, tm, mult, primes, offsets, 2, h1, token_mask=mask)
+    h2 = np.zeros((3, 40), dtype=np.int64)
+    parts = [oracle.hash_ids(ids[:, a:b], tm, mult, primes, offsets, 2, h2, start_pos=a,
+                             token_mask=mask[:, a:b]) for a, b in ((0, 17), (17, 18), (18, 40))]
+    assert np.array_equal(np.concatenate(parts, axis=1), whole) and np.array_equal(h1, h2)
+    # a dead token: right after it, the n-gram sees only the current token, as at a sequence
+    # start; at the dead position itself every look-back reads pad
+    b, t = np.argwhere(~mask[:, 1:-1])[0] + [0, 1]
+    if mask[b, t + 1]:
+        fresh = oracle.hash_ids(ids[b:b + 1, t + 1:t + 2], tm, mult, primes, offsets, 2,
+                                np.zeros((1, 1), dtype=np.int64))
+        assert np.array_equal(whole[b, t + 1], fresh[0, 0])
+    pads = oracle.hash_ids(np.zeros((1, 1), dtype=np.int64), np.array([2]), mult, primes, offsets,
+                           2, np.zeros((1, 1), dtype=np.int64))
+    assert np.array_equal(whole[b, t], pads[0, 0])
