@@ -34,6 +34,12 @@ class EngramLayout(ctypes.Structure):
                 ("clamp", ctypes.c_float)]
 
 
+class HashLayout(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("max_ngram", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("pad_id", ctypes.c_int32), ("vocab", ctypes.c_int64),
+                ("history_len", ctypes.c_int64)]
+
+
 class EngramError(RuntimeError):
     def __init__(self, where: str, status: int):
         msg = _lib.engram_status_str(status).decode()
@@ -56,14 +62,16 @@ _lib.engram_kv_proj.argtypes = [_LP, _vp, _vp, _i64, _i64, _vp, _vp]
 _lib.engram_gate_apply.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.engram_forward.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp,
                                 _sz, _vp, _vp]
+_lib.engram_hash_ids.argtypes = [ctypes.POINTER(HashLayout), _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                 _i64, _i64, _vp, _vp, _vp, _vp]
 for _f in (_lib.engram_layout_check, _lib.engram_param_counts, _lib.engram_gather_dequant,
-           _lib.engram_kv_proj, _lib.engram_gate_apply, _lib.engram_forward):
+           _lib.engram_kv_proj, _lib.engram_gate_apply, _lib.engram_forward, _lib.engram_hash_ids):
     _f.restype = ctypes.c_int
 
 EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_workspace_bytes",
             "engram_forward_staging_bytes",
             "engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
-            "engram_status_str"]
+            "engram_hash_ids", "engram_status_str"]
 
 
 SCALE_FP32, SCALE_E8M0 = 0, 1  # engram_scale_format
@@ -144,6 +152,36 @@ def engram_kv_proj(layout: EngramLayout, emb: torch.Tensor, wkv: torch.Tensor,
     _check("engram_kv_proj", _lib.engram_kv_proj(ctypes.byref(layout), _ptr(emb), _ptr(wkv), B, T,
                                                  _ptr(kv), _stream()))
     return kv
+
+
+def make_hash_layout(n_layers: int, max_ngram: int, n_heads: int, pad_id: int, vocab: int,
+                     history_len: int) -> HashLayout:
+    return HashLayout(n_layers, max_ngram, n_heads, pad_id, vocab, history_len)
+
+
+def engram_hash_ids(layout: HashLayout, token_map: torch.Tensor, multipliers: torch.Tensor,
+                    primes: torch.Tensor, offsets: torch.Tensor, input_ids: torch.Tensor,
+                    history: torch.Tensor, start_pos: int = 0,
+                    token_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row ids [n_layers, B, L, (max_ngram - 1) * n_heads] int64 of tokens input_ids [B, L] at
+    positions start_pos.. (engram_hash_ids in include/engram.h); history [B, history_len] int64
+    is read and updated in place."""
+    B, L = input_ids.shape
+    _contig("token_map", token_map, (torch.int32, torch.uint32) if hasattr(torch, "uint32") else torch.int32)
+    for name, t in (("multipliers", multipliers), ("primes", primes), ("offsets", offsets),
+                    ("input_ids", input_ids), ("history", history)):
+        _contig(name, t, torch.int64)
+    if token_mask is not None:
+        _contig("token_mask", token_mask, (torch.uint8, torch.bool))
+    n_cols = (layout.max_ngram - 1) * layout.n_heads
+    if out is None:
+        out = torch.empty((layout.n_layers, B, L, n_cols), dtype=torch.int64, device=input_ids.device)
+    _check("engram_hash_ids", _lib.engram_hash_ids(
+        ctypes.byref(layout), _ptr(token_map), _ptr(multipliers), _ptr(primes), _ptr(offsets),
+        _ptr(input_ids), _ptr(token_mask), B, L, start_pos, _ptr(history), _ptr(out),
+        _ptr(err_count), _stream()))
+    return out
 
 
 def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,

@@ -20,7 +20,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-flush-denormals-to-zero", "-Wno-unused-command-line-argument"]
 
-ENGRAM_SRC = ["engram_api.hip", "gather_gate.hip", "stream.hip", "tiled.hip"]
+ENGRAM_SRC = ["engram_api.hip", "gather_gate.hip", "hash.hip", "stream.hip", "tiled.hip"]
 LIB_ENGRAM = os.path.join(HERE, "libengram.so")
 LIB_SYNTH = os.path.join(ROOT, "synth", "libsynth_fill.so")
 

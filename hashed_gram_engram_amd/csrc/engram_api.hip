@@ -100,7 +100,7 @@ const char* engram_status_str(engram_status s) {
     case ENGRAM_E_NULL: return "a required pointer is NULL";
     case ENGRAM_E_LAYOUT: return "invalid layout";
     case ENGRAM_E_SHAPE: return "invalid token count";
-    case ENGRAM_E_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ENGRAM_E_ALIGN: return "tensor pointer not aligned as required";
     case ENGRAM_E_WORKSPACE: return "workspace missing or too small";
     case ENGRAM_E_HIP: return "HIP runtime error";
     case ENGRAM_E_DEVICE: return "current device is not gfx950";
@@ -208,6 +208,53 @@ engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const 
   return launch_kv_proj_stream(a, di.cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? ENGRAM_OK
              : ENGRAM_E_HIP;
+}
+
+engram_status engram_hash_ids(const engram_hash_layout* hl, const uint32_t* token_map,
+                              const int64_t* multipliers, const int64_t* primes,
+                              const int64_t* offsets, const int64_t* input_ids,
+                              const uint8_t* token_mask, int64_t B, int64_t L, int64_t start_pos,
+                              int64_t* history, int64_t* hash_ids, int32_t* err_count,
+                              engram_stream_t stream) {
+  if (hl == nullptr) return ENGRAM_E_NULL;
+  if (hl->n_layers < 1 || hl->max_ngram < 2 || hl->max_ngram > 8 || hl->n_heads < 1 || hl->vocab < 1 ||
+      hl->history_len < 1 || int64_t(hl->n_layers) * (hl->max_ngram - 1) * hl->n_heads > (1 << 20))
+    return ENGRAM_E_LAYOUT;
+  if (B < 0 || L < 0 || start_pos < 0) return ENGRAM_E_SHAPE;
+  if (B > 0 && L > (int64_t(1) << 40) / B) return ENGRAM_E_SHAPE;
+  if (start_pos + L > hl->history_len) return ENGRAM_E_SHAPE;
+  if (B * L == 0) return ENGRAM_OK;
+  if (!token_map || !multipliers || !primes || !offsets || !input_ids || !history || !hash_ids)
+    return ENGRAM_E_NULL;
+  if ((reinterpret_cast<uintptr_t>(token_map) & 3u) || (reinterpret_cast<uintptr_t>(multipliers) & 7u) ||
+      (reinterpret_cast<uintptr_t>(primes) & 7u) || (reinterpret_cast<uintptr_t>(offsets) & 7u) ||
+      (reinterpret_cast<uintptr_t>(input_ids) & 7u) || (reinterpret_cast<uintptr_t>(history) & 7u) ||
+      (reinterpret_cast<uintptr_t>(hash_ids) & 7u))
+    return ENGRAM_E_ALIGN;
+  engram_status st;
+  DeviceInfo di;
+  if ((st = device_info(&di)) != ENGRAM_OK) return st;
+  HashArgs a;
+  memset(&a, 0, sizeof(a));
+  a.token_map = token_map;
+  a.multipliers = multipliers;
+  a.primes = primes;
+  a.offsets = offsets;
+  a.input_ids = input_ids;
+  a.token_mask = token_mask;
+  a.history = history;
+  a.hash_ids = hash_ids;
+  a.err_count = err_count;
+  a.B = B;
+  a.L = L;
+  a.start_pos = start_pos;
+  a.vocab = hl->vocab;
+  a.history_len = hl->history_len;
+  a.n_layers = hl->n_layers;
+  a.max_ngram = hl->max_ngram;
+  a.n_heads = hl->n_heads;
+  a.pad_id = hl->pad_id;
+  return launch_hash_ids(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP;
 }
 
 engram_status engram_gate_apply(const engram_layout* l, const uint16_t* x, const uint16_t* kv,

@@ -61,6 +61,23 @@ struct StreamArgs {
   uint32_t spin_budget;
 };
 
+// The hash step: token ids -> row ids of every Engram layer.
+constexpr int64_t kDead = -1;  // compressed id of a token that takes no part in an n-gram
+struct HashArgs {
+  const uint32_t* token_map;   // [vocab]
+  const int64_t* multipliers;  // [n_layers, max_ngram]
+  const int64_t* primes;       // [n_layers, max_ngram - 1, n_heads]
+  const int64_t* offsets;      // [n_layers, (max_ngram - 1) * n_heads]
+  const int64_t* input_ids;    // [B, L]
+  const uint8_t* token_mask;   // [B, L] or null
+  int64_t* history;            // [B, history_len]
+  int64_t* hash_ids;           // [n_layers, B, L, (max_ngram - 1) * n_heads]
+  int32_t* err_count;
+  int64_t B, L, start_pos, vocab, history_len;
+  int n_layers, max_ngram, n_heads, pad_id;
+};
+hipError_t launch_hash_ids(const HashArgs& a, hipStream_t stream);
+
 hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream);
 hipError_t launch_gate_apply(const GateArgs& a, hipStream_t stream);
 

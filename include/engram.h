@@ -37,7 +37,7 @@ typedef enum {
   ENGRAM_E_NULL = -1,      /* a required pointer is NULL                        */
   ENGRAM_E_LAYOUT = -2,    /* the layout violates a constraint listed above      */
   ENGRAM_E_SHAPE = -3,     /* negative B or T, or a size that overflows          */
-  ENGRAM_E_ALIGN = -4,     /* a tensor pointer is not 16-byte aligned            */
+  ENGRAM_E_ALIGN = -4,     /* a tensor pointer is not aligned as required        */
   ENGRAM_E_WORKSPACE = -5, /* workspace missing or smaller than required         */
   ENGRAM_E_HIP = -6,       /* the HIP runtime refused a launch or query          */
   ENGRAM_E_DEVICE = -7     /* the current device is not gfx950                   */
@@ -148,6 +148,48 @@ engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
                              const float* q_weight, const float* k_weight, int64_t B, int64_t T,
                              uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream);
+
+/* The hash step in front of the path (engram-second page, code panel, the hash module's
+ * forward; "DeepSeek's Other Modules", Engram, The lookup pipeline): raw token ids -> the
+ * n_cols = (max_ngram - 1) * n_heads global row ids of every Engram layer.  The model's values:
+ * n_layers = 2 (layers 1 and 14), max_ngram = 4 (2-, 3- and 4-grams), n_heads = 8, pad_id = 2,
+ * vocab = 129,280 (config.json). */
+typedef struct {
+  int32_t n_layers;
+  int32_t max_ngram;   /* 2 .. 8 */
+  int32_t n_heads;
+  int32_t pad_id;      /* compressed id read for a look-back before the start or past a dead token */
+  int64_t vocab;       /* entries of the token map */
+  int64_t history_len; /* positions per sequence the history holds */
+} engram_hash_layout;
+
+/* Per position p = start_pos + l of sequence b: compressed = token_map[input_ids[b, l]], or
+ * dead (-1) where token_mask is 0 (image spans) or the id lies outside [0, vocab) (counted in
+ * *err_count).  Look-back s (0 <= s < max_ngram) takes the compressed id of position p - s (this
+ * call's tokens, or history[b, p - s] for earlier positions); from the first look-back that lies
+ * before position 0 or is dead on, it takes pad_id.  For layer y the products t_s *
+ * multipliers[y, s] wrap modulo 2^64 (two's complement int64, as the page's tensors); their
+ * running XOR over s = 0..n is the (n+1)-gram hash h_n, and column (n - 1) * n_heads + k is
+ * floor_mod(h_n, primes[y, n - 1, k]) + offsets[y, column].
+ *   token_map   [vocab] uint32       compressed ids
+ *   multipliers [n_layers, max_ngram] int64 (odd on the pages)
+ *   primes      [n_layers, max_ngram - 1, n_heads] int64 > 0 (a non-positive prime writes -1
+ *               and counts an error)
+ *   offsets     [n_layers, n_cols] int64
+ *   input_ids   [B, L] int64; token_mask [B, L] uint8 or NULL (all live)
+ *   history     [B, history_len] int64 in/out: compressed ids of positions < start_pos from
+ *               earlier calls; this call writes positions start_pos .. start_pos + L - 1.
+ *               Requires start_pos + L <= history_len.  Chunked calls over a sequence give the
+ *               row ids of one call over the whole of it.
+ *   hash_ids    [n_layers, B, L, n_cols] int64 out, layer-major (the page returns
+ *               [B, L, n_layers, n_cols]): each layer's [B, L, n_cols] slice is contiguous, the
+ *               hash_ids argument of engram_forward for that layer's module. */
+engram_status engram_hash_ids(const engram_hash_layout* layout, const uint32_t* token_map,
+                              const int64_t* multipliers, const int64_t* primes,
+                              const int64_t* offsets, const int64_t* input_ids,
+                              const uint8_t* token_mask, int64_t B, int64_t L, int64_t start_pos,
+                              int64_t* history, int64_t* hash_ids, int32_t* err_count,
+                              engram_stream_t stream);
 
 /* Static description of a status code. */
 const char* engram_status_str(engram_status status);

@@ -47,6 +47,7 @@ _MASK64 = (1 << 64) - 1
 
 # stream ids (one per tensor kind); an instance index is folded in as stream + 64 * inst
 S_CODES, S_SCALES, S_WKV, S_X, S_QW, S_KW, S_HASH, S_MASK, S_OUTLIER, S_PERM = range(1, 11)
+S_TOKMAP, S_MULT, S_IDS, S_SPAN = range(11, 15)  # hash-step inputs
 
 
 # ----------------------------------------------------------------------------------------
@@ -380,6 +381,44 @@ def zipf_ranks(key: int, i0: int, n: int, N: int, s: float, max_tries: int = 32)
         out[todo[ok]] = k[ok].astype(np.int64)
         todo = todo[~ok]
     return out
+
+
+def hash_inputs(seed: int, B: int, L: int, n_layers: int = 2, max_ngram: int = 4, n_heads: int = 8,
+                vocab: int = 129_280, compressed_vocab: int = 99_092, primes=None,
+                span_frac: float = 0.0, span_len: int = 16) -> dict:
+    """Seeded inputs of the hash step at the model's sizes (config.json: vocab 129,280 raw ids,
+    99,092 compressed; 2 layers, 4-grams, 8 heads).  The real token map and multipliers are not
+    available: token_map is a seeded surjection onto the compressed range (every compressed id
+    hit, the rest uniform), multipliers are seeded odd 64-bit values (int64 bit patterns), the
+    primes are the model's (module y takes the y-th 24 primes above 16,000,000) unless given,
+    offsets are the per-module cumulative range starts.  Input ids are uniform; a fraction
+    span_frac of positions starts a dead span (an image) of span_len tokens (token_mask 0)."""
+    key = lambda s: stream_key(seed, s)
+    n_cols = (max_ngram - 1) * n_heads
+    d = draw(key(S_TOKMAP), np.arange(vocab, dtype=np.int64))
+    token_map = ((d >> _U64(32)) * _U64(compressed_vocab) >> _U64(32)).astype(np.int64)
+    token_map[np.arange(min(vocab, compressed_vocab))] = np.arange(min(vocab, compressed_vocab))
+    perm = (draw(key(S_TOKMAP + 64), np.arange(vocab, dtype=np.int64)) >> _U64(11)).argsort(kind="stable")
+    token_map = token_map[perm].astype(np.uint32)
+    mult = (draw(key(S_MULT), np.arange(n_layers * max_ngram, dtype=np.int64)) | _U64(1))
+    mult = mult.view(np.int64).reshape(n_layers, max_ngram)
+    if primes is None:
+        primes = [model_primes(y, n_cols) for y in range(n_layers)]
+    primes = np.asarray(primes, dtype=np.int64).reshape(n_layers, max_ngram - 1, n_heads)
+    flat = primes.reshape(n_layers, n_cols)
+    offsets = np.concatenate([np.zeros((n_layers, 1), np.int64), np.cumsum(flat, axis=1)[:, :-1]],
+                             axis=1)
+    ids = ((draw(key(S_IDS), np.arange(B * L, dtype=np.int64)) >> _U64(32)) * _U64(vocab)
+           >> _U64(32)).astype(np.int64).reshape(B, L)
+    mask = np.ones((B, L), dtype=np.uint8)
+    if span_frac > 0:
+        start = (draw(key(S_SPAN), np.arange(B * L, dtype=np.int64)) >> _U64(40)).astype(np.int64)
+        starts = np.argwhere(start.reshape(B, L) < int(round(span_frac * (1 << 24))))
+        for b, t in starts:
+            mask[b, t:t + span_len] = 0
+    return {"token_map": token_map, "multipliers": mult, "primes": primes, "offsets": offsets,
+            "input_ids": ids, "token_mask": mask, "pad_id": 2, "n_layers": n_layers,
+            "max_ngram": max_ngram, "n_heads": n_heads, "vocab": vocab}
 
 
 _SEED0 = 0x454E4752

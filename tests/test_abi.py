@@ -22,7 +22,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
                  "engram_forward_workspace_bytes", "engram_layout_check", "engram_param_counts",
-                 "engram_status_str"):
+                 "engram_hash_ids", "engram_status_str"):
         assert want in names
 
 
@@ -84,3 +84,23 @@ def test_entry_points_reject_bad_arguments_before_any_device_work():
 def test_status_strings():
     for st in range(-7, 1):
         assert eg._lib.engram_status_str(st)
+
+
+def test_hash_entry_point_rejects_bad_arguments_before_any_device_work():
+    hl = eg.make_hash_layout(2, 4, 8, 2, 129280, 16)
+    lib = eg._lib
+    null = None
+    assert lib.engram_hash_ids(None, null, null, null, null, null, null, 1, 1, 0, null, null,
+                               null, null) == -1
+    bad = eg.make_hash_layout(2, 1, 8, 2, 129280, 16)  # max_ngram < 2
+    assert lib.engram_hash_ids(ctypes.byref(bad), null, null, null, null, null, null, 1, 1, 0,
+                               null, null, null, null) == -2
+    # positions past the history
+    assert lib.engram_hash_ids(ctypes.byref(hl), null, null, null, null, null, null, 1, 10, 7,
+                               null, null, null, null) == -3
+    # nothing to do: no pointer is looked at
+    assert lib.engram_hash_ids(ctypes.byref(hl), null, null, null, null, null, null, 0, 10, 0,
+                               null, null, null, null) == 0
+    # missing tensors
+    assert lib.engram_hash_ids(ctypes.byref(hl), null, null, null, null, null, null, 1, 10, 0,
+                               null, null, null, null) == -1
