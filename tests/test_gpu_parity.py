@@ -254,6 +254,35 @@ def test_forward_equals_composition_in_place_and_deterministic(dev_decode):
     assert np.abs(oracle.bf16_value(u16(a)) - oracle.bf16_value(u16(e))).max() <= 2e-2
 
 
+def test_split_phase_projection_on_a_side_stream_equals_fused(dev_decode):
+    # The pages' serving schedule ("Engram in DeepSeek V4.1 Flash", the later optimisation that
+    # separates lookup, projection and gating): rows and projection as soon as the hash ids are
+    # known, on a stream of their own while other work runs, the gate at the layer's entry.
+    say("[gpu] split phase: gather + projection on a side stream, gate on the main stream")
+    w, d = DECODE, dev_decode
+    lay = layout(w)
+    fused = forward(w, d)
+    torch.cuda.synchronize()
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    filler = torch.randn(4096, 4096, device="cuda")
+    side.wait_stream(main)
+    with torch.cuda.stream(side):
+        emb = eg.engram_gather_dequant(lay, d["table"], d["scales"], d["hash_ids"])
+        kv = eg.engram_kv_proj(lay, emb, d["wkv"])
+        done = torch.cuda.Event()
+        done.record(side)
+    for _ in range(4):
+        filler = filler @ filler / 64.0  # the backbone's work meanwhile
+    main.wait_event(done)
+    out = eg.engram_gate_apply(lay, d["x"], kv, d["q_weight"], d["k_weight"], d["token_mask"])
+    torch.cuda.synchronize()
+    diff = np.abs(u16(out).astype(np.int32) - u16(fused).astype(np.int32))
+    assert (diff > 1).mean() <= 1e-4
+    assert np.abs(oracle.bf16_value(u16(out)) - oracle.bf16_value(u16(fused))).max() <= 2e-2
+    sel = np.arange(w.M)
+    check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel))
+
+
 def test_forward_bad_ids_read_zero_rows():
     say("[gpu] forward with out-of-range hash ids")
     w = synth.small_variant(TINY, name="tiny_bad_ids", seed=TINY.seed + 7)
