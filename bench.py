@@ -32,7 +32,8 @@ def algorithmic_bytes(w) -> int:
     scale_bytes = 1 if w.scale_format == "e8m0" else 4
     per_token = (w.n_cols * 8 + w.n_cols * w.head_dim + w.n_cols * w.n_blocks * scale_bytes +
                  2 * w.hc * w.dim * 2 + 1)
-    per_call = w.N * w.K * 2 + 2 * w.hc * w.dim * 4
+    wkv = w.N * w.K + w.N * (w.K // 32) if w.wkv_format == "mxfp8" else w.N * w.K * 2
+    per_call = wkv + 2 * w.hc * w.dim * 4
     return per_call + w.M * per_token
 
 
@@ -54,6 +55,15 @@ def kernel_of(w):
 
 KERNEL_LABEL = {"k_tiled_fused": "k_gather_dequant + k_tiled<true> (one forward)",
                 "k_stream_wide_fused": "k_stream_wide<.., true>"}
+
+
+def kernel_label(w) -> str:
+    k = kernel_of(w)[0]
+    if w.wkv_format == "mxfp8":
+        if k == "k_tiled_fused":
+            return "k_expand_mxfp8 + " + KERNEL_LABEL[k]
+        return "k_stream_wide<.., true, .., W8> (FP8 weights)"
+    return KERNEL_LABEL[k]
 
 
 def measured_traffic(w):
@@ -91,7 +101,12 @@ def cpu_baseline(w, n_tokens: int, min_seconds: float = 10.0):
     sel = np.arange(n_tokens)
     mask = w.token_mask().reshape(-1)[sel]
     x0 = w.x_tokens(sel)
-    inputs = [(w.wkv_f32(inst), w.hash_ids(inst).reshape(w.M, w.n_cols)[sel], w.qk(inst),
+    def wkv_of(inst):  # FP8 weights are dequantised once, outside the timed region
+        if w.wkv_format == "mxfp8":
+            return oracle.bf16_value(oracle.wkv_mxfp8_bits(*w.wkv8(inst))).astype(np.float32)
+        return w.wkv_f32(inst)
+
+    inputs = [(wkv_of(inst), w.hash_ids(inst).reshape(w.M, w.n_cols)[sel], w.qk(inst),
                synth.host_fetch(w, inst)) for inst in range(w.n_instances)]
     dt, reps = 0.0, 0
     while reps == 0 or dt < min_seconds:
@@ -148,7 +163,8 @@ def main():
         insts.append(d)
     x0 = insts[0]["x"]
     lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
-                         scale_format=eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32)
+                         scale_format=eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32,
+                         wkv_format=eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16)
     ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
                      device="cuda")
     outs = [torch.empty_like(x0) for _ in insts]
@@ -198,7 +214,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
                 "traffic": measured_traffic(w)}
-    roof["kernel"] = KERNEL_LABEL[kernel_of(w)[0]]
+    roof["kernel"] = kernel_label(w)
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
     roof["ms_per_launch"] = round(ms_launch, 5)
@@ -219,7 +235,7 @@ def main():
         "data": "synthetic (seeded counter-based generator; no trained weights)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
                    "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
-                   "scale_format": w.scale_format,
+                   "scale_format": w.scale_format, "wkv_format": w.wkv_format,
                    "table_rows": w.n_rows, "hash_ids": w.hash_dist,
                    "instances": w.n_instances, "flush_mib": args.flush_mib,
                    "parallelism": "single GPU"},

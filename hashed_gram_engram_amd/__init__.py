@@ -30,8 +30,8 @@ STATUS = {0: "ok", -1: "null pointer", -2: "layout", -3: "shape", -4: "alignment
 class EngramLayout(ctypes.Structure):
     _fields_ = [("hc", ctypes.c_int32), ("dim", ctypes.c_int32), ("n_cols", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("scale_block", ctypes.c_int32),
-                ("scale_format", ctypes.c_int32), ("n_rows", ctypes.c_int64), ("eps", ctypes.c_float),
-                ("clamp", ctypes.c_float)]
+                ("scale_format", ctypes.c_int32), ("wkv_format", ctypes.c_int32),
+                ("n_rows", ctypes.c_int64), ("eps", ctypes.c_float), ("clamp", ctypes.c_float)]
 
 
 class HashLayout(ctypes.Structure):
@@ -75,11 +75,21 @@ EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_worksp
 
 
 SCALE_FP32, SCALE_E8M0 = 0, 1  # engram_scale_format
+WKV_BF16, WKV_MXFP8 = 0, 1     # engram_wkv_format
 
 
 def make_layout(hc: int, dim: int, n_cols: int, head_dim: int, scale_block: int, n_rows: int,
-                eps: float = 1e-20, clamp: float = 1e-6, scale_format: int = SCALE_FP32) -> EngramLayout:
-    return EngramLayout(hc, dim, n_cols, head_dim, scale_block, scale_format, n_rows, eps, clamp)
+                eps: float = 1e-20, clamp: float = 1e-6, scale_format: int = SCALE_FP32,
+                wkv_format: int = WKV_BF16) -> EngramLayout:
+    return EngramLayout(hc, dim, n_cols, head_dim, scale_block, scale_format, wkv_format, n_rows,
+                        eps, clamp)
+
+
+def wkv_bytes(layout: EngramLayout) -> int:
+    """Bytes of the wkv argument: N x K bf16, or for MXFP8 the codes [N, K] followed by the
+    E8M0 scales [N, K / 32] in one uint8 buffer."""
+    n, k = (layout.hc + 1) * layout.dim, layout.n_cols * layout.head_dim
+    return n * k + n * (k // 32) if layout.wkv_format == WKV_MXFP8 else 2 * n * k
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -104,6 +114,13 @@ def _contig(name: str, t: torch.Tensor, dtype=None) -> torch.Tensor:
 
 
 _BF16 = (torch.bfloat16, torch.int16)
+
+
+def _check_wkv(layout: EngramLayout, wkv: torch.Tensor):
+    _contig("wkv", wkv, torch.uint8 if layout.wkv_format == WKV_MXFP8 else _BF16)
+    if wkv.numel() * wkv.element_size() != wkv_bytes(layout):
+        raise ValueError(f"wkv holds {wkv.numel() * wkv.element_size()} bytes, the layout needs "
+                         f"{wkv_bytes(layout)}")
 
 
 def engram_layout_check(layout: EngramLayout) -> int:
@@ -142,10 +159,10 @@ def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: tor
 
 def engram_kv_proj(layout: EngramLayout, emb: torch.Tensor, wkv: torch.Tensor,
                    kv: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """kv [B, T, (hc + 1) * dim] bf16 = emb @ wkv^T."""
+    """kv [B, T, (hc + 1) * dim] bf16 = emb @ wkv^T (wkv in the layout's wkv_format)."""
     B, T, _ = emb.shape
     _contig("emb", emb, _BF16)
-    _contig("wkv", wkv, _BF16)
+    _check_wkv(layout, wkv)
     if kv is None:
         kv = torch.empty((B, T, (layout.hc + 1) * layout.dim), dtype=torch.bfloat16,
                          device=emb.device)
@@ -204,22 +221,35 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
     return out
 
 
+def _layout_key(layout: EngramLayout) -> tuple:
+    return tuple(getattr(layout, f) for f, _ in EngramLayout._fields_)
+
+
 class Workspace:
-    """Zero-filled device workspace for engram_forward, grown on demand (the library leaves its
-    control words zero after every call, except the time-out counter in word 0; the staging
-    area at its end holds scratch rows)."""
+    """Zero-filled device workspace for engram_forward, grown on demand.
+
+    The library leaves its control words zero after every call (except the time-out counter
+    in word 0), and the staging area at the buffer's end holds scratch data; calls with one
+    layout never place control words where another call's staging lies.  Calls with another
+    layout may, so when the layout changes the buffer is cleared again (a fill kernel on the
+    current stream), keeping word 0."""
 
     def __init__(self, device=None):
         self.device = device
         self.buf: Optional[torch.Tensor] = None
+        self.layout = None
 
     def get(self, layout: EngramLayout, B: int, T: int) -> torch.Tensor:
         need = max(256, engram_forward_workspace_bytes(layout, B, T))
+        key = _layout_key(layout)
         if self.buf is None or self.buf.numel() < need:
             old = self.buf
             self.buf = torch.zeros(need, dtype=torch.uint8, device=self.device or "cuda")
             if old is not None:  # keep the time-out counter across growth
                 self.buf[:4].copy_(old[:4])
+        elif self.layout is not None and key != self.layout:
+            self.buf[4:].zero_()
+        self.layout = key
         return self.buf
 
 
@@ -237,7 +267,7 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
     _contig("hash_ids", hash_ids, torch.int64)
     _contig("table", table, torch.uint8)
     _contig("scales", scales, torch.uint8 if layout.scale_format == SCALE_E8M0 else torch.float32)
-    _contig("wkv", wkv, _BF16)
+    _check_wkv(layout, wkv)
     _contig("q_weight", q_weight, torch.float32)
     _contig("k_weight", k_weight, torch.float32)
     if token_mask is not None:

@@ -95,6 +95,19 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// D = A * B + C for a 16x16 output block, K = 128, A and B fp8 e4m3 codes with one E8M0 scale
+// per 32 values (v_mfma_scale_f32_16x16x128_f8f6f4).  Lane l supplies row / column l % 16 of
+// A / B: bytes 0..15 at K = 16 (l / 16) + [0, 16), bytes 16..31 at K = 64 + 16 (l / 16) + [0, 16),
+// and the scale of K block l / 16 (K [32 (l / 16), 32 (l / 16) + 32)) of that row / column in the
+// low byte of sa / sb.  (Layout checked on the device against a host evaluation.)
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_mx16x16x128(u32x4 a_lo, u32x4 a_hi, int sa, u32x4 b_lo, u32x4 b_hi, int sb,
+                                                  f32x4 c) {
+  const i32x8 a = {int(a_lo.x), int(a_lo.y), int(a_lo.z), int(a_lo.w), int(a_hi.x), int(a_hi.y), int(a_hi.z), int(a_hi.w)};
+  const i32x8 b = {int(b_lo.x), int(b_lo.y), int(b_lo.z), int(b_lo.w), int(b_hi.x), int(b_hi.y), int(b_hi.z), int(b_hi.w)};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
 // ------------------------------------------------------------------ reductions
 
 __device__ __forceinline__ float wave_sum(float v) {

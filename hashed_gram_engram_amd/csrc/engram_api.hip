@@ -61,6 +61,16 @@ bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
          tiled_shape_ok(int(N_of(l)), int(K_of(l)), l->dim, fused);
 }
 
+bool wkv_mxfp8(const engram_layout* l) { return l->wkv_format == ENGRAM_WKV_MXFP8; }
+
+// The fused weight-streaming kernel reads MXFP8 weights itself for one token block; every other
+// forward with MXFP8 weights first expands them to bf16 in the staging area.
+bool forward_w8_native(const engram_layout* l, int64_t M, int cus) {
+  const int N = int(N_of(l));
+  return wkv_mxfp8(l) && M <= 64 && stream_w8_ok(int(K_of(l)), N, l->head_dim, l->scale_block, cus, true) &&
+         stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim;
+}
+
 // Workspace of engram_forward for M tokens: control words at the start (the schedule in use
 // leaves them zero), then room for the staging area of the tiled schedule, which sits at the
 // END of the caller's buffer.  control(M) is the larger of the two schedules' control sizes for
@@ -82,12 +92,23 @@ size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   return (c + 255) & ~size_t(255);
 }
 
-size_t forward_staging(const engram_layout* l, int64_t M) {
-  return use_tiled(l, M, true) ? tiled_staging_bytes(M, int(K_of(l)), int(N_of(l))) + 256 : 0;
+// Staging area: [tiled schedule: dequantised rows + split partials][MXFP8 weights expanded to
+// bf16], each part 256-byte aligned, plus alignment slack for its start.  Neither part
+// decreases with M (the expansion is absent only for M <= 64 where the fused kernel reads the
+// MXFP8 weights itself).
+size_t forward_staging_tiled(const engram_layout* l, int64_t M) {
+  return use_tiled(l, M, true) ? (tiled_staging_bytes(M, int(K_of(l)), int(N_of(l))) + 255) & ~size_t(255) : 0;
+}
+size_t forward_staging_wkv(const engram_layout* l, int64_t M, int cus) {
+  return wkv_mxfp8(l) && !forward_w8_native(l, M, cus) ? size_t(N_of(l)) * size_t(K_of(l)) * 2 : 0;
+}
+size_t forward_staging(const engram_layout* l, int64_t M, int cus) {
+  const size_t b = forward_staging_tiled(l, M) + forward_staging_wkv(l, M, cus);
+  return b > 0 ? b + 256 : 0;
 }
 
 size_t forward_workspace(const engram_layout* l, int64_t M, int cus) {
-  return forward_control(l, M, cus) + forward_staging(l, M);
+  return forward_control(l, M, cus) + forward_staging(l, M, cus);
 }
 
 }  // namespace
@@ -119,6 +140,7 @@ engram_status engram_layout_check(const engram_layout* l) {
   if (int64_t(l->n_cols) * l->head_dim > (int64_t(1) << 20)) return ENGRAM_E_LAYOUT;
   if (l->n_rows <= 0) return ENGRAM_E_LAYOUT;
   if (l->scale_format != ENGRAM_SCALE_FP32 && l->scale_format != ENGRAM_SCALE_E8M0) return ENGRAM_E_LAYOUT;
+  if (l->wkv_format != ENGRAM_WKV_BF16 && l->wkv_format != ENGRAM_WKV_MXFP8) return ENGRAM_E_LAYOUT;
   // E8M0 scales of a row are whole dwords (the streaming kernel copies them dword-wise)
   if (l->scale_format == ENGRAM_SCALE_E8M0 && (l->head_dim / l->scale_block) % 4 != 0) return ENGRAM_E_LAYOUT;
   if (!(l->eps >= 0.0f) || !isfinite(l->eps) || !(l->clamp >= 0.0f) || !isfinite(l->clamp))
@@ -149,7 +171,9 @@ size_t engram_forward_staging_bytes(const engram_layout* l, int64_t B, int64_t T
   if (engram_layout_check(l) != ENGRAM_OK) return 0;
   int64_t M = 0;
   if (check_tokens(B, T, &M) != ENGRAM_OK) return 0;
-  return forward_staging(l, M);
+  DeviceInfo di;
+  int cus = (device_info(&di) == ENGRAM_OK) ? di.cus : 256;
+  return forward_staging(l, M, cus);
 }
 
 engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table, const void* scales,
@@ -172,7 +196,7 @@ engram_status engram_gather_dequant(const engram_layout* l, const uint8_t* table
                                                                                         : ENGRAM_E_HIP;
 }
 
-engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const uint16_t* wkv, int64_t B,
+engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const void* wkv, int64_t B,
                              int64_t T, uint16_t* kv, engram_stream_t stream) {
   engram_status st = engram_layout_check(l);
   if (st != ENGRAM_OK) return st;
@@ -183,10 +207,28 @@ engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const 
   if (!aligned16(emb) || !aligned16(wkv) || !aligned16(kv)) return ENGRAM_E_ALIGN;
   DeviceInfo di;
   if ((st = device_info(&di)) != ENGRAM_OK) return st;
+  if (wkv_mxfp8(l)) {
+    // MXFP8 weights: the weight-streaming kernel for every token count
+    if (!stream_w8_ok(int(K_of(l)), int(N_of(l)), l->head_dim, l->scale_block, di.cus, false)) return ENGRAM_E_LAYOUT;
+    StreamArgs a;
+    memset(&a, 0, sizeof(a));
+    a.w8 = 1;
+    a.wkv8 = static_cast<const uint8_t*>(wkv);
+    a.wkv8s = a.wkv8 + size_t(N_of(l)) * size_t(K_of(l));
+    a.M = M;
+    a.K = int(K_of(l));
+    a.N = int(N_of(l));
+    a.dim = l->dim;
+    a.emb = emb;
+    a.kv = kv;
+    return launch_kv_proj_stream(a, di.cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? ENGRAM_OK
+                                                                                                  : ENGRAM_E_HIP;
+  }
+  const uint16_t* wkv16 = static_cast<const uint16_t*>(wkv);
   if (use_tiled(l, M, false)) {
     TiledArgs a;
     memset(&a, 0, sizeof(a));
-    a.wkv = wkv;
+    a.wkv = wkv16;
     a.M = M;
     a.K = int(K_of(l));
     a.N = int(N_of(l));
@@ -198,7 +240,7 @@ engram_status engram_kv_proj(const engram_layout* l, const uint16_t* emb, const 
   }
   StreamArgs a;
   memset(&a, 0, sizeof(a));
-  a.wkv = wkv;
+  a.wkv = wkv16;
   a.M = M;
   a.K = int(K_of(l));
   a.N = int(N_of(l));
@@ -279,7 +321,7 @@ engram_status engram_gate_apply(const engram_layout* l, const uint16_t* x, const
 
 engram_status engram_forward(const engram_layout* l, const uint16_t* x, const int64_t* hash_ids,
                              const uint8_t* token_mask, const uint8_t* table, const void* scales,
-                             const uint16_t* wkv, const float* q_weight, const float* k_weight, int64_t B,
+                             const void* wkv_arg, const float* q_weight, const float* k_weight, int64_t B,
                              int64_t T, uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream) {
   engram_status st = engram_layout_check(l);
@@ -287,8 +329,8 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   int64_t M = 0;
   if ((st = check_tokens(B, T, &M)) != ENGRAM_OK) return st;
   if (M == 0) return ENGRAM_OK;
-  if (!x || !hash_ids || !table || !scales || !wkv || !q_weight || !k_weight || !out) return ENGRAM_E_NULL;
-  if (!aligned16(x) || !aligned16(table) || !aligned16(wkv) || !aligned16(q_weight) || !aligned16(k_weight) ||
+  if (!x || !hash_ids || !table || !scales || !wkv_arg || !q_weight || !k_weight || !out) return ENGRAM_E_NULL;
+  if (!aligned16(x) || !aligned16(table) || !aligned16(wkv_arg) || !aligned16(q_weight) || !aligned16(k_weight) ||
       !aligned16(out) || (reinterpret_cast<uintptr_t>(scales) & 3u) || (reinterpret_cast<uintptr_t>(hash_ids) & 7u))
     return ENGRAM_E_ALIGN;
   DeviceInfo di;
@@ -296,6 +338,21 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   const int N = int(N_of(l));
   const size_t need = forward_workspace(l, M, di.cus);
   if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  // the staging area: the last forward_staging() bytes of the buffer, 256-byte aligned
+  const size_t stg = forward_staging(l, M, di.cus);
+  const uintptr_t stg_start =
+      (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes - stg + 255) & ~uintptr_t(255);
+  const bool native8 = forward_w8_native(l, M, di.cus);
+  const uint16_t* wkv = static_cast<const uint16_t*>(wkv_arg);
+  if (wkv_mxfp8(l) && !native8) {
+    // MXFP8 weights for a bf16 schedule: expand them behind the tiled part of the staging area
+    uint16_t* copy = reinterpret_cast<uint16_t*>(stg_start + forward_staging_tiled(l, M));
+    const uint8_t* codes = static_cast<const uint8_t*>(wkv_arg);
+    if (launch_expand_mxfp8(codes, codes + size_t(N) * size_t(K_of(l)), N, int(K_of(l)), copy,
+                            reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+      return ENGRAM_E_HIP;
+    wkv = copy;
+  }
   if (use_tiled(l, M, true)) {
     TiledArgs a;
     memset(&a, 0, sizeof(a));
@@ -324,10 +381,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     a.spin_budget = kSpinBudget;
     GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
                  l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, nullptr, err_count};
-    // the staging area: the last forward_staging() bytes of the buffer, 256-byte aligned
-    const size_t stg = forward_staging(l, M);
-    const uintptr_t start = (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes - stg + 255) & ~uintptr_t(255);
-    return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(start),
+    return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(stg_start),
                                 reinterpret_cast<hipStream_t>(stream)) == hipSuccess
                ? ENGRAM_OK
                : ENGRAM_E_HIP;
@@ -337,6 +391,11 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   StreamArgs a;
   memset(&a, 0, sizeof(a));
   a.wkv = wkv;
+  if (native8) {
+    a.w8 = 1;
+    a.wkv8 = static_cast<const uint8_t*>(wkv_arg);
+    a.wkv8s = a.wkv8 + size_t(N) * size_t(K_of(l));
+  }
   a.M = M;
   a.K = int(K_of(l));
   a.N = N;

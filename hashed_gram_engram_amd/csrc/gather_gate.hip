@@ -133,6 +133,33 @@ __global__ __launch_bounds__(256) void k_gate_apply(GateArgs a) {
   }
 }
 
+// ----------------------------------------------------------------------------------------
+// MXFP8 weights -> bf16 (for the schedules that stream bf16 weights): one thread per 16
+// codes of a row, which share one E8M0 scale (16-aligned pieces of 32-feature blocks).
+// ----------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t n16,
+                                                       int K, uint16_t* out) {
+  const int64_t g = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (g >= n16) return;
+  const int64_t e = g * 16;  // flat element index n * K + k
+  const int64_t n = e / K;
+  const int64_t k = e - n * K;
+  const u32x4 c = *reinterpret_cast<const u32x4*>(codes + e);
+  u32x4 o0, o1;
+  dequant16(c, e8m0_to_f32(scales[n * (K / 32) + k / 32]), o0, o1);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + e);
+  dst[0] = o0;
+  dst[1] = o1;
+}
+
+hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t N, int K, uint16_t* out,
+                               hipStream_t stream) {
+  const int64_t n16 = N * K / 16;
+  const int64_t blocks = (n16 + 255) / 256;
+  hipLaunchKernelGGL(k_expand_mxfp8, dim3(unsigned(blocks)), dim3(256), 0, stream, codes, scales, n16, K, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream) {
   const int64_t threads = a.n_pairs * (a.head_dim >> 4);
   const int64_t blocks = (threads + 255) / 256;

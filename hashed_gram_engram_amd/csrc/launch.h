@@ -37,6 +37,10 @@ struct GateArgs {
 // Engram forward).  Token blocks are 64 tokens; the grid is persistent.
 struct StreamArgs {
   const uint16_t* wkv;  // [N, K] bf16
+  // or, when w8, MXFP8 weights: e4m3fn codes [N, K] and E8M0 scales [N, K / 32]
+  const uint8_t* wkv8;
+  const uint8_t* wkv8s;
+  int w8;
   int64_t M;
   int K, N, dim;
   // projection alone
@@ -91,6 +95,15 @@ int stream_grid(int N, int num_cus);
 // Most rows of wkv one workgroup of the weight-streaming schedule owns.
 int stream_rows_per_group(int N, int G);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
+// Whether the weight-streaming kernels take MXFP8 weights for this shape (the wide K loop:
+// K / 4 a multiple of 128, 1..7 row blocks per workgroup; fused: head_dim a multiple of 128 and
+// scale_block of 32).  The fused kernel takes them for one token block (M <= 64).
+bool stream_w8_ok(int K, int N, int head_dim, int scale_block, int num_cus, bool fused);
+
+// MXFP8 weights -> bf16 [N, K]: out[n, k] = bf16(fp32(e4m3(codes[n, k]) * 2^(scales[n, k / 32] - 127))),
+// the dequantisation rule of the table rows (K a multiple of 32).
+hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t N, int K, uint16_t* out,
+                               hipStream_t stream);
 
 // Arguments of the tiled kernels (256-token x 256-column tiles, for large token counts).
 struct TiledArgs {

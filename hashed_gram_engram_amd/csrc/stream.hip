@@ -22,6 +22,14 @@
 //    constant so no load sits behind a branch.
 //  * narrow (any shape the library accepts): fragments are loaded in MFMA layout directly
 //    (16 rows x 64 bytes per instruction) with a ring of U steps in flight.
+//  * wide with MXFP8 weights (e4m3fn codes, one E8M0 scale per 32 features of a row): the
+//    same schedule over half the bytes.  A row block's slot holds 16 rows x 128 bytes of codes
+//    (8 rows x 128 bytes per copy instruction: 128-byte runs stream as fast as 256-byte ones when
+//    the rows are 6 KB apart) and the chunk's scale dword of each row.  With a table of fp32
+//    scales the fragments are dequantised to bf16 in registers, exactly (a power-of-two scale),
+//    and meet the same bf16 MFMA.  With an MXFP8 table both operands stay fp8 codes and one
+//    scaled fp8 MFMA (16 x 16 x 128, E8M0 scales per 32 features on both sides) takes a whole
+//    chunk: a quarter of the MFMA instructions and no dequantisation at all.
 // In the fused kernel the token operand is gathered: each lane loads the 8 fp8 codes and the
 // scale it needs straight from the table rows named by the hash ids (staged once per token
 // block in LDS) and dequantises them in registers, one chunk ahead of use.
@@ -43,6 +51,8 @@
 // workspace header instead of hanging.  Partial sums and gates pass between workgroups through
 // device-coherent atomic loads and stores ordered by store completion and barriers; counters
 // and gate slots are reset by their last user, so a call leaves them zero.
+#include <string.h>
+
 #include "common.h"
 #include "launch.h"
 
@@ -53,13 +63,15 @@ namespace {
 constexpr int kTB = 64;                          // tokens per token block
 constexpr int kRedBytes = 4 * 2 * 4 * 64 * 16;   // K-partial reduction buffer (two row blocks)
 constexpr int kWBlk = 16 * 256;                  // LDS slot of one row block x 128 features
+constexpr int kWBlk8 = 16 * 128 + 64 * 4;        // the same with MXFP8 weights: codes + scale dwords
 constexpr int kTokBuf_ = 9 * 1024;               // fused wide loop: token buffer per wave
 // LDS in front of the staged hash ids: the weight slots of the wide loop (4 waves x nblk row
-// blocks), which the K-partial reduction reuses afterwards.
-// (The one-round K-partial reduction needs nblk x 16 KB: exactly the weight slots.)
-__host__ __device__ constexpr int wide_lds_bytes(int nblk, bool fused) {
-  return 4 * nblk * kWBlk + (fused ? 4 * kTokBuf_ : 0) > kRedBytes ? 4 * nblk * kWBlk + (fused ? 4 * kTokBuf_ : 0)
-                                                                  : kRedBytes;
+// blocks) and the token buffers, which the one-round K-partial reduction (nblk x 16 KB) reuses
+// afterwards.
+__host__ __device__ constexpr int wide_lds_bytes(int nblk, bool fused, bool w8) {
+  return (4 * nblk * (w8 ? kWBlk8 : kWBlk) + (fused ? 4 * kTokBuf_ : 0)) > (nblk * 16384 > kRedBytes ? nblk * 16384 : kRedBytes)
+             ? 4 * nblk * (w8 ? kWBlk8 : kWBlk) + (fused ? 4 * kTokBuf_ : 0)
+             : (nblk * 16384 > kRedBytes ? nblk * 16384 : kRedBytes);
 }
 
 // First row of workgroup w (rows are dealt in groups of four: Q = N / 4 groups).
@@ -207,6 +219,69 @@ __device__ __forceinline__ void wide_copy_w(char* slot, const StreamArgs& a, con
   }
 }
 
+// MXFP8 weights, unit (row block i, chunk c): copy k in 0..1 fills slot bytes [1024 k, 1024 k +
+// 1024), lane l at 16 l: row 8 k + l / 8, position l % 8, which holds the 16-byte part
+// (l % 8) ^ ((row >> 1) & 7) of the row's 128 chunk bytes (rows 128 bytes apart: with this
+// permutation the 16 rows of a fragment read cover all banks).  Copy 2 puts, for lane l, the
+// dword of E8M0 scales of row l % 16 at features [f, f + 128) (four scales: the chunk is
+// 32-aligned and rows are K / 32 bytes, a multiple of 4) at slot byte 2048 + 4 l.  Not live:
+// the first 128 bytes and scale dword of rows 0..15 (cache resident).
+__device__ __forceinline__ void wide_copy_w8(char* slot, const StreamArgs& a, const Rows& rw, int i, int f_chunk,
+                                             bool live, int lane) {
+  const int rbase = live ? rw.r0 + 16 * i : 0;
+  const int rlast = live ? rw.r1 - 1 : 15;
+  const size_t fbase = live ? size_t(f_chunk) : 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int rr = 8 * k + (lane >> 3);
+    const int r = rbase + rr;
+    const size_t row = size_t(r < rlast ? r : rlast);
+    const int part = (lane & 7) ^ ((rr >> 1) & 7);
+    __builtin_amdgcn_global_load_lds((const void*)(a.wkv8 + row * a.K + fbase + 16 * part),
+                                     (lds_ptr_t)(slot + k * 1024), 16, 0, 2);
+  }
+  const int r = rbase + (lane & 15);
+  const size_t row = size_t(r < rlast ? r : rlast);
+  __builtin_amdgcn_global_load_lds((const void*)(a.wkv8s + row * size_t(a.K / 32) + fbase / 32),
+                                   (lds_ptr_t)(slot + 2048), 4, 0, 0);
+}
+
+// Raw MXFP8 fragment of one lane: codes of its row (l % 16) at features 32 (l / 16) + [0, 32)
+// (parts 2 (l / 16) and 2 (l / 16) + 1) and the scale dword.
+struct Frag8 {
+  u32x4 c0, c1;
+  uint32_t sdw;
+};
+__device__ __forceinline__ Frag8 wide_read_w8(const char* slot, int lane) {
+  const int rr = lane & 15, p0 = 2 * (lane >> 4), sw = (rr >> 1) & 7;
+  Frag8 f;
+  f.c0 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * (p0 ^ sw));
+  f.c1 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * ((p0 + 1) ^ sw));
+  f.sdw = *reinterpret_cast<const uint32_t*>(slot + 2048 + 4 * lane);
+  return f;
+}
+// Raw fragment in the scaled fp8 MFMA's layout: row l % 16 at chunk features 16 (l / 16) +
+// [0, 16) and 64 + 16 (l / 16) + [0, 16) (parts l / 16 and l / 16 + 4), and the scale dword
+// (the MFMA takes the scale of features 32 (l / 16) .. from this lane: byte l / 16).
+__device__ __forceinline__ Frag8 wide_read_w8_mx(const char* slot, int lane) {
+  const int rr = lane & 15, g = lane >> 4, sw = (rr >> 1) & 7;
+  Frag8 f;
+  f.c0 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * (g ^ sw));
+  f.c1 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * ((g + 4) ^ sw));
+  f.sdw = *reinterpret_cast<const uint32_t*>(slot + 2048 + 4 * lane);
+  return f;
+}
+
+// The four bf16 operands (steps s = 0..3: features 8 s .. 8 s + 7 of the lane's 32); the
+// lane's 32 features share the scale in byte l / 16 of the dword.
+__device__ __forceinline__ void wide_operands_w8(u32x4 (&wf)[4], const Frag8& f, int lane) {
+  const float sc = e8m0_to_f32((f.sdw >> (8 * (lane >> 4))) & 0xFFu);
+  wf[0] = dequant8(u32x2{f.c0.x, f.c0.y}, sc);
+  wf[1] = dequant8(u32x2{f.c0.z, f.c0.w}, sc);
+  wf[2] = dequant8(u32x2{f.c1.x, f.c1.y}, sc);
+  wf[3] = dequant8(u32x2{f.c1.z, f.c1.w}, sc);
+}
+
 // Dense token operands (the projection alone) of one chunk for one lane: sub-block t, features
 // f_chunk + 32 * (lane / 16) + [0, 32) of emb, four dwordx4 per sub-block, loaded into
 // registers one chunk ahead.  (The fused kernel copies gathered codes into LDS instead.)
@@ -295,17 +370,37 @@ __device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char*
   }
 }
 
+// Token operands of one chunk for the scaled fp8 MFMA (MXFP8 table): sub-block t, token
+// 16 t + lane % 16, parts lane / 16 and lane / 16 + 4 of its 128 chunk bytes as raw codes, and
+// its E8M0 scale of features 32 (lane / 16) ..  Rows that read as zeros get zero codes and scale
+// 2^0 (a NaN scale of the substitute row must not reach the sum).
+__device__ __forceinline__ void wide_tok_operands_mx(u32x4 (&lo)[4], u32x4 (&hi)[4], int (&sc)[4], const char* tbuf,
+                                                     const uint32_t (&keep)[4], int lane, uint32_t e8m0_shift) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int tok = 16 * t + (lane & 15);
+    const int sw = (tok >> 1) & 7;
+    const int g = lane >> 4;
+    lo[t] = masked(*reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * (g ^ sw)), keep[t]);
+    hi[t] = masked(*reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * ((g + 4) ^ sw)), keep[t]);
+    const uint32_t sw32 = *reinterpret_cast<const uint32_t*>(tbuf + 8192 + t * 256 + 4 * lane);
+    sc[t] = keep[t] ? int((sw32 >> e8m0_shift) & 0xFFu) : 127;
+  }
+}
+
 // Vector memory instructions of one chunk's token operands of a lane (fused: copies).
 template <bool FUSED>
 constexpr int kTokLoads = FUSED ? 12 : 16;
 
-template <int NRB, bool FUSED>
+template <int NRB, bool FUSED, bool W8, bool MX>
 __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
                                           char* slots, int64_t m0, const Rows& rw, int lane, int wv) {
+  constexpr int kSlot = W8 ? kWBlk8 : kWBlk;
+  constexpr int kWIns = W8 ? 3 : 4;  // copy instructions per row block and chunk
   const int q0 = wv * (a.K >> 2);
   const int nch = (a.K >> 2) / 128;
-  char* my_slots = slots + wv * NRB * kWBlk;
-  char* my_tok = slots + 4 * NRB * kWBlk + wv * kTokBuf;  // fused only
+  char* my_slots = slots + wv * NRB * kSlot;
+  char* my_tok = slots + 4 * NRB * kSlot + wv * kTokBuf;  // fused only
   WideTok tk;              // dense only
   uint32_t keep[4];        // fused only
   // prologue in the loop's issue order (tokens, then row blocks)
@@ -314,28 +409,32 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    wide_copy_w(my_slots + i * kWBlk, a, rw, i, q0, true, lane);
+    if constexpr (W8) wide_copy_w8(my_slots + i * kSlot, a, rw, i, q0, true, lane);
+    else wide_copy_w(my_slots + i * kSlot, a, rw, i, q0, true, lane);
     asm volatile("" ::: "memory");
   }
   // Issue order per chunk c: the tokens of chunk c + 1, then (as row block i of chunk c is read)
   // the copies of row block i of chunk c + 1.  So when row block i of chunk c is read, the
   // copies of blocks i + 1 .. NRB - 1 of chunk c, the tokens of chunk c + 1 and the copies of
-  // blocks 0 .. i - 1 of chunk c + 1 -- always 4 (NRB - 1) + kTokLoads instructions -- may still
-  // be in flight.
-  constexpr int kInFlight = 4 * (NRB - 1) + kTokLoads<FUSED>;
+  // blocks 0 .. i - 1 of chunk c + 1 -- always kWIns (NRB - 1) + kTokLoads instructions -- may
+  // still be in flight.
+  constexpr int kInFlight = kWIns * (NRB - 1) + kTokLoads<FUSED>;
   static_assert(kInFlight <= 63, "vmcnt range");
   const int fl = (lane & 15) * 256;  // this lane's fragment row in a slot
   for (int c = 0; c < nch; ++c) {
     const bool live = c + 1 < nch;
     const int fn = q0 + 128 * (live ? c + 1 : c);  // next chunk (tokens re-read the last one)
     u32x4 bt[4][4];
+    u32x4 bx_lo[4], bx_hi[4];  // MX: raw token codes and scales
+    int bx_sc[4];
     if constexpr (FUSED) {
       // the token copies of chunk c have landed once only the weight copies of chunk c remain
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * NRB) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWIns * NRB) : "memory");
       // the lane's E8M0 scale byte within its dword (row scales are whole dwords)
       const int cc_cur = (q0 + 128 * c) % a.head_dim + 32 * (lane >> 4);
       const uint32_t e8m0_shift = uint32_t((cc_cur / a.scale_block) & 3) * 8u;
-      wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
+      if constexpr (MX) wide_tok_operands_mx(bx_lo, bx_hi, bx_sc, my_tok, keep, lane, e8m0_shift);
+      else wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
       wide_copy_tok(my_tok, keep, a, s_ids, fn, lane);
     } else {
@@ -348,19 +447,37 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-      char* slot = my_slots + i * kWBlk;
+      char* slot = my_slots + i * kSlot;
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
       u32x4 wf[4];
+      if constexpr (MX) {
+        const Frag8 f8 = wide_read_w8_mx(slot, lane);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wide_copy_w8(slot, a, rw, i, fn, live, lane);
+        const int wsc = int((f8.sdw >> (8 * (lane >> 4))) & 0xFFu);
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        wf[s] = *reinterpret_cast<const u32x4*>(slot + fl + 16 * ((4 * (lane >> 4) + s) ^ (lane & 15)));
-      // the slot is read (into registers) before its next copy is issued
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      wide_copy_w(slot, a, rw, i, fn, live, lane);
+        for (int t = 0; t < 4; ++t)
+          acc[i][t] = mfma_mx16x16x128(f8.c0, f8.c1, wsc, bx_lo[t], bx_hi[t], bx_sc[t], acc[i][t]);
+      } else if constexpr (W8) {
+        const Frag8 f8 = wide_read_w8(slot, lane);
+        // the slot is read (into registers) before its next copy is issued
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wide_copy_w8(slot, a, rw, i, fn, live, lane);
+        wide_operands_w8(wf, f8, lane);
+      } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s)
+          wf[s] = *reinterpret_cast<const u32x4*>(slot + fl + 16 * ((4 * (lane >> 4) + s) ^ (lane & 15)));
+        // the slot is read (into registers) before its next copy is issued
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        wide_copy_w(slot, a, rw, i, fn, live, lane);
+      }
+      if constexpr (!MX) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[s], bt[s][t], acc[i][t]);
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[s], bt[s][t], acc[i][t]);
+      }
       asm volatile("" ::: "memory");
     }
   }
@@ -701,12 +818,12 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 }
 
 // One 64-token block: stage the hash ids, run the K loop, reduce, finish.
-template <int NRB, bool WIDE, int U, bool FUSED>
+template <int NRB, bool WIDE, int U, bool FUSED, bool W8 = false, bool MX = false>
 __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w,
                                             const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t m0 = tb * kTB;
-  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + (WIDE ? wide_lds_bytes(NRB, FUSED) : kRedBytes));
+  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + (WIDE ? wide_lds_bytes(NRB, FUSED, W8) : kRedBytes));
   KeyPre<NRB> kp;
   if constexpr (FUSED) {
     // hash ids of the token block, checked once: -1 marks a row that reads as zeros.  Eight
@@ -738,7 +855,7 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WIDE) wide_loop<NRB, FUSED>(acc, a, s_ids, smem, m0, rw, lane, wv);
+  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, m0, rw, lane, wv);
   else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rw, lane, wv);
   // the key columns' epilogue inputs are loaded now, so that their latency hides under the
   // K-partial reduction (loaded before the K loop they slow it down: registers)
@@ -766,7 +883,7 @@ __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
 // ONE_TB: the call has a single token block.  Without a loop over token blocks the compiler
 // has nothing to hoist above the hash-id loads; with one it computes every loop-invariant
 // address of the K loop and the epilogue first, about 3 us before the first memory access.
-template <int NLO, int NHI, bool FUSED, bool ONE_TB>
+template <int NLO, int NHI, bool FUSED, bool ONE_TB, bool W8, bool MX = false>
 __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
@@ -775,20 +892,20 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   const Rows rw = rows_of(w, a.N, G);
   if constexpr (ONE_TB) {
     if constexpr (NLO == NHI) {
-      token_block<NLO, true, 1, FUSED>(a, smem, sh, 0, w, rw);
+      token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
     } else {
-      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, 0, w, rw);
-      else token_block<NHI, true, 1, FUSED>(a, smem, sh, 0, w, rw);
+      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
+      else token_block<NHI, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
     }
     return;
   }
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   for (int64_t tb = 0; tb < n_tb; ++tb) {
     if constexpr (NLO == NHI) {
-      token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rw);
+      token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, tb, w, rw);
     } else {
-      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED>(a, smem, sh, tb, w, rw);
-      else token_block<NHI, true, 1, FUSED>(a, smem, sh, tb, w, rw);
+      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, tb, w, rw);
+      else token_block<NHI, true, 1, FUSED, W8, MX>(a, smem, sh, tb, w, rw);
     }
   }
 }
@@ -800,26 +917,36 @@ void* pick_narrow(int nstep) {
   return reinterpret_cast<void*>(&k_stream_narrow<NRB, 1, FUSED>);
 }
 
-template <int NLO, bool FUSED>
+// With MXFP8 weights the fused kernel runs a single token block (larger calls expand the
+// weights and take a bf16 schedule) and the projection alone always loops over token blocks,
+// which halves the instantiations.
+template <int NLO, bool FUSED, bool W8, bool MX>
 void* pick_wide_n(bool same, bool one_tb) {
-  if (one_tb)
-    return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, true>)
-                : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, true>);
-  return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, false>)
-              : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, false>);
+  if constexpr (W8) one_tb = FUSED;
+  if (one_tb) {
+    if constexpr (W8 && !FUSED) return nullptr;
+    else
+      return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, true, W8, MX>)
+                  : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, true, W8, MX>);
+  }
+  if constexpr (MX) return nullptr;
+  if constexpr (W8 && FUSED) return nullptr;
+  else
+    return same ? reinterpret_cast<void*>(&k_stream_wide<NLO, NLO, FUSED, false, W8>)
+                : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, false, W8>);
 }
 
-template <bool FUSED>
+template <bool FUSED, bool W8, bool MX = false>
 void* pick_wide(int nlo, int nhi, bool one_tb) {
   const bool same = nlo == nhi;
   switch (nlo) {
-    case 1: return pick_wide_n<1, FUSED>(same, one_tb);
-    case 2: return pick_wide_n<2, FUSED>(same, one_tb);
-    case 3: return pick_wide_n<3, FUSED>(same, one_tb);
-    case 4: return pick_wide_n<4, FUSED>(same, one_tb);
-    case 5: return pick_wide_n<5, FUSED>(same, one_tb);
-    case 6: return pick_wide_n<6, FUSED>(same, one_tb);
-    case 7: return pick_wide_n<7, FUSED>(same, one_tb);
+    case 1: return pick_wide_n<1, FUSED, W8, MX>(same, one_tb);
+    case 2: return pick_wide_n<2, FUSED, W8, MX>(same, one_tb);
+    case 3: return pick_wide_n<3, FUSED, W8, MX>(same, one_tb);
+    case 4: return pick_wide_n<4, FUSED, W8, MX>(same, one_tb);
+    case 5: return pick_wide_n<5, FUSED, W8, MX>(same, one_tb);
+    case 6: return pick_wide_n<6, FUSED, W8, MX>(same, one_tb);
+    case 7: return pick_wide_n<7, FUSED, W8, MX>(same, one_tb);
     default: return nullptr;
   }
 }
@@ -840,8 +967,14 @@ template <bool FUSED>
 hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   void* fn = nullptr;
   const bool wide = use_wide(a, G, FUSED);
-  if (wide) {
-    fn = pick_wide<FUSED>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
+  if (a.w8) {
+    // MXFP8 weights: the wide loop only; the fused kernel takes one token block
+    if (!wide || (FUSED && a.M > kTB)) return hipErrorInvalidValue;
+    // an MXFP8 table too: both operands stay fp8 (the scaled MFMA)
+    if (FUSED && a.scale_e8m0) fn = pick_wide<true, true, true>(min_blocks(a.N, G), max_blocks(a.N, G), true);
+    else fn = pick_wide<FUSED, true>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
+  } else if (wide) {
+    fn = pick_wide<FUSED, false>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
   } else {
     const int per_wg = max_blocks(a.N, G);
     const int nstep = (a.K / 4) / 32;
@@ -853,7 +986,7 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   if (fn == nullptr) return hipErrorInvalidValue;
   StreamArgs arg = a;
   void* params[] = {&arg};
-  size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(a.N, G), FUSED) : kRedBytes) +
+  size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(a.N, G), FUSED, a.w8 != 0) : kRedBytes) +
                (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
   if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
   if (lds > 163840) return hipErrorInvalidValue;
@@ -891,6 +1024,16 @@ int stream_grid(int N, int num_cus) {
 }
 
 int stream_rows_per_group(int N, int G) { return 4 * ((N / 4 + G - 1) / G); }
+
+bool stream_w8_ok(int K, int N, int head_dim, int scale_block, int num_cus, bool fused) {
+  StreamArgs a;
+  memset(&a, 0, sizeof(a));
+  a.K = K;
+  a.N = N;
+  a.head_dim = head_dim;
+  a.scale_block = scale_block;
+  return use_wide(a, stream_grid(N, num_cus), fused);
+}
 
 // Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
 // block at a fixed stride that depends only on the grid.

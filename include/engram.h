@@ -48,6 +48,15 @@ typedef enum {
  * scale, value 2^(e - 127), 0xFF = NaN). */
 typedef enum { ENGRAM_SCALE_FP32 = 0, ENGRAM_SCALE_E8M0 = 1 } engram_scale_format;
 
+/* Storage of the wkv projection.  BF16: [(hc + 1) * dim, K] bf16, the Linear weight.  MXFP8: the
+ * same matrix as e4m3fn codes with one E8M0 scale per 32 consecutive input features, in ONE
+ * buffer: codes [(hc + 1) * dim, K] uint8, immediately followed by scales [(hc + 1) * dim, K / 32]
+ * uint8 (N * K * 33 / 32 bytes).  Weight (n, k) is bf16(fp32(e4m3(code[n, k]) * 2^(scale[n, k / 32]
+ * - 127))), the table rows' rule, so the projection is that of the bf16 matrix of these values.
+ * (The pages state that the projections are stored in FP8 ("DeepSeek's Other Modules", Engram)
+ * without their scale layout; this one is the MX layout of the tables along the input features.) */
+typedef enum { ENGRAM_WKV_BF16 = 0, ENGRAM_WKV_MXFP8 = 1 } engram_wkv_format;
+
 /* Sizes of one Engram instance (engram-second page, Engram.__init__ and config.json:
  * hc_mult = 4, dim = 5120, n_hash_cols = (engram_max_ngram_size - 1) * engram_n_heads = 24,
  * engram_head_dim = 256, norm_eps = 1e-20, clamp value 1e-6).  scale_block is the number of
@@ -61,6 +70,7 @@ typedef struct {
   int32_t head_dim;
   int32_t scale_block;
   int32_t scale_format; /* engram_scale_format */
+  int32_t wkv_format;   /* engram_wkv_format */
   int64_t n_rows;   /* rows of the table: the sum of the prime range lengths */
   float eps;
   float clamp;
@@ -90,9 +100,10 @@ size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, in
 /* Bytes at the end of the workspace that engram_forward uses as a staging area for B x T
  * tokens: the dequantised rows (B x T x n_cols x head_dim bf16), room for the fp32 partial
  * tiles of a K loop split over two workgroups (taken when a call has few tiles; a fixed amount
- * per layout, 25.6 MB at the decode layout), alignment slack; 0 where the fused
- * weight-streaming schedule runs (up to 64 tokens), which keeps the rows on chip.  Included in
- * engram_forward_workspace_bytes(). */
+ * per layout, 25.6 MB at the decode layout), with MXFP8 weights above 64 tokens (or on shapes
+ * the streaming kernel does not take) the weights expanded to bf16 (N x K x 2 bytes), alignment
+ * slack; 0 where the fused weight-streaming schedule runs (up to 64 tokens), which keeps the
+ * rows on chip.  Included in engram_forward_workspace_bytes(). */
 size_t engram_forward_staging_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
 /* S1 + S2: row gather and dequantisation (engram-second page,
@@ -112,12 +123,15 @@ engram_status engram_gather_dequant(const engram_layout* layout, const uint8_t* 
 /* S3: the wkv projection (engram-second page, self.wkv, a Linear from n_cols * head_dim to
  * (hc + 1) * dim features):
  *   emb [B, T, K] bf16 with K = n_cols * head_dim
- *   wkv [(hc + 1) * dim, K] bf16 (Linear weight layout [out, in])
+ *   wkv [(hc + 1) * dim, K] bf16 (Linear weight layout [out, in]), or the MXFP8 buffer of
+ *       layout->wkv_format (then K / 4 must be a multiple of 128 and the weight-streaming
+ *       schedule must give every compute unit 1 to 8 blocks of 16 rows, as at the model's
+ *       25,600 rows on 256 compute units, else ENGRAM_E_LAYOUT)
  *   kv  [B, T, (hc + 1) * dim] bf16 out: kv[m, n] = bf16(sum_k emb[m, k] * wkv[n, k]),
  *       fp32 accumulation, rounded to nearest even.  Columns [s * dim, (s + 1) * dim) are
  *       the key of stream s; the last dim columns are the shared value. */
 engram_status engram_kv_proj(const engram_layout* layout, const uint16_t* emb,
-                             const uint16_t* wkv, int64_t B, int64_t T, uint16_t* kv,
+                             const void* wkv, int64_t B, int64_t T, uint16_t* kv,
                              engram_stream_t stream);
 
 /* S4 - S6: gate and residual add from a given kv (engram-second page, Engram.forward after
@@ -137,14 +151,14 @@ engram_status engram_gate_apply(const engram_layout* layout, const uint16_t* x,
                                 int64_t T, uint16_t* out, float* gate, engram_stream_t stream);
 
 /* The whole Engram forward in one call (engram-second page, Engram.forward): S1 - S6 with
- * the arguments above.  Key and value stay on chip; only small per-tile partial sums pass
+ * the arguments above (wkv in either format of layout->wkv_format).  Key and value stay on chip; only small per-tile partial sums pass
  * through `workspace` (engram_forward_workspace_bytes), and at large token counts the
  * dequantised rows pass through its staging area.  out may equal x.  Results equal
  * engram_gate_apply(engram_kv_proj(engram_gather_dequant(...))) up to the summation order of
  * the gate reductions. */
 engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
                              const int64_t* hash_ids, const uint8_t* token_mask,
-                             const uint8_t* table, const void* scales, const uint16_t* wkv,
+                             const uint8_t* table, const void* scales, const void* wkv,
                              const float* q_weight, const float* k_weight, int64_t B, int64_t T,
                              uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream);

@@ -171,6 +171,25 @@ def kv_proj(emb_bits: np.ndarray, wkv: np.ndarray, chunk: int = 4096,
     return (out, exact) if with_exact else out
 
 
+def wkv_mxfp8_bits(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns [N, K] of a wkv stored in FP8.
+
+    "DeepSeek's Other Modules", section Engram: the four key projections and the value
+    projection fuse into one FP8 matmul ("The lookup pipeline"), and the projections are FP8
+    like the tables ("V4.1's two tables, reconciled"); the pages give no scale layout for the
+    projection.  Reading: the tables' MXFP8 form applied along the projection's input features,
+    e4m3fn codes [N, K] with one E8M0 scale per 32 consecutive inputs [N, K / 32], dequantised
+    by the tables' rule (fp32 product, then bf16).  The projection is then the bf16 one of
+    ``kv_proj`` over these weights.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    N, K = codes.shape
+    scale = e8m0_value(np.asarray(scales, dtype=np.uint8).reshape(N, K // 32))
+    with np.errstate(invalid="ignore", over="ignore"):
+        prod = e4m3fn_value(codes) * np.repeat(scale, 32, axis=1)
+    return bf16_bits_from_fp32(round_fp32(prod))
+
+
 # ----------------------------------------------------------------------------------------
 # S4 + S5: per-(token, stream) gate
 # ----------------------------------------------------------------------------------------
@@ -327,7 +346,7 @@ def bytes_per_token(n_cols: int, head_dim: int, scale_block: int, scale_bytes: i
 __all__ = [
     "e4m3fn_value", "e8m0_value", "scale_value", "round_fp32", "bf16_bits_from_fp32", "bf16_value",
     "array_fetch",
-    "gather_dequant", "kv_proj", "gate", "residual", "gate_apply", "forward", "hash_ids",
+    "gather_dequant", "kv_proj", "wkv_mxfp8_bits", "gate", "residual", "gate_apply", "forward", "hash_ids",
     "param_counts",
     "bytes_per_token",
 ]

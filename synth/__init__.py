@@ -48,6 +48,7 @@ _MASK64 = (1 << 64) - 1
 # stream ids (one per tensor kind); an instance index is folded in as stream + 64 * inst
 S_CODES, S_SCALES, S_WKV, S_X, S_QW, S_KW, S_HASH, S_MASK, S_OUTLIER, S_PERM = range(1, 11)
 S_TOKMAP, S_MULT, S_IDS, S_SPAN = range(11, 15)  # hash-step inputs
+S_WKV8, S_WKV8S = range(15, 17)  # MXFP8 wkv: codes, E8M0 scales
 
 
 # ----------------------------------------------------------------------------------------
@@ -214,6 +215,9 @@ class Workload:
     scale_format: str = "fp32"        # or "e8m0": one exponent byte per block (MXFP8 tables)
     e8m0_lo: int = 120                # E8M0 exponents drawn uniformly in [lo, hi] (2^-7 .. 2^-3)
     e8m0_hi: int = 124
+    wkv_format: str = "bf16"          # or "mxfp8": e4m3fn codes + one E8M0 scale per 32 inputs
+    wkv_e8m0_lo: int = 119            # wkv scale exponents uniform in [lo, hi] (2^-8 .. 2^-6)
+    wkv_e8m0_hi: int = 121
     eps: float = 1e-20
     clamp: float = 1e-6
 
@@ -265,6 +269,30 @@ class Workload:
         n = (n_hi - n_lo) * self.K
         return normal_bf16(self.key(S_WKV, inst), n_lo * self.K, n, 0.0, self.wkv_std).reshape(
             n_hi - n_lo, self.K)
+
+    def wkv8_rows(self, n_lo: int, n_hi: int, inst: int = 0):
+        """MXFP8 wkv rows [n_lo, n_hi): e4m3fn codes [n, K] (the table codes' distribution) and
+        E8M0 exponents [n, K / 32] uniform in [wkv_e8m0_lo, wkv_e8m0_hi]."""
+        rows = np.arange(n_lo, n_hi, dtype=np.int64)
+        k = np.arange(self.K, dtype=np.int64)
+        codes = codes_from_draws(draw(self.key(S_WKV8, inst), rows[:, None] * self.K + k[None, :]))
+        b = np.arange(self.K // 32, dtype=np.int64)
+        d = draw(self.key(S_WKV8S, inst), rows[:, None] * (self.K // 32) + b[None, :])
+        return codes, e8m0_from_draws(d, self.wkv_e8m0_lo, self.wkv_e8m0_hi)
+
+    def wkv8(self, inst: int = 0, chunk_rows: int = 512, threads: int = 0):
+        """All MXFP8 wkv rows: (codes [N, K] uint8, scales [N, K / 32] uint8)."""
+        codes = np.empty((self.N, self.K), dtype=np.uint8)
+        scales = np.empty((self.N, self.K // 32), dtype=np.uint8)
+
+        def fill(lo):
+            hi = min(self.N, lo + chunk_rows)
+            codes[lo:hi], scales[lo:hi] = self.wkv8_rows(lo, hi, inst)
+
+        n = threads or min(16, os.cpu_count() or 1)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as pool:
+            list(pool.map(fill, range(0, self.N, chunk_rows)))
+        return codes, scales
 
     def wkv_f32(self, inst: int = 0, chunk_rows: int = 512, threads: int = 0) -> np.ndarray:
         """All of wkv as fp32 values; chunks of rows are generated on a thread pool (numpy
@@ -445,7 +473,12 @@ def workloads() -> dict:
     # the decode workload over a table in the pages' MXFP8 format (E8M0 scale per 32 features)
     decode_mx = dataclasses.replace(decode, name="decode_b64_mxfp8", scale_block=32,
                                     scale_format="e8m0")
-    return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d, decode_mx)}
+    # ... and with the projection stored in FP8 as well (MXFP8 along its input features)
+    decode_fp8 = dataclasses.replace(decode_mx, name="decode_b64_fp8", wkv_format="mxfp8")
+    prefill_fp8 = dataclasses.replace(prefill, name="prefill_t8192_fp8", scale_block=32,
+                                      scale_format="e8m0", wkv_format="mxfp8")
+    return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d, decode_mx, decode_fp8,
+                                prefill_fp8)}
 
 
 def get(name: str) -> Workload:
@@ -538,8 +571,15 @@ def device_inputs(w: Workload, inst: int = 0, device: str = "cuda", with_table: 
             fill.scales(scales.data_ptr(), 0, w.n_rows, w.n_blocks, w.key(S_SCALES, inst),
                         w.scale_lo, w.scale_hi, stream)
         out["table"], out["scales"] = table, scales
-    wkv = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev)
-    fill.normal_bf16(wkv.data_ptr(), 0, w.N * w.K, w.key(S_WKV, inst), 0.0, w.wkv_std, stream)
+    if w.wkv_format == "mxfp8":
+        # one buffer: codes [N, K], then scales [N, K / 32]
+        wkv = torch.empty(w.N * w.K + w.N * (w.K // 32), dtype=torch.uint8, device=dev)
+        fill.codes(wkv.data_ptr(), 0, w.N, w.K, w.key(S_WKV8, inst), stream)
+        fill.e8m0(wkv.data_ptr() + w.N * w.K, 0, w.N, w.K // 32, w.key(S_WKV8S, inst),
+                  w.wkv_e8m0_lo, w.wkv_e8m0_hi, stream)
+    else:
+        wkv = torch.empty((w.N, w.K), dtype=torch.bfloat16, device=dev)
+        fill.normal_bf16(wkv.data_ptr(), 0, w.N * w.K, w.key(S_WKV, inst), 0.0, w.wkv_std, stream)
     out["wkv"] = wkv
     q, k = w.qk(inst)
     out["q_weight"] = torch.from_numpy(q).to(dev)

@@ -31,20 +31,25 @@ def u16(t):
 
 def layout(w):
     fmt = eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32
+    wfmt = eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16
     return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
-                          scale_format=fmt)
+                          scale_format=fmt, wkv_format=wfmt)
 
 
 _WKV = {}
 
 
 def host_wkv(w, inst=0, keep=1):
-    """wkv of instance `inst` as fp32 values on the host; the last `keep` are cached."""
-    key = (w.seed, w.N, w.K, inst)
+    """wkv of instance `inst` as fp32 values on the host (FP8 weights dequantised by the
+    oracle); the last `keep` are cached."""
+    key = (w.seed, w.N, w.K, w.wkv_format, inst)
     if key not in _WKV:
         while len(_WKV) >= keep:
             _WKV.pop(next(iter(_WKV)))
-        _WKV[key] = w.wkv_f32(inst)
+        if w.wkv_format == "mxfp8":
+            _WKV[key] = oracle.bf16_value(oracle.wkv_mxfp8_bits(*w.wkv8(inst))).astype(np.float32)
+        else:
+            _WKV[key] = w.wkv_f32(inst)
     return _WKV[key]
 
 

@@ -79,7 +79,8 @@ def _gather_case(w, d, sel_tokens=None):
     got = u16(emb).reshape(w.M, -1)
     ids = w.hash_ids().reshape(w.M, w.n_cols)
     sel = np.arange(w.M) if sel_tokens is None else sel_tokens
-    ref = oracle.gather_dequant(ids[sel], synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    ref = oracle.gather_dequant(ids[sel], synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block,
+                                scale_format=w.scale_format)
     assert np.array_equal(got[sel], ref)
 
 
@@ -131,7 +132,8 @@ def _kv_case(w, d, sel=None):
     got = u16(kv).reshape(w.M, -1)
     sel = np.arange(w.M) if sel is None else sel
     ids = w.hash_ids().reshape(w.M, w.n_cols)[sel]
-    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block,
+                                    scale_format=w.scale_format)
     ref, exact = oracle.kv_proj(emb_ref, host_wkv(w), with_exact=True)
     # fp32 accumulation (any order) then one bf16 rounding: |got - exact| <= ulp(exact) plus the
     # classical sum-of-products bound K * 2^-24 * sum |a| |b|
@@ -163,7 +165,8 @@ def test_kv_proj_decode(dev_decode):
 
 def _gate_case(w, d, in_place=False):
     ids = w.hash_ids().reshape(w.M, w.n_cols)
-    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block)
+    emb_ref = oracle.gather_dequant(ids, synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block,
+                                    scale_format=w.scale_format)
     kv_ref = oracle.kv_proj(emb_ref, host_wkv(w))
     x_bits = w.x_tokens(np.arange(w.M))
     q, k = w.qk()
@@ -434,6 +437,24 @@ def test_workspace_sizes_never_decrease_with_token_count():
             stg = eg.engram_forward_staging_bytes(lay, 1, M)
             assert ws >= last_ws and stg >= last_stg and ws - stg >= last_ctrl, (w.name, M)
             last_ws, last_stg, last_ctrl = ws, stg, ws - stg
+
+
+def test_binding_workspace_shared_by_two_layouts():
+    say("[gpu] the binding's workspace across layouts: a tiled call (staging at the end) "
+        "then three streamed token blocks of another layout (control words over that staging)")
+    a, b = E8M0_TILED, STREAM_ONLY
+    assert (eg.engram_forward_workspace_bytes(layout(b), b.B, b.T) >
+            eg.engram_forward_workspace_bytes(layout(a), a.B, a.T) - eg.engram_forward_staging_bytes(layout(a), a.B, a.T))
+    da, db = synth.device_inputs(a), synth.device_inputs(b)
+    wso = eg.Workspace()  # sized by the first call; the second fits without growing
+    forward(a, da, ws=wso.get(layout(a), a.B, a.T))
+    got = forward(b, db, ws=wso.get(layout(b), b.B, b.T))
+    fresh = torch.zeros(eg.engram_forward_workspace_bytes(layout(b), b.B, b.T), dtype=torch.uint8, device="cuda")
+    want = forward(b, db, ws=fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    del da, db
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------------------- E8M0 scales

@@ -138,6 +138,41 @@ def test_dequant_e8m0_matches_torch_conversions_all_codes_and_exponents():
     assert all(oracle.bf16_value(ours[e, 0x38]) == 2.0 ** (e - 127) for e in range(1, 255))
 
 
+def test_wkv_mxfp8_matches_torch_conversions_all_codes_and_exponents():
+    # FP8 projection weights: row e holds every e4m3 code (in a 256-wide row, 8 scale blocks)
+    # with exponent e in every block; torch's float8 types give the reference values
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    exps = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 256 // 32, axis=1)
+    ours = oracle.wkv_mxfp8_bits(codes, exps)
+    v = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()
+    sc = torch.from_numpy(exps).view(torch.float8_e8m0fnu).float()
+    ref = (v * sc[:, torch.arange(256) // 32]).to(torch.bfloat16).view(torch.int16).numpy()
+    ref = ref.view(np.uint16)
+    nan = np.isnan(oracle.bf16_value(ref))
+    assert np.array_equal(nan, ours == 0x7FC0)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_wkv_mxfp8_scale_of_each_input_block():
+    # all weights 1.0 (code 0x38) at exponent 127, except one scale byte: only the 32 inputs
+    # of that (row, block) change, a transposed or shifted scale index would move them
+    N, K = 5, 256
+    codes = np.full((N, K), 0x38, dtype=np.uint8)
+    exps = np.full((N, K // 32), 127, dtype=np.uint8)
+    exps[2, 5] = 130
+    exps[4, 0] = 125
+    w = oracle.bf16_value(oracle.wkv_mxfp8_bits(codes, exps))
+    want = np.ones((N, K))
+    want[2, 160:192] = 8.0
+    want[4, 0:32] = 0.25
+    assert np.array_equal(w, want)
+    # and a projection through these weights is the bf16 projection of the same values
+    emb = synth.normal_bf16(5, 0, 3 * K, 0.0, 1.0).reshape(3, K)
+    got = oracle.kv_proj(emb, oracle.wkv_mxfp8_bits(codes, exps))
+    ref = F.linear(torch.from_numpy(oracle.bf16_value(emb)), torch.from_numpy(want))
+    assert np.array_equal(got, oracle.bf16_bits_from_fp32(ref.numpy()))
+
+
 def test_gather_brute_force_flatten_and_scale_blocks():
     """Scalar loops with struct rounding: feature c of column j at j*hd + c, scale c // sb."""
     rng = np.random.default_rng(5)
