@@ -25,6 +25,7 @@ import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
 
 def algorithmic_bytes(w) -> int:
@@ -44,16 +45,22 @@ def algorithmic_flops(w) -> int:
 TILED_MIN_TOKENS = 65  # the whole forward switches from weight streaming to 256 x 256 tiles here
 
 
+def fp8_mfma(w) -> bool:
+    """Both operands of the projection stay fp8 (MXFP8 table and weights: the scaled fp8 MFMA)."""
+    return w.wkv_format == "mxfp8" and w.scale_format == "e8m0" and w.scale_block % 32 == 0
+
+
 def kernel_of(w):
     """(profile name, sources) of the kernels that engram_forward runs for this workload: the
     fused weight-streaming kernel for small token counts; for large ones the row gather into the
     staging area followed by the fused tiled kernel (timed together: one forward)."""
     if w.M >= TILED_MIN_TOKENS:
-        return "k_tiled_fused", ("tiled.hip", "gather_gate.hip", "common.h")
+        return ("k_tiled_mx_fused" if fp8_mfma(w) else "k_tiled_fused"), ("tiled.hip", "gather_gate.hip", "common.h")
     return "k_stream_wide_fused", ("stream.hip", "common.h")
 
 
 KERNEL_LABEL = {"k_tiled_fused": "k_gather_dequant + k_tiled<true> (one forward)",
+                "k_tiled_mx_fused": "k_gather_mx + k_tiled<true, true> (fp8 operands; one forward)",
                 "k_stream_wide_fused": "k_stream_wide<.., true>"}
 
 
@@ -62,7 +69,9 @@ def kernel_label(w) -> str:
     if w.wkv_format == "mxfp8":
         if k == "k_tiled_fused":
             return "k_expand_mxfp8 + " + KERNEL_LABEL[k]
-        return "k_stream_wide<.., true, .., W8> (FP8 weights)"
+        if k == "k_stream_wide_fused":
+            return ("k_stream_wide<.., true, .., W8, MX> (fp8 operands)" if fp8_mfma(w)
+                    else "k_stream_wide<.., true, .., W8> (FP8 weights, bf16 MFMA)")
     return KERNEL_LABEL[k]
 
 
@@ -211,8 +220,9 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w)}
     else:
         ach = algorithmic_flops(w) / (ms_launch * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(ach / BF16_PEAK_TFLOPS, 4),
+        peak = FP8_PEAK_TFLOPS if fp8_mfma(w) else BF16_PEAK_TFLOPS  # the contraction's own dtype
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": measured_traffic(w)}
     roof["kernel"] = kernel_label(w)
     roof["per_launch_bytes"] = algorithmic_bytes(w)
@@ -231,7 +241,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 (e4m3 x E8M0)" if fp8_mfma(w) else "bf16",
         "data": "synthetic (seeded counter-based generator; no trained weights)",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
                    "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,

@@ -101,11 +101,17 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 // and the scale of K block l / 16 (K [32 (l / 16), 32 (l / 16) + 32)) of that row / column in the
 // low byte of sa / sb.  (Layout checked on the device against a host evaluation.)
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+// The two 16-byte parts of a lane's operand as one 8-register tuple.
+__device__ __forceinline__ i32x8 mx_operand(u32x4 lo, u32x4 hi) {
+  return __builtin_shufflevector(__builtin_bit_cast(i32x4, lo), __builtin_bit_cast(i32x4, hi), 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f32x4 mfma_mx16x16x128(i32x8 a, int sa, i32x8 b, int sb, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
 __device__ __forceinline__ f32x4 mfma_mx16x16x128(u32x4 a_lo, u32x4 a_hi, int sa, u32x4 b_lo, u32x4 b_hi, int sb,
                                                   f32x4 c) {
-  const i32x8 a = {int(a_lo.x), int(a_lo.y), int(a_lo.z), int(a_lo.w), int(a_hi.x), int(a_hi.y), int(a_hi.z), int(a_hi.w)};
-  const i32x8 b = {int(b_lo.x), int(b_lo.y), int(b_lo.z), int(b_lo.w), int(b_hi.x), int(b_hi.y), int(b_hi.z), int(b_hi.w)};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+  return mfma_mx16x16x128(mx_operand(a_lo, a_hi), sa, mx_operand(b_lo, b_hi), sb, c);
 }
 
 // ------------------------------------------------------------------ reductions

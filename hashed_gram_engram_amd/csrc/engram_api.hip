@@ -92,15 +92,28 @@ size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   return (c + 255) & ~size_t(255);
 }
 
-// Staging area: [tiled schedule: dequantised rows + split partials][MXFP8 weights expanded to
-// bf16], each part 256-byte aligned, plus alignment slack for its start.  Neither part
-// decreases with M (the expansion is absent only for M <= 64 where the fused kernel reads the
-// MXFP8 weights itself).
+// The tiled schedule in fp8 (MXFP8 weights and an MXFP8 table): rows staged as codes + scales,
+// weights read as they are.
+bool forward_tiled_mx(const engram_layout* l, int64_t M) {
+  return wkv_mxfp8(l) && l->scale_format == ENGRAM_SCALE_E8M0 && use_tiled(l, M, true) &&
+         tiled_mx_ok(int(N_of(l)), int(K_of(l)), l->dim, l->scale_block);
+}
+
+// Staging area: [tiled schedule: staged rows + split partials][MXFP8 weights expanded to bf16],
+// each part 256-byte aligned, plus alignment slack for its start.  Neither part decreases with M
+// (the expansion is absent where a kernel reads the MXFP8 weights itself: the fused streaming
+// kernel up to 64 tokens, the fp8 tiled kernel above, both with an MXFP8 table; with fp32 table
+// scales only the former).
 size_t forward_staging_tiled(const engram_layout* l, int64_t M) {
-  return use_tiled(l, M, true) ? (tiled_staging_bytes(M, int(K_of(l)), int(N_of(l))) + 255) & ~size_t(255) : 0;
+  if (!use_tiled(l, M, true)) return 0;
+  const size_t b = forward_tiled_mx(l, M) ? tiled_staging_bytes_mx(M, int(K_of(l)), int(N_of(l)))
+                                          : tiled_staging_bytes(M, int(K_of(l)), int(N_of(l)));
+  return (b + 255) & ~size_t(255);
 }
 size_t forward_staging_wkv(const engram_layout* l, int64_t M, int cus) {
-  return wkv_mxfp8(l) && !forward_w8_native(l, M, cus) ? size_t(N_of(l)) * size_t(K_of(l)) * 2 : 0;
+  return wkv_mxfp8(l) && !forward_w8_native(l, M, cus) && !forward_tiled_mx(l, M)
+             ? size_t(N_of(l)) * size_t(K_of(l)) * 2
+             : 0;
 }
 size_t forward_staging(const engram_layout* l, int64_t M, int cus) {
   const size_t b = forward_staging_tiled(l, M) + forward_staging_wkv(l, M, cus);
@@ -343,8 +356,9 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   const uintptr_t stg_start =
       (reinterpret_cast<uintptr_t>(workspace) + workspace_bytes - stg + 255) & ~uintptr_t(255);
   const bool native8 = forward_w8_native(l, M, di.cus);
+  const bool tiled8 = forward_tiled_mx(l, M);
   const uint16_t* wkv = static_cast<const uint16_t*>(wkv_arg);
-  if (wkv_mxfp8(l) && !native8) {
+  if (wkv_mxfp8(l) && !native8 && !tiled8) {
     // MXFP8 weights for a bf16 schedule: expand them behind the tiled part of the staging area
     uint16_t* copy = reinterpret_cast<uint16_t*>(stg_start + forward_staging_tiled(l, M));
     const uint8_t* codes = static_cast<const uint8_t*>(wkv_arg);
@@ -357,6 +371,11 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     TiledArgs a;
     memset(&a, 0, sizeof(a));
     a.wkv = wkv;
+    if (tiled8) {
+      a.mx = 1;
+      a.wkv8 = static_cast<const uint8_t*>(wkv_arg);
+      a.wkv8s = a.wkv8 + size_t(N) * size_t(K_of(l));
+    }
     a.M = M;
     a.K = int(K_of(l));
     a.N = N;

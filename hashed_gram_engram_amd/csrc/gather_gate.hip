@@ -134,6 +134,39 @@ __global__ __launch_bounds__(256) void k_gate_apply(GateArgs a) {
 }
 
 // ----------------------------------------------------------------------------------------
+// Row gather without dequantisation, for the fp8 tiled schedule (E8M0 table scales): the codes
+// as they are and one E8M0 byte per 32 features (a table scale covers scale_block / 32 of
+// them).  One thread per 16 codes; the even ones also write their 32-feature block's scale.
+// ----------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gather_mx(GatherArgs a, uint8_t* codes8, uint8_t* scales8) {
+  const int chunks = a.head_dim >> 4;
+  const int nb = a.head_dim / a.scale_block;
+  const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t pair = gid / chunks;
+  const int ch = int(gid - pair * chunks);
+  if (pair >= a.n_pairs) return;
+  const int64_t r = a.hash_ids[pair];
+  const bool ok = r >= 0 && r < a.n_rows;
+  u32x4 c = {0u, 0u, 0u, 0u};
+  uint8_t sc = 127;
+  if (ok) {
+    c = *reinterpret_cast<const u32x4*>(a.table + r * a.head_dim + ch * 16);
+    sc = static_cast<const uint8_t*>(a.scales)[r * nb + (ch * 16) / a.scale_block];
+  } else if (ch == 0 && a.err_count != nullptr) {
+    atomicAdd(a.err_count, 1);
+  }
+  *reinterpret_cast<u32x4*>(codes8 + pair * a.head_dim + ch * 16) = c;
+  if ((ch & 1) == 0) scales8[pair * (a.head_dim / 32) + ch / 2] = sc;
+}
+
+hipError_t launch_gather_mx(const GatherArgs& a, uint8_t* codes8, uint8_t* scales8, hipStream_t stream) {
+  const int64_t threads = a.n_pairs * (a.head_dim >> 4);
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(k_gather_mx, dim3(unsigned(blocks)), dim3(256), 0, stream, a, codes8, scales8);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------------------
 // MXFP8 weights -> bf16 (for the schedules that stream bf16 weights): one thread per 16
 // codes of a row, which share one E8M0 scale (16-aligned pieces of 32-feature blocks).
 // ----------------------------------------------------------------------------------------

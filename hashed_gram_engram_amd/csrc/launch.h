@@ -83,6 +83,10 @@ struct HashArgs {
 hipError_t launch_hash_ids(const HashArgs& a, hipStream_t stream);
 
 hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream);
+// Gather without dequantisation (E8M0 tables): codes [pairs, head_dim] to codes8 and one E8M0
+// byte per 32 features to scales8 [pairs, head_dim / 32]; rows that read as zeros get zero codes
+// and scale 127 (2^0).
+hipError_t launch_gather_mx(const GatherArgs& a, uint8_t* codes8, uint8_t* scales8, hipStream_t stream);
 hipError_t launch_gate_apply(const GateArgs& a, hipStream_t stream);
 
 // Projection alone: kv = bf16(emb @ wkv^T).
@@ -108,6 +112,13 @@ hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
 // Arguments of the tiled kernels (256-token x 256-column tiles, for large token counts).
 struct TiledArgs {
   const uint16_t* wkv;  // [N, K] bf16
+  // fp8 schedule (MXFP8 weights and an MXFP8 table): weight codes [N, K] and E8M0 scales
+  // [N, K / 32]; the gathered rows are staged as codes [M, K] and E8M0 scales [M, K / 32]
+  int mx;
+  const uint8_t* wkv8;
+  const uint8_t* wkv8s;
+  const uint8_t* tok8;
+  const uint8_t* tok8s;
   int64_t M;
   int K, N, dim;
   // projection alone
@@ -140,11 +151,15 @@ struct TiledArgs {
 
 // Shapes the tiled kernels take: N a multiple of 256, K of 64 (fused: also dim of 256).
 bool tiled_shape_ok(int N, int K, int dim, bool fused);
+// The fp8 tiled schedule (fused only): also K a multiple of 128, and the table's E8M0 scales
+// covering whole 32-feature blocks (scale_block a multiple of 32).
+bool tiled_mx_ok(int N, int K, int dim, int scale_block);
 // Control words of the fused tiled schedule (zero before and after every call) and its staging
 // area: the dequantised rows (M x K bf16) and room for the split-K partial tiles (contents
 // unspecified after a call).  Neither size decreases with M.
 size_t tiled_control_bytes(int64_t M, int dim);
 size_t tiled_staging_bytes(int64_t M, int K, int N);
+size_t tiled_staging_bytes_mx(int64_t M, int K, int N);  // rows as fp8 codes + E8M0 scales
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream);
 // Whole forward, tiled schedule: the gather pass `g` writes the dequantised rows into `staging`
 // (tiled_staging_bytes, 256-byte aligned), then the tiled kernel runs with `workspace` as its

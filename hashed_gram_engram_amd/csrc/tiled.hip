@@ -25,6 +25,15 @@
 // workgroups compute each tile, one over each half of K; the first to finish leaves its fp32
 // partial tile in the staging area and the second adds it and runs the epilogue (split_merge).
 //
+// fp8 schedule (MXFP8 weights and an MXFP8 table, fused forward only): the gather pass stages
+// the rows as fp8 codes plus one E8M0 byte per 32 features, and both operands stay fp8.  A stage
+// is 128 features (128-byte rows, the same LDS row layout and copy instructions) plus each row's
+// dword of four scales; both operands have rings of two slots (copied one stage ahead; 4 x 32 KB
+// + 4 KB of scales).  The MFMA is v_mfma_scale_f32_16x16x128_f8f6f4 (twice the bf16 rate; a
+// lane supplies 16-byte parts l / 16 and l / 16 + 4 of its row and the scale of 32-feature block
+// l / 16); a half stage is 4 wkv row blocks x 4 token blocks (16 MFMAs of K = 128, as long as the
+// 32 bf16 MFMAs of a bf16 half stage), the token fragments being read once per stage.
+//
 // Tile order: token blocks are taken in groups of 32; inside a group, workgroup b takes token
 // block b % 32 and column block b / 32 (a last, smaller group likewise with its own size), so
 // the 256 tiles resident at one time cover 32 token panels and 8 weight panels, each XCD
@@ -230,6 +239,192 @@ __device__ __forceinline__ void tile_gemm(TileAcc& acc, const TiledArgs& a, char
     k_loop<0>(acc, p, lds, ns);
   else
     k_loop<1>(acc, p, lds, ns);
+}
+
+// ---------------------------------------------------------------- fp8 schedule
+constexpr int kMxK = 128;                        // features per stage
+constexpr int kMxScaleOff = 4 * kOpB;            // scale slots: wkv 2 x 1 KB, then tokens 2 x 1 KB
+constexpr int kMxBOff = 2 * kOpB;                // token ring offset
+static_assert(kMxScaleOff + 4096 <= kLds, "fp8 schedule LDS");
+
+struct PipeMx {
+  const char* a_src[kCopies];  // per-lane global source of each wkv copy at stage 0
+  const char* b_src[kCopies];  // the same for the token copies
+  const char* s_src;           // this lane's scale dword source at stage 0 (wkv rows for waves 0-3)
+  uint32_t s_dst;              // byte offset of the wave's 256 scale bytes within a scale slot pair
+  uint32_t lo_off, hi_off;     // per-lane offsets of the two 16-byte parts of a fragment read
+  int wv_u;
+  int a_off, b_off;            // byte offsets of this wave's first wkv row and first token row
+  int sa_off, sb_off;          // byte offsets of their scale dwords in a scale slot
+};
+
+// Stage t of both operands and their scales into ring slot t & 1: 4 + 4 + 1 copy instructions.
+__device__ __forceinline__ void copy_stage_mx(const PipeMx& p, char* lds, int t) {
+  const int r = t & 1;
+  copy_op(p.a_src, lds + r * kOpB, p.wv_u, t);
+  copy_op(p.b_src, lds + kMxBOff + r * kOpB, p.wv_u, t);
+  __builtin_amdgcn_global_load_lds((const void*)(p.s_src + size_t(t) * 4),
+                                   (lds_ptr_t)(lds + kMxScaleOff + r * 1024 + p.s_dst), 4, 0, 0);
+}
+
+struct FragMx {
+  i32x8 a[4];  // wkv row blocks of the half stage: parts l / 16, l / 16 + 4
+  int sa[4];
+  i32x8 b[4];  // token blocks
+  int sb[4];
+};
+
+__device__ __forceinline__ int scale_byte(uint32_t dw, int lane) { return int((dw >> (8 * (lane >> 4))) & 0xFFu); }
+
+// wkv fragments of half hh (row blocks 4 hh .. 4 hh + 3 of the wave's 8) of the stage in slot r.
+__device__ __forceinline__ void read_a_mx(FragMx& F, const PipeMx& p, const char* lds, int r, int hh, int lane) {
+  const char* A = lds + r * kOpB + p.a_off;
+  const char* S = lds + kMxScaleOff + r * 1024 + p.sa_off;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * hh + k;
+    F.a[k] = mx_operand(*reinterpret_cast<const u32x4*>(A + i * 16 * kRowB + p.lo_off),
+                        *reinterpret_cast<const u32x4*>(A + i * 16 * kRowB + p.hi_off));
+    F.sa[k] = scale_byte(*reinterpret_cast<const uint32_t*>(S + i * 64), lane);
+  }
+}
+__device__ __forceinline__ void read_b_mx(FragMx& F, const PipeMx& p, const char* lds, int r, int lane) {
+  const char* B = lds + kMxBOff + r * kOpB + p.b_off;
+  const char* S = lds + kMxScaleOff + 2048 + r * 1024 + p.sb_off;
+#pragma unroll
+  for (int j = 0; j < kBJ; ++j) {
+    F.b[j] = mx_operand(*reinterpret_cast<const u32x4*>(B + j * 16 * kRowB + p.lo_off),
+                        *reinterpret_cast<const u32x4*>(B + j * 16 * kRowB + p.hi_off));
+    F.sb[j] = scale_byte(*reinterpret_cast<const uint32_t*>(S + j * 64), lane);
+  }
+}
+// (The empty asm statements pin the MFMAs to their phase: otherwise the compiler sinks them
+// past the phase barrier, next to the following phase's fragment reads, with both halves'
+// fragments live at once.)
+__device__ __forceinline__ void half_mma_mx(TileAcc& acc, const FragMx& F, int hh) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j)
+      acc[4 * hh + k][j] = mfma_mx16x16x128(F.a[k], F.sa[k], F.b[j], F.sb[j], acc[4 * hh + k][j]);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) asm volatile("" : "+v"(acc[4 * hh + k][j]));
+}
+
+// The fp8 K loop of group G over S stages of 128 features, rings of two slots:
+//   group 0: phase 4 J multiplies half 0 of stage J, 4 J + 1 reads half 1, 4 J + 2 multiplies
+//            it, 4 J + 3 issues the copies of stage J + 2 and reads half 0 (and the token
+//            fragments) of stage J + 1;
+//   group 1: phase 4 J reads half 0 (and the token fragments) of stage J, 4 J + 1 multiplies
+//            it, 4 J + 2 reads half 1, 4 J + 3 issues the copies of stage J + 2 and multiplies
+//            half 1.
+// Stage J's slots are last read in phase 4 J + 2, so stage J + 2 may overwrite them from phase
+// 4 J + 3 on; at the end of phase 4 J + 2 every wave waits for all its copies (stage J + 1, the
+// only ones in flight), which group 0 starts reading in phase 4 J + 3.
+template <int G>
+__device__ __forceinline__ void k_loop_mx(TileAcc& acc, const PipeMx& p, char* lds, int S, int lane) {
+  FragMx F;
+  copy_stage_mx(p, lds, 0);
+  if (S > 1) copy_stage_mx(p, lds, 1);
+  if (S > 1) wait_copies<9>();
+  else wait_copies<0>();
+  phase_end();
+  if constexpr (G == 0) {
+    read_a_mx(F, p, lds, 0, 0, lane);
+    read_b_mx(F, p, lds, 0, lane);
+    wait_frags();
+  }
+  phase_end();
+  for (int J = 0; J < S; ++J) {
+    const int r = J & 1;
+    if constexpr (G == 0) {
+      half_mma_mx(acc, F, 0);                                     // 4 J
+      phase_end();
+      read_a_mx(F, p, lds, r, 1, lane);                           // 4 J + 1
+      wait_frags();
+      phase_end();
+      half_mma_mx(acc, F, 1);                                     // 4 J + 2
+      wait_copies<0>();
+      phase_end();
+      if (J + 2 < S) copy_stage_mx(p, lds, J + 2);                // 4 J + 3
+      if (J + 1 < S) {
+        read_a_mx(F, p, lds, r ^ 1, 0, lane);
+        read_b_mx(F, p, lds, r ^ 1, lane);
+        wait_frags();
+      }
+      phase_end();
+    } else {
+      read_a_mx(F, p, lds, r, 0, lane);                           // 4 J
+      read_b_mx(F, p, lds, r, lane);
+      wait_frags();
+      phase_end();
+      half_mma_mx(acc, F, 0);                                     // 4 J + 1
+      phase_end();
+      read_a_mx(F, p, lds, r, 1, lane);                           // 4 J + 2
+      wait_frags();
+      wait_copies<0>();
+      phase_end();
+      if (J + 2 < S) copy_stage_mx(p, lds, J + 2);                // 4 J + 3
+      half_mma_mx(acc, F, 1);
+      phase_end();
+    }
+  }
+  wait_copies<0>();
+  phase_end();
+}
+
+// Stages [s0, s0 + ns) of the tile's fp8 K loop.
+__device__ __forceinline__ void tile_gemm_mx(TileAcc& acc, const TiledArgs& a, char* lds, int64_t m0, int n0, int s0,
+                                             int ns, int tid) {
+  const int lane = tid & 63, wv = tid >> 6;
+  PipeMx p;
+  p.wv_u = __builtin_amdgcn_readfirstlane(wv);
+  const size_t k0 = size_t(s0) * kMxK;
+  {
+    const int rr = lane >> 3, chunk = (lane & 7) ^ rr;
+    const size_t row_bytes = size_t(a.K);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      const int r = (4 * p.wv_u + i) * 8 + rr;  // row of the tile
+      p.a_src[i] = reinterpret_cast<const char*>(a.wkv8) + size_t(n0 + r) * row_bytes + k0 + 16 * chunk;
+      int64_t m = m0 + r;
+      m = m < a.M ? m : a.M - 1;  // rows past the last token repeat it (their results are dropped)
+      p.b_src[i] = reinterpret_cast<const char*>(a.tok8) + size_t(m) * row_bytes + k0 + 16 * chunk;
+    }
+  }
+  {
+    // scale dwords: waves 0-3 the wkv rows 64 (w & 3) + l, waves 4-7 the token rows
+    const size_t srow = size_t(a.K / 32);
+    const int r = 64 * (p.wv_u & 3) + lane;
+    if (p.wv_u < 4) {
+      p.s_src = reinterpret_cast<const char*>(a.wkv8s) + size_t(n0 + r) * srow + k0 / 32;
+      p.s_dst = uint32_t(256 * (p.wv_u & 3));
+    } else {
+      int64_t m = m0 + r;
+      m = m < a.M ? m : a.M - 1;
+      p.s_src = reinterpret_cast<const char*>(a.tok8s) + size_t(m) * srow + k0 / 32;
+      p.s_dst = uint32_t(2048 + 256 * (p.wv_u & 3));
+    }
+  }
+  {
+    const int r = lane & 15, g = lane >> 4;
+    p.lo_off = uint32_t(r * kRowB + 16 * (g ^ (r & 7)));
+    p.hi_off = uint32_t(r * kRowB + 16 * ((g + 4) ^ (r & 7)));
+    p.a_off = (wv >> 2) * 128 * kRowB;
+    p.b_off = (wv & 3) * 64 * kRowB;
+    p.sa_off = ((wv >> 2) * 128 + r) * 4;
+    p.sb_off = ((wv & 3) * 64 + r) * 4;
+  }
+#pragma unroll
+  for (int i = 0; i < kBI; ++i)
+#pragma unroll
+    for (int j = 0; j < kBJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (__builtin_amdgcn_readfirstlane(wv) < 4)
+    k_loop_mx<0>(acc, p, lds, ns, lane);
+  else
+    k_loop_mx<1>(acc, p, lds, ns, lane);
 }
 
 // ---------------------------------------------------------------- split K
@@ -511,7 +706,7 @@ __device__ __forceinline__ void value_epilogue(const TiledArgs& a, char* lds, in
   }
 }
 
-template <bool FUSED>
+template <bool FUSED, bool MX = false>
 __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -528,10 +723,11 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   const int n0 = cb * kTN;
 
   TileAcc acc;
-  const int S = a.K / kTK, sh = S / 2;
+  const int S = a.K / (MX ? kMxK : kTK), sh = S / 2;
   const int s0 = half_k <= 0 ? 0 : sh;
   const int ns = half_k < 0 ? S : (half_k == 0 ? sh : S - sh);
-  tile_gemm(acc, a, lds, m0, n0, s0, ns, tid);
+  if constexpr (MX) tile_gemm_mx(acc, a, lds, m0, n0, s0, ns, tid);
+  else tile_gemm(acc, a, lds, m0, n0, s0, ns, tid);
   if (half_k >= 0 && !split_merge(acc, a, b, lds, tid)) return;
   // the K loop ended with a barrier after its last LDS access: the ring is free
   acc_to_lds(acc, lds, lane, wv >> 2, wv & 3);
@@ -554,13 +750,16 @@ hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream)
   int64_t tiles = n_tb * (a.N / kTN);
   if (fused && a.ksplit == 2) tiles *= 2;
   if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
-  const void* fn = fused ? reinterpret_cast<const void*>(&k_tiled<true>)
-                         : reinterpret_cast<const void*>(&k_tiled<false>);
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[fused]) {
+  if (a.mx && !fused) return hipErrorInvalidValue;
+  const void* fn = a.mx ? reinterpret_cast<const void*>(&k_tiled<true, true>)
+                        : fused ? reinterpret_cast<const void*>(&k_tiled<true>)
+                                : reinterpret_cast<const void*>(&k_tiled<false>);
+  const int kind = a.mx ? 2 : (fused ? 1 : 0);
+  static bool attr_set[3] = {false, false, false};
+  if (!attr_set[kind]) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kLds);
     if (e != hipSuccess) return e;
-    attr_set[fused] = true;
+    attr_set[kind] = true;
   }
   TiledArgs args = a;
   void* params[] = {&args};
@@ -569,9 +768,9 @@ hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream)
 
 // Split K pays while the tiles fill at most half of a 256-CU device: two workgroups per tile.
 constexpr int64_t kSplitMaxTiles = 128;
-int tiled_ksplit(int64_t M, int N, int K) {
+int tiled_ksplit(int64_t M, int N, int K, bool mx) {
   const int64_t tiles = (M + kTM - 1) / kTM * (N / kTN);
-  return tiles <= kSplitMaxTiles && K / kTK >= 2 ? 2 : 1;
+  return tiles <= kSplitMaxTiles && K / (mx ? kMxK : kTK) >= 2 ? 2 : 1;
 }
 
 // Control words of the fused schedule: header, per-(token block, stream) counters, split-K
@@ -613,10 +812,21 @@ bool tiled_shape_ok(int N, int K, int dim, bool fused) {  // K: stages of 64 fea
   return true;
 }
 
+bool tiled_mx_ok(int N, int K, int dim, int scale_block) {
+  return tiled_shape_ok(N, K, dim, true) && K % kMxK == 0 && scale_block % 32 == 0;
+}
+
 size_t tiled_control_bytes(int64_t M, int dim) { return tiled_control_layout(nullptr, M, dim); }
 
 size_t tiled_staging_bytes(int64_t M, int K, int N) {
   return ((size_t(M) * K * 2 + 255) & ~size_t(255)) + split_partial_bytes(N);
+}
+
+// fp8 schedule: codes [M, K], then E8M0 scales [M, K / 32], then the split partial tiles
+size_t mx_codes_bytes(int64_t M, int K) { return (size_t(M) * K + 255) & ~size_t(255); }
+size_t mx_scales_bytes(int64_t M, int K) { return (size_t(M) * (K / 32) + 255) & ~size_t(255); }
+size_t tiled_staging_bytes_mx(int64_t M, int K, int N) {
+  return mx_codes_bytes(M, K) + mx_scales_bytes(M, K) + split_partial_bytes(N);
 }
 
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream) { return launch_tiled_impl(a, false, stream); }
@@ -624,14 +834,25 @@ hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream) { return
 hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging,
                                 hipStream_t stream) {
   GatherArgs ga = g;
-  ga.emb = reinterpret_cast<uint16_t*>(staging);
-  hipError_t e = launch_gather_dequant(ga, stream);
+  char* stg = static_cast<char*>(staging);
+  hipError_t e;
+  if (a.mx) {
+    uint8_t* codes8 = reinterpret_cast<uint8_t*>(stg);
+    uint8_t* scales8 = reinterpret_cast<uint8_t*>(stg + mx_codes_bytes(a.M, a.K));
+    e = launch_gather_mx(ga, codes8, scales8, stream);
+    a.tok8 = codes8;
+    a.tok8s = scales8;
+    a.kpart = reinterpret_cast<float*>(stg + mx_codes_bytes(a.M, a.K) + mx_scales_bytes(a.M, a.K));
+  } else {
+    ga.emb = reinterpret_cast<uint16_t*>(staging);
+    e = launch_gather_dequant(ga, stream);
+    a.emb = reinterpret_cast<const uint16_t*>(staging);
+    a.kpart = reinterpret_cast<float*>(stg + ((size_t(a.M) * a.K * 2 + 255) & ~size_t(255)));
+  }
   if (e != hipSuccess) return e;
   a.ws = workspace;
-  a.emb = reinterpret_cast<const uint16_t*>(staging);
   tiled_control_layout(&a, a.M, a.dim);
-  a.ksplit = tiled_ksplit(a.M, a.N, a.K);
-  a.kpart = reinterpret_cast<float*>(static_cast<char*>(staging) + ((size_t(a.M) * a.K * 2 + 255) & ~size_t(255)));
+  a.ksplit = tiled_ksplit(a.M, a.N, a.K, a.mx != 0);
   return launch_tiled_impl(a, true, stream);
 }
 

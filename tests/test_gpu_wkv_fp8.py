@@ -5,9 +5,10 @@ Up to 64 tokens the fused weight-streaming kernel reads the FP8 weights itself: 
 fp32 scales it dequantises them exactly to bf16 in registers (the bf16 MFMA, so results equal
 the bf16 path on the oracle's dequantised weights bit for bit); with an MXFP8 table both
 operands stay fp8 and meet the scaled fp8 MFMA (the same exact products summed in another
-order, so results agree to rounding).  Larger calls, and shapes that kernel does not take,
-expand the weights to bf16 in the staging area and run the bf16 schedules (bit for bit equal to
-the bf16 path).  Everything is checked against the oracle at the forward tolerance.
+order, so results agree to rounding).  Above 64 tokens an MXFP8 table takes the fp8 tiled
+kernel (scaled fp8 MFMA as well); otherwise the weights are expanded to bf16 in the staging area
+for the bf16 schedules (bit for bit equal to the bf16 path).  Everything is checked against the
+oracle at the forward tolerance.
 """
 import numpy as np
 import pytest
@@ -33,6 +34,9 @@ FP8_T100 = synth.small_variant(FP8_B64, name="decode_dims_fp8_t100", B=1, T=100,
                                seed=DECODE_FP8.seed + 501)
 FP8_KV = synth.small_variant(FP8_B64, name="decode_dims_fp8_b3_t37", B=3, T=37,
                              seed=DECODE_FP8.seed + 502)
+# the fp8 tiled kernel without split K: three token blocks (the last one ragged), 300 tiles
+FP8_T600 = synth.small_variant(FP8_B64, name="decode_dims_fp8_b2_t300", B=2, T=300,
+                               seed=DECODE_FP8.seed + 506)
 # fp32-scaled table, FP8 weights, a layout without a tiled schedule: 60 tokens (fused FP8
 # kernel) and 150 tokens (expansion + weight streaming over three token blocks)
 FP8_SMALL = synth.small_variant(WORKLOADS["tiny"], name="dim320_fp8_b2_t30", B=2, T=30, dim=320,
@@ -63,7 +67,16 @@ def test_device_fill_mxfp8_wkv_matches_host_generator():
     assert eg.wkv_bytes(layout(w)) == blob.size
 
 
-@pytest.mark.parametrize("w", [FP8_B64, FP8_T100, FP8_SMALL, FP8_SMALL_T75], ids=lambda w: w.name)
+def _fp8_kernels(w):
+    """(the fused streaming kernel reads the FP8 weights, the fp8 tiled kernel does)"""
+    native = w.M <= 64 and w.head_dim % 128 == 0 and (w.K // 4) % 128 == 0
+    tiled8 = (w.M > 64 and w.scale_format == "e8m0" and w.scale_block % 32 == 0 and w.dim % 256 == 0
+              and w.K % 128 == 0)
+    return native, tiled8
+
+
+@pytest.mark.parametrize("w", [FP8_B64, FP8_T100, FP8_T600, FP8_SMALL, FP8_SMALL_T75],
+                         ids=lambda w: w.name)
 def test_forward_fp8_wkv(w):
     say(f"[gpu] forward with FP8 weights: {w.name} (B={w.B} T={w.T}, dim {w.dim}, table "
         f"{w.scale_format}/{w.scale_block})")
@@ -71,9 +84,9 @@ def test_forward_fp8_wkv(w):
     lay = layout(w)
     ws = eg.engram_forward_workspace_bytes(lay, w.B, w.T)
     stg = eg.engram_forward_staging_bytes(lay, w.B, w.T)
-    native = w.M <= 64
-    # the expansion needs N x K bf16 of staging; the fused FP8 kernel needs none
-    assert (stg >= 2 * w.N * w.K) == (not native), (stg, w.N * w.K)
+    native, tiled8 = _fp8_kernels(w)
+    # the expansion needs N x K bf16 of staging; the kernels that read FP8 weights need none
+    assert (stg >= 2 * w.N * w.K) == (not native and not tiled8), (stg, w.N * w.K)
     buf = torch.zeros(ws + 4096, dtype=torch.uint8, device="cuda")
     buf[ws:] = 0xA5
     out = forward(w, d, ws=buf[:ws])
@@ -84,7 +97,7 @@ def test_forward_fp8_wkv(w):
     w16, d16 = _bf16_twin(w, d)
     out16 = forward(w16, d16)
     torch.cuda.synchronize()
-    if native and w.scale_format == "e8m0":
+    if (native and w.scale_format == "e8m0") or tiled8:
         # scaled fp8 MFMA: equal up to the summation order of the projection
         diff = np.abs(u16(out).astype(np.int32) - u16(out16).astype(np.int32))
         say(f"    vs bf16 path: {float((diff > 0).mean()):.2e} of outputs differ, "
@@ -121,6 +134,23 @@ def test_forward_fp8_wkv_mxfp8_table_bad_ids_nan_substitute_row():
                          oracle.array_fetch(codes, scales), w.n_rows, w.head_dim, w.scale_block,
                          host_wkv(w), q, k, eps=w.eps, clamp=w.clamp, scale_format="e8m0")
     say("   ", check_out(w, np.arange(w.M), u16(out).reshape(w.M, w.hc, w.dim), ref))
+
+
+@pytest.mark.slow
+def test_forward_prefill_fp8_sampled():
+    say("[gpu] forward prefill_t8192_fp8 (MXFP8 table and weights, fp8 tiled kernel), sampled tokens")
+    w = WORKLOADS["prefill_t8192_fp8"]
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    mask = w.token_mask().reshape(-1)
+    closed = np.nonzero(mask == 0)[0][:4]
+    sel = np.unique(np.concatenate([[0, 63, 64, 255, 256, w.M - 1], closed, rng.integers(0, w.M, 40)]))
+    got = u16(out).reshape(w.M, w.hc, w.dim)[sel]
+    del d, out
+    torch.cuda.empty_cache()
+    say("   ", check_out(w, sel, got, oracle_for(w, sel)))
 
 
 def test_kv_proj_fp8_wkv_two_token_blocks():
