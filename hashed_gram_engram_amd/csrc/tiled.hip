@@ -28,8 +28,8 @@
 // fp8 schedule (MXFP8 weights and an MXFP8 table, fused forward only): the gather pass stages
 // the rows as fp8 codes plus one E8M0 byte per 32 features, and both operands stay fp8.  A stage
 // is 128 features (128-byte rows, the same LDS row layout and copy instructions) plus each row's
-// dword of four scales; both operands have rings of two slots (copied one stage ahead; 4 x 32 KB
-// + 4 KB of scales).  The MFMA is v_mfma_scale_f32_16x16x128_f8f6f4 (twice the bf16 rate; a
+// dword of four scales; both operands have rings of two slots (4 x 32 KB + 4 KB of scales), each
+// part of a stage copied as soon as its slot's last reader is done (see k_loop_mx).  The MFMA is v_mfma_scale_f32_16x16x128_f8f6f4 (twice the bf16 rate; a
 // lane supplies 16-byte parts l / 16 and l / 16 + 4 of its row and the scale of 32-feature block
 // l / 16); a half stage is 4 wkv row blocks x 4 token blocks (16 MFMAs of K = 128, as long as the
 // 32 bf16 MFMAs of a bf16 half stage), the token fragments being read once per stage.
@@ -258,13 +258,20 @@ struct PipeMx {
   int sa_off, sb_off;          // byte offsets of their scale dwords in a scale slot
 };
 
-// Stage t of both operands and their scales into ring slot t & 1: 4 + 4 + 1 copy instructions.
-__device__ __forceinline__ void copy_stage_mx(const PipeMx& p, char* lds, int t) {
-  const int r = t & 1;
-  copy_op(p.a_src, lds + r * kOpB, p.wv_u, t);
-  copy_op(p.b_src, lds + kMxBOff + r * kOpB, p.wv_u, t);
+// Copies of one stage of the fp8 schedule, each wave its share, into ring slot `slot`; `t` is the
+// stage copied (past the last stage the last one is repeated into the free slot, so that every
+// phase issues the same number of copies).  Tokens: rows 32 w .. 32 w + 31 (4 instructions);
+// wkv: the same rows, so waves 0-3 copy the rows of group 0 and waves 4-7 those of group 1
+// (4 instructions); scales: one instruction, waves 0-3 the wkv rows' dwords, 4-7 the tokens'.
+__device__ __forceinline__ void copy_b_mx(const PipeMx& p, char* lds, int t, int slot) {
+  copy_op(p.b_src, lds + kMxBOff + slot * kOpB, p.wv_u, t);
+}
+__device__ __forceinline__ void copy_a_mx(const PipeMx& p, char* lds, int t, int slot) {
+  copy_op(p.a_src, lds + slot * kOpB, p.wv_u, t);
+}
+__device__ __forceinline__ void copy_s_mx(const PipeMx& p, char* lds, int t, int slot) {
   __builtin_amdgcn_global_load_lds((const void*)(p.s_src + size_t(t) * 4),
-                                   (lds_ptr_t)(lds + kMxScaleOff + r * 1024 + p.s_dst), 4, 0, 0);
+                                   (lds_ptr_t)(lds + kMxScaleOff + slot * 1024 + p.s_dst), 4, 0, 0);
 }
 
 struct FragMx {
@@ -315,21 +322,27 @@ __device__ __forceinline__ void half_mma_mx(TileAcc& acc, const FragMx& F, int h
 
 // The fp8 K loop of group G over S stages of 128 features, rings of two slots:
 //   group 0: phase 4 J multiplies half 0 of stage J, 4 J + 1 reads half 1, 4 J + 2 multiplies
-//            it, 4 J + 3 issues the copies of stage J + 2 and reads half 0 (and the token
-//            fragments) of stage J + 1;
-//   group 1: phase 4 J reads half 0 (and the token fragments) of stage J, 4 J + 1 multiplies
-//            it, 4 J + 2 reads half 1, 4 J + 3 issues the copies of stage J + 2 and multiplies
-//            half 1.
-// Stage J's slots are last read in phase 4 J + 2, so stage J + 2 may overwrite them from phase
-// 4 J + 3 on; at the end of phase 4 J + 2 every wave waits for all its copies (stage J + 1, the
-// only ones in flight), which group 0 starts reading in phase 4 J + 3.
+//            it, 4 J + 3 reads half 0 (and the token fragments and scales) of stage J + 1;
+//   group 1: phase 4 J reads half 0 (and the token fragments and scales) of stage J, 4 J + 1
+//            multiplies it, 4 J + 2 reads half 1, 4 J + 3 multiplies it.
+// Each part of stage J + 2 is copied into stage J's slot as soon as stage J's last reader of that
+// part is done: the tokens and their scales are read once per stage (last in phase 4 J), so they
+// are copied in phase 4 J + 1; the wkv rows of group 0 in phase 4 J + 2, those of group 1 and the
+// wkv scales in phase 4 J + 3.  Stage J + 2 is first read in phase 4 J + 7.  At the end of phase
+// 4 J + 2 each wave waits until only its copies of stage J + 2 are in flight (group 0: tokens and
+// wkv rows, 8 instructions; group 1: tokens and their scales, 5), so stage J + 1 has landed
+// everywhere before group 0 reads it in phase 4 J + 3.
 template <int G>
 __device__ __forceinline__ void k_loop_mx(TileAcc& acc, const PipeMx& p, char* lds, int S, int lane) {
   FragMx F;
-  copy_stage_mx(p, lds, 0);
-  if (S > 1) copy_stage_mx(p, lds, 1);
-  if (S > 1) wait_copies<9>();
-  else wait_copies<0>();
+  // prologue: stages 0 and 1 (9 copies each); stage 0 lands
+  for (int t = 0; t < 2; ++t) {
+    const int ts = t < S ? t : S - 1;
+    copy_b_mx(p, lds, ts, t);
+    copy_a_mx(p, lds, ts, t);
+    copy_s_mx(p, lds, ts, t);
+  }
+  wait_copies<9>();
   phase_end();
   if constexpr (G == 0) {
     read_a_mx(F, p, lds, 0, 0, lane);
@@ -339,16 +352,19 @@ __device__ __forceinline__ void k_loop_mx(TileAcc& acc, const PipeMx& p, char* l
   phase_end();
   for (int J = 0; J < S; ++J) {
     const int r = J & 1;
+    const int t2 = J + 2 < S ? J + 2 : S - 1;  // the stage copied into slot r
     if constexpr (G == 0) {
       half_mma_mx(acc, F, 0);                                     // 4 J
       phase_end();
-      read_a_mx(F, p, lds, r, 1, lane);                           // 4 J + 1
+      copy_b_mx(p, lds, t2, r);                                   // 4 J + 1
+      read_a_mx(F, p, lds, r, 1, lane);
       wait_frags();
       phase_end();
-      half_mma_mx(acc, F, 1);                                     // 4 J + 2
-      wait_copies<0>();
+      copy_a_mx(p, lds, t2, r);                                   // 4 J + 2
+      half_mma_mx(acc, F, 1);
+      wait_copies<8>();
       phase_end();
-      if (J + 2 < S) copy_stage_mx(p, lds, J + 2);                // 4 J + 3
+      copy_s_mx(p, lds, t2, r);                                   // 4 J + 3
       if (J + 1 < S) {
         read_a_mx(F, p, lds, r ^ 1, 0, lane);
         read_b_mx(F, p, lds, r ^ 1, lane);
@@ -360,17 +376,20 @@ __device__ __forceinline__ void k_loop_mx(TileAcc& acc, const PipeMx& p, char* l
       read_b_mx(F, p, lds, r, lane);
       wait_frags();
       phase_end();
-      half_mma_mx(acc, F, 0);                                     // 4 J + 1
+      copy_b_mx(p, lds, t2, r);                                   // 4 J + 1
+      copy_s_mx(p, lds, t2, r);
+      half_mma_mx(acc, F, 0);
       phase_end();
       read_a_mx(F, p, lds, r, 1, lane);                           // 4 J + 2
       wait_frags();
-      wait_copies<0>();
+      wait_copies<5>();
       phase_end();
-      if (J + 2 < S) copy_stage_mx(p, lds, J + 2);                // 4 J + 3
+      copy_a_mx(p, lds, t2, r);                                   // 4 J + 3
       half_mma_mx(acc, F, 1);
       phase_end();
     }
   }
+  // the repeated copies may still be landing: every copy done before LDS is reused
   wait_copies<0>();
   phase_end();
 }
