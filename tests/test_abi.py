@@ -43,9 +43,15 @@ def test_layout_checks():
     # MXFP8 tables: E8M0 scales, one per 32 features of a 256-feature row
     assert eg.engram_layout_check(eg.make_layout(4, 5120, 24, 256, 32, 16803844,
                                                  scale_format=eg.SCALE_E8M0)) == 0
+    # FP8 projection weights (MXFP8 along the inputs), alone and with an MXFP8 table
+    assert eg.engram_layout_check(eg.make_layout(4, 5120, 24, 256, 128, 16803844,
+                                                 wkv_format=eg.WKV_MXFP8)) == 0
+    assert eg.engram_layout_check(eg.make_layout(4, 5120, 24, 256, 32, 16803844,
+                                                 scale_format=eg.SCALE_E8M0,
+                                                 wkv_format=eg.WKV_MXFP8)) == 0
     bad = [dict(hc=3), dict(dim=5000), dict(head_dim=96), dict(scale_block=24),
            dict(scale_block=512), dict(n_rows=0), dict(eps=float("nan")), dict(n_cols=0),
-           dict(scale_format=2), dict(scale_format=-1),
+           dict(scale_format=2), dict(scale_format=-1), dict(wkv_format=2), dict(wkv_format=-1),
            # E8M0 with 2 scales per row (not whole dwords)
            dict(scale_format=1, scale_block=128)]
     for change in bad:
@@ -57,6 +63,22 @@ def test_layout_checks():
 
 def test_param_counts_on_host():
     assert eg.engram_param_counts(good()) == (98308270592, 157286400, 40960)
+    # the counts are elements, whatever the storage of the projection
+    fp8 = eg.make_layout(4, 5120, 24, 256, 128, 384016682, wkv_format=eg.WKV_MXFP8)
+    assert eg.engram_param_counts(fp8) == (98308270592, 157286400, 40960)
+    # bytes of the wkv argument: 2 per weight, or 1 per weight + 1 per 32 (codes then scales)
+    assert eg.wkv_bytes(good()) == 2 * 157286400
+    assert eg.wkv_bytes(fp8) == 157286400 + 157286400 // 32 == 162201600
+
+
+def test_layout_struct_matches_the_header():
+    # field order and offsets of engram_layout as declared in include/engram.h
+    hdr = open(os.path.join(ROOT, "include", "engram.h")).read()
+    body = hdr[hdr.index("typedef struct {", hdr.index("engram_wkv_format")):]
+    body = body[:body.index("} engram_layout;")]
+    names = [line.split(";")[0].split()[-1] for line in body.splitlines()[1:] if ";" in line]
+    assert names == [f for f, _ in eg.EngramLayout._fields_]
+    assert eg.EngramLayout.n_rows.offset == 32 and ctypes.sizeof(eg.EngramLayout) == 48
 
 
 def test_entry_points_reject_bad_arguments_before_any_device_work():
