@@ -222,7 +222,10 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
 
 
 def _layout_key(layout: EngramLayout) -> tuple:
-    return tuple(getattr(layout, f) for f, _ in EngramLayout._fields_)
+    # the fields that place control words and staging data (not n_rows, eps, clamp: the two
+    # Engram modules of the model differ only in n_rows and share a workspace without clearing)
+    return (layout.hc, layout.dim, layout.n_cols, layout.head_dim, layout.scale_block,
+            layout.scale_format, layout.wkv_format)
 
 
 class Workspace:
