@@ -205,3 +205,34 @@ def test_workspace_sizes_never_decrease_with_token_count_fp8():
             stg = eg.engram_forward_staging_bytes(lay, 1, M)
             assert ws >= last_ws and stg >= last_stg and ws - stg >= last_ctrl, (w.name, M)
             last_ws, last_stg, last_ctrl = ws, stg, ws - stg
+
+
+def test_fp8_weight_dequantisation_every_code_and_exponent():
+    say("[gpu] FP8 weights through the projection alone with one-hot rows: every code at every "
+        "exponent 0..245 dequantised bit for bit")
+    # dim 320, 4 columns of 128: N = 1600 weight rows of K = 512; scale block B = 16 n + b takes
+    # exponent B % 246 and codes 32 ((B // 246) % 8) + 0..31, so every (code, exponent) pair occurs.
+    # NaN codes are replaced by 0x00, and exponents stop at 245 so that no weight overflows bf16
+    # (a zero times an infinite or NaN weight would poison every sum)
+    w = synth.small_variant(FP8_SMALL, wkv_format="mxfp8")
+    N, K = w.N, w.K
+    blk = np.arange(N * (K // 32)).reshape(N, K // 32)
+    exps = (blk % 246).astype(np.uint8)
+    off = 32 * ((blk // 246) % 8)
+    codes = (np.repeat(off, 32, axis=1) + np.tile(np.arange(32), K // 32)[None, :]).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    covered = {(int(c), int(e)) for c, e in zip(codes.reshape(-1), np.repeat(exps, 32, axis=1).reshape(-1))}
+    assert len(covered) >= 254 * 246
+    blob = torch.from_numpy(np.concatenate([codes.reshape(-1), exps.reshape(-1)])).cuda()
+    # token m selects input feature m
+    emb = torch.zeros((1, K, K), dtype=torch.bfloat16, device="cuda")
+    emb[0, torch.arange(K), torch.arange(K)] = 1.0
+    kv = eg.engram_kv_proj(layout(w), emb, blob)
+    torch.cuda.synchronize()
+    got = u16(kv).reshape(K, N).T
+    want = oracle.wkv_mxfp8_bits(codes, exps)
+    # a -0 weight comes out of the sum as +0 (-0 + +0 = +0): the one sign the projection loses
+    want = np.where(want == 0x8000, np.uint16(0), want)
+    assert (want != 0).mean() > 0.9
+    bad = np.nonzero(got != want)
+    assert bad[0].size == 0, (bad[0][:5], bad[1][:5], got[bad][:5], want[bad][:5])
