@@ -274,12 +274,22 @@ __device__ __forceinline__ Frag8 wide_read_w8_mx(const char* slot, int lane) {
 
 // The four bf16 operands (steps s = 0..3: features 8 s .. 8 s + 7 of the lane's 32); the
 // lane's 32 features share the scale in byte l / 16 of the dword.
+// (v_cvt_scalef32_pk_bf16_fp8: two codes times the scale to two bf16 in one instruction; the
+// product of an fp8 value and a power of two is a bf16 number wherever it is not subnormal.)
+template <bool HI>
+__device__ __forceinline__ uint32_t cvt2_scaled(uint32_t c, float sc) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c, sc, HI));
+}
+__device__ __forceinline__ u32x4 dequant8_scaled(uint32_t c0, uint32_t c1, float sc) {
+  return u32x4{cvt2_scaled<false>(c0, sc), cvt2_scaled<true>(c0, sc), cvt2_scaled<false>(c1, sc),
+               cvt2_scaled<true>(c1, sc)};
+}
 __device__ __forceinline__ void wide_operands_w8(u32x4 (&wf)[4], const Frag8& f, int lane) {
   const float sc = e8m0_to_f32((f.sdw >> (8 * (lane >> 4))) & 0xFFu);
-  wf[0] = dequant8(u32x2{f.c0.x, f.c0.y}, sc);
-  wf[1] = dequant8(u32x2{f.c0.z, f.c0.w}, sc);
-  wf[2] = dequant8(u32x2{f.c1.x, f.c1.y}, sc);
-  wf[3] = dequant8(u32x2{f.c1.z, f.c1.w}, sc);
+  wf[0] = dequant8_scaled(f.c0.x, f.c0.y, sc);
+  wf[1] = dequant8_scaled(f.c0.z, f.c0.w, sc);
+  wf[2] = dequant8_scaled(f.c1.x, f.c1.y, sc);
+  wf[3] = dequant8_scaled(f.c1.z, f.c1.w, sc);
 }
 
 // Dense token operands (the projection alone) of one chunk for one lane: sub-block t, features

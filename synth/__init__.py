@@ -475,10 +475,12 @@ def workloads() -> dict:
                                     scale_format="e8m0")
     # ... and with the projection stored in FP8 as well (MXFP8 along its input features)
     decode_fp8 = dataclasses.replace(decode_mx, name="decode_b64_fp8", wkv_format="mxfp8")
+    # FP8 weights with the benchmark tables' fp32 scales (the weights are dequantised to bf16)
+    decode_w8 = dataclasses.replace(decode, name="decode_b64_w8", wkv_format="mxfp8")
     prefill_fp8 = dataclasses.replace(prefill, name="prefill_t8192_fp8", scale_block=32,
                                       scale_format="e8m0", wkv_format="mxfp8")
     return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d, decode_mx, decode_fp8,
-                                prefill_fp8)}
+                                prefill_fp8, decode_w8)}
 
 
 def get(name: str) -> Workload:
