@@ -63,7 +63,7 @@ namespace {
 constexpr int kTB = 64;                          // tokens per token block
 constexpr int kRedBytes = 4 * 2 * 4 * 64 * 16;   // K-partial reduction buffer (two row blocks)
 constexpr int kWBlk = 16 * 256;                  // LDS slot of one row block x 128 features
-constexpr int kWBlk8 = 16 * 128 + 64 * 4;        // the same with MXFP8 weights: codes + scale dwords
+constexpr int kWBlk8 = 16 * 128;                 // the same with MXFP8 weights (codes)
 constexpr int kTokBuf_ = 9 * 1024;               // fused wide loop: token buffer per wave
 // LDS in front of the staged hash ids: the weight slots of the wide loop (4 waves x nblk row
 // blocks) and the token buffers, which the one-round K-partial reduction (nblk x 16 KB) reuses
@@ -222,10 +222,10 @@ __device__ __forceinline__ void wide_copy_w(char* slot, const StreamArgs& a, con
 // MXFP8 weights, unit (row block i, chunk c): copy k in 0..1 fills slot bytes [1024 k, 1024 k +
 // 1024), lane l at 16 l: row 8 k + l / 8, position l % 8, which holds the 16-byte part
 // (l % 8) ^ ((row >> 1) & 7) of the row's 128 chunk bytes (rows 128 bytes apart: with this
-// permutation the 16 rows of a fragment read cover all banks).  Copy 2 puts, for lane l, the
-// dword of E8M0 scales of row l % 16 at features [f, f + 128) (four scales: the chunk is
-// 32-aligned and rows are K / 32 bytes, a multiple of 4) at slot byte 2048 + 4 l.  Not live:
-// the first 128 bytes and scale dword of rows 0..15 (cache resident).
+// permutation the 16 rows of a fragment read cover all banks).  Not live: the first 128 bytes of
+// rows 0..15 (cache resident).  The E8M0 scales of the workgroup's rows are not copied per
+// chunk: the whole table of its rows sits in LDS (load_scale_table), because one 4-byte read per
+// row and chunk, rows K / 32 bytes apart, cost ~6 us of the decode call.
 __device__ __forceinline__ void wide_copy_w8(char* slot, const StreamArgs& a, const Rows& rw, int i, int f_chunk,
                                              bool live, int lane) {
   const int rbase = live ? rw.r0 + 16 * i : 0;
@@ -240,10 +240,29 @@ __device__ __forceinline__ void wide_copy_w8(char* slot, const StreamArgs& a, co
     __builtin_amdgcn_global_load_lds((const void*)(a.wkv8 + row * a.K + fbase + 16 * part),
                                      (lds_ptr_t)(slot + k * 1024), 16, 0, 2);
   }
-  const int r = rbase + (lane & 15);
-  const size_t row = size_t(r < rlast ? r : rlast);
-  __builtin_amdgcn_global_load_lds((const void*)(a.wkv8s + row * size_t(a.K / 32) + fbase / 32),
-                                   (lds_ptr_t)(slot + 2048), 4, 0, 0);
+}
+
+// The E8M0 scales of rows [r0, r1): one contiguous run of (r1 - r0) K / 32 bytes (a multiple of
+// 16, at a 16-byte aligned offset: r0 is a multiple of 4 and K of 128), copied 16 bytes per lane
+// by the workgroup's 256 threads.  Not waited for here.
+__device__ __forceinline__ void load_scale_table(char* table, const StreamArgs& a, const Rows& rw, int tid) {
+  const int n16 = (rw.r1 - rw.r0) * (a.K / 32) / 16;
+  const char* src = reinterpret_cast<const char*>(a.wkv8s) + size_t(rw.r0) * (a.K / 32);
+  const int wv = tid >> 6, lane = tid & 63;
+  for (int base = 64 * wv; base < n16; base += 256) {
+    if (base + lane < n16)
+      __builtin_amdgcn_global_load_lds((const void*)(src + 16 * size_t(base + lane)), (lds_ptr_t)(table + 16 * base),
+                                       16, 0, 0);
+  }
+}
+
+// The scale dword of the lane's row (l % 16 of row block i, the last row for rows past the
+// workgroup's end) at features [f, f + 128).
+__device__ __forceinline__ uint32_t table_scales(const char* table, const StreamArgs& a, const Rows& rw, int i,
+                                                 int f_chunk, int lane) {
+  const int r = 16 * i + (lane & 15);
+  const int rl = rw.r1 - rw.r0 - 1;
+  return *reinterpret_cast<const uint32_t*>(table + (r < rl ? r : rl) * (a.K / 32) + f_chunk / 32);
 }
 
 // Raw MXFP8 fragment of one lane: codes of its row (l % 16) at features 32 (l / 16) + [0, 32)
@@ -252,23 +271,23 @@ struct Frag8 {
   u32x4 c0, c1;
   uint32_t sdw;
 };
-__device__ __forceinline__ Frag8 wide_read_w8(const char* slot, int lane) {
+__device__ __forceinline__ Frag8 wide_read_w8(const char* slot, uint32_t sdw, int lane) {
   const int rr = lane & 15, p0 = 2 * (lane >> 4), sw = (rr >> 1) & 7;
   Frag8 f;
   f.c0 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * (p0 ^ sw));
   f.c1 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * ((p0 + 1) ^ sw));
-  f.sdw = *reinterpret_cast<const uint32_t*>(slot + 2048 + 4 * lane);
+  f.sdw = sdw;
   return f;
 }
 // Raw fragment in the scaled fp8 MFMA's layout: row l % 16 at chunk features 16 (l / 16) +
 // [0, 16) and 64 + 16 (l / 16) + [0, 16) (parts l / 16 and l / 16 + 4), and the scale dword
 // (the MFMA takes the scale of features 32 (l / 16) .. from this lane: byte l / 16).
-__device__ __forceinline__ Frag8 wide_read_w8_mx(const char* slot, int lane) {
+__device__ __forceinline__ Frag8 wide_read_w8_mx(const char* slot, uint32_t sdw, int lane) {
   const int rr = lane & 15, g = lane >> 4, sw = (rr >> 1) & 7;
   Frag8 f;
   f.c0 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * (g ^ sw));
   f.c1 = *reinterpret_cast<const u32x4*>(slot + rr * 128 + 16 * ((g + 4) ^ sw));
-  f.sdw = *reinterpret_cast<const uint32_t*>(slot + 2048 + 4 * lane);
+  f.sdw = sdw;
   return f;
 }
 
@@ -404,9 +423,10 @@ constexpr int kTokLoads = FUSED ? 12 : 16;
 
 template <int NRB, bool FUSED, bool W8, bool MX>
 __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
-                                          char* slots, int64_t m0, const Rows& rw, int lane, int wv) {
+                                          char* slots, const char* stable, int64_t m0, const Rows& rw, int lane,
+                                          int wv) {
   constexpr int kSlot = W8 ? kWBlk8 : kWBlk;
-  constexpr int kWIns = W8 ? 3 : 4;  // copy instructions per row block and chunk
+  constexpr int kWIns = W8 ? 2 : 4;  // copy instructions per row block and chunk
   const int q0 = wv * (a.K >> 2);
   const int nch = (a.K >> 2) / 128;
   char* my_slots = slots + wv * NRB * kSlot;
@@ -461,7 +481,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
       u32x4 wf[4];
       if constexpr (MX) {
-        const Frag8 f8 = wide_read_w8_mx(slot, lane);
+        const Frag8 f8 = wide_read_w8_mx(slot, table_scales(stable, a, rw, i, q0 + 128 * c, lane), lane);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wide_copy_w8(slot, a, rw, i, fn, live, lane);
         const int wsc = int((f8.sdw >> (8 * (lane >> 4))) & 0xFFu);
@@ -469,7 +489,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
         for (int t = 0; t < 4; ++t)
           acc[i][t] = mfma_mx16x16x128(f8.c0, f8.c1, wsc, bx_lo[t], bx_hi[t], bx_sc[t], acc[i][t]);
       } else if constexpr (W8) {
-        const Frag8 f8 = wide_read_w8(slot, lane);
+        const Frag8 f8 = wide_read_w8(slot, table_scales(stable, a, rw, i, q0 + 128 * c, lane), lane);
         // the slot is read (into registers) before its next copy is issued
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wide_copy_w8(slot, a, rw, i, fn, live, lane);
@@ -834,6 +854,18 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t m0 = tb * kTB;
   int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + (WIDE ? wide_lds_bytes(NRB, FUSED, W8) : kRedBytes));
+  // MXFP8 weights: the table of the workgroup's weight scales behind the staged ids, loaded with
+  // the first token block (with the hash ids' loads in flight, in the fused kernel)
+  char* const stable = reinterpret_cast<char*>(s_ids) + (FUSED ? kTB * a.n_cols * 8 : 0);
+  if constexpr (W8) {
+    if (tb == 0) {
+      load_scale_table(stable, a, rw, tid);
+      if constexpr (!FUSED) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
+    }
+  }
   KeyPre<NRB> kp;
   if constexpr (FUSED) {
     // hash ids of the token block, checked once: -1 marks a row that reads as zeros.  Eight
@@ -858,6 +890,8 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
         if (i < n_ids) s_ids[i] = r;
       }
     }
+    // (the scale table's copies of every wave have landed before the barrier)
+    if constexpr (W8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   f32x4 acc[NRB][4];
@@ -865,7 +899,7 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, m0, rw, lane, wv);
+  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, stable, m0, rw, lane, wv);
   else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rw, lane, wv);
   // the key columns' epilogue inputs are loaded now, so that their latency hides under the
   // K-partial reduction (loaded before the K loop they slow it down: registers)
@@ -997,7 +1031,8 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   StreamArgs arg = a;
   void* params[] = {&arg};
   size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(a.N, G), FUSED, a.w8 != 0) : kRedBytes) +
-               (FUSED ? size_t(kTB) * a.n_cols * 8 : 0);
+               (FUSED ? size_t(kTB) * a.n_cols * 8 : 0) +
+               (a.w8 ? size_t(stream_rows_per_group(a.N, G)) * (a.K / 32) : 0);
   if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
   if (lds > 163840) return hipErrorInvalidValue;
   if (lds > 65536) {
@@ -1042,7 +1077,12 @@ bool stream_w8_ok(int K, int N, int head_dim, int scale_block, int num_cus, bool
   a.N = N;
   a.head_dim = head_dim;
   a.scale_block = scale_block;
-  return use_wide(a, stream_grid(N, num_cus), fused);
+  const int G = stream_grid(N, num_cus);
+  if (!use_wide(a, G, fused)) return false;
+  // weight slots, token buffers, staged ids and the scale table fit in the LDS
+  const size_t lds = size_t(wide_lds_bytes(max_blocks(N, G), fused, true)) +
+                     (fused ? size_t(kTB) * (K / head_dim) * 8 : 0) + size_t(stream_rows_per_group(N, G)) * (K / 32);
+  return lds <= 163840;
 }
 
 // Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
