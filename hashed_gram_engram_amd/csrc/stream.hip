@@ -351,6 +351,7 @@ __device__ __forceinline__ u32x4 wide_operand(const WideTok& tk, int t, int s) {
 // hash id names a table row.
 constexpr int kTokBuf = kTokBuf_;
 
+template <bool SCALES = true>
 __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], const StreamArgs& a,
                                               const int64_t* s_ids, int f_chunk, int lane) {
   const int j = f_chunk / a.head_dim;
@@ -372,9 +373,37 @@ __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], c
     const int64_t r = s_ids[(16 * t + (lane & 15)) * a.n_cols + j];
     const int64_t rr = r >= 0 ? r : 0;
     keep[t] = r >= 0 ? 0xFFFFFFFFu : 0u;
-    const size_t off = size_t(rr * nb + cc / a.scale_block) * sbyte;
-    __builtin_amdgcn_global_load_lds((const void*)(static_cast<const char*>(a.scales) + (off & ~size_t(3))),
-                                     (lds_ptr_t)(tbuf + 8192 + t * 256), 4, 0, 0);
+    if constexpr (SCALES) {
+      const size_t off = size_t(rr * nb + cc / a.scale_block) * sbyte;
+      __builtin_amdgcn_global_load_lds((const void*)(static_cast<const char*>(a.scales) + (off & ~size_t(3))),
+                                       (lds_ptr_t)(tbuf + 8192 + t * 256), 4, 0, 0);
+    }
+  }
+}
+
+// Scaled fp8 MFMA (E8M0 table): the E8M0 scales of the gathered rows of this wave's columns,
+// gathered once per token block into a wave-private table instead of one dword per token and
+// chunk with the codes.  The wave's K quarter covers whole columns j0 .. j0 + ncw - 1 (the host
+// asks K / 4 to be a multiple of head_dim); entry (token, jj) holds the row's head_dim /
+// scale_block bytes (whole dwords).  Not waited for here: the K loop's first waits cover them
+// (issued earlier, they complete earlier).
+__device__ __forceinline__ int tok_table_bytes(const StreamArgs& a) {
+  return kTB * ((a.K >> 2) / a.head_dim) * (a.head_dim / a.scale_block);
+}
+__device__ __forceinline__ void load_tok_scales(char* tab, const StreamArgs& a, const int64_t* s_ids, int q0,
+                                                int lane) {
+  const int ncw = (a.K >> 2) / a.head_dim, nb = a.head_dim / a.scale_block, nd = nb >> 2;
+  const int j0 = q0 / a.head_dim;
+  const int n = kTB * ncw * nd;
+  for (int base = 0; base < n; base += 64) {
+    const int e = base + lane;
+    if (e < n) {
+      const int tok = e / (ncw * nd), jj = (e / nd) % ncw, d = e % nd;
+      const int64_t r = s_ids[tok * a.n_cols + j0 + jj];
+      const int64_t rr = r >= 0 ? r : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(static_cast<const char*>(a.scales) + rr * nb + 4 * d),
+                                       (lds_ptr_t)(tab + 4 * base), 4, 0, 0);
+    }
   }
 }
 
@@ -403,8 +432,11 @@ __device__ __forceinline__ void wide_tok_operands(u32x4 (&bt)[4][4], const char*
 // 16 t + lane % 16, parts lane / 16 and lane / 16 + 4 of its 128 chunk bytes as raw codes, and
 // its E8M0 scale of features 32 (lane / 16) ..  Rows that read as zeros get zero codes and scale
 // 2^0 (a NaN scale of the substitute row must not reach the sum).
+// `ts` points at the lane's scale dword of token 0 in the wave's scale table (token stride
+// `tstride` bytes).
 __device__ __forceinline__ void wide_tok_operands_mx(u32x4 (&lo)[4], u32x4 (&hi)[4], int (&sc)[4], const char* tbuf,
-                                                     const uint32_t (&keep)[4], int lane, uint32_t e8m0_shift) {
+                                                     const uint32_t (&keep)[4], int lane, const char* ts,
+                                                     int tstride, uint32_t e8m0_shift) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int tok = 16 * t + (lane & 15);
@@ -412,19 +444,19 @@ __device__ __forceinline__ void wide_tok_operands_mx(u32x4 (&lo)[4], u32x4 (&hi)
     const int g = lane >> 4;
     lo[t] = masked(*reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * (g ^ sw)), keep[t]);
     hi[t] = masked(*reinterpret_cast<const u32x4*>(tbuf + tok * 128 + 16 * ((g + 4) ^ sw)), keep[t]);
-    const uint32_t sw32 = *reinterpret_cast<const uint32_t*>(tbuf + 8192 + t * 256 + 4 * lane);
+    const uint32_t sw32 = *reinterpret_cast<const uint32_t*>(ts + tok * tstride);
     sc[t] = keep[t] ? int((sw32 >> e8m0_shift) & 0xFFu) : 127;
   }
 }
 
 // Vector memory instructions of one chunk's token operands of a lane (fused: copies).
-template <bool FUSED>
-constexpr int kTokLoads = FUSED ? 12 : 16;
+template <bool FUSED, bool MX = false>
+constexpr int kTokLoads = MX ? 8 : (FUSED ? 12 : 16);
 
 template <int NRB, bool FUSED, bool W8, bool MX>
 __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int64_t* s_ids,
-                                          char* slots, const char* stable, int64_t m0, const Rows& rw, int lane,
-                                          int wv) {
+                                          char* slots, const char* stable, const char* ttable, int64_t m0,
+                                          const Rows& rw, int lane, int wv) {
   constexpr int kSlot = W8 ? kWBlk8 : kWBlk;
   constexpr int kWIns = W8 ? 2 : 4;  // copy instructions per row block and chunk
   const int q0 = wv * (a.K >> 2);
@@ -434,7 +466,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   WideTok tk;              // dense only
   uint32_t keep[4];        // fused only
   // prologue in the loop's issue order (tokens, then row blocks)
-  if constexpr (FUSED) wide_copy_tok(my_tok, keep, a, s_ids, q0, lane);
+  if constexpr (FUSED) wide_copy_tok<!MX>(my_tok, keep, a, s_ids, q0, lane);
   else wide_issue_tok(tk, a, m0, q0, lane);
   asm volatile("" ::: "memory");
 #pragma unroll
@@ -448,7 +480,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   // copies of blocks i + 1 .. NRB - 1 of chunk c, the tokens of chunk c + 1 and the copies of
   // blocks 0 .. i - 1 of chunk c + 1 -- always kWIns (NRB - 1) + kTokLoads instructions -- may
   // still be in flight.
-  constexpr int kInFlight = kWIns * (NRB - 1) + kTokLoads<FUSED>;
+  constexpr int kInFlight = kWIns * (NRB - 1) + kTokLoads<FUSED, MX>;
   static_assert(kInFlight <= 63, "vmcnt range");
   const int fl = (lane & 15) * 256;  // this lane's fragment row in a slot
   for (int c = 0; c < nch; ++c) {
@@ -463,10 +495,18 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
       // the lane's E8M0 scale byte within its dword (row scales are whole dwords)
       const int cc_cur = (q0 + 128 * c) % a.head_dim + 32 * (lane >> 4);
       const uint32_t e8m0_shift = uint32_t((cc_cur / a.scale_block) & 3) * 8u;
-      if constexpr (MX) wide_tok_operands_mx(bx_lo, bx_hi, bx_sc, my_tok, keep, lane, e8m0_shift);
-      else wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
+      if constexpr (MX) {
+        // the lane's dword in the wave's scale table: column jj of the quarter, block cc_cur / sb
+        const int nb = a.head_dim / a.scale_block;
+        const int jj = (q0 + 128 * c) / a.head_dim - q0 / a.head_dim;
+        const int tstride = ((a.K >> 2) / a.head_dim) * nb;
+        const char* ts = ttable + jj * nb + ((cc_cur / a.scale_block) & ~3);
+        wide_tok_operands_mx(bx_lo, bx_hi, bx_sc, my_tok, keep, lane, ts, tstride, e8m0_shift);
+      } else {
+        wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
+      }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
-      wide_copy_tok(my_tok, keep, a, s_ids, fn, lane);
+      wide_copy_tok<!MX>(my_tok, keep, a, s_ids, fn, lane);
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -857,6 +897,8 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   // MXFP8 weights: the table of the workgroup's weight scales behind the staged ids, loaded with
   // the first token block (with the hash ids' loads in flight, in the fused kernel)
   char* const stable = reinterpret_cast<char*>(s_ids) + (FUSED ? kTB * a.n_cols * 8 : 0);
+  // MX: the waves' token-scale tables behind the weight-scale table
+  char* const ttable = stable + (((rw.r1 - rw.r0) * (a.K / 32) + 15) & ~15) + (MX ? wv * tok_table_bytes(a) : 0);
   if constexpr (W8) {
     if (tb == 0) {
       load_scale_table(stable, a, rw, tid);
@@ -893,13 +935,14 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
     // (the scale table's copies of every wave have landed before the barrier)
     if constexpr (W8) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if constexpr (MX) load_tok_scales(ttable, a, s_ids, wv * (a.K >> 2), lane);
   }
   f32x4 acc[NRB][4];
 #pragma unroll
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, stable, m0, rw, lane, wv);
+  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, stable, ttable, m0, rw, lane, wv);
   else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rw, lane, wv);
   // the key columns' epilogue inputs are loaded now, so that their latency hides under the
   // K-partial reduction (loaded before the K loop they slow it down: registers)
@@ -1007,15 +1050,37 @@ bool use_wide(const StreamArgs& a, int G, bool fused) {
   return (a.K / 4) % 128 == 0 && hd_ok && lo >= 1 && lo <= 7 && hi <= lo + 1;
 }
 
+// LDS of a launch: the wide loop's slots and buffers (or the narrow loop's reduction buffer), the
+// staged hash ids, and with MXFP8 weights the weight-scale table and (scaled fp8 MFMA) the
+// waves' token-scale tables.
+size_t stream_lds(int N, int K, int n_cols, int head_dim, int scale_block, int G, bool fused, bool wide, bool w8,
+                  bool mx) {
+  size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(N, G), fused, w8) : kRedBytes) +
+               (fused ? size_t(kTB) * n_cols * 8 : 0);
+  if (w8) lds += (size_t(stream_rows_per_group(N, G)) * (K / 32) + 15) & ~size_t(15);
+  if (mx) lds += 4 * size_t(kTB) * ((K / 4) / head_dim) * (head_dim / scale_block);
+  if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
+  return lds;
+}
+
+// The scaled fp8 MFMA in the fused kernel: an MXFP8 table whose rows' scales for a wave's K
+// quarter form whole columns, and LDS for the token-scale tables.
+bool stream_mx_ok(const StreamArgs& a, int G) {
+  return a.scale_e8m0 && (a.K / 4) % a.head_dim == 0 &&
+         stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, true, true, true, true) <= 163840;
+}
+
 template <bool FUSED>
 hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   void* fn = nullptr;
   const bool wide = use_wide(a, G, FUSED);
+  bool mx = false;
   if (a.w8) {
     // MXFP8 weights: the wide loop only; the fused kernel takes one token block
     if (!wide || (FUSED && a.M > kTB)) return hipErrorInvalidValue;
     // an MXFP8 table too: both operands stay fp8 (the scaled MFMA)
-    if (FUSED && a.scale_e8m0) fn = pick_wide<true, true, true>(min_blocks(a.N, G), max_blocks(a.N, G), true);
+    mx = FUSED && stream_mx_ok(a, G);
+    if (mx) fn = pick_wide<true, true, true>(min_blocks(a.N, G), max_blocks(a.N, G), true);
     else fn = pick_wide<FUSED, true>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
   } else if (wide) {
     fn = pick_wide<FUSED, false>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
@@ -1030,10 +1095,7 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   if (fn == nullptr) return hipErrorInvalidValue;
   StreamArgs arg = a;
   void* params[] = {&arg};
-  size_t lds = size_t(wide ? wide_lds_bytes(max_blocks(a.N, G), FUSED, a.w8 != 0) : kRedBytes) +
-               (FUSED ? size_t(kTB) * a.n_cols * 8 : 0) +
-               (a.w8 ? size_t(stream_rows_per_group(a.N, G)) * (a.K / 32) : 0);
-  if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
+  const size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
   if (lds > 163840) return hipErrorInvalidValue;
   if (lds > 65536) {
     // above the default limit: raise it once per kernel (a kernel's need is fixed by its shape
@@ -1080,9 +1142,7 @@ bool stream_w8_ok(int K, int N, int head_dim, int scale_block, int num_cus, bool
   const int G = stream_grid(N, num_cus);
   if (!use_wide(a, G, fused)) return false;
   // weight slots, token buffers, staged ids and the scale table fit in the LDS
-  const size_t lds = size_t(wide_lds_bytes(max_blocks(N, G), fused, true)) +
-                     (fused ? size_t(kTB) * (K / head_dim) * 8 : 0) + size_t(stream_rows_per_group(N, G)) * (K / 32);
-  return lds <= 163840;
+  return stream_lds(N, K, K / head_dim, head_dim, scale_block, G, fused, true, true, false) <= 163840;
 }
 
 // Workspace: a 256-byte header (word 0 counts wait time-outs), then one block per 64-token
