@@ -84,3 +84,19 @@ def test_masks_and_outliers():
                                        ("fulltable_b4_t4096", 384_016_682)])
 def test_workload_table_sizes(name, rows):
     assert synth.get(name).n_rows == rows
+
+
+def test_fp8_projection_weights_spread_like_the_bf16_ones():
+    # MXFP8 wkv of the decode layout with FP8 weights: rows regenerate identically in any chunk,
+    # codes are finite, exponents stay in [lo, hi], and the weights' spread is that of the bf16
+    # N(0, 0.02) weights within a factor (codes ~ U(-4, 4) x 2^(-8 .. -6))
+    w = synth.get("decode_b64_fp8")
+    codes, exps = w.wkv8_rows(100, 164)
+    c2, e2 = w.wkv8_rows(130, 140)
+    assert np.array_equal(codes[30:40], c2) and np.array_equal(exps[30:40], e2)
+    assert codes.shape == (64, w.K) and exps.shape == (64, w.K // 32)
+    assert not ((codes & 0x7F) == 0x7F).any()
+    assert exps.min() >= w.wkv_e8m0_lo and exps.max() <= w.wkv_e8m0_hi
+    assert set(np.unique(exps)) == set(range(w.wkv_e8m0_lo, w.wkv_e8m0_hi + 1))
+    vals = oracle.bf16_value(oracle.wkv_mxfp8_bits(codes, exps))
+    assert 0.01 < vals.std() < 0.03 and abs(vals.mean()) < 1e-3
