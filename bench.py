@@ -6,10 +6,13 @@ two-instance workloads, two calls, the second consuming the first one's output.
 Prints one JSON line.  `value` is tokens per second of the whole job (one GPU).
 
   python bench.py [--steps K] [--warmup W] [--workload decode_b64|prefill_t8192|...]
-                  [--flush-mib F]
+                  [--flush-mib F] [--standalone]
 
 With --flush-mib, F MiB are written between steps (evicting the L2s and the Infinity Cache) and
-each step is timed by its own event pair.
+each step is timed by its own event pair.  With --standalone the line also holds the three
+entry points of the split path timed alone on the same inputs (first instance): the row gather
+(engram_gather_dequant), the projection (engram_kv_proj) and the gate with the residual add
+(engram_gate_apply), each against its roofline.
 """
 import argparse
 import json
@@ -96,6 +99,60 @@ def measured_traffic(w):
     return int(fields["traffic_bytes_per_launch"])
 
 
+def standalone_bytes(w) -> dict:
+    """Algorithmic bytes of the three split-path entry points: every input read once, every output
+    written once."""
+    scale_bytes = 1 if w.scale_format == "e8m0" else 4
+    wkv = w.N * w.K + w.N * (w.K // 32) if w.wkv_format == "mxfp8" else w.N * w.K * 2
+    gather = w.M * (w.n_cols * 8 + w.n_cols * w.head_dim + w.n_cols * w.n_blocks * scale_bytes + w.K * 2)
+    proj = wkv + w.M * (w.K * 2 + w.N * 2)
+    gate = 2 * w.hc * w.dim * 4 + w.M * (w.hc * w.dim * 2 + w.N * 2 + 1 + w.hc * w.dim * 2)
+    return {"gather": gather, "proj": proj, "gate": gate}
+
+
+def time_calls(fn, steps: int, warmup: int, stream) -> list:
+    """Per-call milliseconds of `fn` over `steps` back-to-back calls (event pairs on `stream`)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def standalone(eg, lay, w, d, steps: int, warmup: int, stream) -> dict:
+    """The split path's entry points timed alone (mean per call; HBM roofline for all three, bf16
+    or fp8 MFMA roofline for the projection as well)."""
+    emb = eg.engram_gather_dequant(lay, d["table"], d["scales"], d["hash_ids"])
+    kv = eg.engram_kv_proj(lay, emb, d["wkv"])
+    out = torch.empty_like(d["x"])
+    calls = {
+        "gather": ("engram_gather_dequant (k_gather_dequant)",
+                   lambda: eg.engram_gather_dequant(lay, d["table"], d["scales"], d["hash_ids"], emb=emb)),
+        "proj": ("engram_kv_proj", lambda: eg.engram_kv_proj(lay, emb, d["wkv"], kv=kv)),
+        "gate": ("engram_gate_apply (k_gate_apply)",
+                 lambda: eg.engram_gate_apply(lay, d["x"], kv, d["q_weight"], d["k_weight"],
+                                              d["token_mask"], out=out)),
+    }
+    nbytes = standalone_bytes(w)
+    res = {}
+    for key, (label, fn) in calls.items():
+        ms = float(np.mean(time_calls(fn, steps, warmup, stream)))
+        gbs = nbytes[key] / (ms * 1e-3) / 1e9
+        r = {"call": label, "ms": round(ms, 5), "bytes": nbytes[key], "GB/s": round(gbs, 1),
+             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        if key == "proj":
+            peak = BF16_PEAK_TFLOPS  # bf16 activations: the projection alone multiplies in bf16
+            tf = algorithmic_flops(w) / (ms * 1e-3) / 1e12
+            r.update({"TFLOP/s": round(tf, 1), "mfma_peak": peak, "mfma_frac": round(tf / peak, 4)})
+        res[key] = r
+    return res
+
+
 def cpu_baseline(w, n_tokens: int, min_seconds: float = 10.0):
     """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload (every
     instance of it in turn, each consuming the previous one's output), repeated until at least
@@ -142,6 +199,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB between steps and time each step alone")
+    ap.add_argument("--standalone", action="store_true",
+                    help="also time the split path's three entry points alone")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (scales HBM byte counters)")
     args = ap.parse_args()
@@ -237,6 +296,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "ms_p10_median_p90": [round(float(v), 5) for v in np.percentile(per_step_ms, [10, 50, 90])],
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -251,6 +311,8 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof,
     }
+    if args.standalone:
+        res["standalone"] = standalone(eg, lay, w, insts[0] | {"x": x0}, args.steps, args.warmup, stream)
     if not args.no_cpu_baseline:
         n = args.cpu_tokens or min(w.M, 64)
         res["cpu_baseline"] = cpu_baseline(w, n)

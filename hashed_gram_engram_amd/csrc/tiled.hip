@@ -580,19 +580,20 @@ __device__ __forceinline__ void key_epilogue(const TiledArgs& a, char* lds, int6
     wq[4] = q1.x * k1.x; wq[5] = q1.y * k1.y; wq[6] = q1.z * k1.z; wq[7] = q1.w * k1.w;
   }
   float* P = tpartial(a, tb, s, cbs);
-  // 16 passes of 16 rows (8 waves x 2 half-waves); the x loads of 8 passes are in flight at once
+  // 16 passes of 16 rows (8 waves x 2 half-waves); the x loads of all 16 are in flight at once
+  // (the accumulators are in LDS by now, so the registers are free: one memory round trip)
 #pragma unroll
-  for (int p0 = 0; p0 < 16; p0 += 8) {
-    u32x4 xv[8];
+  for (int p0 = 0; p0 < 16; p0 += 16) {
+    u32x4 xv[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int t = (p0 + q) * 16 + wv * 2 + half;
       const int64_t m = m0 + t;
       const int64_t mm = m < a.M ? m : a.M - 1;
       xv[q] = *reinterpret_cast<const u32x4*>(a.x + (mm * 4 + s) * a.dim + d);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 16; ++q) {
       const int t = (p0 + q) * 16 + wv * 2 + half;
       float h[8], key[8];
       unpack8(xv[q], h);
@@ -691,18 +692,19 @@ __device__ __forceinline__ void value_epilogue(const TiledArgs& a, char* lds, in
   }
   __syncthreads();
   const int d = dseg + 8 * l32;
-  // 1024 rows (token r >> 2, stream r & 3) in 64 passes of 16; 8 passes of x loads in flight
-  for (int p0 = 0; p0 < 64; p0 += 8) {
-    u32x4 xv[8];
+  // 1024 rows (token r >> 2, stream r & 3) in 64 passes of 16; 32 passes of x loads in flight
+  // (two memory round trips per tile)
+  for (int p0 = 0; p0 < 64; p0 += 32) {
+    u32x4 xv[32];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 32; ++q) {
       const int r = (p0 + q) * 16 + wv * 2 + half;
       const int64_t m = m0 + (r >> 2);
       const int64_t mm = m < a.M ? m : a.M - 1;
       xv[q] = *reinterpret_cast<const u32x4*>(a.x + (mm * 4 + (r & 3)) * a.dim + d);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < 32; ++q) {
       const int r = (p0 + q) * 16 + wv * 2 + half;
       const int t = r >> 2, s2 = r & 3;
       const int64_t m = m0 + t;
