@@ -400,7 +400,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     a.spin_budget = kSpinBudget;
     GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
                  l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, nullptr, err_count};
-    return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(stg_start),
+    return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(stg_start), di.cus,
                                 reinterpret_cast<hipStream_t>(stream)) == hipSuccess
                ? ENGRAM_OK
                : ENGRAM_E_HIP;

@@ -142,11 +142,12 @@ struct TiledArgs {
   void* ws;
   int n_vcb;
   size_t slot_off, part_off;
-  // split K (fused schedule, at most 128 tiles): each tile is computed by two workgroups over
-  // the two halves of K; the first to finish leaves its fp32 partial tile in kpart
-  int ksplit;
-  size_t split_off;  // per-tile arrival and hand-off words (control words)
-  float* kpart;      // [tile][256 x 256] fp32 (staging area)
+  // split K (fused schedule): tiles split_from .. tiles - 1 (at most 128) are each computed by
+  // two workgroups over the two halves of K; the first to finish leaves its fp32 partial tile in
+  // kpart.  split_from = tiles: no split.
+  int64_t split_from;
+  size_t split_off;  // per-split-tile arrival and hand-off words (control words)
+  float* kpart;      // [split tile][256 x 256] fp32 (staging area)
 };
 
 // Shapes the tiled kernels take: N a multiple of 256, K of 64 (fused: also dim of 256).
@@ -163,8 +164,9 @@ size_t tiled_staging_bytes_mx(int64_t M, int K, int N);  // rows as fp8 codes + 
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream);
 // Whole forward, tiled schedule: the gather pass `g` writes the dequantised rows into `staging`
 // (tiled_staging_bytes, 256-byte aligned), then the tiled kernel runs with `workspace` as its
-// control words (tiled_control_bytes, zero on entry, left zero).
-hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging,
+// control words (tiled_control_bytes, zero on entry, left zero).  num_cus: compute units of the
+// device (the last, partial round of tiles is split over K).
+hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging, int num_cus,
                                 hipStream_t stream);
 
 }  // namespace engram

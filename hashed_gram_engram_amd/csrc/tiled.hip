@@ -24,6 +24,10 @@
 // Split K: when a call has at most 128 tiles (up to 256 tokens at the decode layout), two
 // workgroups compute each tile, one over each half of K; the first to finish leaves its fp32
 // partial tile in the staging area and the second adds it and runs the epilogue (split_merge).
+// With more tiles (bf16 schedule), the tiles of a last, partial round of the grid (tiles mod
+// CUs, when at most 128 and at most half the CUs) are split the same way: that round then takes
+// half a tile's time on twice as many CUs (3200 tiles at 8192 tokens: 12 full rounds, then 128
+// tiles as 256 halves).
 //
 // fp8 schedule (MXFP8 weights and an MXFP8 table, fused forward only): the gather pass stages
 // the rows as fp8 codes plus one E8M0 byte per 32 features, and both operands stay fp8.  A stage
@@ -67,6 +71,7 @@ constexpr int kLds = (kARing + kBRing) * kOpB;  // 160 KB, all of a CU's LDS
 constexpr int kCopies = 4;                  // copy instructions per wave per operand and stage
 constexpr int kBI = 8;                      // 16-column blocks per wave
 constexpr int kBJ = 4;                      // 16-token blocks per wave
+constexpr int64_t kSplitMaxTiles = 128;     // most tiles split over K in one call
 
 typedef f32x4 TileAcc[kBI][kBJ];
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -732,8 +737,21 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
-  const int64_t b = FUSED && a.ksplit == 2 ? int64_t(blockIdx.x) >> 1 : int64_t(blockIdx.x);  // the tile
-  const int half_k = FUSED && a.ksplit == 2 ? int(blockIdx.x & 1) : -1;
+  // the tile: workgroups from split_from on take half of K of a split tile.  They come in runs
+  // of 16 (the last run shorter): half 0 of 8 consecutive split tiles, then half 1 of the same 8,
+  // so that both halves of tile b run on the XCD that the tile order gives b (workgroup ids are
+  // dealt to the 8 XCDs round robin)
+  const int64_t bi = int64_t(blockIdx.x);
+  const bool split = FUSED && bi >= a.split_from;
+  int64_t b = bi;
+  int half_k = -1;
+  if (split) {
+    const int64_t rel = bi - a.split_from, q = rel >> 4, n_wg = int64_t(gridDim.x) - a.split_from;
+    const int64_t run = n_wg - 16 * q >= 16 ? 8 : (n_wg - 16 * q) >> 1;  // tiles in this run
+    const int64_t w = rel - 16 * q;
+    half_k = int(w / run);
+    b = a.split_from + 8 * q + (w - half_k * run);
+  }
   const int64_t per_group = int64_t(kGroupTb) * (a.N / kTN);
   const int64_t g = b / per_group;
   const int64_t g_size = n_tb - g * kGroupTb < kGroupTb ? n_tb - g * kGroupTb : kGroupTb;
@@ -749,7 +767,7 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
   const int ns = half_k < 0 ? S : (half_k == 0 ? sh : S - sh);
   if constexpr (MX) tile_gemm_mx(acc, a, lds, m0, n0, s0, ns, tid);
   else tile_gemm(acc, a, lds, m0, n0, s0, ns, tid);
-  if (half_k >= 0 && !split_merge(acc, a, b, lds, tid)) return;
+  if (half_k >= 0 && !split_merge(acc, a, b - a.split_from, lds, tid)) return;
   // the K loop ended with a barrier after its last LDS access: the ring is free
   acc_to_lds(acc, lds, lane, wv >> 2, wv & 3);
   __syncthreads();
@@ -769,7 +787,10 @@ __global__ __launch_bounds__(kThreads) void k_tiled(TiledArgs a) {
 hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream) {
   const int64_t n_tb = (a.M + kTM - 1) / kTM;
   int64_t tiles = n_tb * (a.N / kTN);
-  if (fused && a.ksplit == 2) tiles *= 2;
+  if (fused) {
+    if (a.split_from < 0 || a.split_from > tiles || tiles - a.split_from > kSplitMaxTiles) return hipErrorInvalidValue;
+    tiles += tiles - a.split_from;  // one more workgroup per split tile
+  }
   if (tiles <= 0 || tiles > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (a.mx && !fused) return hipErrorInvalidValue;
   const void* fn = a.mx ? reinterpret_cast<const void*>(&k_tiled<true, true>)
@@ -787,11 +808,17 @@ hipError_t launch_tiled_impl(const TiledArgs& a, bool fused, hipStream_t stream)
   return hipLaunchKernel(fn, dim3(unsigned(tiles)), dim3(kThreads), params, kLds, stream);
 }
 
-// Split K pays while the tiles fill at most half of a 256-CU device: two workgroups per tile.
-constexpr int64_t kSplitMaxTiles = 128;
-int tiled_ksplit(int64_t M, int N, int K, bool mx) {
+// The first split tile: every tile while they fill at most half of a 256-CU device; else, in
+// the bf16 schedule, the tiles of the last, partial round when they fill at most half of the
+// device (so that their halves fit in one round); tiles (no split) otherwise.  (Measured at 8192
+// tokens in same-process A/Bs: the bf16 forward 2243 -> 2200 us with its last 128 tiles split;
+// the fp8 forward 1391 -> 1432 us, so the fp8 schedule does not split a last round.)
+int64_t tiled_split_from(int64_t M, int N, int K, bool mx, int cus) {
   const int64_t tiles = (M + kTM - 1) / kTM * (N / kTN);
-  return tiles <= kSplitMaxTiles && K / (mx ? kMxK : kTK) >= 2 ? 2 : 1;
+  if (K / (mx ? kMxK : kTK) < 2) return tiles;
+  if (tiles <= kSplitMaxTiles) return 0;
+  const int64_t r = cus > 0 ? tiles % cus : 0;
+  return !mx && r > 0 && r <= kSplitMaxTiles && 2 * r <= cus ? tiles - r : tiles;
 }
 
 // Control words of the fused schedule: header, per-(token block, stream) counters, split-K
@@ -817,12 +844,11 @@ size_t tiled_control_layout(TiledArgs* a, int64_t M, int dim) {
   return off;
 }
 
-// fp32 partial tiles of split K: as many tiles as any token count of this layout splits (the
-// largest multiple of N / 256 not above kSplitMaxTiles), so the staging size grows with M.
+// fp32 partial tiles of split K: room for the most tiles any call splits (a fixed amount per
+// layout, so the staging size does not decrease with M).
 size_t split_partial_bytes(int N) {
-  const int64_t per_tb = N / kTN;
-  if (per_tb <= 0 || per_tb > kSplitMaxTiles) return 0;
-  return size_t(kSplitMaxTiles / per_tb * per_tb) * kTM * kTN * 4;
+  if (N / kTN <= 0) return 0;
+  return size_t(kSplitMaxTiles) * kTM * kTN * 4;
 }
 
 }  // namespace
@@ -852,7 +878,7 @@ size_t tiled_staging_bytes_mx(int64_t M, int K, int N) {
 
 hipError_t launch_kv_proj_tiled(const TiledArgs& a, hipStream_t stream) { return launch_tiled_impl(a, false, stream); }
 
-hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging,
+hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspace, void* staging, int num_cus,
                                 hipStream_t stream) {
   GatherArgs ga = g;
   char* stg = static_cast<char*>(staging);
@@ -873,7 +899,7 @@ hipError_t launch_forward_tiled(TiledArgs a, const GatherArgs& g, void* workspac
   if (e != hipSuccess) return e;
   a.ws = workspace;
   tiled_control_layout(&a, a.M, a.dim);
-  a.ksplit = tiled_ksplit(a.M, a.N, a.K, a.mx != 0);
+  a.split_from = tiled_split_from(a.M, a.N, a.K, a.mx != 0, num_cus);
   return launch_tiled_impl(a, true, stream);
 }
 

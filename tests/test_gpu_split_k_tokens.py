@@ -1,10 +1,13 @@
-"""The fused forward for 65..256 tokens at the decode layout, against the CPU oracle: the gather pass
-and the tiled schedule with split K (at most 128 tiles of 256 x 256: two workgroups per tile,
-each over half of K, the second adding the first one's fp32 partial tile).
+"""Split K in the tiled schedule, against the CPU oracle: with at most 128 tiles of 256 x 256 every
+tile is computed by two workgroups, each over half of K (the second adds the first one's fp32
+partial tile); with more tiles, the tiles of a last, partial round of the grid (tiles mod the
+CU count, when at most 128) are split the same way.
 
-Token counts: 256 (one full tile row), 193 (a last 64-token block of one token), 65 and 128;
-skewed ids, closed tokens, outlier streams, out-of-range ids, in-place output.  Every result is
-also checked for run-to-run identity, control words left zero and no timed-out wait.
+The decode layout at 65..256 tokens: 256 (one full tile row), 193 (a last 64-token block of one
+token), 65 and 128; skewed ids, closed tokens, outlier streams, out-of-range ids, in-place
+output.  Tiny dims at 13,300 tokens: 260 tiles, the last 4 (value tiles of the last four token
+blocks, the ragged one among them) split, every token checked.  Every result is also checked
+for run-to-run identity, control words left zero and no timed-out wait.
 """
 import numpy as np
 import pytest
@@ -18,6 +21,7 @@ import synth  # noqa: E402
 from gpu_common import check_out, forward, host_wkv, layout, oracle_for, say, u16  # noqa: E402
 
 DECODE = synth.workloads()["decode_b64"]
+TINY = synth.workloads()["tiny"]
 
 
 def variant(B, T, seed):
@@ -88,3 +92,21 @@ def test_forward_split_k_bad_ids_in_place():
                          synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block, host_wkv(w), q, k,
                          eps=w.eps, clamp=w.clamp, scale_format=w.scale_format)
     say("   ", check_out(w, sel, got, ref))
+
+
+def test_forward_last_round_split_tiny_dims():
+    w = synth.small_variant(TINY, name="tiny_dims_b1_t13300", B=1, T=13300, hash_dist="zipf",
+                            mask_false_frac=0.1, outlier_frac=0.02, masked_positions=(),
+                            seed=TINY.seed + 506)
+    n_tiles = -(-w.M // 256) * (w.N // 256)
+    assert n_tiles == 260  # 256 CUs: one full round, then 4 tiles split over K
+    say(f"[gpu] forward {w.name}: {n_tiles} tiles, the last {n_tiles % 256} split over K")
+    d = synth.device_inputs(w)
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = run_twice(w, d, err=err)
+    assert int(err.item()) == 0
+    sel = np.arange(w.M)
+    got = u16(out).reshape(w.M, w.hc, w.dim)
+    del d, out
+    torch.cuda.empty_cache()
+    say("   ", check_out(w, sel, got, oracle_for(w, sel)))
