@@ -8,6 +8,7 @@ missing, importing the binding raises: there is no fallback path.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional
 
@@ -116,6 +117,56 @@ def _contig(name: str, t: torch.Tensor, dtype=None) -> torch.Tensor:
 _BF16 = (torch.bfloat16, torch.int16)
 
 
+# The library takes plain pointers and cannot see buffer sizes: every tensor's shape (or size) is
+# checked here against the layout, so that a mismatch raises instead of reading or writing past
+# a buffer on the device.
+def _shape(name: str, t: torch.Tensor, shape: tuple):
+    if t.shape != shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _numel(name: str, t: torch.Tensor, shape: tuple):
+    """t holds exactly the elements of `shape` (in any shape: the library sees a flat buffer)."""
+    need = math.prod(shape)
+    if t.numel() != need:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {need} elements {tuple(shape)}")
+
+
+def _nbytes(name: str, t: torch.Tensor, need: int, exact: bool = True):
+    have = t.numel() * t.element_size()
+    if (have != need) if exact else (have < need):
+        raise ValueError(f"{name} holds {have} bytes, expected {'' if exact else 'at least '}{need}")
+
+
+def _same_device(ref: torch.Tensor, **ts):
+    dev = ref.device
+    if dev.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {dev}")
+    for name, t in ts.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _dims(layout: EngramLayout):
+    """(K, N, scale bytes per table row) of a layout."""
+    k, n = layout.n_cols * layout.head_dim, (layout.hc + 1) * layout.dim
+    nb = layout.head_dim // layout.scale_block if layout.scale_block > 0 else 0
+    return k, n, nb * (1 if layout.scale_format == SCALE_E8M0 else 4)
+
+
+def _check_table(layout: EngramLayout, table: torch.Tensor, scales: torch.Tensor):
+    _, _, sbytes = _dims(layout)
+    _nbytes("table", table, layout.n_rows * layout.head_dim, exact=False)
+    _nbytes("scales", scales, layout.n_rows * sbytes, exact=False)
+
+
+def _check_err(err_count: Optional[torch.Tensor]):
+    if err_count is not None:
+        _contig("err_count", err_count, torch.int32)
+        if err_count.numel() < 1:
+            raise ValueError("err_count needs one int32")
+
+
 def _check_wkv(layout: EngramLayout, wkv: torch.Tensor):
     _contig("wkv", wkv, torch.uint8 if layout.wkv_format == WKV_MXFP8 else _BF16)
     if wkv.numel() * wkv.element_size() != wkv_bytes(layout):
@@ -145,12 +196,20 @@ def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: tor
                           hash_ids: torch.Tensor, emb: Optional[torch.Tensor] = None,
                           err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
     """emb [B, T, n_cols * head_dim] bf16 from hash_ids [B, T, n_cols] int64."""
+    if hash_ids.dim() != 3:
+        raise ValueError(f"hash_ids has shape {tuple(hash_ids.shape)}, expected [B, T, n_cols]")
     B, T, C = hash_ids.shape
+    _shape("hash_ids", hash_ids, (B, T, layout.n_cols))
     _contig("hash_ids", hash_ids, torch.int64)
     _contig("table", table, torch.uint8)
     _contig("scales", scales, torch.uint8 if layout.scale_format == SCALE_E8M0 else torch.float32)
+    _check_table(layout, table, scales)
+    _check_err(err_count)
     if emb is None:
         emb = torch.empty((B, T, C * layout.head_dim), dtype=torch.bfloat16, device=hash_ids.device)
+    _numel("emb", emb, (B, T, C * layout.head_dim))
+    _contig("emb", emb, _BF16)
+    _same_device(hash_ids, table=table, scales=scales, emb=emb, err_count=err_count)
     _check("engram_gather_dequant", _lib.engram_gather_dequant(
         ctypes.byref(layout), _ptr(table), _ptr(scales), _ptr(hash_ids), B, T, _ptr(emb),
         _ptr(err_count), _stream()))
@@ -160,12 +219,18 @@ def engram_gather_dequant(layout: EngramLayout, table: torch.Tensor, scales: tor
 def engram_kv_proj(layout: EngramLayout, emb: torch.Tensor, wkv: torch.Tensor,
                    kv: Optional[torch.Tensor] = None) -> torch.Tensor:
     """kv [B, T, (hc + 1) * dim] bf16 = emb @ wkv^T (wkv in the layout's wkv_format)."""
+    if emb.dim() != 3:
+        raise ValueError(f"emb has shape {tuple(emb.shape)}, expected [B, T, n_cols * head_dim]")
     B, T, _ = emb.shape
+    K, N, _ = _dims(layout)
+    _shape("emb", emb, (B, T, K))
     _contig("emb", emb, _BF16)
     _check_wkv(layout, wkv)
     if kv is None:
-        kv = torch.empty((B, T, (layout.hc + 1) * layout.dim), dtype=torch.bfloat16,
-                         device=emb.device)
+        kv = torch.empty((B, T, N), dtype=torch.bfloat16, device=emb.device)
+    _numel("kv", kv, (B, T, N))
+    _contig("kv", kv, _BF16)
+    _same_device(emb, wkv=wkv, kv=kv)
     _check("engram_kv_proj", _lib.engram_kv_proj(ctypes.byref(layout), _ptr(emb), _ptr(wkv), B, T,
                                                  _ptr(kv), _stream()))
     return kv
@@ -184,16 +249,29 @@ def engram_hash_ids(layout: HashLayout, token_map: torch.Tensor, multipliers: to
     """Row ids [n_layers, B, L, (max_ngram - 1) * n_heads] int64 of tokens input_ids [B, L] at
     positions start_pos.. (engram_hash_ids in include/engram.h); history [B, history_len] int64
     is read and updated in place."""
+    if input_ids.dim() != 2:
+        raise ValueError(f"input_ids has shape {tuple(input_ids.shape)}, expected [B, L]")
     B, L = input_ids.shape
     _contig("token_map", token_map, (torch.int32, torch.uint32) if hasattr(torch, "uint32") else torch.int32)
     for name, t in (("multipliers", multipliers), ("primes", primes), ("offsets", offsets),
                     ("input_ids", input_ids), ("history", history)):
         _contig(name, t, torch.int64)
+    n_cols = (layout.max_ngram - 1) * layout.n_heads
+    _numel("token_map", token_map, (layout.vocab,))
+    _numel("multipliers", multipliers, (layout.n_layers, layout.max_ngram))
+    _numel("primes", primes, (layout.n_layers, layout.max_ngram - 1, layout.n_heads))
+    _numel("offsets", offsets, (layout.n_layers, n_cols))
+    _numel("history", history, (B, layout.history_len))
     if token_mask is not None:
         _contig("token_mask", token_mask, (torch.uint8, torch.bool))
-    n_cols = (layout.max_ngram - 1) * layout.n_heads
+        _numel("token_mask", token_mask, (B, L))
+    _check_err(err_count)
     if out is None:
         out = torch.empty((layout.n_layers, B, L, n_cols), dtype=torch.int64, device=input_ids.device)
+    _numel("out", out, (layout.n_layers, B, L, n_cols))
+    _contig("out", out, torch.int64)
+    _same_device(input_ids, token_map=token_map, multipliers=multipliers, primes=primes,
+                 offsets=offsets, history=history, token_mask=token_mask, out=out, err_count=err_count)
     _check("engram_hash_ids", _lib.engram_hash_ids(
         ctypes.byref(layout), _ptr(token_map), _ptr(multipliers), _ptr(primes), _ptr(offsets),
         _ptr(input_ids), _ptr(token_mask), B, L, start_pos, _ptr(history), _ptr(out),
@@ -206,15 +284,30 @@ def engram_gate_apply(layout: EngramLayout, x: torch.Tensor, kv: torch.Tensor,
                       token_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                       gate: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out [B, T, hc, dim] bf16 = x + gate * value (gate per token and stream)."""
+    if x.dim() != 4:
+        raise ValueError(f"x has shape {tuple(x.shape)}, expected [B, T, hc, dim]")
     B, T = x.shape[0], x.shape[1]
+    _, N, _ = _dims(layout)
+    _shape("x", x, (B, T, layout.hc, layout.dim))
     _contig("x", x, _BF16)
+    _numel("kv", kv, (B, T, N))
     _contig("kv", kv, _BF16)
     _contig("q_weight", q_weight, torch.float32)
     _contig("k_weight", k_weight, torch.float32)
+    _numel("q_weight", q_weight, (layout.hc, layout.dim))
+    _numel("k_weight", k_weight, (layout.hc, layout.dim))
     if token_mask is not None:
         _contig("token_mask", token_mask, (torch.uint8, torch.bool))
+        _numel("token_mask", token_mask, (B, T))
     if out is None:
         out = torch.empty_like(x)
+    _numel("out", out, tuple(x.shape))
+    _contig("out", out, _BF16)
+    if gate is not None:
+        _numel("gate", gate, (B, T, layout.hc))
+        _contig("gate", gate, torch.float32)
+    _same_device(x, kv=kv, q_weight=q_weight, k_weight=k_weight, token_mask=token_mask, out=out,
+                 gate=gate)
     _check("engram_gate_apply", _lib.engram_gate_apply(
         ctypes.byref(layout), _ptr(x), _ptr(kv), _ptr(q_weight), _ptr(k_weight), _ptr(token_mask),
         B, T, _ptr(out), _ptr(gate), _stream()))
@@ -265,18 +358,34 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                    err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole Engram forward: out [B, T, hc, dim] bf16 (may be x itself)."""
+    if x.dim() != 4:
+        raise ValueError(f"x has shape {tuple(x.shape)}, expected [B, T, hc, dim]")
     B, T = x.shape[0], x.shape[1]
+    _shape("x", x, (B, T, layout.hc, layout.dim))
     _contig("x", x, _BF16)
+    _numel("hash_ids", hash_ids, (B, T, layout.n_cols))
     _contig("hash_ids", hash_ids, torch.int64)
     _contig("table", table, torch.uint8)
     _contig("scales", scales, torch.uint8 if layout.scale_format == SCALE_E8M0 else torch.float32)
+    _check_table(layout, table, scales)
     _check_wkv(layout, wkv)
     _contig("q_weight", q_weight, torch.float32)
     _contig("k_weight", k_weight, torch.float32)
+    _numel("q_weight", q_weight, (layout.hc, layout.dim))
+    _numel("k_weight", k_weight, (layout.hc, layout.dim))
     if token_mask is not None:
         _contig("token_mask", token_mask, (torch.uint8, torch.bool))
+        _numel("token_mask", token_mask, (B, T))
+    _check_err(err_count)
     if out is None:
         out = torch.empty_like(x)
+    _numel("out", out, tuple(x.shape))
+    _contig("out", out, _BF16)
+    if workspace is not None:
+        _contig("workspace", workspace)
+    _same_device(x, hash_ids=hash_ids, table=table, scales=scales, wkv=wkv, q_weight=q_weight,
+                 k_weight=k_weight, token_mask=token_mask, out=out, workspace=workspace,
+                 err_count=err_count)
     if workspace is None:
         dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
         workspace = _default_ws.setdefault(dev, Workspace(x.device)).get(layout, B, T)
