@@ -2,7 +2,8 @@
 
   libengram.so       the Engram forward library (hashed_gram_engram_amd/csrc, include/engram.h)
   libsynth_fill.so   device-side fill of seeded synthetic inputs (synth/fill.hip)
-  liboracle_c.so     not built: the oracle is numpy
+  liboracle.so       the CPU oracle (oracle/engram_oracle.cc, plain C++ built with g++; test
+                     infrastructure, never linked into libengram.so)
 """
 from __future__ import annotations
 
@@ -23,6 +24,10 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
 ENGRAM_SRC = ["engram_api.hip", "gather_gate.hip", "hash.hip", "stream.hip", "tiled.hip"]
 LIB_ENGRAM = os.path.join(HERE, "libengram.so")
 LIB_SYNTH = os.path.join(ROOT, "synth", "libsynth_fill.so")
+LIB_ORACLE = os.path.join(ROOT, "oracle", "liboracle.so")
+CXX = os.environ.get("CXX", "g++")
+# IEEE double throughout: no fused multiply-add, no reassociation, no fast-math
+ORACLE_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-shared", "-pthread", "-ffp-contract=off"]
 
 
 def _run(cmd):
@@ -45,8 +50,12 @@ def build(verbose: bool = False) -> None:
     synth_o = os.path.join(obj_dir, "synth_fill.o")
     jobs.append((synth_o, [HIPCC] + COMMON + ["-ffp-contract=off", "-c",
                                               os.path.join(ROOT, "synth", "fill.hip"), "-o", synth_o]))
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        outs = list(ex.map(lambda j: _run(j[1]), jobs))
+    oracle_tmp = LIB_ORACLE + ".tmp"
+    jobs_all = jobs + [(oracle_tmp, [CXX] + ORACLE_FLAGS + [
+        os.path.join(ROOT, "oracle", "engram_oracle.cc"), "-o", oracle_tmp])]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs_all))) as ex:
+        outs = list(ex.map(lambda j: _run(j[1]), jobs_all))
+    os.replace(oracle_tmp, LIB_ORACLE)
     if verbose:
         for o in outs:
             if o.strip():
@@ -61,4 +70,4 @@ def build(verbose: bool = False) -> None:
 
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)
-    print("built", LIB_ENGRAM, LIB_SYNTH)
+    print("built", LIB_ENGRAM, LIB_SYNTH, LIB_ORACLE)

@@ -1,4 +1,4 @@
-"""Pins of the CPU oracle against things other than itself (CPU only).
+"""Pins of the CPU oracle (oracle/engram_oracle.cc) against things other than itself (CPU only).
 
 Each test checks the oracle against a library routine, a closed form, a number printed on the
 pages, or a brute-force evaluation on tiny inputs written in a different way (scalar loops,
@@ -550,3 +550,128 @@ def test_hash_chunked_calls_equal_one_call_and_dead_blocks_lookback():
     pads = oracle.hash_ids(np.zeros((1, 1), dtype=np.int64), np.array([2]), mult, primes, offsets,
                            2, np.zeros((1, 1), dtype=np.int64))
     assert np.array_equal(whole[b, t], pads[0, 0])
+
+
+def _hash_brute_force_unbounded(ids, token_map, mult, primes, offsets, pad_id):
+    """The page demo's loop over Python integers (no wrap): per token, the look-backs blocked at
+    the sequence start, products summed with XOR, each order's value modulo each head's prime."""
+    B, L = ids.shape
+    n_layers, max_ngram = mult.shape
+    n_heads = primes.shape[2]
+    out = np.zeros((B, L, n_layers, (max_ngram - 1) * n_heads), dtype=object)
+    for b in range(B):
+        comp = [int(token_map[i]) for i in ids[b]]
+        for t in range(L):
+            toks = [comp[t - sh] if t - sh >= 0 else pad_id for sh in range(max_ngram)]
+            for sh in range(1, max_ngram):
+                if t - sh < 0:
+                    toks[sh:] = [pad_id] * (max_ngram - sh)
+                    break
+            for layer in range(n_layers):
+                h = 0
+                for i in range(max_ngram):
+                    h ^= toks[i] * int(mult[layer, i])
+                    if i >= 1:
+                        for k in range(n_heads):
+                            col = (i - 1) * n_heads + k
+                            out[b, t, layer, col] = h % int(primes[layer, i - 1, k]) + int(offsets[layer, col])
+    return out
+
+
+def test_hash_wide_mode_matches_unbounded_brute_force():
+    # 64-bit odd multipliers above 2^63 (as on the page): the 128-bit mode keeps every product
+    rng = np.random.default_rng(31)
+    ids, tm, _, primes, offsets = _hash_case(rng, 2, 9)
+    mult = np.array([[int(v) | 1 | (1 << 63) for v in rng.integers(0, 2 ** 62, 4)] for _ in range(2)],
+                    dtype=object)
+    got = oracle.hash_ids(ids.astype(object), tm, mult, primes.astype(object),
+                          offsets.astype(object), 2, np.zeros((2, 9), dtype=object))
+    ref = _hash_brute_force_unbounded(ids, tm, mult, primes, offsets, 2)
+    assert np.array_equal(got.astype(object), ref)
+    # and the 64-bit mode on the same inputs is the unbounded value's two's-complement reduction
+    wrap = oracle.hash_ids(ids, tm, np.array([[v - (1 << 64) for v in r] for r in mult],
+                                             dtype=np.int64), primes, offsets, 2,
+                           np.zeros((2, 9), np.int64))
+    assert np.array_equal(wrap, _hash_brute_force_int64(ids, tm, np.array(
+        [[v - (1 << 64) for v in r] for r in mult], dtype=np.int64), primes, offsets, 2))
+    assert not np.array_equal(wrap, got.astype(np.int64))  # the two readings do differ
+
+
+def _tiny_forward_inputs(seed=41, M=7):
+    rng = np.random.default_rng(seed)
+    hc, dim, C, hd, sb, n_rows = 4, 64, 6, 32, 16, 97
+    table = rng.integers(0, 256, (n_rows, hd), dtype=np.uint8)
+    table[(table & 0x7F) == 0x7F] = 0x21        # no NaN codes: results compare bit for bit
+    scales = rng.uniform(0.01, 0.1, (n_rows, hd // sb)).astype(np.float32)
+    ids = rng.integers(0, n_rows, (M, C)).astype(np.int64)
+    ids[2, 3] = n_rows + 5                      # out of range: a zero row
+    wkv = _bits(rng.standard_normal(((hc + 1) * dim, C * hd)) * 0.05)
+    x = _bits(rng.standard_normal((M, hc, dim)))
+    q = rng.uniform(0.5, 1.5, (hc, dim)).astype(np.float32)
+    k = rng.uniform(0.5, 1.5, (hc, dim)).astype(np.float32)
+    mask = np.ones(M, np.uint8)
+    mask[4] = 0
+    return dict(x=x, ids=ids, mask=mask, table=table, scales=scales, n_rows=n_rows, hd=hd, sb=sb,
+                wkv=wkv, q=q, k=k)
+
+
+def _run_forward(a, fetch):
+    return oracle.forward(a["x"], a["ids"], a["mask"], fetch, a["n_rows"], a["hd"], a["sb"],
+                          a["wkv"], a["q"], a["k"])
+
+
+def test_forward_same_bits_for_any_thread_count(monkeypatch):
+    a = _tiny_forward_inputs()
+    monkeypatch.setenv("ORACLE_THREADS", "1")
+    one = _run_forward(a, oracle.array_fetch(a["table"], a["scales"]))
+    monkeypatch.setenv("ORACLE_THREADS", "5")
+    many = _run_forward(a, oracle.array_fetch(a["table"], a["scales"]))
+    for key in one:
+        assert np.array_equal(one[key], many[key]), key
+
+
+def test_held_rows_lookup_equals_whole_table():
+    """A row provider that hands over only the rows the tokens name (ascending) gives the same
+    results as the whole table; a provider that leaves one out is an error."""
+    a = _tiny_forward_inputs(seed=43)
+    dense = _run_forward(a, oracle.array_fetch(a["table"], a["scales"]))
+    asked = []
+
+    def fetch(rows):
+        asked.append(np.asarray(rows).copy())
+        return a["table"][rows], a["scales"][rows]
+
+    held = _run_forward(a, fetch)
+    for key in dense:
+        assert np.array_equal(dense[key], held[key]), key
+    rows = asked[0]
+    assert np.all(np.diff(rows) > 0) and rows.max() < a["n_rows"]   # in range, ascending, unique
+
+    def lossy(rows):  # one row short: the last id the tokens name is not held
+        return a["table"][rows[:-1]], a["scales"][rows[:-1]]
+
+    with pytest.raises(ValueError):
+        oracle.gather_dequant(a["ids"], lossy, a["n_rows"], a["hd"], a["sb"])
+    # a whole-table view shorter than n_rows: an in-range id past its end is not held
+    short = oracle.array_fetch(a["table"][:50], a["scales"][:50])
+    assert a["ids"].max() >= 50
+    with pytest.raises(RuntimeError):
+        oracle.gather_dequant(a["ids"], short, a["n_rows"], a["hd"], a["sb"])
+    with pytest.raises(RuntimeError):
+        _run_forward(a, short)
+
+
+def test_kv_full_width_against_torch_double_linear():
+    """K = 6144 (the model's 24 x 256 inputs): the oracle's in-order double sums, rounded to fp32
+    and then bf16, against torch's double Linear rounded the same way."""
+    rng = np.random.default_rng(12)
+    M, K, N = 3, 6144, 96
+    emb = oracle.bf16_bits_from_fp32(rng.standard_normal((M, K)) * 0.05)
+    wkv = oracle.bf16_bits_from_fp32(rng.standard_normal((N, K)) * 0.02)
+    ours, exact = oracle.kv_proj(emb, wkv, with_exact=True)
+    t_emb = torch.from_numpy(emb.view(np.int16)).view(torch.bfloat16).double()
+    t_w = torch.from_numpy(wkv.view(np.int16)).view(torch.bfloat16).double()
+    ref64 = F.linear(t_emb, t_w)
+    assert np.allclose(exact, ref64.numpy(), rtol=1e-12, atol=1e-14)
+    ref = ref64.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (ours != ref).mean() <= 1e-3
