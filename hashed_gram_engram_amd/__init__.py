@@ -7,6 +7,7 @@ missing, importing the binding raises: there is no fallback path.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import math
 import os
@@ -24,8 +25,9 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 ENGRAM_OK = 0
+ENGRAM_E_TIMEOUT = -8
 STATUS = {0: "ok", -1: "null pointer", -2: "layout", -3: "shape", -4: "alignment",
-          -5: "workspace", -6: "hip", -7: "device"}
+          -5: "workspace", -6: "hip", -7: "device", -8: "timeout"}
 
 
 class EngramLayout(ctypes.Structure):
@@ -65,14 +67,18 @@ _lib.engram_forward.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i6
                                 _sz, _vp, _vp]
 _lib.engram_hash_ids.argtypes = [ctypes.POINTER(HashLayout), _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                  _i64, _i64, _vp, _vp, _vp, _vp]
+_lib.engram_forward_check.argtypes = [_vp, _sz, _vp]
+_lib.engram_set_spin_budget.argtypes = [ctypes.c_uint32]
+_lib.engram_set_spin_budget.restype = ctypes.c_uint32
 for _f in (_lib.engram_layout_check, _lib.engram_param_counts, _lib.engram_gather_dequant,
-           _lib.engram_kv_proj, _lib.engram_gate_apply, _lib.engram_forward, _lib.engram_hash_ids):
+           _lib.engram_kv_proj, _lib.engram_gate_apply, _lib.engram_forward, _lib.engram_hash_ids,
+           _lib.engram_forward_check):
     _f.restype = ctypes.c_int
 
 EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_workspace_bytes",
             "engram_forward_staging_bytes",
             "engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
-            "engram_hash_ids", "engram_status_str"]
+            "engram_hash_ids", "engram_status_str", "engram_forward_check", "engram_set_spin_budget"]
 
 
 SCALE_FP32, SCALE_E8M0 = 0, 1  # engram_scale_format
@@ -349,15 +355,61 @@ class Workspace:
         return self.buf
 
 
-_default_ws: dict = {}  # one per device
+# One default workspace per (device, stream): calls that overlap in time must not share one, and
+# calls on different streams may overlap.
+_default_ws: dict = {}
+
+
+def workspace_for(dev: int, stream_handle: int) -> "Workspace":
+    """The default Workspace of a (device index, HIP stream handle): one each, made on first use
+    (it allocates nothing until its first get())."""
+    key = (int(dev), int(stream_handle))
+    if key not in _default_ws:
+        _default_ws[key] = Workspace(torch.device("cuda", int(dev)))
+    return _default_ws[key]
+
+
+def default_workspace(layout: EngramLayout, B: int, T: int, device: torch.device) -> torch.Tensor:
+    """The workspace engram_forward uses when the caller passes none: the one of x's device and
+    the current stream, grown on demand."""
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    return workspace_for(dev, torch.cuda.current_stream(dev).cuda_stream).get(layout, B, T)
+
+
+def release_default_workspaces() -> None:
+    """Frees the default workspaces (after the work on them has finished).  Registered to run at
+    interpreter exit, so that no device buffer of this module outlives the program's own
+    teardown of the HIP runtime or of a profiler attached to it."""
+    if _default_ws and torch.cuda.is_initialized():
+        torch.cuda.synchronize()
+    _default_ws.clear()
+
+
+atexit.register(release_default_workspaces)
+
+
+def engram_forward_check(workspace: torch.Tensor) -> None:
+    """Waits for the current stream and raises EngramError (status ENGRAM_E_TIMEOUT) if a
+    cross-workgroup wait of an engram_forward call on `workspace` gave up since the last check;
+    the library then zero-fills the workspace, so it can be used again."""
+    _contig("workspace", workspace)
+    _check("engram_forward_check", _lib.engram_forward_check(
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+
+
+def engram_set_spin_budget(polls: int) -> int:
+    """Bound of the cross-workgroup waits in polls (0 restores the default); returns the old one."""
+    return int(_lib.engram_set_spin_budget(polls))
 
 
 def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
                    token_mask: Optional[torch.Tensor], table: torch.Tensor, scales: torch.Tensor,
                    wkv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
                    out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                   err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """The whole Engram forward: out [B, T, hc, dim] bf16 (may be x itself)."""
+                   err_count: Optional[torch.Tensor] = None, check: bool = False) -> torch.Tensor:
+    """The whole Engram forward: out [B, T, hc, dim] bf16 (may be x itself).  With ``check`` the
+    call waits for its stream and raises if a cross-workgroup wait timed out
+    (engram_forward_check); without it the caller checks when it chooses to."""
     if x.dim() != 4:
         raise ValueError(f"x has shape {tuple(x.shape)}, expected [B, T, hc, dim]")
     B, T = x.shape[0], x.shape[1]
@@ -387,10 +439,11 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
                  k_weight=k_weight, token_mask=token_mask, out=out, workspace=workspace,
                  err_count=err_count)
     if workspace is None:
-        dev = x.device.index if x.device.index is not None else torch.cuda.current_device()
-        workspace = _default_ws.setdefault(dev, Workspace(x.device)).get(layout, B, T)
+        workspace = default_workspace(layout, B, T, x.device)
     _check("engram_forward", _lib.engram_forward(
         ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
         _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(err_count), _stream()))
+    if check:
+        engram_forward_check(workspace)
     return out

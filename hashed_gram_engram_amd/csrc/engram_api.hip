@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/engram.h"
 #include "launch.h"
 
@@ -11,7 +13,8 @@ using namespace engram;
 
 namespace {
 
-constexpr uint32_t kSpinBudget = 1u << 22;  // ~1 s of sleeping polls before a wait gives up
+constexpr uint32_t kSpinBudgetDefault = 1u << 22;  // ~1 s of sleeping polls before a wait gives up
+std::atomic<uint32_t> g_spin_budget{kSpinBudgetDefault};
 
 // From this many tokens on, the tiled schedule (256 x 256 MFMA tiles, each weight panel read
 // once per 256 tokens) replaces weight streaming (all of wkv read once per 64-token block).
@@ -138,8 +141,26 @@ const char* engram_status_str(engram_status s) {
     case ENGRAM_E_WORKSPACE: return "workspace missing or too small";
     case ENGRAM_E_HIP: return "HIP runtime error";
     case ENGRAM_E_DEVICE: return "current device is not gfx950";
+    case ENGRAM_E_TIMEOUT: return "a cross-workgroup wait of engram_forward timed out (outputs are wrong)";
   }
   return "unknown status";
+}
+
+uint32_t engram_set_spin_budget(uint32_t polls) {
+  return g_spin_budget.exchange(polls == 0 ? kSpinBudgetDefault : polls);
+}
+
+engram_status engram_forward_check(void* workspace, size_t workspace_bytes, engram_stream_t stream) {
+  if (workspace == nullptr) return ENGRAM_E_NULL;
+  if (workspace_bytes < 4 || !aligned16(workspace)) return ENGRAM_E_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return ENGRAM_E_HIP;
+  uint32_t timeouts = 0;
+  if (hipMemcpy(&timeouts, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return ENGRAM_E_HIP;
+  if (timeouts == 0) return ENGRAM_OK;
+  if (hipMemsetAsync(workspace, 0, workspace_bytes, st) != hipSuccess) return ENGRAM_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return ENGRAM_E_HIP;
+  return ENGRAM_E_TIMEOUT;
 }
 
 engram_status engram_layout_check(const engram_layout* l) {
@@ -397,7 +418,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
     a.eps = l->eps;
     a.clamp = l->clamp;
     a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
-    a.spin_budget = kSpinBudget;
+    a.spin_budget = g_spin_budget.load(std::memory_order_relaxed);
     GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
                  l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, nullptr, err_count};
     return launch_forward_tiled(a, g, workspace, reinterpret_cast<void*>(stg_start), di.cus,
@@ -436,7 +457,7 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   a.eps = l->eps;
   a.clamp = l->clamp;
   a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
-  a.spin_budget = kSpinBudget;
+  a.spin_budget = g_spin_budget.load(std::memory_order_relaxed);
   return launch_forward_stream(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? ENGRAM_OK
              : ENGRAM_E_HIP;

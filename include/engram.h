@@ -40,7 +40,9 @@ typedef enum {
   ENGRAM_E_ALIGN = -4,     /* a tensor pointer is not aligned as required        */
   ENGRAM_E_WORKSPACE = -5, /* workspace missing or smaller than required         */
   ENGRAM_E_HIP = -6,       /* the HIP runtime refused a launch or query          */
-  ENGRAM_E_DEVICE = -7     /* the current device is not gfx950                   */
+  ENGRAM_E_DEVICE = -7,    /* the current device is not gfx950                   */
+  ENGRAM_E_TIMEOUT = -8    /* a cross-workgroup wait of engram_forward gave up: the outputs of
+                              the calls since the last engram_forward_check are wrong         */
 } engram_status;
 
 /* Block scales of the fp8 table: one fp32 value per block, or one E8M0 byte per block (the
@@ -93,8 +95,8 @@ engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
  * layout and any B x T it is large enough for, on one stream without clearing, provided every
  * call on it passes the same workspace_bytes (neither part shrinks as B x T grows, so the
  * control words of any call then lie below the staging area of every other).  The exception is word 0, which counts cross-workgroup waits
- * that timed out (0 in correct operation); after a time-out the workspace must be zero-filled
- * again.  Calls that overlap in time must use different workspaces. */
+ * that timed out (0 in correct operation); engram_forward_check reports it and zero-fills the
+ * workspace after a time-out.  Calls that overlap in time must use different workspaces. */
 size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, int64_t T);
 
 /* Bytes at the end of the workspace that engram_forward uses as a staging area for B x T
@@ -164,6 +166,26 @@ engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
                              const float* q_weight, const float* k_weight, int64_t B, int64_t T,
                              uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream);
+
+/* Reports whether the engram_forward calls that used `workspace` since the last check ran
+ * correctly.  The fused schedules hand partial sums and gates between workgroups of one launch
+ * through the workspace; a workgroup waits for a hand-off only on work of lower-numbered
+ * workgroups that never waits itself, which is deadlock-free because the hardware dispatches a
+ * launch's workgroups in increasing order and the grids are at most one round of workgroups
+ * (every workgroup that is waited on has started).  Each wait is still bounded (about a second
+ * of polling, see engram_set_spin_budget); a wait that gives up counts itself in workspace word 0
+ * and the call's outputs are then wrong.
+ * This call waits for `stream` (hipStreamSynchronize), reads word 0, and returns ENGRAM_OK if it
+ * is zero.  Otherwise it zero-fills the whole workspace (a late hand-off may have left control
+ * words set) on `stream`, waits for that, and returns ENGRAM_E_TIMEOUT; the workspace is then
+ * ready for further calls.  It cannot be recorded into a graph (it synchronises). */
+engram_status engram_forward_check(void* workspace, size_t workspace_bytes, engram_stream_t stream);
+
+/* Bound of every cross-workgroup wait of engram_forward, in polls (each a short sleep): 0
+ * restores the default (2^22 polls, about a second).  Process-wide; applies to launches made
+ * after the call; returns the previous bound.  A small bound makes waits give up early, which is
+ * how a caller (a test) can drive the time-out path while every kernel still exits normally. */
+uint32_t engram_set_spin_budget(uint32_t polls);
 
 /* The hash step in front of the path (engram-second page, code panel, the hash module's
  * forward; "DeepSeek's Other Modules", Engram, The lookup pipeline): raw token ids -> the

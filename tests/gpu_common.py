@@ -94,7 +94,9 @@ def check_out(w, sel, got_bits, ref, x_bits=None):
     return err.max(), err.mean(), float((d > 0).mean())
 
 
-def forward(w, d, out=None, ws=None, err=None):
+def forward(w, d, out=None, ws=None, err=None, check=True):
+    """engram_forward through the binding; with ``check`` (the default) the call waits for its
+    stream and raises if a cross-workgroup wait timed out (engram_forward_check)."""
     return eg.engram_forward(layout(w), d["x"], d["hash_ids"], d["token_mask"], d["table"],
                              d["scales"], d["wkv"], d["q_weight"], d["k_weight"], out=out,
-                             workspace=ws, err_count=err)
+                             workspace=ws, err_count=err, check=check)

@@ -1,6 +1,8 @@
 """The binding's argument checks (CPU, no GPU call): the library takes plain pointers, so every
 tensor is checked against the layout before a call.  A wrong shape, size or dtype raises; so do
 correctly shaped tensors in host memory (the last check before the library is called)."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -106,3 +108,43 @@ def test_hash_entry_point_checks_its_tensors():
         eg.engram_hash_ids(hl, **(args | {"history": torch.zeros((2, 7), dtype=torch.int64)}))
     with pytest.raises(ValueError, match="token_map has shape"):
         eg.engram_hash_ids(hl, **(args | {"token_map": args["token_map"][:-1].contiguous()}))
+
+
+def test_default_workspace_is_one_per_device_and_stream():
+    """Calls on different streams may overlap in time and so must not share a workspace: the
+    binding keeps one per (device, stream); the same pair gets the same one back."""
+    saved = dict(eg._default_ws)
+    eg._default_ws.clear()
+    try:
+        a = eg.workspace_for(0, 0x1000)
+        assert eg.workspace_for(0, 0x1000) is a
+        b = eg.workspace_for(0, 0x2000)
+        c = eg.workspace_for(1, 0x1000)
+        assert b is not a and c is not a and c is not b
+        assert a.buf is None  # nothing is allocated before the first call
+        eg.release_default_workspaces()
+        assert not eg._default_ws
+    finally:
+        eg._default_ws.clear()
+        eg._default_ws.update(saved)
+
+
+def test_forward_check_validates_before_touching_the_device():
+    lib = eg._lib
+    assert lib.engram_forward_check(None, 256, None) == -1            # NULL workspace
+    buf = (ctypes.c_uint8 * 64)()
+    off = (16 - ctypes.addressof(buf) % 16) % 16
+    assert lib.engram_forward_check(ctypes.c_void_p(ctypes.addressof(buf) + off + 1), 32, None) == -5
+    assert lib.engram_forward_check(ctypes.c_void_p(ctypes.addressof(buf) + off), 2, None) == -5
+    assert eg.STATUS[-8] == "timeout" and eg.ENGRAM_E_TIMEOUT == -8
+    assert "timed out" in lib.engram_status_str(-8).decode()
+
+
+def test_spin_budget_setter_returns_the_previous_bound():
+    old = eg.engram_set_spin_budget(7)
+    try:
+        assert eg.engram_set_spin_budget(9) == 7
+        assert eg.engram_set_spin_budget(0) == 9          # 0 restores the default ...
+        assert eg.engram_set_spin_budget(0) == 1 << 22    # ... 2^22 polls
+    finally:
+        eg.engram_set_spin_budget(old)
