@@ -6,7 +6,11 @@ two-instance workloads, two calls, the second consuming the first one's output.
 Prints one JSON line.  `value` is tokens per second of the whole job (one GPU).
 
   python bench.py [--steps K] [--warmup W] [--workload decode_b64|prefill_t8192|...]
-                  [--flush-mib F] [--standalone]
+                  [--prefill-workload prefill_t8192|none] [--flush-mib F] [--standalone]
+
+By default the line reports the decode workload (64 tokens; `value`) and, in a nested object
+"prefill", the prefill workload (8192 tokens), each with its roofline and CPU baseline: the
+metric names both.
 
 With --flush-mib, F MiB are written between steps (evicting the L2s and the Infinity Cache) and
 each step is timed by its own event pair.  With --standalone the line also holds the three
@@ -153,40 +157,174 @@ def standalone(eg, lay, w, d, steps: int, warmup: int, stream) -> dict:
     return res
 
 
+def host_facts() -> dict:
+    """CPU model and RAM of the host the oracle runs on."""
+    model, mem_kib = "unknown", 0
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                mem_kib = int(line.split()[1])
+                break
+    except OSError:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "ram_gib": round(mem_kib / 2 ** 20, 1)}
+
+
 def cpu_baseline(w, n_tokens: int, min_seconds: float = 10.0):
-    """The CPU oracle, as it stands, on the first n_tokens tokens of the same workload (every
-    instance of it in turn, each consuming the previous one's output), repeated until at least
-    min_seconds of oracle time have accumulated."""
+    """The CPU oracle (oracle/engram_oracle.cc: plain C++, IEEE double, threads over tokens), as
+    it stands, on the first n_tokens tokens of the same workload (every instance of it in turn,
+    each consuming the previous one's output), repeated until at least min_seconds of oracle time
+    have accumulated.  Input generation (table rows, wkv) is outside the timed region."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
     sel = np.arange(n_tokens)
     mask = w.token_mask().reshape(-1)[sel]
     x0 = w.x_tokens(sel)
+
     def wkv_of(inst):  # FP8 weights are dequantised once, outside the timed region
         if w.wkv_format == "mxfp8":
-            return oracle.bf16_value(oracle.wkv_mxfp8_bits(*w.wkv8(inst))).astype(np.float32)
+            return oracle.wkv_mxfp8_bits(*w.wkv8(inst))
         return w.wkv_f32(inst)
 
-    inputs = [(wkv_of(inst), w.hash_ids(inst).reshape(w.M, w.n_cols)[sel], w.qk(inst),
-               synth.host_fetch(w, inst)) for inst in range(w.n_instances)]
+    inputs = []
+    for inst in range(w.n_instances):
+        ids = w.hash_ids(inst).reshape(w.M, w.n_cols)[sel]
+        # the rows these tokens name are generated once, outside the timed region; the oracle
+        # asks for exactly those rows (ascending) on every pass
+        flat = ids.reshape(-1)
+        need = np.unique(flat[(flat >= 0) & (flat < w.n_rows)])
+        rows = synth.host_fetch(w, inst)(need)
+
+        def provider(r, need=need, rows=rows):
+            assert np.array_equal(r, need)
+            return rows
+        inputs.append((wkv_of(inst), ids, w.qk(inst), provider))
     dt, reps = 0.0, 0
     while reps == 0 or dt < min_seconds:
         x = x0
         for wkv, ids, (q, k), fetch in inputs:
             t0 = time.perf_counter()
             x = oracle.forward(x, ids, mask, fetch, w.n_rows, w.head_dim, w.scale_block, wkv, q,
-                               k, eps=w.eps, clamp=w.clamp, scale_format=w.scale_format)["out_bits"]
+                               k, eps=w.eps, clamp=w.clamp, scale_format=w.scale_format,
+                               want=("out_bits",))["out_bits"]
             dt += time.perf_counter() - t0
         reps += 1
-    return {"value": n_tokens * reps / dt, "unit": "tokens/s", "cores": int(cores),
+    return {"value": round(n_tokens * reps / dt, 2), "unit": "tokens/s", "cores": oracle.threads(),
             "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of {w.name} (full layer dims, fp64 numpy), "
-                      f"{reps} passes, {dt:.2f} s"}
+            "sample": f"first {n_tokens} tokens of {w.name} (full layer dims; C++ oracle, IEEE "
+                      f"double, {oracle.threads()} threads over tokens), {reps} passes, {dt:.2f} s",
+            **host_facts()}
+
+
+def layout_of(eg, w):
+    return eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
+                          scale_format=eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32,
+                          wkv_format=eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16)
+
+
+def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone: bool = False) -> dict:
+    """Times `steps` steps of the workload (one step: every instance's engram_forward, the second
+    on the first one's output) after `warmup` untimed ones, inputs resident in HBM.
+
+    Events on the stream the kernels run on: one pair around every engram_forward launch (its
+    duration: the roofline's time per launch) and the first and last of them around the whole
+    timed region (its mean per step: the throughput).  With flush_mib, that many MiB are written
+    before each step (cold L2s and Infinity Cache) and the throughput is the mean of the steps'
+    own durations."""
+    import synth
+    insts = []
+    for inst in range(w.n_instances):
+        d = synth.device_inputs(w, inst=inst)
+        if inst:
+            del d["x"]  # a later instance reads the previous one's output
+        insts.append(d)
+    x0 = insts[0]["x"]
+    lay = layout_of(eg, w)
+    ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty_like(x0) for _ in insts]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flush = (torch.empty(flush_mib << 18, dtype=torch.float32, device="cuda") if flush_mib else None)
+    stream = torch.cuda.current_stream()
+    n_launch = steps * len(insts)
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+
+    def step(i=None):
+        x = x0
+        for j, (d, out) in enumerate(zip(insts, outs)):
+            if i is not None:
+                ev_a[i * len(insts) + j].record(stream)
+            eg.engram_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                              d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws,
+                              err_count=err)
+            if i is not None:
+                ev_b[i * len(insts) + j].record(stream)
+            x = out
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(float(i))
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
+    step_ms = [sum(launch_ms[i * len(insts):(i + 1) * len(insts)]) for i in range(steps)]
+    if flush is None:
+        ms = ev_a[0].elapsed_time(ev_b[-1]) / steps      # whole timed region, launch gaps included
+    else:
+        ms = float(np.mean(step_ms))
+    ms_launch = float(np.mean(launch_ms))
+    assert int(err.item()) == 0, "hash ids out of range"
+    eg.engram_forward_check(ws)   # raises if a cross-workgroup wait timed out
+
+    mode = "hbm" if w.M <= 512 else "mfma"
+    if mode == "hbm":
+        ach = algorithmic_bytes(w) / (ms_launch * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w)}
+    else:
+        ach = algorithmic_flops(w) / (ms_launch * 1e-3) / 1e12
+        peak = FP8_PEAK_TFLOPS if fp8_mfma(w) else BF16_PEAK_TFLOPS  # the contraction's own dtype
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(w)}
+    roof["kernel"] = kernel_label(w)
+    roof["per_launch_bytes"] = algorithmic_bytes(w)
+    roof["per_launch_flops"] = algorithmic_flops(w)
+    roof["ms_per_launch"] = round(ms_launch, 5)
+    roof["timing"] = "HIP events around each launch, on its stream"
+    res = {
+        "value": round(w.M / (ms * 1e-3), 1),
+        "ms_per_step": round(ms, 5),
+        "ms_p10_median_p90": [round(float(v), 5) for v in np.percentile(step_ms, [10, 50, 90])],
+        "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "dtype": "fp8 (e4m3 x E8M0)" if fp8_mfma(w) else "bf16",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
+                   "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
+                   "scale_format": w.scale_format, "wkv_format": w.wkv_format,
+                   "table_rows": w.n_rows, "hash_ids": w.hash_dist,
+                   "instances": w.n_instances, "flush_mib": flush_mib,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if with_standalone:
+        res["standalone"] = standalone(eg, lay, w, insts[0] | {"x": x0}, steps, warmup, stream)
+    del insts, outs, ws, flush
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+METRIC = "Engram forward tokens/sec at T=64 decode and T=8192 prefill; % HBM/MFMA roofline"
 
 
 def main():
@@ -195,6 +333,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode_b64")
+    ap.add_argument("--prefill-workload", default="prefill_t8192",
+                    help="second workload reported in a nested object ('none' to skip); only "
+                         "with the default --workload")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush-mib", type=int, default=0,
@@ -221,101 +362,41 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    w = synth.get(args.workload)
     torch.cuda.set_device(0)
-    insts = []
-    for inst in range(w.n_instances):
-        d = synth.device_inputs(w, inst=inst)
-        if inst:
-            del d["x"]  # a later instance reads the previous one's output
-        insts.append(d)
-    x0 = insts[0]["x"]
-    lay = eg.make_layout(w.hc, w.dim, w.n_cols, w.head_dim, w.scale_block, w.n_rows, w.eps, w.clamp,
-                         scale_format=eg.SCALE_E8M0 if w.scale_format == "e8m0" else eg.SCALE_FP32,
-                         wkv_format=eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16)
-    ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
-                     device="cuda")
-    outs = [torch.empty_like(x0) for _ in insts]
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    flush = (torch.empty(args.flush_mib << 18, dtype=torch.float32, device="cuda")
-             if args.flush_mib else None)
-
-    def step():
-        x = x0
-        for d, out in zip(insts, outs):
-            eg.engram_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"], d["scales"],
-                              d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws,
-                              err_count=err)
-            x = out
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i))
-            ev[2 * i].record(stream)
-        step()
-        ev[2 * i + 1].record(stream)
-        if flush is None:
-            ev[2 * i + 2] = ev[2 * i + 1]
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_step_ms = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
-    ms = float(np.mean(per_step_ms))
-    ms_launch = ms / w.n_instances
-    assert int(err.item()) == 0, "hash ids out of range"
-    assert int(ws[:4].view(torch.int32).item()) == 0, "a cross-workgroup wait timed out"
-
-    mode = "hbm" if w.M <= 512 else "mfma"
-    if mode == "hbm":
-        ach = algorithmic_bytes(w) / (ms_launch * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w)}
-    else:
-        ach = algorithmic_flops(w) / (ms_launch * 1e-3) / 1e12
-        peak = FP8_PEAK_TFLOPS if fp8_mfma(w) else BF16_PEAK_TFLOPS  # the contraction's own dtype
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(w)}
-    roof["kernel"] = kernel_label(w)
-    roof["per_launch_bytes"] = algorithmic_bytes(w)
-    roof["per_launch_flops"] = algorithmic_flops(w)
-    roof["ms_per_launch"] = round(ms_launch, 5)
-
+    w = synth.get(args.workload)
+    head = measure(eg, w, args.steps, args.warmup, args.flush_mib, args.standalone)
     res = {
-        "metric": "Engram forward tokens/sec",
-        "value": round(w.M / (ms * 1e-3), 1),
+        "metric": METRIC,
+        "value": head["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 5),
-        "ms_p10_median_p90": [round(float(v), 5) for v in np.percentile(per_step_ms, [10, 50, 90])],
-        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "ms_per_step": head["ms_per_step"],
+        "ms_p10_median_p90": head["ms_p10_median_p90"],
+        "wall_ms_per_step": head["wall_ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8 (e4m3 x E8M0)" if fp8_mfma(w) else "bf16",
+        "dtype": head["dtype"],
         "data": "synthetic (seeded counter-based generator; no trained weights)",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
-                   "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
-                   "scale_format": w.scale_format, "wkv_format": w.wkv_format,
-                   "table_rows": w.n_rows, "hash_ids": w.hash_dist,
-                   "instances": w.n_instances, "flush_mib": args.flush_mib,
-                   "parallelism": "single GPU"},
-        "roofline": roof,
+        "config": head["config"],
+        "roofline": head["roofline"],
     }
-    if args.standalone:
-        res["standalone"] = standalone(eg, lay, w, insts[0] | {"x": x0}, args.steps, args.warmup, stream)
+    if "standalone" in head:
+        res["standalone"] = head["standalone"]
     if not args.no_cpu_baseline:
-        n = args.cpu_tokens or min(w.M, 64)
-        res["cpu_baseline"] = cpu_baseline(w, n)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens or min(w.M, 64))
+    second = args.prefill_workload if args.workload == "decode_b64" else "none"
+    if second and second != "none":
+        w2 = synth.get(second)
+        p = measure(eg, w2, args.steps, args.warmup, args.flush_mib)
+        p = {"workload": w2.name, "value": p["value"], "unit": "tokens/s",
+             **{k: p[k] for k in ("ms_per_step", "ms_p10_median_p90", "wall_ms_per_step", "dtype",
+                                  "config", "roofline")}}
+        if not args.no_cpu_baseline:
+            p["cpu_baseline"] = cpu_baseline(w2, args.cpu_tokens or 256)
+        res["prefill"] = p
     print(json.dumps(res), flush=True)
 
 
