@@ -67,6 +67,8 @@ _lib.engram_forward.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i6
                                 _sz, _vp, _vp]
 _lib.engram_hash_ids.argtypes = [ctypes.POINTER(HashLayout), _vp, _vp, _vp, _vp, _vp, _vp, _i64,
                                  _i64, _i64, _vp, _vp, _vp, _vp]
+_lib.engram_forward_noalloc.argtypes = [_LP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.engram_forward_noalloc.restype = ctypes.c_int
 _lib.engram_forward_check.argtypes = [_vp, _sz, _vp]
 _lib.engram_set_spin_budget.argtypes = [ctypes.c_uint32]
 _lib.engram_set_spin_budget.restype = ctypes.c_uint32
@@ -78,7 +80,8 @@ for _f in (_lib.engram_layout_check, _lib.engram_param_counts, _lib.engram_gathe
 EXPORTED = ["engram_layout_check", "engram_param_counts", "engram_forward_workspace_bytes",
             "engram_forward_staging_bytes",
             "engram_gather_dequant", "engram_kv_proj", "engram_gate_apply", "engram_forward",
-            "engram_hash_ids", "engram_status_str", "engram_forward_check", "engram_set_spin_budget"]
+            "engram_hash_ids", "engram_status_str", "engram_forward_check", "engram_set_spin_budget",
+            "engram_forward_noalloc"]
 
 
 SCALE_FP32, SCALE_E8M0 = 0, 1  # engram_scale_format
@@ -410,6 +413,44 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
     """The whole Engram forward: out [B, T, hc, dim] bf16 (may be x itself).  With ``check`` the
     call waits for its stream and raises if a cross-workgroup wait timed out
     (engram_forward_check); without it the caller checks when it chooses to."""
+    if out is None:
+        out = torch.empty_like(x)
+    B, T = _check_forward_args(layout, x, hash_ids, token_mask, table, scales, wkv, q_weight,
+                               k_weight, out, err_count)
+    if workspace is not None:
+        _contig("workspace", workspace)
+    _same_device(x, workspace=workspace)
+    if workspace is None:
+        workspace = default_workspace(layout, B, T, x.device)
+    _check("engram_forward", _lib.engram_forward(
+        ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
+        _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(err_count), _stream()))
+    if check:
+        engram_forward_check(workspace)
+    return out
+
+
+def engram_forward_noalloc(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
+                           token_mask: Optional[torch.Tensor], table: torch.Tensor,
+                           scales: torch.Tensor, wkv: torch.Tensor, q_weight: torch.Tensor,
+                           k_weight: torch.Tensor, out: torch.Tensor,
+                           err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """engram_forward without a workspace argument and without any allocation: the library's
+    fixed per-GPU scratch array serves as the workspace (at most 4 MiB of it: up to 64 tokens at
+    the model's layout; larger calls raise with status ENGRAM_E_WORKSPACE).  `out` must be
+    given; calls on one GPU that overlap in time race on the scratch."""
+    B, T = _check_forward_args(layout, x, hash_ids, token_mask, table, scales, wkv, q_weight,
+                               k_weight, out, err_count)
+    _check("engram_forward_noalloc", _lib.engram_forward_noalloc(
+        ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
+        _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(err_count), _stream()))
+    return out
+
+
+def _check_forward_args(layout: EngramLayout, x, hash_ids, token_mask, table, scales, wkv,
+                        q_weight, k_weight, out, err_count):
+    """Checks the tensors of a whole forward against the layout; returns (B, T)."""
     if x.dim() != 4:
         raise ValueError(f"x has shape {tuple(x.shape)}, expected [B, T, hc, dim]")
     B, T = x.shape[0], x.shape[1]
@@ -429,21 +470,8 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
         _contig("token_mask", token_mask, (torch.uint8, torch.bool))
         _numel("token_mask", token_mask, (B, T))
     _check_err(err_count)
-    if out is None:
-        out = torch.empty_like(x)
     _numel("out", out, tuple(x.shape))
     _contig("out", out, _BF16)
-    if workspace is not None:
-        _contig("workspace", workspace)
     _same_device(x, hash_ids=hash_ids, table=table, scales=scales, wkv=wkv, q_weight=q_weight,
-                 k_weight=k_weight, token_mask=token_mask, out=out, workspace=workspace,
-                 err_count=err_count)
-    if workspace is None:
-        workspace = default_workspace(layout, B, T, x.device)
-    _check("engram_forward", _lib.engram_forward(
-        ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table), _ptr(scales),
-        _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out), _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(err_count), _stream()))
-    if check:
-        engram_forward_check(workspace)
-    return out
+                 k_weight=k_weight, token_mask=token_mask, out=out, err_count=err_count)
+    return B, T

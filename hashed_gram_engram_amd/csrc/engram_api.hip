@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/engram.h"
 #include "launch.h"
@@ -125,6 +126,74 @@ size_t forward_staging(const engram_layout* l, int64_t M, int cus) {
 
 size_t forward_workspace(const engram_layout* l, int64_t M, int cus) {
   return forward_control(l, M, cus) + forward_staging(l, M, cus);
+}
+
+// ---- the workspace of engram_forward_noalloc: a fixed device array, one copy per GPU
+constexpr size_t kScratchBytes = size_t(4) << 20;
+
+// Per device: the address of that device's copy of `scratch` (from hipGetSymbolAddress; the
+// array's name in host code is not a device address) and whether it has been cleared.
+struct ScratchSlot {
+  void* ptr = nullptr;
+  bool cleared = false;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[64];
+
+// Runs in front of every no-allocation forward, one workgroup: on a device's first call it
+// zero-fills the scratch; later, if word 0 (wait time-outs of an earlier call) is set, the
+// earlier call may have left control words set, so it zero-fills the scratch again and adds the
+// time-outs to *err_count (when given).  Otherwise it only reads word 0.
+__global__ __launch_bounds__(256) void k_scratch_guard(uint32_t* s, size_t n16, int first, int32_t* err_count) {
+  __shared__ uint32_t timeouts;
+  if (threadIdx.x == 0) timeouts = s[0];
+  __syncthreads();
+  const uint32_t t = timeouts;
+  if (!first && t == 0u) return;
+  __syncthreads();
+  if (threadIdx.x == 0 && !first && err_count != nullptr) atomicAdd(err_count, int32_t(t));
+  uint4* p = reinterpret_cast<uint4*>(s);
+  for (size_t i = threadIdx.x; i < n16; i += blockDim.x) p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+}  // namespace
+
+// The scratch array itself: file scope, one copy per GPU the library runs on, held until the
+// process ends.  Host code uses it only through the per-device address above.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// This device's scratch address, looked up once per device with the device current; `dev`
+// receives the device, `first` whether its scratch has not been cleared yet.
+engram_status scratch_of_device(void** ptr, int* dev, bool* first) {
+  if (hipGetDevice(dev) != hipSuccess || *dev < 0 || *dev >= 64) return ENGRAM_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[*dev];
+  if (sl.ptr == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ENGRAM_E_HIP;
+    sl.ptr = p;
+  }
+  *ptr = sl.ptr;
+  *first = !sl.cleared;
+  return ENGRAM_OK;
+}
+
+void scratch_mark_cleared(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch[dev].cleared = true;
+}
+
+// The synchronous checks engram_forward makes of its tensor pointers.
+engram_status check_forward_pointers(const uint16_t* x, const int64_t* hash_ids, const uint8_t* table,
+                                     const void* scales, const void* wkv, const float* q_weight,
+                                     const float* k_weight, const uint16_t* out) {
+  if (!x || !hash_ids || !table || !scales || !wkv || !q_weight || !k_weight || !out) return ENGRAM_E_NULL;
+  if (!aligned16(x) || !aligned16(table) || !aligned16(wkv) || !aligned16(q_weight) || !aligned16(k_weight) ||
+      !aligned16(out) || (reinterpret_cast<uintptr_t>(scales) & 3u) || (reinterpret_cast<uintptr_t>(hash_ids) & 7u))
+    return ENGRAM_E_ALIGN;
+  return ENGRAM_OK;
 }
 
 }  // namespace
@@ -363,10 +432,8 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   int64_t M = 0;
   if ((st = check_tokens(B, T, &M)) != ENGRAM_OK) return st;
   if (M == 0) return ENGRAM_OK;
-  if (!x || !hash_ids || !table || !scales || !wkv_arg || !q_weight || !k_weight || !out) return ENGRAM_E_NULL;
-  if (!aligned16(x) || !aligned16(table) || !aligned16(wkv_arg) || !aligned16(q_weight) || !aligned16(k_weight) ||
-      !aligned16(out) || (reinterpret_cast<uintptr_t>(scales) & 3u) || (reinterpret_cast<uintptr_t>(hash_ids) & 7u))
-    return ENGRAM_E_ALIGN;
+  if ((st = check_forward_pointers(x, hash_ids, table, scales, wkv_arg, q_weight, k_weight, out)) != ENGRAM_OK)
+    return st;
   DeviceInfo di;
   if ((st = device_info(&di)) != ENGRAM_OK) return st;
   const int N = int(N_of(l));
@@ -461,6 +528,33 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   return launch_forward_stream(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
              ? ENGRAM_OK
              : ENGRAM_E_HIP;
+}
+
+engram_status engram_forward_noalloc(const engram_layout* l, const uint16_t* x, const int64_t* hash_ids,
+                                     const uint8_t* token_mask, const uint8_t* table, const void* scales,
+                                     const void* wkv, const float* q_weight, const float* k_weight, int64_t B,
+                                     int64_t T, uint16_t* out, int32_t* err_count, engram_stream_t stream) {
+  engram_status st = engram_layout_check(l);
+  if (st != ENGRAM_OK) return st;
+  int64_t M = 0;
+  if ((st = check_tokens(B, T, &M)) != ENGRAM_OK) return st;
+  if (M == 0) return ENGRAM_OK;
+  if ((st = check_forward_pointers(x, hash_ids, table, scales, wkv, q_weight, k_weight, out)) != ENGRAM_OK)
+    return st;
+  DeviceInfo di;
+  if ((st = device_info(&di)) != ENGRAM_OK) return st;
+  if (forward_workspace(l, M, di.cus) > kScratchBytes) return ENGRAM_E_WORKSPACE;
+  void* ptr = nullptr;
+  int dev = 0;
+  bool first = false;
+  if ((st = scratch_of_device(&ptr, &dev, &first)) != ENGRAM_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_scratch_guard, dim3(1), dim3(256), 0, hs, static_cast<uint32_t*>(ptr), kScratchBytes / 16,
+                     first ? 1 : 0, err_count);
+  if (hipGetLastError() != hipSuccess) return ENGRAM_E_HIP;
+  if (first) scratch_mark_cleared(dev);
+  return engram_forward(l, x, hash_ids, token_mask, table, scales, wkv, q_weight, k_weight, B, T, out, ptr,
+                        kScratchBytes, err_count, stream);
 }
 
 }  // extern "C"

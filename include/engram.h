@@ -167,6 +167,25 @@ engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
                              uint16_t* out, void* workspace, size_t workspace_bytes,
                              int32_t* err_count, engram_stream_t stream);
 
+/* engram_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same computation and results, with
+ * no workspace argument.  The workspace is a fixed array of the library, `scratch`, 4 MiB per GPU
+ * (a static device array: each GPU the library runs on holds its own copy until the process
+ * ends); that covers calls of up to 64 tokens at the model's layout (the fused weight-streaming
+ * schedule); a call that needs more returns ENGRAM_E_WORKSPACE before anything is enqueued.
+ * Nothing is allocated, here or in the kernels.  Each call first enqueues a one-workgroup guard
+ * kernel: on a GPU's first call it zero-fills the scratch; later it reads the scratch's time-out
+ * word and, if an earlier call's wait timed out (its outputs were wrong), zero-fills the scratch
+ * again and adds the time-outs to *err_count (when err_count is not NULL).  All calls on one GPU
+ * share its scratch: calls that overlap in time on one GPU (different streams, host threads)
+ * race and give wrong results; serialise them.  Other arguments as engram_forward. */
+engram_status engram_forward_noalloc(const engram_layout* layout, const uint16_t* x,
+                                     const int64_t* hash_ids, const uint8_t* token_mask,
+                                     const uint8_t* table, const void* scales, const void* wkv,
+                                     const float* q_weight, const float* k_weight, int64_t B,
+                                     int64_t T, uint16_t* out, int32_t* err_count,
+                                     engram_stream_t stream);
+
 /* Reports whether the engram_forward calls that used `workspace` since the last check ran
  * correctly.  The fused schedules hand partial sums and gates between workgroups of one launch
  * through the workspace; a workgroup waits for a hand-off only on work of lower-numbered
