@@ -324,6 +324,129 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     return res
 
 
+class StandInBackbone:
+    """Load on the main stream standing in for the transformer layers around the Engram layers
+    (the Engram modules sit at the entries of zero-based layers 1 and 14): per layer two bf16
+    GEMMs [M, dim] x [dim, dim], each layer with weights of its own (no cache reuse across
+    layers).  Its numbers are not used; it only occupies the GPU as a backbone would."""
+
+    def __init__(self, M: int, dim: int, n_layers: int, device="cuda"):
+        g = torch.Generator(device=device).manual_seed(7)
+        self.h = torch.randn((M, dim), generator=g, device=device, dtype=torch.bfloat16)
+        self.tmp = torch.empty_like(self.h)
+        self.w = [(torch.randn((dim, dim), generator=g, device=device, dtype=torch.bfloat16) * 0.01,
+                   torch.randn((dim, dim), generator=g, device=device, dtype=torch.bfloat16) * 0.01)
+                  for _ in range(n_layers)]
+
+    def layer(self, i: int):
+        w1, w2 = self.w[i]
+        torch.matmul(self.h, w1, out=self.tmp)
+        torch.matmul(self.tmp, w2, out=self.h)
+
+
+def measure_split_phase(eg, w, steps: int, warmup: int, engram_layers=(1, 14)) -> dict:
+    """The split-phase schedule of the pages' serving engine (lookup and projection early, gate at
+    the layer's entry) against the fused forward, both inside a stand-in backbone.
+
+    Per step, with the layers 0 .. engram_layers[-1] of the stand-in backbone on the main stream:
+      fused:  each Engram layer's entry runs engram_forward on the main stream;
+      split:  at step start a side stream runs engram_gather_dequant + engram_kv_proj of every
+              instance (their inputs, the hash ids, are known before the first layer); at each
+              Engram layer's entry the main stream waits for that instance's kv and runs
+              engram_gate_apply;
+      alone:  the backbone without Engram.
+    The Engram cost a step exposes is its time minus the backbone's alone.  Instance i + 1 reads
+    instance i's output, as in the model."""
+    import synth
+    assert w.n_instances == len(engram_layers)
+    insts = []
+    for inst in range(w.n_instances):
+        d = synth.device_inputs(w, inst=inst)
+        if inst:
+            del d["x"]
+        insts.append(d)
+    x0 = insts[0]["x"]
+    lay = layout_of(eg, w)
+    ws = torch.zeros(max(256, eg.engram_forward_workspace_bytes(lay, w.B, w.T)), dtype=torch.uint8,
+                     device="cuda")
+    outs = [torch.empty_like(x0) for _ in insts]
+    embs = [torch.empty((w.B, w.T, w.K), dtype=torch.bfloat16, device="cuda") for _ in insts]
+    kvs = [torch.empty((w.B, w.T, w.N), dtype=torch.bfloat16, device="cuda") for _ in insts]
+    n_layers = engram_layers[-1] + 1
+    bb = StandInBackbone(w.M, w.dim, n_layers)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ready = [torch.cuda.Event() for _ in insts]
+
+    def step(mode: str):
+        if mode == "split":
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                for j, d in enumerate(insts):
+                    eg.engram_gather_dequant(lay, d["table"], d["scales"], d["hash_ids"], emb=embs[j])
+                    eg.engram_kv_proj(lay, embs[j], d["wkv"], kv=kvs[j])
+                    ready[j].record(side)
+        x = x0
+        j = 0
+        for layer in range(n_layers):
+            if mode != "alone" and layer in engram_layers:
+                d = insts[j]
+                if mode == "fused":
+                    eg.engram_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                                      d["wkv"], d["q_weight"], d["k_weight"], out=outs[j], workspace=ws)
+                else:
+                    main.wait_event(ready[j])
+                    eg.engram_gate_apply(lay, x, kvs[j], d["q_weight"], d["k_weight"], d["token_mask"],
+                                         out=outs[j])
+                x = outs[j]
+                j += 1
+            bb.layer(layer)
+        if mode == "split":
+            main.wait_stream(side)  # the side stream's buffers are reused by the next step
+
+    def timed(mode: str) -> float:
+        for _ in range(warmup):
+            step(mode)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        for _ in range(steps):
+            step(mode)
+        b.record(main)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {}
+    for mode in ("alone", "fused", "split", "alone"):   # the backbone alone before and after
+        ms = timed(mode)
+        res[mode] = min(ms, res.get(mode, ms))
+    check = {}
+    step("fused")
+    fused = [o.clone() for o in outs]
+    step("split")
+    torch.cuda.synchronize()
+    normal = torch.from_numpy(~w.outlier_tokens()).to(x0.device)
+    for j in range(len(insts)):
+        a, b = fused[j].reshape(w.M, -1), outs[j].reshape(w.M, -1)
+        ulp = (a.view(torch.int16).int() - b.view(torch.int16).int()).abs()
+        check[f"instance{j + 1}_vs_fused"] = {
+            "max_abs_diff": float((a.float() - b.float()).abs()[normal].max().item()),
+            "frac_beyond_1_ulp": float((ulp > 1).float().mean().item())}
+    eg.engram_forward_check(ws)
+    out = {
+        "engram_layers": list(engram_layers), "backbone": f"stand-in: {n_layers} layers x 2 bf16 "
+        f"GEMMs [{w.M}, {w.dim}] x [{w.dim}, {w.dim}] on the main stream",
+        "ms_backbone_alone": round(res["alone"], 5),
+        "ms_fused": round(res["fused"], 5), "ms_split": round(res["split"], 5),
+        "ms_exposed_fused": round(res["fused"] - res["alone"], 5),
+        "ms_exposed_split": round(res["split"] - res["alone"], 5), **check,
+    }
+    del insts, outs, embs, kvs, ws, bb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 METRIC = "Engram forward tokens/sec at T=64 decode and T=8192 prefill; % HBM/MFMA roofline"
 
 
@@ -342,6 +465,10 @@ def main():
                     help="write this many MiB between steps and time each step alone")
     ap.add_argument("--standalone", action="store_true",
                     help="also time the split path's three entry points alone")
+    ap.add_argument("--split-phase", action="store_true",
+                    help="also time the split-phase schedule (gather + projection on a side stream "
+                         "ahead of a stand-in backbone, gate at each layer entry) against the fused "
+                         "forward (two-instance workloads)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (scales HBM byte counters)")
     args = ap.parse_args()
@@ -385,6 +512,9 @@ def main():
     }
     if "standalone" in head:
         res["standalone"] = head["standalone"]
+    if args.split_phase:
+        res["split_phase"] = measure_split_phase(eg, w, args.steps, args.warmup,
+                                                 engram_layers=(1, 14)[:w.n_instances])
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_tokens or min(w.M, 64))
     second = args.prefill_workload if args.workload == "decode_b64" else "none"
