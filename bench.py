@@ -31,6 +31,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+WARMUP_MIN_S = 0.1          # least wall time of untimed warm-up steps per workload
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
@@ -266,8 +267,15 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
                 ev_b[i * len(insts) + j].record(stream)
             x = out
 
-    for _ in range(warmup):
+    # warm-up: `warmup` steps, and more until 100 ms of them have run (on a fresh GPU the first
+    # few milliseconds of launches run up to 20% slower while clocks and caches settle)
+    n_warm = 0
+    tw = time.perf_counter()
+    while n_warm < warmup or time.perf_counter() - tw < WARMUP_MIN_S:
         step()
+        n_warm += 1
+        if n_warm % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -303,6 +311,7 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     roof["ms_per_launch"] = round(ms_launch, 5)
     roof["timing"] = "HIP events around each launch, on its stream"
     res = {
+        "warmup_steps_run": n_warm,
         "value": round(w.M / (ms * 1e-3), 1),
         "ms_per_step": round(ms, 5),
         "ms_p10_median_p90": [round(float(v), 5) for v in np.percentile(step_ms, [10, 50, 90])],
@@ -499,6 +508,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": head["warmup_steps_run"],
         "ms_per_step": head["ms_per_step"],
         "ms_p10_median_p90": head["ms_p10_median_p90"],
         "wall_ms_per_step": head["wall_ms_per_step"],
@@ -522,7 +532,7 @@ def main():
         w2 = synth.get(second)
         p = measure(eg, w2, args.steps, args.warmup, args.flush_mib)
         p = {"workload": w2.name, "value": p["value"], "unit": "tokens/s",
-             **{k: p[k] for k in ("ms_per_step", "ms_p10_median_p90", "wall_ms_per_step", "dtype",
+             **{k: p[k] for k in ("warmup_steps_run", "ms_per_step", "ms_p10_median_p90", "wall_ms_per_step", "dtype",
                                   "config", "roofline")}}
         if not args.no_cpu_baseline:
             p["cpu_baseline"] = cpu_baseline(w2, args.cpu_tokens or 256)

@@ -189,7 +189,8 @@ __device__ __forceinline__ void narrow_loop(f32x4 (&acc)[NRB][4], const StreamAr
 }
 
 // ------------------------------------------------------------------------------ wide K loop
-// Chunk c of a wave covers features [q0 + 128 c, q0 + 128 c + 128) of its quarter q0.  Weight
+// Chunk c of a wave covers features [q0 + 128 c', q0 + 128 c' + 128) of its quarter q0, with
+// c' = (c + 5 w) mod (chunks per quarter) for workgroup w (see wide_loop).  Weight
 // unit (row block i, chunk c): copy instruction k in 0..3 fills LDS bytes [1024 k, 1024 k + 1024)
 // of the row block's slot, lane l at 16 l: row 4 k + l / 16 of the block, position l % 16, which
 // holds the 16-byte chunk (l % 16) ^ row -- four rows of 256 contiguous bytes from HBM.  Each
@@ -461,18 +462,23 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   constexpr int kWIns = W8 ? 2 : 4;  // copy instructions per row block and chunk
   const int q0 = wv * (a.K >> 2);
   const int nch = (a.K >> 2) / 128;
+  // Each workgroup walks its quarter's chunks starting at its own chunk (5 w mod nch), so that
+  // the workgroups' copies in flight spread over many column offsets of the weight rows instead
+  // of all sitting at the same one (a streaming probe of this pattern: 6.25 -> 6.59 TB/s).
+  const int rot = int((5u * blockIdx.x) % uint32_t(nch));
+  auto feat = [&](int c) { return q0 + 128 * ((c + rot) % nch); };
   char* my_slots = slots + wv * NRB * kSlot;
   char* my_tok = slots + 4 * NRB * kSlot + wv * kTokBuf;  // fused only
   WideTok tk;              // dense only
   uint32_t keep[4];        // fused only
   // prologue in the loop's issue order (tokens, then row blocks)
-  if constexpr (FUSED) wide_copy_tok<!MX>(my_tok, keep, a, s_ids, q0, lane);
-  else wide_issue_tok(tk, a, m0, q0, lane);
+  if constexpr (FUSED) wide_copy_tok<!MX>(my_tok, keep, a, s_ids, feat(0), lane);
+  else wide_issue_tok(tk, a, m0, feat(0), lane);
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    if constexpr (W8) wide_copy_w8(my_slots + i * kSlot, a, rw, i, q0, true, lane);
-    else wide_copy_w(my_slots + i * kSlot, a, rw, i, q0, true, lane);
+    if constexpr (W8) wide_copy_w8(my_slots + i * kSlot, a, rw, i, feat(0), true, lane);
+    else wide_copy_w(my_slots + i * kSlot, a, rw, i, feat(0), true, lane);
     asm volatile("" ::: "memory");
   }
   // Issue order per chunk c: the tokens of chunk c + 1, then (as row block i of chunk c is read)
@@ -485,7 +491,8 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
   const int fl = (lane & 15) * 256;  // this lane's fragment row in a slot
   for (int c = 0; c < nch; ++c) {
     const bool live = c + 1 < nch;
-    const int fn = q0 + 128 * (live ? c + 1 : c);  // next chunk (tokens re-read the last one)
+    const int fc = feat(c);                        // this chunk's first feature
+    const int fn = feat(live ? c + 1 : c);         // next chunk (tokens re-read the last one)
     u32x4 bt[4][4];
     u32x4 bx_lo[4], bx_hi[4];  // MX: raw token codes and scales
     int bx_sc[4];
@@ -493,12 +500,12 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
       // the token copies of chunk c have landed once only the weight copies of chunk c remain
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kWIns * NRB) : "memory");
       // the lane's E8M0 scale byte within its dword (row scales are whole dwords)
-      const int cc_cur = (q0 + 128 * c) % a.head_dim + 32 * (lane >> 4);
+      const int cc_cur = fc % a.head_dim + 32 * (lane >> 4);
       const uint32_t e8m0_shift = uint32_t((cc_cur / a.scale_block) & 3) * 8u;
       if constexpr (MX) {
         // the lane's dword in the wave's scale table: column jj of the quarter, block cc_cur / sb
         const int nb = a.head_dim / a.scale_block;
-        const int jj = (q0 + 128 * c) / a.head_dim - q0 / a.head_dim;
+        const int jj = fc / a.head_dim - q0 / a.head_dim;
         const int tstride = ((a.K >> 2) / a.head_dim) * nb;
         const char* ts = ttable + jj * nb + ((cc_cur / a.scale_block) & ~3);
         wide_tok_operands_mx(bx_lo, bx_hi, bx_sc, my_tok, keep, lane, ts, tstride, e8m0_shift);
@@ -521,7 +528,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
       u32x4 wf[4];
       if constexpr (MX) {
-        const Frag8 f8 = wide_read_w8_mx(slot, table_scales(stable, a, rw, i, q0 + 128 * c, lane), lane);
+        const Frag8 f8 = wide_read_w8_mx(slot, table_scales(stable, a, rw, i, fc, lane), lane);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wide_copy_w8(slot, a, rw, i, fn, live, lane);
         const int wsc = int((f8.sdw >> (8 * (lane >> 4))) & 0xFFu);
@@ -529,7 +536,7 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
         for (int t = 0; t < 4; ++t)
           acc[i][t] = mfma_mx16x16x128(f8.c0, f8.c1, wsc, bx_lo[t], bx_hi[t], bx_sc[t], acc[i][t]);
       } else if constexpr (W8) {
-        const Frag8 f8 = wide_read_w8(slot, table_scales(stable, a, rw, i, q0 + 128 * c, lane), lane);
+        const Frag8 f8 = wide_read_w8(slot, table_scales(stable, a, rw, i, fc, lane), lane);
         // the slot is read (into registers) before its next copy is issued
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         wide_copy_w8(slot, a, rw, i, fn, live, lane);

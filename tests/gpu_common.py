@@ -91,10 +91,19 @@ def check_out(w, sel, got_bits, ref, x_bits=None, outliers=None):
         r = np.abs(ref["out_f"][outl])
         ulp = np.exp2(np.floor(np.log2(np.maximum(r, 2.0 ** -126))) - 7)
         assert np.all(err[outl] <= 2e-2 + ulp)
-    # against the oracle's own bf16 rounding nearly everything is exact or one ulp off (larger
-    # ulp counts only where h + g * v nearly cancels)
+    # against the oracle's own bf16 rounding nearly everything is exact or one ulp off.  Where
+    # h + g * v nearly cancels (|out| under a quarter of both |h| and |g v|), a one-ulp rounding
+    # difference of the projection (within its accumulation bound) is several ulps of the small
+    # output: those elements are held to the max / mean bounds above only.
     d = np.abs(got_bits.astype(np.int32) - ref["out_bits"].astype(np.int32))
-    assert (d > 1).mean() <= 1e-3, (d > 1).mean()
+    h = oracle.bf16_value(x_bits)
+    if "kv" in ref and "gate" in ref:
+        dim = h.shape[-1]
+        gv = ref["gate"][:, :, None] * oracle.bf16_value(ref["kv"][:, 4 * dim:5 * dim])[:, None, :]
+        cancel = (np.abs(ref["out_f"]) * 4 < np.abs(h)) & (np.abs(ref["out_f"]) * 4 < np.abs(gv))
+    else:
+        cancel = np.zeros(d.shape, dtype=bool)
+    assert (d[~cancel] > 1).mean() <= 1e-3, (d[~cancel] > 1).mean()
     return err.max(), err.mean(), float((d > 0).mean())
 
 

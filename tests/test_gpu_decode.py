@@ -1,0 +1,63 @@
+"""The whole forward at decode shapes (one token block at the model's dims: the weight-streaming
+schedule) against the oracle (needs an MI355X).
+
+Partial token blocks (1, 5, 33 tokens), closed tokens, x50 outlier streams, out-of-range ids,
+fp32 and E8M0 table scales, in place; a workspace of exactly the reported size followed by guard
+bytes; control words zero after every call; bitwise-identical reruns."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from gpu_common import check_out, eg, forward, host_wkv, layout, say, u16  # noqa: E402
+
+DECODE = synth.workloads()["decode_b64"]
+MX = synth.workloads()["decode_b64_mxfp8"]
+CASES = [
+    synth.small_variant(DECODE, name="decode_dims_b1", B=1, T=1, seed=DECODE.seed + 400),
+    synth.small_variant(DECODE, name="decode_dims_b5_closed_outliers", B=5, T=1, seed=DECODE.seed + 401,
+                        mask_false_frac=0.3, outlier_frac=0.3, hash_dist="zipf"),
+    synth.small_variant(DECODE, name="decode_dims_b33", B=33, T=1, seed=DECODE.seed + 402,
+                        mask_false_frac=0.1, outlier_frac=0.05),
+    synth.small_variant(MX, name="decode_mxfp8_table_b64", seed=MX.seed + 403, mask_false_frac=0.1),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_decode_shapes_against_oracle(w):
+    say(f"[gpu] decode shapes: {w.name} ({w.M} tokens, {w.scale_format} scales)")
+    d = synth.device_inputs(w)
+    ids = w.hash_ids()
+    if w.M >= 5:   # two rows outside the table: zero rows, counted
+        ids[1, 0, 3] = -7
+        ids[w.B - 1, 0, 20] = w.n_rows + 3
+        d["hash_ids"] = torch.from_numpy(ids).cuda()
+    lay = layout(w)
+    need = eg.engram_forward_workspace_bytes(lay, w.B, w.T)
+    stg = eg.engram_forward_staging_bytes(lay, w.B, w.T)
+    buf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    buf[need:] = 0xA5
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = forward(w, d, ws=buf[:need], err=err)
+    again = forward(w, d, ws=buf[:need])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "a kernel wrote past the workspace"
+    assert int(torch.count_nonzero(buf[:need - stg]).item()) == 0, "control words left set"
+    assert torch.equal(out, again)
+    assert int(err.item()) == (2 if w.M >= 5 else 0)
+    sel = np.arange(w.M)
+    q, k = w.qk()
+    ref = oracle.forward(w.x_tokens(sel), ids.reshape(w.M, -1), w.token_mask().reshape(-1),
+                         synth.host_fetch(w), w.n_rows, w.head_dim, w.scale_block, host_wkv(w), q, k,
+                         eps=w.eps, clamp=w.clamp, scale_format=w.scale_format)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), ref))
+    # in place: out is x itself
+    x2 = d["x"].clone()
+    forward(w, d | {"x": x2}, out=x2, ws=buf[:need])
+    torch.cuda.synchronize()
+    assert torch.equal(x2, out)
+    del d, buf
+    torch.cuda.empty_cache()
