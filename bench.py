@@ -31,7 +31,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
-WARMUP_MIN_S = 0.1          # least wall time of untimed warm-up steps per workload
+WARMUP_MIN_MS = 100.0       # least wall time of untimed warm-up steps per workload (default)
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA, published
 
@@ -227,7 +227,8 @@ def layout_of(eg, w):
                           wkv_format=eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16)
 
 
-def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone: bool = False) -> dict:
+def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone: bool = False,
+            min_warmup_ms: float = WARMUP_MIN_MS) -> dict:
     """Times `steps` steps of the workload (one step: every instance's engram_forward, the second
     on the first one's output) after `warmup` untimed ones, inputs resident in HBM.
 
@@ -255,23 +256,29 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
 
+    # each instance's call checked once (argument checks in Python per call would leave the GPU
+    # idle between launches); instance j > 0 reads instance j - 1's output
+    calls = []
+    x = x0
+    for d, out in zip(insts, outs):
+        calls.append(eg.prepare_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"],
+                                        d["scales"], d["wkv"], d["q_weight"], d["k_weight"], out,
+                                        ws, err))
+        x = out
+
     def step(i=None):
-        x = x0
-        for j, (d, out) in enumerate(zip(insts, outs)):
+        for j, call in enumerate(calls):
             if i is not None:
                 ev_a[i * len(insts) + j].record(stream)
-            eg.engram_forward(lay, x, d["hash_ids"], d["token_mask"], d["table"], d["scales"],
-                              d["wkv"], d["q_weight"], d["k_weight"], out=out, workspace=ws,
-                              err_count=err)
+            call()
             if i is not None:
                 ev_b[i * len(insts) + j].record(stream)
-            x = out
 
-    # warm-up: `warmup` steps, and more until 100 ms of them have run (on a fresh GPU the first
-    # few milliseconds of launches run up to 20% slower while clocks and caches settle)
+    # warm-up: `warmup` steps, and more until min_warmup_ms of them have run (on a fresh GPU the
+    # first few milliseconds of launches run up to 20% slower while clocks and caches settle)
     n_warm = 0
     tw = time.perf_counter()
-    while n_warm < warmup or time.perf_counter() - tw < WARMUP_MIN_S:
+    while n_warm < warmup or (time.perf_counter() - tw) * 1e3 < min_warmup_ms:
         step()
         n_warm += 1
         if n_warm % 16 == 0:
@@ -470,6 +477,8 @@ def main():
                          "with the default --workload")
     ap.add_argument("--cpu-tokens", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-warmup-ms", type=float, default=WARMUP_MIN_MS,
+                    help="keep warming up until this much wall time has passed (0: exactly --warmup steps)")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="write this many MiB between steps and time each step alone")
     ap.add_argument("--standalone", action="store_true",
@@ -500,7 +509,7 @@ def main():
 
     torch.cuda.set_device(0)
     w = synth.get(args.workload)
-    head = measure(eg, w, args.steps, args.warmup, args.flush_mib, args.standalone)
+    head = measure(eg, w, args.steps, args.warmup, args.flush_mib, args.standalone, args.min_warmup_ms)
     res = {
         "metric": METRIC,
         "value": head["value"],
@@ -530,7 +539,7 @@ def main():
     second = args.prefill_workload if args.workload == "decode_b64" else "none"
     if second and second != "none":
         w2 = synth.get(second)
-        p = measure(eg, w2, args.steps, args.warmup, args.flush_mib)
+        p = measure(eg, w2, args.steps, args.warmup, args.flush_mib, min_warmup_ms=args.min_warmup_ms)
         p = {"workload": w2.name, "value": p["value"], "unit": "tokens/s",
              **{k: p[k] for k in ("warmup_steps_run", "ms_per_step", "ms_p10_median_p90", "wall_ms_per_step", "dtype",
                                   "config", "roofline")}}

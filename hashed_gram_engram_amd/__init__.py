@@ -431,6 +431,48 @@ def engram_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor
     return out
 
 
+class PreparedForward:
+    """engram_forward with its arguments checked once (prepare_forward): each call passes the same
+    tensors' pointers to the C entry point on the current stream, with no per-call Python checks,
+    so that back-to-back calls queue faster than the kernels run.  The tensors must stay alive and
+    keep their storage while the object is used."""
+
+    def __init__(self, layout, x, hash_ids, token_mask, table, scales, wkv, q_weight, k_weight,
+                 out, workspace, err_count):
+        B, T = _check_forward_args(layout, x, hash_ids, token_mask, table, scales, wkv, q_weight,
+                                   k_weight, out, err_count)
+        _contig("workspace", workspace)
+        _same_device(x, workspace=workspace)
+        need = engram_forward_workspace_bytes(layout, B, T)
+        if workspace.numel() * workspace.element_size() < need:
+            raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, "
+                             f"the call needs {need}")
+        self._keep = (layout, x, hash_ids, token_mask, table, scales, wkv, q_weight, k_weight, out,
+                      workspace, err_count)
+        self._args = (ctypes.byref(layout), _ptr(x), _ptr(hash_ids), _ptr(token_mask), _ptr(table),
+                      _ptr(scales), _ptr(wkv), _ptr(q_weight), _ptr(k_weight), B, T, _ptr(out),
+                      _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(err_count))
+        self._fn = _lib.engram_forward
+        self.out = out
+        self.workspace = workspace
+
+    def __call__(self) -> torch.Tensor:
+        st = self._fn(*self._args, _stream())
+        if st != ENGRAM_OK:
+            raise EngramError("engram_forward", st)
+        return self.out
+
+
+def prepare_forward(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
+                    token_mask: Optional[torch.Tensor], table: torch.Tensor, scales: torch.Tensor,
+                    wkv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
+                    out: torch.Tensor, workspace: torch.Tensor,
+                    err_count: Optional[torch.Tensor] = None) -> PreparedForward:
+    """A repeatable engram_forward on fixed tensors (checked here, once): returns a callable."""
+    return PreparedForward(layout, x, hash_ids, token_mask, table, scales, wkv, q_weight, k_weight,
+                           out, workspace, err_count)
+
+
 def engram_forward_noalloc(layout: EngramLayout, x: torch.Tensor, hash_ids: torch.Tensor,
                            token_mask: Optional[torch.Tensor], table: torch.Tensor,
                            scales: torch.Tensor, wkv: torch.Tensor, q_weight: torch.Tensor,

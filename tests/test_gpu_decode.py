@@ -61,3 +61,26 @@ def test_decode_shapes_against_oracle(w):
     assert torch.equal(x2, out)
     del d, buf
     torch.cuda.empty_cache()
+
+
+def test_prepared_forward_equals_forward():
+    """prepare_forward (checks once, then calls the entry point with the bound pointers) gives
+    the bits of engram_forward, call after call, and still reports an error status."""
+    w = CASES[1]
+    say(f"[gpu] prepared forward: {w.name}")
+    d = synth.device_inputs(w)
+    lay = layout(w)
+    ws = torch.zeros(eg.engram_forward_workspace_bytes(lay, w.B, w.T), dtype=torch.uint8, device="cuda")
+    ref = forward(w, d, ws=ws)
+    out = torch.empty_like(d["x"])
+    call = eg.prepare_forward(lay, d["x"], d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                              d["wkv"], d["q_weight"], d["k_weight"], out, ws)
+    for _ in range(3):
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref)
+    with pytest.raises(ValueError):
+        eg.prepare_forward(lay, d["x"], d["hash_ids"], d["token_mask"], d["table"], d["scales"],
+                           d["wkv"], d["q_weight"], d["k_weight"], out, ws[:256])
+    del d, ws
+    torch.cuda.empty_cache()
