@@ -566,17 +566,22 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
 // Sums the four K-partials in wave order; afterwards wave wv holds token sub-block wv.  With
 // ONE_ROUND (X holds NRB x 16 KB: the wide loop's weight slots) all row blocks pass through LDS
 // at once, else two at a time.
+// A workgroup barrier that completes only the wave's LDS accesses (no wait for memory).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int NRB, bool ONE_ROUND>
 __device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4], f32x4* X, int cnt, int lane,
                                          int wv) {
   if constexpr (ONE_ROUND) {
-    __syncthreads();
+    // (LDS-only barriers: the wide loop's copies have all landed, and the epilogue inputs loaded
+    // just before stay in flight under the exchange; __syncthreads would wait for them)
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
       if (i < cnt)
 #pragma unroll
         for (int t = 0; t < 4; ++t) X[((i * 4 + wv) * 4 + t) * 64 + lane] = acc[i][t];
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
       if (i < cnt) {
@@ -586,7 +591,7 @@ __device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4]
         s += X[((i * 4 + 3) * 4 + wv) * 64 + lane];
         red[i] = s;
       }
-    __syncthreads();  // X overlaps the epilogue's shared words
+    lds_barrier();  // X overlaps the epilogue's shared words
     return;
   }
 #pragma unroll
