@@ -814,9 +814,16 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           // its own slot, sign bit set as the ready mark (gates are >= 0)
           if (tid == 0) store_relaxed(counter_of(a, tb, s), 0u);
           const int v0 = owner_of_row(4 * a.dim, Q, G);
-          for (int i = tid; i < (G - v0) * kTB; i += 256) {
-            const int v = v0 + i / kTB, tt = i % kTB;
-            store_relaxed(gate_slot(a, tb, v, s) + tt, __float_as_uint(sh.red[0][tt][0]) | 0x80000000u);
+          // four words per 16-byte device-coherent store
+          for (int i = tid; i < (G - v0) * (kTB / 4); i += 256) {
+            const int v = v0 + i / (kTB / 4), t4 = 4 * (i % (kTB / 4));
+            const uint32_t off = uint32_t(reinterpret_cast<char*>(gate_slot(a, tb, v, s) + t4) -
+                                          reinterpret_cast<char*>(a.ws_hdr));
+            store_coherent4(wsr, off,
+                            __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
+                                                            __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
+                                                            __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
+                                                            __float_as_uint(sh.red[0][t4 + 3][0]) | 0x80000000u}));
           }
           // the partials are consumed: leave them zero, so that the whole workspace is zero
           // again after the call (any schedule may use it next)
@@ -845,20 +852,12 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       __syncthreads();  // sh.red may still be read by a last-arriver hand-off above
       {
         // thread (s, t) waits for gate t of stream s in this workgroup's slot, then clears it.
-        // Only lane 0 of the stream's wave polls until the first word arrives (the stream's last
-        // arriver writes all 64 words together): a whole workgroup polling device-coherent
-        // words would load the memory path the hand-off itself takes.
+        // (A wave's poll is one 256-byte read, and each poll waits for its read to return, so
+        // the 4 x 51 polling waves add ~50 GB/s at most to the memory system.)
         const int s = tid >> 6, t = tid & 63;
         uint32_t* slot = gate_slot(a, tb, w, s) + t;
         uint32_t bits = 0u;
         uint32_t it = 0;
-        if (t == 0) {
-          while (load_relaxed(slot) == 0u) {
-            __builtin_amdgcn_s_sleep(2);
-            if (++it > a.spin_budget) break;
-          }
-          it = 0;
-        }
         while ((bits = load_relaxed(slot)) == 0u) {
           __builtin_amdgcn_s_sleep(2);
           if (++it > a.spin_budget) {
