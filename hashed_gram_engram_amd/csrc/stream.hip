@@ -637,13 +637,16 @@ __device__ __forceinline__ void prefetch_key(KeyPre<NRB>& kp, const StreamArgs& 
   const int lane = tid & 63, wv = tid >> 6;
   const int64_t m = m0 + 16 * wv + (lane & 15);
   const int64_t mm = m < a.M ? m : a.M - 1;
+  // the workgroup's rows span at most two streams (checked on the host): seg_lo and seg_lo + 1
+  const int seg_lo = rw.r0 / a.dim;
+  const int nb1 = (seg_lo + 1) * a.dim;
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
     int n = rw.r0 + 16 * i + 4 * (lane >> 4);
     n = n < rw.r1 ? n : rw.r1 - 4;
-    int s = n / a.dim;
-    s = s < 4 ? s : 3;  // value columns: unused, any in-range address
-    const int d = n - (n / a.dim) * a.dim;
+    const int s0 = n < nb1 ? seg_lo : seg_lo + 1;
+    const int s = s0 < 4 ? s0 : 3;  // value columns: unused, any in-range address
+    const int d = n - s0 * a.dim;
     kp.x[i] = *reinterpret_cast<const u32x2*>(a.x + (mm * 4 + s) * a.dim + d);
     const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
     const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
@@ -686,6 +689,10 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
   const int cnt = rw.nblk;
   const int seg_lo = rw.r0 / a.dim;
   const int seg_hi = (rw.r1 - 1) / a.dim;
+  // (at most two streams per workgroup: a row is in seg_lo below nb1; value rows from nv on.
+  // Comparisons, not divisions: this code runs once per call, cold in the instruction cache)
+  const int nb1 = (seg_lo + 1) * a.dim;
+  const int nv = 4 * a.dim;
   const int64_t m0 = tb * kTB;
   const int tok = 16 * wv + (lane & 15);
   const int64_t m = m0 + tok;
@@ -708,13 +715,11 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
       const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+      // (dim is a multiple of 4: the lane's four columns share a stream)
       if (i < cnt && n < rw.r1) {
-        const int s = n / a.dim;  // dim is a multiple of 4: the lane's four columns share it
-        if (s < 4) {
-          const int d = n - s * a.dim;
+        if (n < nv) {
           const float key[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
                                 bf16_round(red[i].w)};
-          (void)d;
           const u32x2 xw = mvalid ? kp.x[i] : u32x2{0u, 0u};
           const float h[4] = {bf16_lo(xw.x), bf16_hi(xw.x), bf16_lo(xw.y), bf16_hi(xw.y)};
           const float wq[4] = {kp.wq[i].x, kp.wq[i].y, kp.wq[i].z, kp.wq[i].w};
@@ -725,7 +730,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             sk += key[r] * key[r];
             sd += (h[r] * wq[r]) * key[r];
           }
-          if (s == seg_lo) {
+          if (n < nb1) {
             pa[0] += sa; pk[0] += sk; pd[0] += sd;
           } else {
             pa[1] += sa; pk[1] += sk; pd[1] += sd;
@@ -763,7 +768,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
         }
       }
       __syncthreads();
-#pragma unroll
+#pragma unroll 1
       for (int sl = 0; sl < 2; ++sl) {
         if (sh.last[sl]) {
           __syncthreads();  // sh.red may still be read for the other stream
@@ -773,6 +778,10 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           const int nW = wl - wf + 1;
           const int t = tid & 63, q = tid >> 6;
           const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
+          // a contributor's slot for stream s: the second for the first contributor when its rows
+          // begin in stream s - 1, else the first
+          const int sl_f = row_begin(wf, Q, G) < s * a.dim ? 1 : 0;
+          auto poff = [&](int w2) { return partial_off(a, tb, w2, w2 == wf ? sl_f : 0) + t * 16; };
           // all loads of a group of 16 contributors are issued before any is used (one
           // memory round trip per group, not one per contributor); sums stay in order
           float ra = 0.f, rk = 0.f, rd = 0.f;
@@ -780,9 +789,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
             f32x4 v[16];
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-              const int w2 = base + k < wb1 ? base + k : wb0;
-              const int sl2 = s - row_begin(w2, Q, G) / a.dim;
-              v[k] = load_coherent4(wsr, partial_off(a, tb, w2, sl2) + t * 16);
+              v[k] = load_coherent4(wsr, poff(base + k < wb1 ? base + k : wb0));
             }
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
@@ -827,10 +834,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           }
           // the partials are consumed: leave them zero, so that the whole workspace is zero
           // again after the call (any schedule may use it next)
-          for (int w2 = wb0; w2 < wb1; ++w2) {
-            store_coherent4(wsr, partial_off(a, tb, w2, s - row_begin(w2, Q, G) / a.dim) + t * 16,
-                            f32x4{0.f, 0.f, 0.f, 0.f});
-          }
+          for (int w2 = wb0; w2 < wb1; ++w2) store_coherent4(wsr, poff(w2), f32x4{0.f, 0.f, 0.f, 0.f});
         }
       }
     }
@@ -842,8 +846,8 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
       for (int i = 0; i < NRB; ++i) {
         const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
-        if (i < cnt && n < rw.r1 && n / a.dim == 4 && mvalid) {
-          const int d = n - 4 * a.dim;
+        if (i < cnt && n < rw.r1 && n >= nv && mvalid) {
+          const int d = n - nv;
 #pragma unroll
           for (int s = 0; s < 4; ++s) xs[i][s] = *reinterpret_cast<const u32x2*>(a.x + size_t(m * 4 + s) * a.dim + d);
         }
@@ -876,8 +880,8 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
           const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
-          if (i < cnt && n < rw.r1 && n / a.dim == 4) {
-            const int d = n - 4 * a.dim;
+          if (i < cnt && n < rw.r1 && n >= nv) {
+            const int d = n - nv;
             const float v[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
                                 bf16_round(red[i].w)};
 #pragma unroll
