@@ -678,10 +678,20 @@ __device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, 
   return tb_block(a, tb) + 256 + (size_t(w) * 4 + s) * kTB;
 }
 
-template <int NRB, bool FUSED>
+// Value workgroups of the wide kernel write their output rows through LDS (stage_bytes at the
+// start of the LDS, which then holds no live data except the gates in Shared, read before it is
+// overwritten).  In the MFMA layout a store instruction writes 8 bytes for each of 16 tokens (16
+// separate 32-byte runs); from LDS, each instruction writes 16 bytes per lane along 4 rows (4
+// contiguous runs of up to 256 bytes), and half as many instructions are issued.  Row (s, token)
+// of a wave's 64 rows holds the workgroup's value features of that row, shifted by `shift`
+// features so that the 16-byte pieces line up with 16-byte global addresses.
+__host__ __device__ constexpr int stage_row_bytes(int nrb) { return 32 * nrb + 16; }
+__host__ __device__ constexpr int stage_bytes(int nrb) { return 4 * 64 * stage_row_bytes(nrb) + 256; }
+
+template <int NRB, bool FUSED, bool STAGE = false>
 __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], const KeyPre<NRB>& kp, Shared& sh,
                                          int64_t tb, int w,
-                                         const Rows& rw, int tid) {
+                                         const Rows& rw, int tid, char* stage = nullptr) {
   const int lane = tid & 63, wv = tid >> 6;
   const int G = gridDim.x;
   const int Q = a.N >> 2;
@@ -876,7 +886,57 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       float g[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) g[s] = sh.red[s][tok][0];
-      if (mvalid) {
+      if constexpr (STAGE) {
+        const int cv_lo = rw.r0 > nv ? rw.r0 : nv;  // first value row of this workgroup
+        const int nc = rw.r1 - cv_lo;               // its value features (a multiple of 4)
+        const int shift = (cv_lo - nv) & 7;         // 0 or 4
+        constexpr int rs = stage_row_bytes(NRB);
+        char* const stg = stage + wv * (64 * rs);
+        // bit t: token 16 wv + t is written (lanes 0..15 hold tokens 0..15 of the wave)
+        const uint64_t keep = __ballot(lane < 16 && mvalid && (open || a.out != a.x));
+        lds_barrier();  // every wave has read its gates: the staging covers Shared
+        if (mvalid) {
+#pragma unroll
+          for (int i = 0; i < NRB; ++i) {
+            const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+            if (i < cnt && n < rw.r1 && n >= nv) {
+              const int c = n - cv_lo + shift;
+              const float v[4] = {bf16_round(red[i].x), bf16_round(red[i].y), bf16_round(red[i].z),
+                                  bf16_round(red[i].w)};
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                const u32x2 xw = xs[i][s];
+                u32x2 o = xw;
+                if (open) {
+                  o.x = pack_bf16x2(bf16_lo(xw.x) + g[s] * v[0], bf16_hi(xw.x) + g[s] * v[1]);
+                  o.y = pack_bf16x2(bf16_lo(xw.y) + g[s] * v[2], bf16_hi(xw.y) + g[s] * v[3]);
+                }
+                // rows stream-major: the 16 tokens of a write fall on distinct bank pairs
+                *reinterpret_cast<u32x2*>(stg + (s * 16 + (lane & 15)) * rs + 2 * c) = o;
+              }
+            }
+          }
+        }
+        // (a wave reads only its own rows: its LDS accesses complete in order.)  Lane l covers
+        // features 8 (l % 16) .. of row 4 it + l / 16: both halves, the lower or the upper four.
+        const int rr = lane >> 4, pc = 8 * (lane & 15);
+        const bool lo_ok = pc >= shift && pc + 4 <= shift + nc;
+        const bool hi_ok = pc + 4 >= shift && pc + 8 <= shift + nc;
+        const size_t col0 = size_t(cv_lo - nv - shift + pc);
+        u32x4 piece[16];
+#pragma unroll
+        for (int it = 0; it < 16; ++it) piece[it] = *reinterpret_cast<const u32x4*>(stg + (4 * it + rr) * rs + 2 * pc);
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+          const int s = it >> 2, tt = 4 * (it & 3) + rr;  // row 4 it + rr = 16 s + tt
+          if ((keep >> tt) & 1u) {
+            uint16_t* dst = a.out + size_t((m0 + 16 * wv + tt) * 4 + s) * a.dim + col0;
+            if (lo_ok && hi_ok) *reinterpret_cast<u32x4*>(dst) = piece[it];
+            else if (lo_ok) *reinterpret_cast<u32x2*>(dst) = u32x2{piece[it].x, piece[it].y};
+            else if (hi_ok) *reinterpret_cast<u32x2*>(dst + 4) = u32x2{piece[it].z, piece[it].w};
+          }
+        }
+      } else if (mvalid) {
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
           const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
@@ -963,8 +1023,9 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   // K-partial reduction (loaded before the K loop they slow it down: registers)
   if constexpr (FUSED) prefetch_key<NRB>(kp, a, rw, m0, tid);
   f32x4 red[NRB];
+  static_assert(!WIDE || stage_bytes(NRB) <= wide_lds_bytes(NRB, FUSED, W8), "output staging exceeds the LDS");
   reduce_k<NRB, WIDE>(red, acc, reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
-  epilogue<NRB, FUSED>(a, red, kp, sh, tb, w, rw, tid);
+  epilogue<NRB, FUSED, WIDE>(a, red, kp, sh, tb, w, rw, tid, smem);
   __syncthreads();
 }
 
