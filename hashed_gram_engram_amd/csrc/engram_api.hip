@@ -88,7 +88,7 @@ size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   // the layout has no tiled schedule
   const bool tiled_layout = tiled_shape_ok(N, int(K_of(l)), l->dim, true);
   const int64_t Ms = tiled_layout && M >= kTiledMinTokensFused ? kTiledMinTokensFused - 1 : M;
-  size_t c = stream_workspace_bytes(Ms, N, stream_grid(N, cus));
+  size_t c = stream_workspace_bytes(Ms, N, l->dim, stream_grid(N, cus));
   if (use_tiled(l, M, true)) {
     const size_t t = tiled_control_bytes(M, l->dim);
     c = t > c ? t : c;

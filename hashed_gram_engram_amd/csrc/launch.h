@@ -63,6 +63,9 @@ struct StreamArgs {
   uint32_t* ws_hdr;    // workspace start: [0] wait time-outs, then per-token-block blocks
   size_t tb_stride;    // bytes per token-block block
   uint32_t spin_budget;
+  // grid: G streaming workgroups, then (fused forward of one token block) n_apply workgroups
+  // that apply the gates to the value rows
+  int G, n_apply;
 };
 
 // The hash step: token ids -> row ids of every Engram layer.
@@ -94,7 +97,7 @@ hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t s
 
 // Whole forward, weight-streaming schedule.  Needs a zero-filled workspace of
 // stream_workspace_bytes() whose control words are zero (the kernel leaves them zero).
-size_t stream_workspace_bytes(int64_t M, int N, int grid);
+size_t stream_workspace_bytes(int64_t M, int N, int dim, int grid);
 int stream_grid(int N, int num_cus);
 // Most rows of wkv one workgroup of the weight-streaming schedule owns.
 int stream_rows_per_group(int N, int G);

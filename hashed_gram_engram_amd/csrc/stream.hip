@@ -669,13 +669,36 @@ __device__ __forceinline__ uint32_t* counter_of(const StreamArgs& a, int64_t tb,
 // h q k key, 0), as a byte offset from the workspace start (they are accessed through a buffer
 // resource on it).
 __device__ __forceinline__ uint32_t partial_off(const StreamArgs& a, int64_t tb, int w, int sl) {
-  return uint32_t(256 + size_t(tb) * a.tb_stride + (256 + size_t(gridDim.x) * 4 * kTB) * 4 +
+  return uint32_t(256 + size_t(tb) * a.tb_stride + (256 + size_t(a.G) * 4 * kTB) * 4 +
                   (size_t(w) * 2 + sl) * (kTB * 16));
 }
 // Gate slot of value workgroup w for stream s: 64 words, written once by the stream's last
 // arriver (value bits with the sign bit set), read and cleared by w alone.
 __device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, int w, int s) {
   return tb_block(a, tb) + 256 + (size_t(w) * 4 + s) * kTB;
+}
+
+// Apply workgroups (the fused forward of one token block).  Value workgroup j (the j-th from
+// the first one that owns a value row) does not wait for the gates: it leaves its bf16 values in
+// a tile behind the token block's part of the workspace, one kVRow-byte row per token (its value
+// features, shifted by 0 or 4 features so that 16-byte pieces line up with those of x and out),
+// and marks the tile ready; apply workgroup 2 j + h, one of the last ids of the grid, applies the
+// gates to tokens 32 h .. 32 h + 31 of it.  The apply workgroups run on the CUs that the key
+// workgroups leave, and the value workgroups' output work (64 tokens x 4 streams of their
+// features, issue-bound on one wave per SIMD) is spread over twice as many workgroups.  Slot k of
+// an apply workgroup (32 words): k = 0..3 the gates of stream k for its 32 tokens, k = 4 word 0
+// the tile's ready mark; each written once by its producer, read and cleared by that workgroup
+// alone, which also clears its half of the tile.
+constexpr int kVRow = 240;            // bytes per token row of a value tile (up to 120 features)
+constexpr int kVTile = kTB * kVRow;   // one value workgroup's tile
+__device__ __forceinline__ uint32_t* apply_slot(const StreamArgs& a, int ap, int k) {
+  return tb_block(a, 0) + 256 + (size_t(ap) * 5 + k) * 32;
+}
+__device__ __forceinline__ uint32_t vtile_off(const StreamArgs& a, int j) {
+  return uint32_t(256 + a.tb_stride + size_t(j) * kVTile);
+}
+__device__ __forceinline__ uint32_t ws_off(const StreamArgs& a, const uint32_t* p) {
+  return uint32_t(reinterpret_cast<const char*>(p) - reinterpret_cast<const char*>(a.ws_hdr));
 }
 
 // Value workgroups of the wide kernel write their output rows through LDS (stage_bytes at the
@@ -688,12 +711,12 @@ __device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, 
 __host__ __device__ constexpr int stage_row_bytes(int nrb) { return 32 * nrb + 16; }
 __host__ __device__ constexpr int stage_bytes(int nrb) { return 4 * 64 * stage_row_bytes(nrb) + 256; }
 
-template <int NRB, bool FUSED, bool STAGE = false>
+template <int NRB, bool FUSED, bool STAGE = false, bool APPLY = false>
 __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], const KeyPre<NRB>& kp, Shared& sh,
                                          int64_t tb, int w,
                                          const Rows& rw, int tid, char* stage = nullptr) {
   const int lane = tid & 63, wv = tid >> 6;
-  const int G = gridDim.x;
+  const int G = a.G;
   const int Q = a.N >> 2;
   const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
   const int cnt = rw.nblk;
@@ -832,6 +855,17 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           if (tid == 0) store_relaxed(counter_of(a, tb, s), 0u);
           const int v0 = owner_of_row(4 * a.dim, Q, G);
           // four words per 16-byte device-coherent store
+          if constexpr (APPLY) {
+            // apply workgroup ap takes tokens 32 (ap & 1) .. + 31
+            for (int i = tid; i < a.n_apply * 8; i += 256) {
+              const int ap = i >> 3, t4 = 32 * (ap & 1) + 4 * (i & 7);
+              store_coherent4(wsr, ws_off(a, apply_slot(a, ap, s) + 4 * (i & 7)),
+                              __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
+                                                              __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
+                                                              __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
+                                                              __float_as_uint(sh.red[0][t4 + 3][0]) | 0x80000000u}));
+            }
+          } else
           for (int i = tid; i < (G - v0) * (kTB / 4); i += 256) {
             const int v = v0 + i / (kTB / 4), t4 = 4 * (i % (kTB / 4));
             const uint32_t off = uint32_t(reinterpret_cast<char*>(gate_slot(a, tb, v, s) + t4) -
@@ -849,6 +883,27 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       }
     }
 
+    // ---- value columns, apply workgroups present: the bf16 values into this workgroup's tile
+    if constexpr (APPLY) {
+      if (seg_hi == 4) {
+        const int j = w - owner_of_row(4 * a.dim, Q, G);
+        const int cv_lo = rw.r0 > nv ? rw.r0 : nv;
+        const int shift = (cv_lo - nv) & 7;
+        const uint32_t row = vtile_off(a, j) + uint32_t(tok) * kVRow;
+#pragma unroll
+        for (int i = 0; i < NRB; ++i) {
+          const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+          if (i < cnt && n < rw.r1 && n >= nv)
+            __builtin_amdgcn_raw_buffer_store_b64(
+                u32x2{pack_bf16x2(red[i].x, red[i].y), pack_bf16x2(red[i].z, red[i].w)}, wsr,
+                row + 2 * uint32_t(n - cv_lo + shift), 0, kCpolSc1);
+        }
+        drain_memory_ops();
+        __syncthreads();
+        if (tid < 2) store_relaxed(apply_slot(a, 2 * j + tid, 4), 0x80000000u);
+      }
+      return;
+    }
     // ---- value columns: wait for the four gates, then out = h + g * value on every stream
     if (seg_hi == 4) {
       // the streams of this workgroup's features are read before waiting
@@ -963,7 +1018,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 }
 
 // One 64-token block: stage the hash ids, run the K loop, reduce, finish.
-template <int NRB, bool WIDE, int U, bool FUSED, bool W8 = false, bool MX = false>
+template <int NRB, bool WIDE, int U, bool FUSED, bool W8 = false, bool MX = false, bool APPLY = false>
 __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w,
                                             const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1025,7 +1080,7 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   f32x4 red[NRB];
   static_assert(!WIDE || stage_bytes(NRB) <= wide_lds_bytes(NRB, FUSED, W8), "output staging exceeds the LDS");
   reduce_k<NRB, WIDE>(red, acc, reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
-  epilogue<NRB, FUSED, WIDE>(a, red, kp, sh, tb, w, rw, tid, smem);
+  epilogue<NRB, FUSED, WIDE, APPLY>(a, red, kp, sh, tb, w, rw, tid, smem);
   __syncthreads();
 }
 
@@ -1035,10 +1090,111 @@ __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
-  const int G = gridDim.x, w = blockIdx.x;
+  const int G = a.G, w = blockIdx.x;
   const Rows rw = rows_of(w, a.N, G);
   const int64_t n_tb = (a.M + kTB - 1) / kTB;
   for (int64_t tb = 0; tb < n_tb; ++tb) token_block<NRB, false, U, FUSED>(a, smem, sh, tb, w, rw);
+}
+
+// Apply workgroup ap (value tile j = ap / 2, tokens 32 (ap & 1) .. + 31): out = h + g * value
+// on all four streams of the tile's features.  Thread pairs (token t, 16-byte piece p) of the
+// rows, t = idx / 16 and p = idx % 16 for idx = tid, tid + 256; x is loaded before waiting.
+__device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap) {
+  const int tid = threadIdx.x, G = a.G, Q = a.N >> 2;
+  const int j = ap >> 1, th = ap & 1;
+  const Rows rw = rows_of(owner_of_row(4 * a.dim, Q, G) + j, a.N, G);
+  const int nv = 4 * a.dim;
+  const int cv_lo = rw.r0 > nv ? rw.r0 : nv, nc = rw.r1 - cv_lo, shift = (cv_lo - nv) & 7;
+  const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
+  float* const gl = reinterpret_cast<float*>(smem);  // gates [stream][token]
+  u32x4 xv[2][4];
+  bool lo_ok[2], hi_ok[2], open[2];
+  size_t col[2];
+  int64_t m[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int idx = tid + 256 * k, t = idx >> 4, pc = 8 * (idx & 15);
+    m[k] = 32 * th + t;
+    const bool mv = m[k] < a.M;
+    lo_ok[k] = mv && pc >= shift && pc + 4 <= shift + nc;
+    hi_ok[k] = mv && pc + 4 >= shift && pc + 8 <= shift + nc;
+    col[k] = size_t(cv_lo - nv - shift + pc);
+    open[k] = mv && (a.token_mask == nullptr || a.token_mask[m[k]] != 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint16_t* src = a.x + size_t(m[k] * 4 + s) * a.dim + col[k];
+      xv[k][s] = u32x4{0u, 0u, 0u, 0u};
+      if (lo_ok[k] && hi_ok[k]) xv[k][s] = *reinterpret_cast<const u32x4*>(src);
+      else if (lo_ok[k]) { const u32x2 h = *reinterpret_cast<const u32x2*>(src); xv[k][s].x = h.x; xv[k][s].y = h.y; }
+      else if (hi_ok[k]) { const u32x2 h = *reinterpret_cast<const u32x2*>(src + 4); xv[k][s].z = h.x; xv[k][s].w = h.y; }
+    }
+  }
+  // the tile is ready, then the gates (each waited for by one thread, bounded)
+  if (tid == 0) {
+    uint32_t* flag = apply_slot(a, ap, 4);
+    uint32_t it = 0;
+    while (load_relaxed(flag) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it > a.spin_budget) {
+        atomic_add_relaxed(&a.ws_hdr[0], 1u);
+        break;
+      }
+    }
+    store_relaxed(flag, 0u);
+  }
+  __syncthreads();
+  f32x4 vv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    // (pieces that hold a feature end inside the row: 8 p + 4 <= shift + nc <= 116)
+    vv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lo_ok[k] || hi_ok[k])
+      vv[k] = load_coherent4(wsr, vtile_off(a, j) + uint32_t(m[k]) * kVRow + 16 * uint32_t((tid + 256 * k) & 15));
+  }
+  if (tid < 128) {
+    const int s = tid >> 5, t = tid & 31;
+    uint32_t* slot = apply_slot(a, ap, s) + t;
+    uint32_t bits = 0u, it = 0;
+    while ((bits = load_relaxed(slot)) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++it > a.spin_budget) {
+        atomic_add_relaxed(&a.ws_hdr[0], 1u);
+        break;
+      }
+    }
+    store_relaxed(slot, 0u);
+    gl[s * 32 + t] = __uint_as_float(bits & 0x7FFFFFFFu);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = (tid + 256 * k) >> 4;
+    const u32x4 v4 = __builtin_bit_cast(u32x4, vv[k]);
+    const float v[8] = {bf16_lo(v4.x), bf16_hi(v4.x), bf16_lo(v4.y), bf16_hi(v4.y),
+                        bf16_lo(v4.z), bf16_hi(v4.z), bf16_lo(v4.w), bf16_hi(v4.w)};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const float g = gl[s * 32 + t];
+      const u32x4 xw = xv[k][s];
+      u32x4 o = xw;
+      if (open[k]) {
+        o.x = pack_bf16x2(bf16_lo(xw.x) + g * v[0], bf16_hi(xw.x) + g * v[1]);
+        o.y = pack_bf16x2(bf16_lo(xw.y) + g * v[2], bf16_hi(xw.y) + g * v[3]);
+        o.z = pack_bf16x2(bf16_lo(xw.z) + g * v[4], bf16_hi(xw.z) + g * v[5]);
+        o.w = pack_bf16x2(bf16_lo(xw.w) + g * v[6], bf16_hi(xw.w) + g * v[7]);
+      }
+      if (open[k] || a.out != a.x) {
+        uint16_t* dst = a.out + size_t(m[k] * 4 + s) * a.dim + col[k];
+        if (lo_ok[k] && hi_ok[k]) *reinterpret_cast<u32x4*>(dst) = o;
+        else if (lo_ok[k]) *reinterpret_cast<u32x2*>(dst) = u32x2{o.x, o.y};
+        else if (hi_ok[k]) *reinterpret_cast<u32x2*>(dst + 4) = u32x2{o.z, o.w};
+      }
+    }
+  }
+  // every thread's tile loads have returned (their values are used above): clear this half
+  __syncthreads();
+  for (int i = tid; i < 32 * kVRow / 16; i += 256)
+    store_coherent4(wsr, vtile_off(a, j) + uint32_t(32 * th) * kVRow + 16 * uint32_t(i), f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 // Wide kernel: every workgroup has NLO or NHI = NLO + 1 row blocks, each compiled exactly (only
@@ -1051,14 +1207,20 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
-  const int G = gridDim.x, w = blockIdx.x;
+  const int G = a.G, w = blockIdx.x;
+  if constexpr (ONE_TB && FUSED) {
+    if (w >= G) {
+      apply_wg(a, smem, w - G);
+      return;
+    }
+  }
   const Rows rw = rows_of(w, a.N, G);
   if constexpr (ONE_TB) {
     if constexpr (NLO == NHI) {
-      token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
+      token_block<NLO, true, 1, FUSED, W8, MX, FUSED>(a, smem, sh, 0, w, rw);
     } else {
-      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
-      else token_block<NHI, true, 1, FUSED, W8, MX>(a, smem, sh, 0, w, rw);
+      if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED, W8, MX, FUSED>(a, smem, sh, 0, w, rw);
+      else token_block<NHI, true, 1, FUSED, W8, MX, FUSED>(a, smem, sh, 0, w, rw);
     }
     return;
   }
@@ -1112,6 +1274,13 @@ void* pick_wide(int nlo, int nhi, bool one_tb) {
     case 7: return pick_wide_n<7, FUSED, W8, MX>(same, one_tb);
     default: return nullptr;
   }
+}
+
+// Workgroups that own a value row (the owner of the first value row, 4 dim, and all after it).
+int value_groups(int N, int dim, int G) {
+  const int Q = N / 4;
+  const int v0 = int((uint32_t((4 * dim) / 4 + 1) * uint32_t(G) - 1u) / uint32_t(Q));
+  return G - v0;
 }
 
 // Fewest and most 16-row blocks of a workgroup (rows per workgroup: 4 floor(Q / G) or
@@ -1170,6 +1339,15 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   }
   if (fn == nullptr) return hipErrorInvalidValue;
   StreamArgs arg = a;
+  arg.G = G;
+  arg.n_apply = 0;
+  if (FUSED && wide && (a.w8 || a.M <= kTB)) {
+    // the one-token-block fused kernel: two apply workgroups per value workgroup, whose slots
+    // (5 x 32 words each) fit in the token block's gate-slot region (G x 4 x 64 words)
+    const int V = value_groups(a.N, a.dim, G);
+    if (V < 1 || 2 * V * 160 > G * 256) return hipErrorInvalidValue;
+    arg.n_apply = 2 * V;
+  }
   void* params[] = {&arg};
   const size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
   if (lds > 163840) return hipErrorInvalidValue;
@@ -1192,7 +1370,7 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
       }
     }
   }
-  return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
+  return hipLaunchKernel(fn, dim3(G + arg.n_apply), dim3(256), params, lds, stream);
 }
 
 
@@ -1227,10 +1405,14 @@ size_t stream_tb_stride(int grid) {
   return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 16;
 }
 
-size_t stream_workspace_bytes(int64_t M, int N, int grid) {
+// One token block of the fused forward also needs the value tiles behind its block (cleared
+// again by the apply workgroups); the larger of the two layouts, so that the size never
+// decreases with M.
+size_t stream_workspace_bytes(int64_t M, int N, int dim, int grid) {
   const int64_t n_tb = (M + kTB - 1) / kTB;
-  (void)N;
-  return 256 + size_t(n_tb) * stream_tb_stride(grid);
+  const size_t blocks = size_t(n_tb) * stream_tb_stride(grid);
+  const size_t one = stream_tb_stride(grid) + size_t(value_groups(N, dim, grid)) * kVTile;
+  return 256 + (blocks > one ? blocks : one);
 }
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
