@@ -1166,29 +1166,36 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
     gl[s * 32 + t] = __uint_as_float(bits & 0x7FFFFFFFu);
   }
   __syncthreads();
+  // the eight gates first (one LDS round trip), then branch-free stores: a half piece that is
+  // not written goes to an offset past the end of out, which the buffer store drops
+  float g[2][4];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) g[k][s] = gl[s * 32 + ((tid + 256 * k) >> 4)];
+  const size_t out_bytes = size_t(a.M) * 4 * size_t(a.dim) * 2;
+  const __amdgpu_buffer_rsrc_t outr = __builtin_amdgcn_make_buffer_rsrc(
+      a.out, (short)0, int(out_bytes < 0x7FFFFFFFu ? out_bytes : 0x7FFFFFFFu), 0x00020000);
+  const bool wr = a.out != a.x;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int t = (tid + 256 * k) >> 4;
     const u32x4 v4 = __builtin_bit_cast(u32x4, vv[k]);
     const float v[8] = {bf16_lo(v4.x), bf16_hi(v4.x), bf16_lo(v4.y), bf16_hi(v4.y),
                         bf16_lo(v4.z), bf16_hi(v4.z), bf16_lo(v4.w), bf16_hi(v4.w)};
+    const bool st = open[k] || wr;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float g = gl[s * 32 + t];
+      const float gs = open[k] ? g[k][s] : 0.0f;
       const u32x4 xw = xv[k][s];
-      u32x4 o = xw;
-      if (open[k]) {
-        o.x = pack_bf16x2(bf16_lo(xw.x) + g * v[0], bf16_hi(xw.x) + g * v[1]);
-        o.y = pack_bf16x2(bf16_lo(xw.y) + g * v[2], bf16_hi(xw.y) + g * v[3]);
-        o.z = pack_bf16x2(bf16_lo(xw.z) + g * v[4], bf16_hi(xw.z) + g * v[5]);
-        o.w = pack_bf16x2(bf16_lo(xw.w) + g * v[6], bf16_hi(xw.w) + g * v[7]);
-      }
-      if (open[k] || a.out != a.x) {
-        uint16_t* dst = a.out + size_t(m[k] * 4 + s) * a.dim + col[k];
-        if (lo_ok[k] && hi_ok[k]) *reinterpret_cast<u32x4*>(dst) = o;
-        else if (lo_ok[k]) *reinterpret_cast<u32x2*>(dst) = u32x2{o.x, o.y};
-        else if (hi_ok[k]) *reinterpret_cast<u32x2*>(dst + 4) = u32x2{o.z, o.w};
-      }
+      u32x4 o;
+      o.x = pack_bf16x2(bf16_lo(xw.x) + gs * v[0], bf16_hi(xw.x) + gs * v[1]);
+      o.y = pack_bf16x2(bf16_lo(xw.y) + gs * v[2], bf16_hi(xw.y) + gs * v[3]);
+      o.z = pack_bf16x2(bf16_lo(xw.z) + gs * v[4], bf16_hi(xw.z) + gs * v[5]);
+      o.w = pack_bf16x2(bf16_lo(xw.w) + gs * v[6], bf16_hi(xw.w) + gs * v[7]);
+      if (!open[k]) o = xw;  // closed tokens pass through unchanged (a select, not a branch)
+      const uint32_t off = uint32_t((size_t(m[k] * 4 + s) * a.dim + col[k]) * 2);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{o.x, o.y}, outr, st && lo_ok[k] ? off : 0xFFFFFFF0u, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{o.z, o.w}, outr, st && hi_ok[k] ? off + 8 : 0xFFFFFFF0u, 0, 0);
     }
   }
   // every thread's tile loads have returned (their values are used above): clear this half
