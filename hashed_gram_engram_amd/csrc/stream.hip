@@ -41,16 +41,18 @@
 // and h * q * k * key over their features; each workgroup posts one partial per (token,
 // stream) and bumps a per-stream counter.  The workgroup that arrives last for a stream sums
 // the partials of all contributing workgroups in workgroup order (deterministic), evaluates
-// the gate of the 64 tokens and writes it into a slot of every value workgroup.  Workgroups
-// holding value columns wait for their four slots, then write out = bf16(h + g * value) for
-// their features on all four streams.
-// Value columns belong to the highest workgroup ids and only value workgroups wait, on key
-// work of lower ids that never waits.  Workgroups are dispatched in id order and the grid is at
-// most one workgroup per CU, so every key workgroup is running or done before a value
-// workgroup can wait on it; each wait is bounded as well, and a time-out is recorded in the
-// workspace header instead of hanging.  Partial sums and gates pass between workgroups through
-// device-coherent atomic loads and stores ordered by store completion and barriers; counters
-// and gate slots are reset by their last user, so a call leaves them zero.
+// the gate of the 64 tokens and writes it into the slots of the workgroups that apply it.  With
+// one token block (decode), value workgroups leave their bf16 values in tiles and exit, and
+// apply workgroups (ids after the streaming ones) wait for a tile and its gates, then write
+// out = bf16(h + g * value) for the tile's features on all four streams; over several token
+// blocks, the value workgroups themselves wait for their slots and write out.
+// Only workgroups of higher ids wait, on work of lower ids that never waits (value columns
+// belong to the highest streaming ids, apply workgroups come after them).  Workgroups are
+// dispatched in id order and at most one runs per CU, so every workgroup that one waits on is
+// running or done before the wait starts; each wait is bounded as well, and a time-out is
+// recorded in the workspace header instead of hanging.  Partial sums, tiles and gates pass
+// between workgroups through device-coherent loads and stores ordered by store completion and
+// barriers; counters, slots and tiles are reset by their last user, so a call leaves them zero.
 #include <string.h>
 
 #include "common.h"
