@@ -418,6 +418,32 @@ def test_forward_streaming_token_blocks_exact_workspace_with_guard():
     say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
 
 
+@pytest.mark.parametrize("T", [37, 64])
+def test_forward_one_token_block_apply_workgroups_small_layout(T):
+    """One token block on the layout without a tiled schedule: the weight-streaming kernel with
+    apply workgroups at one or two 4-row groups per workgroup (value tiles of 4 or 8 features,
+    shifted by 4 for half of them), a partial second token half at 37 tokens; a workspace of
+    exactly the reported size followed by guard bytes, every control word (tiles included) left
+    zero, in place as well."""
+    w = synth.small_variant(STREAM_ONLY, name=f"dim320_b1_t{T}", B=1, T=T, seed=TINY.seed + 310 + T)
+    say(f"[gpu] forward {w.name}: one token block, apply workgroups, small layout")
+    lay = layout(w)
+    d = synth.device_inputs(w)
+    need = eg.engram_forward_workspace_bytes(lay, w.B, w.T)
+    buf = torch.zeros(need + 4096, dtype=torch.uint8, device="cuda")
+    buf[need:] = 0xA5
+    out = forward(w, d, ws=buf[:need])
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "a kernel wrote past the workspace"
+    assert int(torch.count_nonzero(buf[:need]).item()) == 0
+    sel = np.arange(w.M)
+    say("   ", check_out(w, sel, u16(out).reshape(w.M, w.hc, w.dim), oracle_for(w, sel)))
+    x2 = d["x"].clone()
+    forward(w, d | {"x": x2}, out=x2, ws=buf[:need])
+    torch.cuda.synchronize()
+    assert torch.equal(x2, out)
+
+
 def test_kv_proj_streaming_two_token_blocks():
     say("[gpu] kv_proj decode dims, B=3 T=37 (weight streaming, two token blocks)")
     w = RAGGED
