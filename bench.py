@@ -232,11 +232,13 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     """Times `steps` steps of the workload (one step: every instance's engram_forward, the second
     on the first one's output) after `warmup` untimed ones, inputs resident in HBM.
 
-    Events on the stream the kernels run on: one pair around every engram_forward launch (its
-    duration: the roofline's time per launch) and the first and last of them around the whole
-    timed region (its mean per step: the throughput).  With flush_mib, that many MiB are written
-    before each step (cold L2s and Infinity Cache) and the throughput is the mean of the steps'
-    own durations."""
+    Two passes of `steps` steps each, events on the stream the kernels run on.  The throughput
+    pass records one event before the first step and one after the last, nothing in between
+    (an event recorded between two launches adds its own gap on the GPU); its mean per step is
+    the throughput.  The second pass records a pair around every engram_forward launch: their
+    durations give the roofline's time per launch and the step-time percentiles.  With
+    flush_mib, that many MiB are written before each step (cold L2s and Infinity Cache) and the
+    throughput is the mean of the second pass's step durations."""
     import synth
     insts = []
     for inst in range(w.n_instances):
@@ -255,6 +257,7 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     n_launch = steps * len(insts)
     ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
     ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(n_launch)]
+    ev_run = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
 
     # each instance's call checked once (argument checks in Python per call would leave the GPU
     # idle between launches); instance j > 0 reads instance j - 1's output
@@ -284,20 +287,37 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
         if n_warm % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    # throughput pass: the timed steps back to back, an event on each side of the region
+    wall = None
+    if flush is None:
+        t0 = time.perf_counter()
+        ev_run[0].record(stream)
+        for i in range(steps):
+            step()
+        ev_run[1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    # per-launch pass: an event pair around every launch
+    t1 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
             flush.fill_(float(i))
         step(i)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    if wall is None:
+        wall = time.perf_counter() - t1
     launch_ms = [a.elapsed_time(b) for a, b in zip(ev_a, ev_b)]
     step_ms = [sum(launch_ms[i * len(insts):(i + 1) * len(insts)]) for i in range(steps)]
     if flush is None:
-        ms = ev_a[0].elapsed_time(ev_b[-1]) / steps      # whole timed region, launch gaps included
+        ms = ev_run[0].elapsed_time(ev_run[1]) / steps   # whole timed region, launch gaps included
+        ms_events = ev_a[0].elapsed_time(ev_b[-1]) / steps  # the same with events between launches
     else:
         ms = float(np.mean(step_ms))
-    ms_launch = float(np.mean(launch_ms))
+        ms_events = ms
+    # time per launch: the throughput pass's region over its launches (back to back, nothing
+    # recorded between them); with flushing, the mean of the per-launch event pairs
+    ms_launch_events = float(np.mean(launch_ms))
+    ms_launch = ms * steps / n_launch if flush is None else ms_launch_events
     assert int(err.item()) == 0, "hash ids out of range"
     eg.engram_forward_check(ws)   # raises if a cross-workgroup wait timed out
 
@@ -316,13 +336,18 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     roof["per_launch_bytes"] = algorithmic_bytes(w)
     roof["per_launch_flops"] = algorithmic_flops(w)
     roof["ms_per_launch"] = round(ms_launch, 5)
-    roof["timing"] = "HIP events around each launch, on its stream"
+    roof["ms_per_launch_events"] = round(ms_launch_events, 5)
+    roof["timing"] = ("HIP events on the launches' stream around the timed region of back-to-back "
+                      "launches, divided by the launches (ms_per_launch_events: the mean of event "
+                      "pairs around each launch, which add their own gaps)" if flush is None else
+                      "HIP events around each launch, on its stream")
     res = {
         "warmup_steps_run": n_warm,
         "value": round(w.M / (ms * 1e-3), 1),
         "ms_per_step": round(ms, 5),
         "ms_p10_median_p90": [round(float(v), 5) for v in np.percentile(step_ms, [10, 50, 90])],
         "wall_ms_per_step": round(wall * 1e3 / steps, 5),
+        "ms_per_step_with_launch_events": round(ms_events, 5),
         "dtype": "fp8 (e4m3 x E8M0)" if fp8_mfma(w) else "bf16",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "hc": w.hc, "dim": w.dim,
                    "n_cols": w.n_cols, "head_dim": w.head_dim, "scale_block": w.scale_block,
@@ -521,6 +546,7 @@ def main():
         "ms_per_step": head["ms_per_step"],
         "ms_p10_median_p90": head["ms_p10_median_p90"],
         "wall_ms_per_step": head["wall_ms_per_step"],
+        "ms_per_step_with_launch_events": head["ms_per_step_with_launch_events"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -541,8 +567,8 @@ def main():
         w2 = synth.get(second)
         p = measure(eg, w2, args.steps, args.warmup, args.flush_mib, min_warmup_ms=args.min_warmup_ms)
         p = {"workload": w2.name, "value": p["value"], "unit": "tokens/s",
-             **{k: p[k] for k in ("warmup_steps_run", "ms_per_step", "ms_p10_median_p90", "wall_ms_per_step", "dtype",
-                                  "config", "roofline")}}
+             **{k: p[k] for k in ("warmup_steps_run", "ms_per_step", "ms_p10_median_p90", "wall_ms_per_step",
+                                  "ms_per_step_with_launch_events", "dtype", "config", "roofline")}}
         if not args.no_cpu_baseline:
             p["cpu_baseline"] = cpu_baseline(w2, args.cpu_tokens or 256)
         res["prefill"] = p
