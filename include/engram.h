@@ -87,8 +87,9 @@ engram_status engram_layout_check(const engram_layout* layout);
 engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
 
 /* Bytes of workspace engram_forward needs for B x T tokens on the current device (0 on an
- * invalid layout).  The workspace holds control words at its start (counters, gate slots and
- * partial sums) and, for token counts where the tiled schedule runs, a staging area for the
+ * invalid layout).  The workspace holds control words at its start (counters, gate slots,
+ * partial sums and, for up to 64 tokens, the bf16 value tiles that the weight-streaming kernel
+ * hands to its apply workgroups) and, for token counts where the tiled schedule runs, a staging area for the
  * dequantised rows in its last engram_forward_staging_bytes() bytes.  It must be zero-filled
  * before its first use.  Every call leaves all control words zero again; the staging area's
  * contents are unspecified after a call.  So one workspace serves any number of calls with one
@@ -190,8 +191,8 @@ engram_status engram_forward_noalloc(const engram_layout* layout, const uint16_t
  * correctly.  The fused schedules hand partial sums and gates between workgroups of one launch
  * through the workspace; a workgroup waits for a hand-off only on work of lower-numbered
  * workgroups that never waits itself, which is deadlock-free because the hardware dispatches a
- * launch's workgroups in increasing order and the grids are at most one round of workgroups
- * (every workgroup that is waited on has started).  Each wait is still bounded (about a second
+ * launch's workgroups in increasing order (every workgroup that is waited on has started before
+ * the wait, and finishes since it waits for nothing).  Each wait is still bounded (about a second
  * of polling, see engram_set_spin_budget); a wait that gives up counts itself in workspace word 0
  * and the call's outputs are then wrong.
  * This call waits for `stream` (hipStreamSynchronize), reads word 0, and returns ENGRAM_OK if it
