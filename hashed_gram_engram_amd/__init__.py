@@ -479,7 +479,7 @@ def engram_forward_noalloc(layout: EngramLayout, x: torch.Tensor, hash_ids: torc
                            k_weight: torch.Tensor, out: torch.Tensor,
                            err_count: Optional[torch.Tensor] = None) -> torch.Tensor:
     """engram_forward without a workspace argument and without any allocation: the library's
-    fixed per-GPU scratch array serves as the workspace (at most 4 MiB of it: up to 64 tokens at
+    fixed per-GPU scratch array serves as the workspace (at most 4 MiB of it: up to 128 tokens at
     the model's layout; larger calls raise with status ENGRAM_E_WORKSPACE).  `out` must be
     given; calls on one GPU that overlap in time race on the scratch."""
     B, T = _check_forward_args(layout, x, hash_ids, token_mask, table, scales, wkv, q_weight,

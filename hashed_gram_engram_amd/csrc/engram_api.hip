@@ -67,6 +67,19 @@ bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
 
 bool wkv_mxfp8(const engram_layout* l) { return l->wkv_format == ENGRAM_WKV_MXFP8; }
 
+// The layout admits the two-token-block weight-streaming kernel (bf16 weights, workgroups
+// spanning at most two streams), which then takes every forward of 65..128 tokens.
+bool tb2_layout(const engram_layout* l, int cus) {
+  const int N = int(N_of(l));
+  return !wkv_mxfp8(l) && stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim &&
+         stream_tb2_ok(int(K_of(l)), N, l->n_cols, l->head_dim, l->scale_block, cus);
+}
+bool use_tb2(const engram_layout* l, int64_t M, int cus) { return M > 64 && M <= 128 && tb2_layout(l, cus); }
+// the tiled schedule for the whole forward
+bool use_tiled_fused(const engram_layout* l, int64_t M, int cus) {
+  return use_tiled(l, M, true) && !use_tb2(l, M, cus);
+}
+
 // The fused weight-streaming kernel reads MXFP8 weights itself for one token block; every other
 // forward with MXFP8 weights first expands them to bf16 in the staging area.
 bool forward_w8_native(const engram_layout* l, int64_t M, int cus) {
@@ -84,12 +97,13 @@ bool forward_w8_native(const engram_layout* l, int64_t M, int cus) {
 // call leaves behind never sit where a later call expects zeros.
 size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   const int N = int(N_of(l));
-  // token counts the streaming schedule takes: up to the tiled threshold, or all of them when
-  // the layout has no tiled schedule
+  // token counts the streaming schedules take: up to the tiled threshold (128 tokens where the
+  // two-token-block kernel fits the layout), or all of them when the layout has no tiled schedule
   const bool tiled_layout = tiled_shape_ok(N, int(K_of(l)), l->dim, true);
-  const int64_t Ms = tiled_layout && M >= kTiledMinTokensFused ? kTiledMinTokensFused - 1 : M;
+  const int64_t cap = tb2_layout(l, cus) ? 128 : kTiledMinTokensFused - 1;
+  const int64_t Ms = tiled_layout && M > cap ? cap : M;
   size_t c = stream_workspace_bytes(Ms, N, l->dim, stream_grid(N, cus));
-  if (use_tiled(l, M, true)) {
+  if (use_tiled_fused(l, M, cus)) {
     const size_t t = tiled_control_bytes(M, l->dim);
     c = t > c ? t : c;
   }
@@ -108,8 +122,8 @@ bool forward_tiled_mx(const engram_layout* l, int64_t M) {
 // (the expansion is absent where a kernel reads the MXFP8 weights itself: the fused streaming
 // kernel up to 64 tokens, the fp8 tiled kernel above, both with an MXFP8 table; with fp32 table
 // scales only the former).
-size_t forward_staging_tiled(const engram_layout* l, int64_t M) {
-  if (!use_tiled(l, M, true)) return 0;
+size_t forward_staging_tiled(const engram_layout* l, int64_t M, int cus) {
+  if (!use_tiled_fused(l, M, cus)) return 0;
   const size_t b = forward_tiled_mx(l, M) ? tiled_staging_bytes_mx(M, int(K_of(l)), int(N_of(l)))
                                           : tiled_staging_bytes(M, int(K_of(l)), int(N_of(l)));
   return (b + 255) & ~size_t(255);
@@ -120,7 +134,7 @@ size_t forward_staging_wkv(const engram_layout* l, int64_t M, int cus) {
              : 0;
 }
 size_t forward_staging(const engram_layout* l, int64_t M, int cus) {
-  const size_t b = forward_staging_tiled(l, M) + forward_staging_wkv(l, M, cus);
+  const size_t b = forward_staging_tiled(l, M, cus) + forward_staging_wkv(l, M, cus);
   return b > 0 ? b + 256 : 0;
 }
 
@@ -448,14 +462,14 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   const uint16_t* wkv = static_cast<const uint16_t*>(wkv_arg);
   if (wkv_mxfp8(l) && !native8 && !tiled8) {
     // MXFP8 weights for a bf16 schedule: expand them behind the tiled part of the staging area
-    uint16_t* copy = reinterpret_cast<uint16_t*>(stg_start + forward_staging_tiled(l, M));
+    uint16_t* copy = reinterpret_cast<uint16_t*>(stg_start + forward_staging_tiled(l, M, di.cus));
     const uint8_t* codes = static_cast<const uint8_t*>(wkv_arg);
     if (launch_expand_mxfp8(codes, codes + size_t(N) * size_t(K_of(l)), N, int(K_of(l)), copy,
                             reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
       return ENGRAM_E_HIP;
     wkv = copy;
   }
-  if (use_tiled(l, M, true)) {
+  if (use_tiled_fused(l, M, di.cus)) {
     TiledArgs a;
     memset(&a, 0, sizeof(a));
     a.wkv = wkv;
@@ -525,9 +539,10 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   a.clamp = l->clamp;
   a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
   a.spin_budget = g_spin_budget.load(std::memory_order_relaxed);
-  return launch_forward_stream(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
-             ? ENGRAM_OK
-             : ENGRAM_E_HIP;
+  const hipError_t e = use_tb2(l, M, di.cus)
+                          ? launch_forward_tb2(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream))
+                          : launch_forward_stream(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP;
 }
 
 engram_status engram_forward_noalloc(const engram_layout* l, const uint16_t* x, const int64_t* hash_ids,

@@ -102,6 +102,9 @@ int stream_grid(int N, int num_cus);
 // Most rows of wkv one workgroup of the weight-streaming schedule owns.
 int stream_rows_per_group(int N, int G);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
+// 65..128 tokens in one pass over bf16 weights (workspace as the streaming kernel's, two blocks)
+bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int num_cus);
+hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 // Whether the weight-streaming kernels take MXFP8 weights for this shape (the wide K loop:
 // K / 4 a multiple of 128, 1..7 row blocks per workgroup; fused: head_dim a multiple of 128 and
 // scale_block of 32).  The fused kernel takes them for one token block (M <= 64).

@@ -55,6 +55,8 @@
 // barriers; counters, slots and tiles are reset by their last user, so a call leaves them zero.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -1244,6 +1246,222 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------ two token blocks
+// The fused forward of 65..128 tokens in one pass over the weights, the one-block kernel's
+// layout kept (one workgroup per CU over its row blocks, four waves each on a K quarter, every
+// wave streaming its own weight rows, no barrier in the K loop) with two 64-token blocks per
+// wave: chunks of 64 features, so that a wave's weight slots (NRB x 2 KB) and its tokens' codes
+// (128 tokens x 64 bytes, and their scales) fit the LDS together.  Per chunk a wave issues the
+// next chunk's token copies, then each row block's copy for the next chunk right after reading
+// it (24 copies in flight when a block is read, as in the one-block kernel), and multiplies
+// NRB x 2 x 8 MFMAs.  Afterwards each token block goes through the K-partial reduction and the
+// epilogue of the several-token-block schedule (value workgroups wait for their gates).
+constexpr int kC2 = 64;                 // features per chunk
+constexpr int kW2Slot = 16 * kC2 * 2;   // LDS slot of one row block (2 KB)
+constexpr int kTok2 = 2 * kTB * kC2 + 4 * 256;  // per wave: 128 tokens' codes, 2 x 128 scales
+__host__ __device__ constexpr int tb2_lds(int nrb, int n_cols) {
+  return (4 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 8) > nrb * 16384
+             ? 4 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 8
+             : nrb * 16384;
+}
+template <int NRB>
+constexpr int kT2Copies = 2 * NRB + 12;  // per wave and chunk: weights, codes, scales
+
+// Weight copy h of row block i: rows 8 h .. 8 h + 7, lane l at 16 l: row 8 h + l / 8, position
+// l % 8, holding the 16-byte part (l % 8) ^ (row & 7) of the row's 128 chunk bytes.  Not live
+// (after the last chunk): rows 0..15 at feature 0, a cache-resident 2 KB.
+__device__ __forceinline__ void tb2_copy_w(char* slot, const StreamArgs& a, const Rows& rw, int i, int f, bool live,
+                                           int lane) {
+  const int rbase = live ? rw.r0 + 16 * i : 0;
+  const int rlast = live ? rw.r1 - 1 : 15;
+  const size_t fbase = live ? size_t(f) : 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rr = 8 * h + (lane >> 3);
+    const int r = rbase + rr;
+    const size_t row = size_t(r < rlast ? r : rlast);
+    __builtin_amdgcn_global_load_lds((const void*)(a.wkv + row * a.K + fbase + 8 * ((lane & 7) ^ (rr & 7))),
+                                     (lds_ptr_t)(slot + h * 1024), 16, 0, 2);
+  }
+}
+// This wave's 128 tokens at features f .. f + 63 (inside one column): copy k holds tokens
+// 16 k .. 16 k + 15, four lanes each, part p of token t at position p ^ ((t >> 2) & 3); then the
+// scales of features f .. f + 31 and f + 32 .. f + 63 of every token (the fp32 scale, or the
+// aligned dword that holds the E8M0 byte) at 8192 + 512 s + 4 t.
+__device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, const int64_t* s_ids, int f, int lane) {
+  const int j = f / a.head_dim;
+  const int cc = f - j * a.head_dim;
+  int64_t rid[10];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rid[k] = s_ids[(16 * k + (lane >> 2)) * a.n_cols + j];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) rid[8 + k] = s_ids[(64 * k + lane) * a.n_cols + j];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int t = 16 * k + (lane >> 2);
+    const int64_t rr = rid[k] >= 0 ? rid[k] : 0;
+    __builtin_amdgcn_global_load_lds((const void*)(a.table + rr * a.head_dim + cc + 16 * ((lane & 3) ^ ((t >> 2) & 3))),
+                                     (lds_ptr_t)(tbuf + k * 1024), 16, 0, 0);
+  }
+  const int nb = a.head_dim / a.scale_block;
+  const int sbyte = a.scale_e8m0 ? 1 : 4;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int64_t rr = rid[8 + k] >= 0 ? rid[8 + k] : 0;
+      const size_t off = size_t(rr * nb + (cc + 32 * s) / a.scale_block) * sbyte;
+      __builtin_amdgcn_global_load_lds((const void*)(static_cast<const char*>(a.scales) + (off & ~size_t(3))),
+                                       (lds_ptr_t)(tbuf + 8192 + s * 512 + k * 256), 4, 0, 0);
+    }
+}
+
+template <int NRB, bool E8>
+__device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamArgs& a, const int64_t* s_ids,
+                                         char* smem, const Rows& rw, int lane, int wv) {
+  const int q0 = wv * (a.K >> 2);
+  const int nch = (a.K >> 2) / kC2;
+  const int rot = int((5u * blockIdx.x) % uint32_t(nch));
+  auto feat = [&](int c) { return q0 + kC2 * ((c + rot) % nch); };
+  char* my_slots = smem + wv * NRB * kW2Slot;
+  char* my_tok = smem + 4 * NRB * kW2Slot + wv * kTok2;
+  tb2_copy_tok(my_tok, a, s_ids, feat(0), lane);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+    tb2_copy_w(my_slots + i * kW2Slot, a, rw, i, feat(0), true, lane);
+    asm volatile("" ::: "memory");
+  }
+  constexpr int kInFlight = 2 * (NRB - 1) + 12;
+  static_assert(kInFlight <= 63, "vmcnt range");
+  const int wr = lane & 15;
+  for (int c = 0; c < nch; ++c) {
+    const bool live = c + 1 < nch;
+    const int fc = feat(c);
+    const int fn = feat(live ? c + 1 : c);
+    const int j = fc / a.head_dim;
+    const int cc = fc - j * a.head_dim;
+    // the token copies of chunk c have landed once only its weight copies remain
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NRB) : "memory");
+    // every token-side read of the chunk first (one wait), then the dequantisation
+    u32x2 code[2][2][4];
+    uint32_t sw[2][2][4];
+    int64_t id[2][4];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int tok = 64 * b + 16 * t + (lane & 15);
+        id[b][t] = s_ids[tok * a.n_cols + j];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const int p = 2 * s + (lane >> 5);
+          code[s][b][t] = *reinterpret_cast<const u32x2*>(my_tok + tok * 64 + 16 * (p ^ ((tok >> 2) & 3)) +
+                                                          8 * ((lane >> 4) & 1));
+          sw[s][b][t] = *reinterpret_cast<const uint32_t*>(my_tok + 8192 + s * 512 + 4 * tok);
+        }
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
+    u32x4 bt[2][2][4];  // [step][token block][sub-block]
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t shift8 = uint32_t(((cc + 32 * s) / a.scale_block) & 3) * 8u;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float sc = E8 ? e8m0_to_f32((sw[s][b][t] >> shift8) & 0xFFu) : __uint_as_float(sw[s][b][t]);
+          bt[s][b][t] = masked(dequant8(code[s][b][t], sc), id[b][t] >= 0 ? 0xFFFFFFFFu : 0u);
+        }
+    }
+    tb2_copy_tok(my_tok, a, s_ids, fn, lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      char* slot = my_slots + i * kW2Slot;
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
+      u32x4 wf[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        wf[s] = *reinterpret_cast<const u32x4*>(slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      tb2_copy_w(slot, a, rw, i, fn, live, lane);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) acc[b][i][t] = mfma16x16x32(wf[s], bt[s][b][t], acc[b][i][t]);
+      asm volatile("" ::: "memory");
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int NRB>
+__device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + 4 * NRB * kW2Slot + 4 * kTok2);
+  {
+    // hash ids of both token blocks, checked once: -1 marks a row that reads as zeros
+    const int n_ids = 2 * kTB * a.n_cols;
+    const int64_t n_valid = a.M * a.n_cols;
+    for (int base = 0; base < n_ids; base += 8 * 256) {
+      int64_t v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = base + q * 256 + tid;
+        v[q] = i < n_valid ? a.hash_ids[i] : -1;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int i = base + q * 256 + tid;
+        int64_t r = v[q];
+        if (i < n_valid && (r < 0 || r >= a.n_rows)) {
+          if (w == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+          r = -1;
+        }
+        if (i < n_ids) s_ids[i] = r;
+      }
+    }
+    __syncthreads();
+  }
+  f32x4 acc[2][NRB][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[b][i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (a.scale_e8m0) tb2_loop<NRB, true>(acc, a, s_ids, smem, rw, lane, wv);
+  else tb2_loop<NRB, false>(acc, a, s_ids, smem, rw, lane, wv);
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    KeyPre<NRB> kp;
+    prefetch_key<NRB>(kp, a, rw, int64_t(b) * kTB, tid);
+    f32x4 red[NRB];
+    reduce_k<NRB, true>(red, acc[b], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
+    epilogue<NRB, true, true, false>(a, red, kp, sh, b, w, rw, tid, smem);
+    __syncthreads();
+  }
+}
+
+template <int NLO, int NHI>
+__global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
+  static_assert(stage_bytes(NHI) <= NHI * 16384, "output staging exceeds the reduction buffer");
+  const int G = a.G, w = blockIdx.x;
+  const Rows rw = rows_of(w, a.N, G);
+  if constexpr (NLO == NHI) {
+    tb2_blocks<NLO>(a, smem, sh, w, rw);
+  } else {
+    if (rw.nblk == NLO) tb2_blocks<NLO>(a, smem, sh, w, rw);
+    else tb2_blocks<NHI>(a, smem, sh, w, rw);
+  }
+}
+
 template <bool FUSED, int NRB>
 void* pick_narrow(int nstep) {
   if (nstep % 3 == 0) return reinterpret_cast<void*>(&k_stream_narrow<NRB, 3, FUSED>);
@@ -1324,6 +1542,31 @@ bool stream_mx_ok(const StreamArgs& a, int G) {
          stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, true, true, true, true) <= 163840;
 }
 
+// Dynamic LDS above the default 64 KB: raise the kernel's limit once (a kernel's need is fixed
+// by its shape class, and the largest value set so far stays in force).
+hipError_t allow_lds(void* fn, size_t lds) {
+  if (lds > 163840) return hipErrorInvalidValue;
+  if (lds <= 65536) return hipSuccess;
+  static std::mutex mu;
+  static void* raised[64];
+  static int raised_lds[64];
+  static int n_raised = 0;
+  std::lock_guard<std::mutex> lock(mu);
+  int k = 0;
+  while (k < n_raised && raised[k] != fn) ++k;
+  if (k == n_raised || raised_lds[k] < int(lds)) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    if (e != hipSuccess) return e;
+    if (k == n_raised && n_raised < 64) {
+      raised[n_raised] = fn;
+      raised_lds[n_raised++] = int(lds);
+    } else if (k < n_raised) {
+      raised_lds[k] = int(lds);
+    }
+  }
+  return hipSuccess;
+}
+
 template <bool FUSED>
 hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   void* fn = nullptr;
@@ -1359,27 +1602,29 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   }
   void* params[] = {&arg};
   const size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
-  if (lds > 163840) return hipErrorInvalidValue;
-  if (lds > 65536) {
-    // above the default limit: raise it once per kernel (a kernel's need is fixed by its shape
-    // class, and the largest value set so far stays in force)
-    static void* raised[64];
-    static int raised_lds[64];
-    static int n_raised = 0;
-    int k = 0;
-    while (k < n_raised && raised[k] != fn) ++k;
-    if (k == n_raised || raised_lds[k] < int(lds)) {
-      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-      if (e != hipSuccess) return e;
-      if (k == n_raised && n_raised < 64) {
-        raised[n_raised] = fn;
-        raised_lds[n_raised++] = int(lds);
-      } else if (k < n_raised) {
-        raised_lds[k] = int(lds);
-      }
-    }
-  }
+  const hipError_t e = allow_lds(fn, lds);
+  if (e != hipSuccess) return e;
   return hipLaunchKernel(fn, dim3(G + arg.n_apply), dim3(256), params, lds, stream);
+}
+
+template <int NLO>
+void* pick_tb2_n(bool same) {
+  return same ? reinterpret_cast<void*>(&k_stream_tb2<NLO, NLO>)
+              : reinterpret_cast<void*>(&k_stream_tb2<NLO, (NLO < 7 ? NLO + 1 : 7)>);
+}
+void* pick_tb2(int nlo, int nhi) {
+  const bool same = nlo == nhi;
+  if (!same && (nhi != nlo + 1 || nhi > 7)) return nullptr;
+  switch (nlo) {
+    case 1: return pick_tb2_n<1>(same);
+    case 2: return pick_tb2_n<2>(same);
+    case 3: return pick_tb2_n<3>(same);
+    case 4: return pick_tb2_n<4>(same);
+    case 5: return pick_tb2_n<5>(same);
+    case 6: return pick_tb2_n<6>(same);
+    case 7: return same ? pick_tb2_n<7>(true) : nullptr;
+    default: return nullptr;
+  }
 }
 
 
@@ -1426,6 +1671,34 @@ size_t stream_workspace_bytes(int64_t M, int N, int dim, int grid) {
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
   return launch_stream_impl<false>(a, stream_grid(a.N, num_cus), stream);
+}
+
+// The two-token-block kernel (65..128 tokens): bf16 weights; 64-feature chunks inside one
+// table column (head_dim a multiple of 64) and 32-feature groups inside one scale block; one or
+// two row-block counts per workgroup, at most seven; its LDS within the CU's.
+bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int num_cus) {
+  const int G = stream_grid(N, num_cus);
+  const int lo = min_blocks(N, G), hi = max_blocks(N, G);
+  return (K / 4) % kC2 == 0 && head_dim % kC2 == 0 && scale_block % 32 == 0 && lo >= 1 && hi <= 7 &&
+         hi <= lo + 1 && tb2_lds(hi, n_cols) <= 163840;
+}
+
+hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
+  if (a.M <= kTB || a.M > 2 * kTB || a.w8 ||
+      !stream_tb2_ok(a.K, a.N, a.n_cols, a.head_dim, a.scale_block, num_cus))
+    return hipErrorInvalidValue;
+  const int G = stream_grid(a.N, num_cus);
+  a.ws_hdr = static_cast<uint32_t*>(workspace);
+  a.tb_stride = stream_tb_stride(G);
+  a.G = G;
+  a.n_apply = 0;
+  void* fn = pick_tb2(min_blocks(a.N, G), max_blocks(a.N, G));
+  if (fn == nullptr) return hipErrorInvalidValue;
+  const size_t lds = size_t(tb2_lds(max_blocks(a.N, G), a.n_cols));
+  const hipError_t e = allow_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  void* params[] = {&a};
+  return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {

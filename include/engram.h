@@ -172,8 +172,8 @@ engram_status engram_forward(const engram_layout* layout, const uint16_t* x,
  * tight serving loops, harnesses that forbid hipMalloc): the same computation and results, with
  * no workspace argument.  The workspace is a fixed array of the library, `scratch`, 4 MiB per GPU
  * (a static device array: each GPU the library runs on holds its own copy until the process
- * ends); that covers calls of up to 64 tokens at the model's layout (the fused weight-streaming
- * schedule); a call that needs more returns ENGRAM_E_WORKSPACE before anything is enqueued.
+ * ends); that covers calls of up to 128 tokens at the model's layout (the fused weight-streaming
+ * schedules); a call that needs more returns ENGRAM_E_WORKSPACE before anything is enqueued.
  * Nothing is allocated, here or in the kernels.  Each call first enqueues a one-workgroup guard
  * kernel: on a GPU's first call it zero-fills the scratch; later it reads the scratch's time-out
  * word and, if an earlier call's wait timed out (its outputs were wrong), zero-fills the scratch

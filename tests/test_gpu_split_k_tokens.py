@@ -3,9 +3,10 @@ tile is computed by two workgroups, each over half of K (the second adds the fir
 partial tile); with more tiles, the tiles of a last, partial round of the grid (tiles mod the
 CU count, when at most 128) are split the same way.
 
-The decode layout at 65..256 tokens: 256 (one full tile row), 193 (a last 64-token block of one
-token), 65 and 128; skewed ids, closed tokens, outlier streams, out-of-range ids, in-place
-output.  Tiny dims at 13,300 tokens: 260 tiles, the last 4 (value tiles of the last four token
+The decode layout at 129..256 tokens: 256 (one full tile row), 193 (a last 64-token block of one
+token), 150; skewed ids, closed tokens, outlier streams, out-of-range ids, in-place output.  The
+same checks at 65 and 128 tokens, which the two-token-block weight-streaming kernel takes on this
+layout.  Tiny dims at 13,300 tokens: 260 tiles, the last 4 (value tiles of the last four token
 blocks, the ragged one among them) split, every token checked.  Every result is also checked
 for run-to-run identity, control words left zero and no timed-out wait.
 """
@@ -56,7 +57,7 @@ def run_twice(w, d, err=None):
 @pytest.mark.parametrize("B,T,seed", [(4, 64, 501), (1, 193, 502), (1, 65, 503), (2, 64, 504)])
 def test_forward_split_k_sampled(B, T, seed):
     w = variant(B, T, seed)
-    say(f"[gpu] forward {w.name}: {w.M} tokens, split-K tiles")
+    say(f"[gpu] forward {w.name}: {w.M} tokens, " + ("split-K tiles" if w.M > 128 else "two token blocks"))
     d = synth.device_inputs(w)
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = run_twice(w, d, err=err)

@@ -2,8 +2,10 @@
 workspace, for callers that cannot allocate (needs an MI355X).
 
 It must give engram_forward's output bit for bit (the same kernels): two calls in a row, the
-second on fewer tokens, at the model's layout (weight-streaming schedule) and at tiny dims; a
-call whose workspace would exceed the scratch is refused before anything is enqueued."""
+second on fewer tokens, at the model's layout (the one-token-block weight-streaming schedule, and
+the two-token-block one at 100 then 65 tokens) and at tiny dims; a call whose workspace would
+exceed the scratch (200 tokens at the model's layout, tiled schedule) is refused before anything
+is enqueued."""
 import numpy as np
 import pytest
 
@@ -15,6 +17,7 @@ from gpu_common import eg, forward, layout, say  # noqa: E402
 
 W = synth.workloads()
 DECODE, TINY = W["decode_b64"], W["tiny"]
+DECODE_B100 = synth.small_variant(DECODE, name="decode_dims_b100", B=100, T=1)
 
 
 def _slice(d, n):
@@ -38,7 +41,8 @@ def _noalloc(w, d, err=None):
                                      err_count=err)
 
 
-@pytest.mark.parametrize("w,n2", [(DECODE, 17), (TINY, 5)], ids=["decode_b64_then_17", "tiny_t16_then_5"])
+@pytest.mark.parametrize("w,n2", [(DECODE, 17), (DECODE_B100, 65), (TINY, 5)],
+                         ids=["decode_b64_then_17", "decode_b100_then_65", "tiny_t16_then_5"])
 def test_noalloc_equals_forward_two_calls_second_smaller(w, n2):
     say(f"[gpu] no-allocation forward: {w.name} ({w.M} tokens), then {n2} tokens")
     d = synth.device_inputs(w)
@@ -54,8 +58,8 @@ def test_noalloc_equals_forward_two_calls_second_smaller(w, n2):
 
 
 def test_noalloc_refuses_calls_beyond_its_scratch():
-    say("[gpu] no-allocation forward refuses 100 tokens at the model's layout (tiled schedule)")
-    w = synth.small_variant(DECODE, name="decode_dims_b100", B=100, T=1)
+    say("[gpu] no-allocation forward refuses 200 tokens at the model's layout (tiled schedule)")
+    w = synth.small_variant(DECODE, name="decode_dims_b200", B=200, T=1)
     d = synth.device_inputs(w)
     out = torch.full_like(d["x"], 7)
     with pytest.raises(eg.EngramError) as e:
