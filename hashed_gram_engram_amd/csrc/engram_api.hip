@@ -68,10 +68,11 @@ bool use_tiled(const engram_layout* l, int64_t M, bool fused) {
 bool wkv_mxfp8(const engram_layout* l) { return l->wkv_format == ENGRAM_WKV_MXFP8; }
 
 // The layout admits the two-token-block weight-streaming kernel (bf16 weights, workgroups
-// spanning at most two streams), which then takes every forward of 65..128 tokens.
+// spanning at most two streams, table row ids that fit 31 bits), which then takes every
+// forward of 65..128 tokens.
 bool tb2_layout(const engram_layout* l, int cus) {
   const int N = int(N_of(l));
-  return !wkv_mxfp8(l) && stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim &&
+  return !wkv_mxfp8(l) && l->n_rows <= 0x7FFFFFFF && stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim &&
          stream_tb2_ok(int(K_of(l)), N, l->n_cols, l->head_dim, l->scale_block, cus);
 }
 bool use_tb2(const engram_layout* l, int64_t M, int cus) { return M > 64 && M <= 128 && tb2_layout(l, cus); }

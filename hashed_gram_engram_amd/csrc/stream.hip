@@ -56,6 +56,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -624,7 +625,13 @@ __device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4]
 struct Shared {
   float red[4][kTB][3];
   int last[2];
+  int last2[2][2];  // the two-token-block kernel: last-arriver marks per (token block, stream slot)
 };
+
+// Parts of the fused epilogue, so that a kernel with two token blocks can interleave them:
+// store the key columns' partial sums; count the workgroup in (last-arriver marks); the last
+// arrivers' gates; the value columns.
+constexpr int kPhStore = 1, kPhCount = 2, kPhGates = 4, kPhValue = 8, kPhAll = 15;
 
 // Inputs of the key columns' partial sums, loaded before the K-partial reduction: per row block,
 // the lane's 4 features of x (token 16 wv + lane % 16, its stream) and the fp32 products q * k of
@@ -715,11 +722,12 @@ __device__ __forceinline__ uint32_t ws_off(const StreamArgs& a, const uint32_t* 
 __host__ __device__ constexpr int stage_row_bytes(int nrb) { return 32 * nrb + 16; }
 __host__ __device__ constexpr int stage_bytes(int nrb) { return 4 * 64 * stage_row_bytes(nrb) + 256; }
 
-template <int NRB, bool FUSED, bool STAGE = false, bool APPLY = false>
+template <int NRB, bool FUSED, bool STAGE = false, bool APPLY = false, int PH = kPhAll>
 __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], const KeyPre<NRB>& kp, Shared& sh,
                                          int64_t tb, int w,
-                                         const Rows& rw, int tid, char* stage = nullptr) {
+                                         const Rows& rw, int tid, char* stage = nullptr, int* lastf = nullptr) {
   const int lane = tid & 63, wv = tid >> 6;
+  int* const lf = lastf != nullptr ? lastf : sh.last;
   const int G = a.G;
   const int Q = a.N >> 2;
   const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
@@ -782,32 +790,36 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
         pk[sl] += __shfl_xor(pk[sl], 16, 64); pk[sl] += __shfl_xor(pk[sl], 32, 64);
         pd[sl] += __shfl_xor(pd[sl], 16, 64); pd[sl] += __shfl_xor(pd[sl], 32, 64);
       }
-      if (lane < 16) {
+      if constexpr ((PH & kPhStore) != 0) {
+        if (lane < 16) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
-            store_coherent4(wsr, partial_off(a, tb, w, sl) + tok * 16, f32x4{pa[sl], pk[sl], pd[sl], 0.f});
+          for (int sl = 0; sl < 2; ++sl) {
+            if (seg_lo + sl <= seg_hi && seg_lo + sl < 4) {
+              store_coherent4(wsr, partial_off(a, tb, w, sl) + tok * 16, f32x4{pa[sl], pk[sl], pd[sl], 0.f});
+            }
           }
         }
       }
-      drain_memory_ops();
-      __syncthreads();
-      if (tid == 0) {
+      if constexpr ((PH & kPhCount) != 0) {
+        drain_memory_ops();
+        __syncthreads();
+        if (tid == 0) {
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const int s = seg_lo + sl;
-          sh.last[sl] = 0;
-          if (s <= seg_hi && s < 4) {
-            const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
-            const uint32_t old = atomic_add_relaxed(counter_of(a, tb, s), 1u);
-            sh.last[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
+          for (int sl = 0; sl < 2; ++sl) {
+            const int s = seg_lo + sl;
+            lf[sl] = 0;
+            if (s <= seg_hi && s < 4) {
+              const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
+              const uint32_t old = atomic_add_relaxed(counter_of(a, tb, s), 1u);
+              lf[sl] = (old == uint32_t(wl - wf)) ? 1 : 0;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
 #pragma unroll 1
       for (int sl = 0; sl < 2; ++sl) {
-        if (sh.last[sl]) {
+        if ((PH & kPhGates) != 0 && lf[sl]) {
           __syncthreads();  // sh.red may still be read for the other stream
           // every contributor has posted: sum the partials in workgroup order
           const int s = seg_lo + sl;
@@ -887,6 +899,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
       }
     }
 
+    if constexpr ((PH & kPhValue) == 0) return;
     // ---- value columns, apply workgroups present: the bf16 values into this workgroup's tile
     if constexpr (APPLY) {
       if (seg_hi == 4) {
@@ -1259,9 +1272,11 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
 constexpr int kC2 = 64;                 // features per chunk
 constexpr int kW2Slot = 16 * kC2 * 2;   // LDS slot of one row block (2 KB)
 constexpr int kTok2 = 2 * kTB * kC2 + 4 * 256;  // per wave: 128 tokens' codes, 2 x 128 scales
+// LDS: two weight stages per wave (NRB slots each), the waves' token buffers, then the staged
+// 32-bit hash ids of both token blocks; after the loop the K-partial reduction's NRB x 16 KB.
 __host__ __device__ constexpr int tb2_lds(int nrb, int n_cols) {
-  return (4 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 8) > nrb * 16384
-             ? 4 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 8
+  return (8 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 4) > nrb * 16384
+             ? 8 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 4
              : nrb * 16384;
 }
 template <int NRB>
@@ -1288,10 +1303,10 @@ __device__ __forceinline__ void tb2_copy_w(char* slot, const StreamArgs& a, cons
 // 16 k .. 16 k + 15, four lanes each, part p of token t at position p ^ ((t >> 2) & 3); then the
 // scales of features f .. f + 31 and f + 32 .. f + 63 of every token (the fp32 scale, or the
 // aligned dword that holds the E8M0 byte) at 8192 + 512 s + 4 t.
-__device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, const int64_t* s_ids, int f, int lane) {
+__device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, const int32_t* s_ids, int f, int lane) {
   const int j = f / a.head_dim;
   const int cc = f - j * a.head_dim;
-  int64_t rid[10];
+  int rid[10];
 #pragma unroll
   for (int k = 0; k < 8; ++k) rid[k] = s_ids[(16 * k + (lane >> 2)) * a.n_cols + j];
 #pragma unroll
@@ -1316,76 +1331,109 @@ __device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, co
     }
 }
 
+// One chunk's token operands as the lane reads them from its wave's buffer: codes [step][token
+// block][sub-block], the scale words, and an all-ones / zero mask per token (ids checked).
+struct Tok2Raw {
+  u32x2 code[2][2][4];
+  uint32_t sw[2][2][4];
+  uint32_t keep[2][4];
+};
+
+__device__ __forceinline__ void tb2_read_tok(Tok2Raw& r, const char* my_tok, const int32_t* s_ids, int j,
+                                             int n_cols, int lane) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int tok = 64 * b + 16 * t + (lane & 15);
+      r.keep[b][t] = s_ids[tok * n_cols + j] >= 0 ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int p = 2 * s + (lane >> 5);
+        r.code[s][b][t] = *reinterpret_cast<const u32x2*>(my_tok + tok * 64 + 16 * (p ^ ((tok >> 2) & 3)) +
+                                                          8 * ((lane >> 4) & 1));
+        r.sw[s][b][t] = *reinterpret_cast<const uint32_t*>(my_tok + 8192 + s * 512 + 4 * tok);
+      }
+    }
+}
+
+// Operand g (step g / 8, token block (g / 4) % 2, sub-block g % 4) of a chunk whose features
+// start at cc inside their column.
+template <bool E8>
+__device__ __forceinline__ void tb2_dequant(u32x4 (&bt)[2][2][4], const Tok2Raw& r, int g, int cc, int scale_block) {
+  const int s = g >> 3, b = (g >> 2) & 1, t = g & 3;
+  const uint32_t shift8 = uint32_t(((cc + 32 * s) / scale_block) & 3) * 8u;
+  const float sc = E8 ? e8m0_to_f32((r.sw[s][b][t] >> shift8) & 0xFFu) : __uint_as_float(r.sw[s][b][t]);
+  bt[s][b][t] = masked(dequant8(r.code[s][b][t], sc), r.keep[b][t]);
+}
+
+// The K loop.  A wave's weight slots form two stages (NRB x 4 KB of its weights in flight, as
+// in the one-block kernel): the slot row block i of chunk c leaves is refilled with chunk c +
+// 2's rows right after it is read.  Per chunk the wave first reads and dequantises its token
+// operands (which frees its token buffer for chunk c + 1's copies), then multiplies row block
+// by row block.
 template <int NRB, bool E8>
-__device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamArgs& a, const int64_t* s_ids,
+__device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamArgs& a, const int32_t* s_ids,
                                          char* smem, const Rows& rw, int lane, int wv) {
   const int q0 = wv * (a.K >> 2);
   const int nch = (a.K >> 2) / kC2;
   const int rot = int((5u * blockIdx.x) % uint32_t(nch));
   auto feat = [&](int c) { return q0 + kC2 * ((c + rot) % nch); };
-  char* my_slots = smem + wv * NRB * kW2Slot;
-  char* my_tok = smem + 4 * NRB * kW2Slot + wv * kTok2;
-  tb2_copy_tok(my_tok, a, s_ids, feat(0), lane);
-  asm volatile("" ::: "memory");
+  char* my_slots = smem + wv * 2 * NRB * kW2Slot;  // stage k: slots k NRB .. k NRB + NRB - 1
+  char* my_tok = smem + 8 * NRB * kW2Slot + wv * kTok2;
+  // copy order: chunk 0's weights, its tokens, chunk 1's weights; then each chunk c issues chunk
+  // c + 1's tokens and one weight copy per row block (chunk c + 2's).  A chunk's tokens are then
+  // always followed by exactly one chunk's weight copies (2 NRB) until they are read, and a row
+  // block's copy by the rest of its chunk's, two chunks' tokens, one chunk's weights and as many
+  // weight copies as blocks already read: 4 NRB + 22 copies.
+  const bool two = nch > 1;
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
     tb2_copy_w(my_slots + i * kW2Slot, a, rw, i, feat(0), true, lane);
     asm volatile("" ::: "memory");
   }
-  constexpr int kInFlight = 2 * (NRB - 1) + 12;
+  tb2_copy_tok(my_tok, a, s_ids, feat(0), lane);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+    tb2_copy_w(my_slots + (NRB + i) * kW2Slot, a, rw, i, feat(two ? 1 : 0), two, lane);
+    asm volatile("" ::: "memory");
+  }
+  constexpr int kInFlight = 4 * NRB + 22;
   static_assert(kInFlight <= 63, "vmcnt range");
   const int wr = lane & 15;
-  for (int c = 0; c < nch; ++c) {
-    const bool live = c + 1 < nch;
+  // one chunk; the stage is a template argument so that the two stages' slot addresses are
+  // constants of their own copy of the body
+  auto chunk = [&](int c, auto stage_tag) {
+    constexpr int st = decltype(stage_tag)::value;
     const int fc = feat(c);
-    const int fn = feat(live ? c + 1 : c);
-    const int j = fc / a.head_dim;
-    const int cc = fc - j * a.head_dim;
-    // the token copies of chunk c have landed once only its weight copies remain
+    const int fn = feat(c + 1 < nch ? c + 1 : c);
+    const bool live2 = c + 2 < nch;
+    const int fnn = feat(live2 ? c + 2 : c);
+    char* stage = my_slots + st * NRB * kW2Slot;
+    // chunk c's token copies have landed once only chunk c + 1's weight copies remain
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NRB) : "memory");
-    // every token-side read of the chunk first (one wait), then the dequantisation
-    u32x2 code[2][2][4];
-    uint32_t sw[2][2][4];
-    int64_t id[2][4];
+    u32x4 bt[2][2][4];
+    {
+      Tok2Raw raw;
+      tb2_read_tok(raw, my_tok, s_ids, fc / a.head_dim, a.n_cols, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
+      const int cc = fc % a.head_dim;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int tok = 64 * b + 16 * t + (lane & 15);
-        id[b][t] = s_ids[tok * a.n_cols + j];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int p = 2 * s + (lane >> 5);
-          code[s][b][t] = *reinterpret_cast<const u32x2*>(my_tok + tok * 64 + 16 * (p ^ ((tok >> 2) & 3)) +
-                                                          8 * ((lane >> 4) & 1));
-          sw[s][b][t] = *reinterpret_cast<const uint32_t*>(my_tok + 8192 + s * 512 + 4 * tok);
-        }
-      }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
-    u32x4 bt[2][2][4];  // [step][token block][sub-block]
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t shift8 = uint32_t(((cc + 32 * s) / a.scale_block) & 3) * 8u;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const float sc = E8 ? e8m0_to_f32((sw[s][b][t] >> shift8) & 0xFFu) : __uint_as_float(sw[s][b][t]);
-          bt[s][b][t] = masked(dequant8(code[s][b][t], sc), id[b][t] >= 0 ? 0xFFFFFFFFu : 0u);
-        }
+      for (int g = 0; g < 16; ++g) tb2_dequant<E8>(bt, raw, g, cc, a.scale_block);
     }
     tb2_copy_tok(my_tok, a, s_ids, fn, lane);
     asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
-      char* slot = my_slots + i * kW2Slot;
+      char* slot = stage + i * kW2Slot;
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
       u32x4 wf[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         wf[s] = *reinterpret_cast<const u32x4*>(slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      tb2_copy_w(slot, a, rw, i, fn, live, lane);
+      tb2_copy_w(slot, a, rw, i, fnn, live2, lane);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -1394,6 +1442,10 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
           for (int t = 0; t < 4; ++t) acc[b][i][t] = mfma16x16x32(wf[s], bt[s][b][t], acc[b][i][t]);
       asm volatile("" ::: "memory");
     }
+  };
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, std::integral_constant<int, 0>{});
+    if (c + 1 < nch) chunk(c + 1, std::integral_constant<int, 1>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
@@ -1401,9 +1453,10 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
 template <int NRB>
 __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + 4 * NRB * kW2Slot + 4 * kTok2);
+  int32_t* const s_ids = reinterpret_cast<int32_t*>(smem + 8 * NRB * kW2Slot + 4 * kTok2);
   {
-    // hash ids of both token blocks, checked once: -1 marks a row that reads as zeros
+    // hash ids of both token blocks, checked once (n_rows < 2^31): -1 marks a row that reads as
+    // zeros
     const int n_ids = 2 * kTB * a.n_cols;
     const int64_t n_valid = a.M * a.n_cols;
     for (int base = 0; base < n_ids; base += 8 * 256) {
@@ -1421,7 +1474,7 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
           if (w == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
           r = -1;
         }
-        if (i < n_ids) s_ids[i] = r;
+        if (i < n_ids) s_ids[i] = int32_t(r);
       }
     }
     __syncthreads();
@@ -1436,15 +1489,48 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
   if (a.scale_e8m0) tb2_loop<NRB, true>(acc, a, s_ids, smem, rw, lane, wv);
   else tb2_loop<NRB, false>(acc, a, s_ids, smem, rw, lane, wv);
   __syncthreads();
+  // Both token blocks' K-partial reductions first; then both blocks' key partial sums are
+  // posted and counted in with one drain and one round of atomics before any last arriver
+  // computes gates, so that block 1's gates do not wait behind block 0's hand-off.
+  KeyPre<NRB> kp[2];
+  f32x4 red[2][NRB];
+  prefetch_key<NRB>(kp[0], a, rw, 0, tid);
+  prefetch_key<NRB>(kp[1], a, rw, kTB, tid);
+  reduce_k<NRB, true>(red[0], acc[0], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
+  reduce_k<NRB, true>(red[1], acc[1], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
+  epilogue<NRB, true, true, false, kPhStore>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
+  epilogue<NRB, true, true, false, kPhStore>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
+  {
+    const int seg_lo = rw.r0 / a.dim, seg_hi = (rw.r1 - 1) / a.dim;
+    drain_memory_ops();
+    __syncthreads();
+    if (tid == 0) {
+      const int Q = a.N >> 2, G = a.G;
+      uint32_t old[2][2];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    KeyPre<NRB> kp;
-    prefetch_key<NRB>(kp, a, rw, int64_t(b) * kTB, tid);
-    f32x4 red[NRB];
-    reduce_k<NRB, true>(red, acc[b], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
-    epilogue<NRB, true, true, false>(a, red, kp, sh, b, w, rw, tid, smem);
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int s = seg_lo + sl;
+          old[b][sl] = s <= seg_hi && s < 4 ? atomic_add_relaxed(counter_of(a, b, s), 1u) : 0u;
+        }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int s = seg_lo + sl;
+          const int s3 = s < 4 ? s : 3;
+          const int wf = owner_of_row(s3 * a.dim, Q, G), wl = owner_of_row((s3 + 1) * a.dim - 1, Q, G);
+          sh.last2[b][sl] = s <= seg_hi && s < 4 && old[b][sl] == uint32_t(wl - wf) ? 1 : 0;
+        }
+    }
     __syncthreads();
   }
+  epilogue<NRB, true, true, false, kPhGates>(a, red[0], kp[0], sh, 0, w, rw, tid, smem, sh.last2[0]);
+  epilogue<NRB, true, true, false, kPhGates>(a, red[1], kp[1], sh, 1, w, rw, tid, smem, sh.last2[1]);
+  epilogue<NRB, true, true, false, kPhValue>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
+  __syncthreads();
+  epilogue<NRB, true, true, false, kPhValue>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
 }
 
 template <int NLO, int NHI>
@@ -1684,7 +1770,7 @@ bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int 
 }
 
 hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
-  if (a.M <= kTB || a.M > 2 * kTB || a.w8 ||
+  if (a.M <= kTB || a.M > 2 * kTB || a.w8 || a.n_rows > 0x7FFFFFFF ||
       !stream_tb2_ok(a.K, a.N, a.n_cols, a.head_dim, a.scale_block, num_cus))
     return hipErrorInvalidValue;
   const int G = stream_grid(a.N, num_cus);
