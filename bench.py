@@ -50,7 +50,8 @@ def algorithmic_flops(w) -> int:
     return 2 * w.M * w.N * w.K
 
 
-TILED_MIN_TOKENS = 65  # the whole forward switches from weight streaming to 256 x 256 tiles here
+TILED_MIN_TOKENS = 65  # the whole forward switches from weight streaming to 256 x 256 tiles here,
+TB2_MAX_TOKENS = 128   # except up to here with bf16 weights (the two-token-block streaming kernel)
 
 
 def fp8_mfma(w) -> bool:
@@ -62,6 +63,8 @@ def kernel_of(w):
     """(profile name, sources) of the kernels that engram_forward runs for this workload: the
     fused weight-streaming kernel for small token counts; for large ones the row gather into the
     staging area followed by the fused tiled kernel (timed together: one forward)."""
+    if TILED_MIN_TOKENS <= w.M <= TB2_MAX_TOKENS and w.wkv_format != "mxfp8":
+        return "k_stream_tb2", ("stream.hip", "common.h")
     if w.M >= TILED_MIN_TOKENS:
         return ("k_tiled_mx_fused" if fp8_mfma(w) else "k_tiled_fused"), ("tiled.hip", "gather_gate.hip", "common.h")
     return "k_stream_wide_fused", ("stream.hip", "common.h")
@@ -69,7 +72,8 @@ def kernel_of(w):
 
 KERNEL_LABEL = {"k_tiled_fused": "k_gather_dequant + k_tiled<true> (one forward)",
                 "k_tiled_mx_fused": "k_gather_mx + k_tiled<true, true> (fp8 operands; one forward)",
-                "k_stream_wide_fused": "k_stream_wide<.., true>"}
+                "k_stream_wide_fused": "k_stream_wide<.., true>",
+                "k_stream_tb2": "k_stream_tb2 (two token blocks per pass over wkv)"}
 
 
 def kernel_label(w) -> str:
@@ -227,6 +231,9 @@ def layout_of(eg, w):
                           wkv_format=eg.WKV_MXFP8 if w.wkv_format == "mxfp8" else eg.WKV_BF16)
 
 
+LEAD_IN = 2  # untimed steps in flight when the throughput pass's start event is recorded
+
+
 def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone: bool = False,
             min_warmup_ms: float = WARMUP_MIN_MS) -> dict:
     """Times `steps` steps of the workload (one step: every instance's engram_forward, the second
@@ -234,8 +241,8 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
 
     Two passes of `steps` steps each, events on the stream the kernels run on.  The throughput
     pass records one event before the first step and one after the last, nothing in between
-    (an event recorded between two launches adds its own gap on the GPU); its mean per step is
-    the throughput.  The second pass records a pair around every engram_forward launch: their
+    (an event recorded between two launches adds its own gap on the GPU), with the last warm-up
+    steps still running when the first one is recorded; its mean per step is the throughput.  The second pass records a pair around every engram_forward launch: their
     durations give the roofline's time per launch and the step-time percentiles.  With
     flush_mib, that many MiB are written before each step (cold L2s and Infinity Cache) and the
     throughput is the mean of the second pass's step durations."""
@@ -287,9 +294,15 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
         if n_warm % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
-    # throughput pass: the timed steps back to back, an event on each side of the region
+    # throughput pass: the timed steps back to back, an event on each side of the region.  The
+    # last LEAD_IN warm-up steps are enqueued just before the start event, without waiting for
+    # them: the GPU is then busy while the host enqueues the start event and the timed steps, so
+    # the region holds the steps back to back and not the host's latency to its first launch
+    # after a synchronisation (~30 us, 1.5 us per step at 20 steps).
     wall = None
     if flush is None:
+        for _ in range(LEAD_IN):
+            step()
         t0 = time.perf_counter()
         ev_run[0].record(stream)
         for i in range(steps):
@@ -338,8 +351,9 @@ def measure(eg, w, steps: int, warmup: int, flush_mib: int = 0, with_standalone:
     roof["ms_per_launch"] = round(ms_launch, 5)
     roof["ms_per_launch_events"] = round(ms_launch_events, 5)
     roof["timing"] = ("HIP events on the launches' stream around the timed region of back-to-back "
-                      "launches, divided by the launches (ms_per_launch_events: the mean of event "
-                      "pairs around each launch, which add their own gaps)" if flush is None else
+                      f"launches ({LEAD_IN} untimed steps in flight at its start), divided by the "
+                      "launches (ms_per_launch_events: the mean of event pairs around each launch, "
+                      "which add their own gaps)" if flush is None else
                       "HIP events around each launch, on its stream")
     res = {
         "warmup_steps_run": n_warm,

@@ -477,10 +477,12 @@ def workloads() -> dict:
     decode_fp8 = dataclasses.replace(decode_mx, name="decode_b64_fp8", wkv_format="mxfp8")
     # FP8 weights with the benchmark tables' fp32 scales (the weights are dequantised to bf16)
     decode_w8 = dataclasses.replace(decode, name="decode_b64_w8", wkv_format="mxfp8")
+    # the decode layout at 128 tokens (two 64-token blocks per pass over the weights)
+    decode_b128 = dataclasses.replace(decode, name="decode_b128", B=128, seed=_SEED0 + 7)
     prefill_fp8 = dataclasses.replace(prefill, name="prefill_t8192_fp8", scale_block=32,
                                       scale_format="e8m0", wkv_format="mxfp8")
     return {w.name: w for w in (tiny, decode, prefill, full, two_p, two_d, decode_mx, decode_fp8,
-                                prefill_fp8, decode_w8)}
+                                prefill_fp8, decode_w8, decode_b128)}
 
 
 def get(name: str) -> Workload:
