@@ -628,9 +628,22 @@ struct Shared {
   int last2[2][2];  // the two-token-block kernel: last-arriver marks per (token block, stream slot)
 };
 
-// Parts of the fused epilogue, so that a kernel with two token blocks can interleave them:
-// store the key columns' partial sums; count the workgroup in (last-arriver marks); the last
-// arrivers' gates; the value columns.
+// The gate of token t from the four quarter sums in sh.red[q][t] (|h|^2, |key|^2, h q k key),
+// added in quarter order: sigmoid of the signed square root of the clamped scaled dot product.
+__device__ __forceinline__ float gate_from_quarters(const StreamArgs& a, const Shared& sh, int t) {
+  const float A = ((sh.red[0][t][0] + sh.red[1][t][0]) + sh.red[2][t][0]) + sh.red[3][t][0];
+  const float Kq = ((sh.red[0][t][1] + sh.red[1][t][1]) + sh.red[2][t][1]) + sh.red[3][t][1];
+  const float D = ((sh.red[0][t][2] + sh.red[1][t][2]) + sh.red[2][t][2]) + sh.red[3][t][2];
+  const float fd = float(a.dim);
+  const float rstd = __frsqrt_rn(A / fd + a.eps) * __frsqrt_rn(Kq / fd + a.eps);
+  const float dot = D * rstd * a.inv_sqrt_dim;
+  const float z = copysignf(sqrtf(fmaxf(fabsf(dot), a.clamp)), dot);
+  return 1.0f / (1.0f + expf(-z));
+}
+
+// Parts of the fused epilogue, so that a kernel with two token blocks can interleave them with
+// its own: store the key columns' partial sums; count the workgroup in (last-arriver marks); the
+// last arrivers' gates; the value columns.
 constexpr int kPhStore = 1, kPhCount = 2, kPhGates = 4, kPhValue = 8, kPhAll = 15;
 
 // Inputs of the key columns' partial sums, loaded before the K-partial reduction: per row block,
@@ -725,9 +738,9 @@ __host__ __device__ constexpr int stage_bytes(int nrb) { return 4 * 64 * stage_r
 template <int NRB, bool FUSED, bool STAGE = false, bool APPLY = false, int PH = kPhAll>
 __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB], const KeyPre<NRB>& kp, Shared& sh,
                                          int64_t tb, int w,
-                                         const Rows& rw, int tid, char* stage = nullptr, int* lastf = nullptr) {
+                                         const Rows& rw, int tid, char* stage = nullptr) {
   const int lane = tid & 63, wv = tid >> 6;
-  int* const lf = lastf != nullptr ? lastf : sh.last;
+  int* const lf = sh.last;
   const int G = a.G;
   const int Q = a.N >> 2;
   const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
@@ -853,18 +866,8 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           sh.red[q][t][1] = rk;
           sh.red[q][t][2] = rd;
           __syncthreads();
-          if (q == 0) {
-            const float A = ((sh.red[0][t][0] + sh.red[1][t][0]) + sh.red[2][t][0]) + sh.red[3][t][0];
-            const float Kq = ((sh.red[0][t][1] + sh.red[1][t][1]) + sh.red[2][t][1]) + sh.red[3][t][1];
-            const float D = ((sh.red[0][t][2] + sh.red[1][t][2]) + sh.red[2][t][2]) + sh.red[3][t][2];
-            const float fd = float(a.dim);
-            const float rstd = __frsqrt_rn(A / fd + a.eps) * __frsqrt_rn(Kq / fd + a.eps);
-            const float dot = D * rstd * a.inv_sqrt_dim;
-            const float z = copysignf(sqrtf(fmaxf(fabsf(dot), a.clamp)), dot);
-            const float g = 1.0f / (1.0f + expf(-z));
-            // (closed tokens keep x: the value workgroups apply the mask)
-            sh.red[0][t][0] = m0 + t < a.M ? g : 0.0f;
-          }
+          // (closed tokens keep x: the value workgroups apply the mask)
+          if (q == 0) sh.red[0][t][0] = m0 + t < a.M ? gate_from_quarters(a, sh, t) : 0.0f;
           __syncthreads();
           // this call is done with the counter; hand the 64 gates to every value workgroup in
           // its own slot, sign bit set as the ready mark (gates are >= 0)
@@ -1450,6 +1453,72 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// The last arrivers' part for both token blocks: for each stream slot this workgroup closed in
+// either block, the partial sums of every contributor of both blocks are loaded in one round
+// (in order, as in the one-block epilogue), then each block's gates go to the value
+// workgroups' slots and its counter and partial sums are cleared.
+__device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const Rows& rw, int tid) {
+  const int Q = a.N >> 2, G = a.G;
+  const int seg_lo = rw.r0 / a.dim;
+  const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
+  const int t = tid & 63, q = tid >> 6;
+  const int v0 = owner_of_row(4 * a.dim, Q, G);
+#pragma unroll 1
+  for (int sl = 0; sl < 2; ++sl) {
+    const bool L0 = sh.last2[0][sl] != 0, L1 = sh.last2[1][sl] != 0;
+    if (!L0 && !L1) continue;
+    const int s = seg_lo + sl;
+    const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
+    const int nW = wl - wf + 1;
+    const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
+    const int sl_f = row_begin(wf, Q, G) < s * a.dim ? 1 : 0;
+    auto poff = [&](int b, int w2) { return partial_off(a, b, w2, w2 == wf ? sl_f : 0) + t * 16; };
+    float r[2][3] = {{0.f, 0.f, 0.f}, {0.f, 0.f, 0.f}};
+    for (int base = wb0; base < wb1; base += 16) {
+      f32x4 v[2][16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int w2 = base + k < wb1 ? base + k : wb0;
+        v[0][k] = L0 ? load_coherent4(wsr, poff(0, w2)) : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[1][k] = L1 ? load_coherent4(wsr, poff(1, w2)) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (base + k < wb1) {
+            r[b][0] += v[b][k].x;
+            r[b][1] += v[b][k].y;
+            r[b][2] += v[b][k].z;
+          }
+    }
+#pragma unroll 1
+    for (int b = 0; b < 2; ++b) {
+      if (!(b == 0 ? L0 : L1)) continue;
+      __syncthreads();  // sh.red is free again
+      sh.red[q][t][0] = r[b][0];
+      sh.red[q][t][1] = r[b][1];
+      sh.red[q][t][2] = r[b][2];
+      __syncthreads();
+      if (q == 0) sh.red[0][t][0] = int64_t(b) * kTB + t < a.M ? gate_from_quarters(a, sh, t) : 0.0f;
+      __syncthreads();
+      if (tid == 0) store_relaxed(counter_of(a, b, s), 0u);
+      for (int i = tid; i < (G - v0) * (kTB / 4); i += 256) {
+        const int v = v0 + i / (kTB / 4), t4 = 4 * (i % (kTB / 4));
+        const uint32_t off = uint32_t(reinterpret_cast<char*>(gate_slot(a, b, v, s) + t4) -
+                                      reinterpret_cast<char*>(a.ws_hdr));
+        store_coherent4(wsr, off,
+                        __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
+                                                        __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
+                                                        __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
+                                                        __float_as_uint(sh.red[0][t4 + 3][0]) | 0x80000000u}));
+      }
+      for (int w2 = wb0; w2 < wb1; ++w2) store_coherent4(wsr, poff(b, w2), f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    __syncthreads();
+  }
+}
+
 template <int NRB>
 __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -1489,16 +1558,17 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
   if (a.scale_e8m0) tb2_loop<NRB, true>(acc, a, s_ids, smem, rw, lane, wv);
   else tb2_loop<NRB, false>(acc, a, s_ids, smem, rw, lane, wv);
   __syncthreads();
-  // Both token blocks' K-partial reductions first; then both blocks' key partial sums are
-  // posted and counted in with one drain and one round of atomics before any last arriver
-  // computes gates, so that block 1's gates do not wait behind block 0's hand-off.
+  // Both token blocks' K-partial reductions and key partial sums first (block 0's stores in
+  // flight under block 1's reduction), counted in with one drain and one round of atomics; then
+  // the last arrivers' gates for both blocks, so that block 1's gates do not wait behind block
+  // 0's hand-off; then the value columns.
   KeyPre<NRB> kp[2];
   f32x4 red[2][NRB];
   prefetch_key<NRB>(kp[0], a, rw, 0, tid);
   prefetch_key<NRB>(kp[1], a, rw, kTB, tid);
   reduce_k<NRB, true>(red[0], acc[0], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
-  reduce_k<NRB, true>(red[1], acc[1], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
   epilogue<NRB, true, true, false, kPhStore>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
+  reduce_k<NRB, true>(red[1], acc[1], reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
   epilogue<NRB, true, true, false, kPhStore>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
   {
     const int seg_lo = rw.r0 / a.dim, seg_hi = (rw.r1 - 1) / a.dim;
@@ -1526,8 +1596,7 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
     }
     __syncthreads();
   }
-  epilogue<NRB, true, true, false, kPhGates>(a, red[0], kp[0], sh, 0, w, rw, tid, smem, sh.last2[0]);
-  epilogue<NRB, true, true, false, kPhGates>(a, red[1], kp[1], sh, 1, w, rw, tid, smem, sh.last2[1]);
+  tb2_gates(a, sh, rw, tid);
   epilogue<NRB, true, true, false, kPhValue>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
   __syncthreads();
   epilogue<NRB, true, true, false, kPhValue>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
