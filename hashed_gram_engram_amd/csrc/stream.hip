@@ -1286,21 +1286,34 @@ template <int NRB>
 constexpr int kT2Copies = 2 * NRB + 12;  // per wave and chunk: weights, codes, scales
 
 // Weight copy h of row block i: rows 8 h .. 8 h + 7, lane l at 16 l: row 8 h + l / 8, position
-// l % 8, holding the 16-byte part (l % 8) ^ (row & 7) of the row's 128 chunk bytes.  Not live
-// (after the last chunk): rows 0..15 at feature 0, a cache-resident 2 KB.
-__device__ __forceinline__ void tb2_copy_w(char* slot, const StreamArgs& a, const Rows& rw, int i, int f, bool live,
-                                           int lane) {
-  const int rbase = live ? rw.r0 + 16 * i : 0;
-  const int rlast = live ? rw.r1 - 1 : 15;
-  const size_t fbase = live ? size_t(f) : 0;
+// l % 8, holding the 16-byte part (l % 8) ^ (row & 7) of the row's 128 chunk bytes.  The copies
+// go through a buffer resource on wkv: a lane's byte offset of its row and part in row block 0,
+// and in the workgroup's last row (rows past it repeat it), are computed once; the chunk's byte
+// offset is a scalar.  Not live (after the last chunk): rows 0..15 at feature 0, a
+// cache-resident 2 KB.
+struct Tb2WOff {
+  uint32_t base[2], last[2], dummy[2];
+  uint32_t block;  // bytes of 16 rows
+};
+__device__ __forceinline__ void tb2_woff(Tb2WOff& wo, const StreamArgs& a, const Rows& rw, int lane) {
+  const uint32_t rowb = uint32_t(a.K) * 2u;
+  wo.block = 16u * rowb;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int rr = 8 * h + (lane >> 3);
-    const int r = rbase + rr;
-    const size_t row = size_t(r < rlast ? r : rlast);
-    __builtin_amdgcn_global_load_lds((const void*)(a.wkv + row * a.K + fbase + 8 * ((lane & 7) ^ (rr & 7))),
-                                     (lds_ptr_t)(slot + h * 1024), 16, 0, 2);
+    const uint32_t part = 16u * uint32_t((lane & 7) ^ (rr & 7));
+    wo.base[h] = uint32_t(rw.r0 + rr) * rowb + part;
+    wo.last[h] = uint32_t(rw.r1 - 1) * rowb + part;
+    wo.dummy[h] = uint32_t(rr) * rowb + part;
   }
+}
+__device__ __forceinline__ uint32_t tb2_wo(const Tb2WOff& wo, int i, int h) {
+  const uint32_t o = wo.base[h] + uint32_t(i) * wo.block;
+  return o < wo.last[h] ? o : wo.last[h];
+}
+__device__ __forceinline__ void tb2_copy_w(char* slot, __amdgpu_buffer_rsrc_t wr, uint32_t o0, uint32_t o1, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)slot, 16, o0, soff, 0, 2);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(slot + 1024), 16, o1, soff, 0, 2);
 }
 // This wave's 128 tokens at features f .. f + 63 (inside one column): copy k holds tokens
 // 16 k .. 16 k + 15, four lanes each, part p of token t at position p ^ ((t >> 2) & 3); then the
@@ -1378,12 +1391,19 @@ __device__ __forceinline__ void tb2_dequant(u32x4 (&bt)[2][2][4], const Tok2Raw&
 template <int NRB, bool E8>
 __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamArgs& a, const int32_t* s_ids,
                                          char* smem, const Rows& rw, int lane, int wv) {
-  const int q0 = wv * (a.K >> 2);
+  // (the wave index as a scalar: the copies' LDS addresses and the chunks' feature offsets are
+  // then scalars too, as a buffer copy's scalar offset must be)
+  const int wvs = __builtin_amdgcn_readfirstlane(wv);
+  const int q0 = wvs * (a.K >> 2);
   const int nch = (a.K >> 2) / kC2;
   const int rot = int((5u * blockIdx.x) % uint32_t(nch));
   auto feat = [&](int c) { return q0 + kC2 * ((c + rot) % nch); };
-  char* my_slots = smem + wv * 2 * NRB * kW2Slot;  // stage k: slots k NRB .. k NRB + NRB - 1
-  char* my_tok = smem + 8 * NRB * kW2Slot + wv * kTok2;
+  char* my_slots = smem + wvs * 2 * NRB * kW2Slot;  // stage k: slots k NRB .. k NRB + NRB - 1
+  char* my_tok = smem + 8 * NRB * kW2Slot + wvs * kTok2;
+  const __amdgpu_buffer_rsrc_t wsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.wkv), (short)0, a.N * a.K * 2, 0x00020000);
+  Tb2WOff wo;
+  tb2_woff(wo, a, rw, lane);
   // copy order: chunk 0's weights, its tokens, chunk 1's weights; then each chunk c issues chunk
   // c + 1's tokens and one weight copy per row block (chunk c + 2's).  A chunk's tokens are then
   // always followed by exactly one chunk's weight copies (2 NRB) until they are read, and a row
@@ -1392,14 +1412,15 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
   const bool two = nch > 1;
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    tb2_copy_w(my_slots + i * kW2Slot, a, rw, i, feat(0), true, lane);
+    tb2_copy_w(my_slots + i * kW2Slot, wsrc, tb2_wo(wo, i, 0), tb2_wo(wo, i, 1), 2 * feat(0));
     asm volatile("" ::: "memory");
   }
   tb2_copy_tok(my_tok, a, s_ids, feat(0), lane);
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
-    tb2_copy_w(my_slots + (NRB + i) * kW2Slot, a, rw, i, feat(two ? 1 : 0), two, lane);
+    if (two) tb2_copy_w(my_slots + (NRB + i) * kW2Slot, wsrc, tb2_wo(wo, i, 0), tb2_wo(wo, i, 1), 2 * feat(1));
+    else tb2_copy_w(my_slots + (NRB + i) * kW2Slot, wsrc, wo.dummy[0], wo.dummy[1], 0);
     asm volatile("" ::: "memory");
   }
   constexpr int kInFlight = 4 * NRB + 22;
@@ -1427,22 +1448,33 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
     }
     tb2_copy_tok(my_tok, a, s_ids, fn, lane);
     asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-      char* slot = stage + i * kW2Slot;
+    // row block i + 1's fragments are read while block i's MFMAs run (its copy is waited for
+    // after the same refills as block i's would be: the count does not change)
+    auto read_wf = [&](u32x4 (&wf)[2], int i) {
       asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kInFlight) : "memory");
-      u32x4 wf[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        wf[s] = *reinterpret_cast<const u32x4*>(slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      tb2_copy_w(slot, a, rw, i, fnn, live2, lane);
+        wf[s] = *reinterpret_cast<const u32x4*>(stage + i * kW2Slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
+    };
+    auto refill = [&](int i) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the slot is read before its refill
+      if (live2) tb2_copy_w(stage + i * kW2Slot, wsrc, tb2_wo(wo, i, 0), tb2_wo(wo, i, 1), 2 * fnn);
+      else tb2_copy_w(stage + i * kW2Slot, wsrc, wo.dummy[0], wo.dummy[1], 0);
+      asm volatile("" ::: "memory");
+    };
+    u32x4 wf[2][2];
+    read_wf(wf[0], 0);
+    refill(0);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      if (i + 1 < NRB) read_wf(wf[(i + 1) & 1], i + 1);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int t = 0; t < 4; ++t) acc[b][i][t] = mfma16x16x32(wf[s], bt[s][b][t], acc[b][i][t]);
+          for (int t = 0; t < 4; ++t) acc[b][i][t] = mfma16x16x32(wf[i & 1][s], bt[s][b][t], acc[b][i][t]);
+      if (i + 1 < NRB) refill(i + 1);
       asm volatile("" ::: "memory");
     }
   };
@@ -1828,14 +1860,15 @@ hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t s
   return launch_stream_impl<false>(a, stream_grid(a.N, num_cus), stream);
 }
 
-// The two-token-block kernel (65..128 tokens): bf16 weights; 64-feature chunks inside one
-// table column (head_dim a multiple of 64) and 32-feature groups inside one scale block; one or
-// two row-block counts per workgroup, at most seven; its LDS within the CU's.
+// The two-token-block kernel (65..128 tokens): bf16 weights of at most 2^31 - 1 bytes (copied
+// through a buffer resource); 64-feature chunks inside one table column (head_dim a multiple of
+// 64) and 32-feature groups inside one scale block; one or two row-block counts per workgroup,
+// at most seven; its LDS within the CU's.
 bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int num_cus) {
   const int G = stream_grid(N, num_cus);
   const int lo = min_blocks(N, G), hi = max_blocks(N, G);
   return (K / 4) % kC2 == 0 && head_dim % kC2 == 0 && scale_block % 32 == 0 && lo >= 1 && hi <= 7 &&
-         hi <= lo + 1 && tb2_lds(hi, n_cols) <= 163840;
+         hi <= lo + 1 && tb2_lds(hi, n_cols) <= 163840 && int64_t(N) * K * 2 <= 0x7FFFFFFF;
 }
 
 hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
