@@ -5,7 +5,8 @@ The decode layout (seven row blocks per workgroup) at a ragged second block with
 in both blocks and the output written over x; a small layout where every workgroup owns one row
 block (dim 320) and one where 16 workgroups own two and the rest one (dim 832: 1040 groups of
 four rows over 256 workgroups), each with a workspace of exactly the reported size followed by
-guard bytes, every token checked, control words left zero, and the in-place result identical.
+guard bytes, every token checked, control words left zero, and the in-place result identical;
+and one workspace shared in turn with the tiled and one-block schedules of the decode layout.
 """
 import numpy as np
 import pytest
@@ -80,3 +81,36 @@ def test_forward_two_token_blocks_decode_bad_ids_in_place():
                          w.head_dim, w.scale_block, host_wkv(w), q, k, eps=w.eps, clamp=w.clamp,
                          scale_format=w.scale_format)
     say("   ", check_out(w, sel, got, ref))
+
+
+def test_workspace_shared_with_the_other_decode_schedules():
+    """One workspace for 150 tokens (tiled, split K: staging behind the control words), 100 (two
+    token blocks) and 64 (one token block, apply workgroups) of the decode layout, twice in turn:
+    every control word zero after each call, every result equal to a call on a fresh workspace."""
+    w150 = synth.small_variant(DECODE, name="decode_dims_b150", B=150, T=1, seed=DECODE.seed + 720)
+    say("[gpu] one workspace for the tiled, two-block and one-block schedules at the decode layout")
+    d = synth.device_inputs(w150)
+    lay = layout(w150)
+    cases = []
+    for n in (150, 100, 64):
+        w = synth.small_variant(w150, name=f"decode_dims_b{n}", B=n)
+        dn = dict(d)
+        for k in ("x", "hash_ids", "token_mask"):
+            dn[k] = d[k][:n].contiguous()
+        cases.append((w, dn))
+    sizes = [eg.engram_forward_workspace_bytes(lay, w.B, w.T) for w, _ in cases]
+    n_ws = max(sizes)
+    ctrl = n_ws - max(eg.engram_forward_staging_bytes(lay, w.B, w.T) for w, _ in cases)
+    assert eg.engram_forward_staging_bytes(lay, 100, 1) == 0 and eg.engram_forward_staging_bytes(lay, 64, 1) == 0
+    ws = torch.zeros(n_ws, dtype=torch.uint8, device="cuda")
+    outs = []
+    for w, dn in cases + cases:
+        outs.append(forward(w, dn, ws=ws))
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws[:ctrl]).item()) == 0, w.name
+    for i, (w, dn) in enumerate(cases):
+        fresh = forward(w, dn, ws=torch.zeros_like(ws))
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i], fresh) and torch.equal(outs[i + 3], fresh), w.name
+    del d, cases, outs, ws
+    torch.cuda.empty_cache()
