@@ -73,7 +73,7 @@ bool wkv_mxfp8(const engram_layout* l) { return l->wkv_format == ENGRAM_WKV_MXFP
 bool tb2_layout(const engram_layout* l, int cus) {
   const int N = int(N_of(l));
   return !wkv_mxfp8(l) && l->n_rows <= 0x7FFFFFFF && stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim &&
-         stream_tb2_ok(int(K_of(l)), N, l->n_cols, l->head_dim, l->scale_block, cus);
+         stream_tb2_ok(int(K_of(l)), N, l->dim, l->n_cols, l->head_dim, l->scale_block, cus);
 }
 bool use_tb2(const engram_layout* l, int64_t M, int cus) { return M > 64 && M <= 128 && tb2_layout(l, cus); }
 // the tiled schedule for the whole forward

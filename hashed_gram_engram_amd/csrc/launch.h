@@ -63,9 +63,9 @@ struct StreamArgs {
   uint32_t* ws_hdr;    // workspace start: [0] wait time-outs, then per-token-block blocks
   size_t tb_stride;    // bytes per token-block block
   uint32_t spin_budget;
-  // grid: G streaming workgroups, then (fused forward of one token block) n_apply workgroups
-  // that apply the gates to the value rows
-  int G, n_apply;
+  // grid: G streaming workgroups, then (fused forward of one or two token blocks) n_apply
+  // workgroups that apply the gates to the value rows, n_apply / n_atb of them per token block
+  int G, n_apply, n_atb;
 };
 
 // The hash step: token ids -> row ids of every Engram layer.
@@ -103,7 +103,7 @@ int stream_grid(int N, int num_cus);
 int stream_rows_per_group(int N, int G);
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 // 65..128 tokens in one pass over bf16 weights (workspace as the streaming kernel's, two blocks)
-bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int num_cus);
+bool stream_tb2_ok(int K, int N, int dim, int n_cols, int head_dim, int scale_block, int num_cus);
 hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 // Whether the weight-streaming kernels take MXFP8 weights for this shape (the wide K loop:
 // K / 4 a multiple of 128, 1..7 row blocks per workgroup; fused: head_dim a multiple of 128 and

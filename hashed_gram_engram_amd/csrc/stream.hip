@@ -702,24 +702,27 @@ __device__ __forceinline__ uint32_t* gate_slot(const StreamArgs& a, int64_t tb, 
   return tb_block(a, tb) + 256 + (size_t(w) * 4 + s) * kTB;
 }
 
-// Apply workgroups (the fused forward of one token block).  Value workgroup j (the j-th from
-// the first one that owns a value row) does not wait for the gates: it leaves its bf16 values in
-// a tile behind the token block's part of the workspace, one kVRow-byte row per token (its value
-// features, shifted by 0 or 4 features so that 16-byte pieces line up with those of x and out),
-// and marks the tile ready; apply workgroup 2 j + h, one of the last ids of the grid, applies the
-// gates to tokens 32 h .. 32 h + 31 of it.  The apply workgroups run on the CUs that the key
+// Apply workgroups (the fused forward of one token block, and of two in the two-token-block
+// kernel).  Value workgroup j (the j-th from the first one that owns a value row) does not wait
+// for the gates: for each token block it leaves its bf16 values in a tile behind the token
+// blocks' part of the workspace, one kVRow-byte row per token (its value features, shifted by 0
+// or 4 features so that 16-byte pieces line up with those of x and out), and marks the tile
+// ready; apply workgroup 2 j + h of the block, among the last ids of the grid, applies the gates
+// to tokens 32 h .. 32 h + 31 of it.  The apply workgroups run on the CUs that the key
 // workgroups leave, and the value workgroups' output work (64 tokens x 4 streams of their
 // features, issue-bound on one wave per SIMD) is spread over twice as many workgroups.  Slot k of
-// an apply workgroup (32 words): k = 0..3 the gates of stream k for its 32 tokens, k = 4 word 0
-// the tile's ready mark; each written once by its producer, read and cleared by that workgroup
-// alone, which also clears its half of the tile.
+// an apply workgroup (32 words, in its token block's gate-slot region): k = 0..3 the gates of
+// stream k for its 32 tokens, k = 4 word 0 the tile's ready mark; each written once by its
+// producer, read and cleared by that workgroup alone, which also clears its half of the tile.
 constexpr int kVRow = 240;            // bytes per token row of a value tile (up to 120 features)
 constexpr int kVTile = kTB * kVRow;   // one value workgroup's tile
-__device__ __forceinline__ uint32_t* apply_slot(const StreamArgs& a, int ap, int k) {
-  return tb_block(a, 0) + 256 + (size_t(ap) * 5 + k) * 32;
+__device__ __forceinline__ uint32_t* apply_slot(const StreamArgs& a, int64_t tb, int ap, int k) {
+  return tb_block(a, tb) + 256 + (size_t(ap) * 5 + k) * 32;
 }
-__device__ __forceinline__ uint32_t vtile_off(const StreamArgs& a, int j) {
-  return uint32_t(256 + a.tb_stride + size_t(j) * kVTile);
+// value workgroup j's tile of token block tb, behind the n_atb token blocks' control words
+__device__ __forceinline__ uint32_t vtile_off(const StreamArgs& a, int64_t tb, int j) {
+  const int V = a.n_apply / (2 * a.n_atb);
+  return uint32_t(256 + size_t(a.n_atb) * a.tb_stride + (size_t(tb) * V + j) * kVTile);
 }
 __device__ __forceinline__ uint32_t ws_off(const StreamArgs& a, const uint32_t* p) {
   return uint32_t(reinterpret_cast<const char*>(p) - reinterpret_cast<const char*>(a.ws_hdr));
@@ -875,10 +878,10 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
           const int v0 = owner_of_row(4 * a.dim, Q, G);
           // four words per 16-byte device-coherent store
           if constexpr (APPLY) {
-            // apply workgroup ap takes tokens 32 (ap & 1) .. + 31
-            for (int i = tid; i < a.n_apply * 8; i += 256) {
+            // apply workgroup ap of the block takes tokens 32 (ap & 1) .. + 31
+            for (int i = tid; i < (a.n_apply / a.n_atb) * 8; i += 256) {
               const int ap = i >> 3, t4 = 32 * (ap & 1) + 4 * (i & 7);
-              store_coherent4(wsr, ws_off(a, apply_slot(a, ap, s) + 4 * (i & 7)),
+              store_coherent4(wsr, ws_off(a, apply_slot(a, tb, ap, s) + 4 * (i & 7)),
                               __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
                                                               __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
                                                               __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
@@ -909,7 +912,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
         const int j = w - owner_of_row(4 * a.dim, Q, G);
         const int cv_lo = rw.r0 > nv ? rw.r0 : nv;
         const int shift = (cv_lo - nv) & 7;
-        const uint32_t row = vtile_off(a, j) + uint32_t(tok) * kVRow;
+        const uint32_t row = vtile_off(a, tb, j) + uint32_t(tok) * kVRow;
 #pragma unroll
         for (int i = 0; i < NRB; ++i) {
           const int n = rw.r0 + 16 * i + 4 * (lane >> 4);
@@ -920,7 +923,7 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
         }
         drain_memory_ops();
         __syncthreads();
-        if (tid < 2) store_relaxed(apply_slot(a, 2 * j + tid, 4), 0x80000000u);
+        if (tid < 2) store_relaxed(apply_slot(a, tb, 2 * j + tid, 4), 0x80000000u);
       }
       return;
     }
@@ -1119,8 +1122,10 @@ __global__ __launch_bounds__(256, 1) void k_stream_narrow(StreamArgs a) {
 // Apply workgroup ap (value tile j = ap / 2, tokens 32 (ap & 1) .. + 31): out = h + g * value
 // on all four streams of the tile's features.  Thread pairs (token t, 16-byte piece p) of the
 // rows, t = idx / 16 and p = idx % 16 for idx = tid, tid + 256; x is loaded before waiting.
-__device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap) {
+__device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int apg) {
   const int tid = threadIdx.x, G = a.G, Q = a.N >> 2;
+  const int napb = a.n_apply / a.n_atb;  // apply workgroups per token block
+  const int b = apg / napb, ap = apg - b * napb;
   const int j = ap >> 1, th = ap & 1;
   const Rows rw = rows_of(owner_of_row(4 * a.dim, Q, G) + j, a.N, G);
   const int nv = 4 * a.dim;
@@ -1134,7 +1139,7 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int idx = tid + 256 * k, t = idx >> 4, pc = 8 * (idx & 15);
-    m[k] = 32 * th + t;
+    m[k] = int64_t(b) * kTB + 32 * th + t;
     const bool mv = m[k] < a.M;
     lo_ok[k] = mv && pc >= shift && pc + 4 <= shift + nc;
     hi_ok[k] = mv && pc + 4 >= shift && pc + 8 <= shift + nc;
@@ -1151,7 +1156,7 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
   }
   // the tile is ready, then the gates (each waited for by one thread, bounded)
   if (tid == 0) {
-    uint32_t* flag = apply_slot(a, ap, 4);
+    uint32_t* flag = apply_slot(a, b, ap, 4);
     uint32_t it = 0;
     while (load_relaxed(flag) == 0u) {
       __builtin_amdgcn_s_sleep(2);
@@ -1169,11 +1174,12 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
     // (pieces that hold a feature end inside the row: 8 p + 4 <= shift + nc <= 116)
     vv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (lo_ok[k] || hi_ok[k])
-      vv[k] = load_coherent4(wsr, vtile_off(a, j) + uint32_t(m[k]) * kVRow + 16 * uint32_t((tid + 256 * k) & 15));
+      vv[k] = load_coherent4(wsr, vtile_off(a, b, j) + uint32_t(m[k] - int64_t(b) * kTB) * kVRow +
+                                       16 * uint32_t((tid + 256 * k) & 15));
   }
   if (tid < 128) {
     const int s = tid >> 5, t = tid & 31;
-    uint32_t* slot = apply_slot(a, ap, s) + t;
+    uint32_t* slot = apply_slot(a, b, ap, s) + t;
     uint32_t bits = 0u, it = 0;
     while ((bits = load_relaxed(slot)) == 0u) {
       __builtin_amdgcn_s_sleep(2);
@@ -1221,7 +1227,7 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
   // every thread's tile loads have returned (their values are used above): clear this half
   __syncthreads();
   for (int i = tid; i < 32 * kVRow / 16; i += 256)
-    store_coherent4(wsr, vtile_off(a, j) + uint32_t(32 * th) * kVRow + 16 * uint32_t(i), f32x4{0.f, 0.f, 0.f, 0.f});
+    store_coherent4(wsr, vtile_off(a, b, j) + uint32_t(32 * th) * kVRow + 16 * uint32_t(i), f32x4{0.f, 0.f, 0.f, 0.f});
 }
 
 // Wide kernel: every workgroup has NLO or NHI = NLO + 1 row blocks, each compiled exactly (only
@@ -1487,14 +1493,14 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
 
 // The last arrivers' part for both token blocks: for each stream slot this workgroup closed in
 // either block, the partial sums of every contributor of both blocks are loaded in one round
-// (in order, as in the one-block epilogue), then each block's gates go to the value
-// workgroups' slots and its counter and partial sums are cleared.
+// (in order, as in the one-block epilogue), then each block's gates go to the slots of its apply
+// workgroups and its counter and partial sums are cleared.
 __device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const Rows& rw, int tid) {
   const int Q = a.N >> 2, G = a.G;
   const int seg_lo = rw.r0 / a.dim;
   const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
   const int t = tid & 63, q = tid >> 6;
-  const int v0 = owner_of_row(4 * a.dim, Q, G);
+  const int napb = a.n_apply / a.n_atb;
 #pragma unroll 1
   for (int sl = 0; sl < 2; ++sl) {
     const bool L0 = sh.last2[0][sl] != 0, L1 = sh.last2[1][sl] != 0;
@@ -1535,11 +1541,10 @@ __device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const
       if (q == 0) sh.red[0][t][0] = int64_t(b) * kTB + t < a.M ? gate_from_quarters(a, sh, t) : 0.0f;
       __syncthreads();
       if (tid == 0) store_relaxed(counter_of(a, b, s), 0u);
-      for (int i = tid; i < (G - v0) * (kTB / 4); i += 256) {
-        const int v = v0 + i / (kTB / 4), t4 = 4 * (i % (kTB / 4));
-        const uint32_t off = uint32_t(reinterpret_cast<char*>(gate_slot(a, b, v, s) + t4) -
-                                      reinterpret_cast<char*>(a.ws_hdr));
-        store_coherent4(wsr, off,
+      // apply workgroup ap of the block takes tokens 32 (ap & 1) .. + 31
+      for (int i = tid; i < napb * 8; i += 256) {
+        const int ap = i >> 3, t4 = 32 * (ap & 1) + 4 * (i & 7);
+        store_coherent4(wsr, ws_off(a, apply_slot(a, b, ap, s) + 4 * (i & 7)),
                         __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
                                                         __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
                                                         __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
@@ -1629,9 +1634,10 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
     __syncthreads();
   }
   tb2_gates(a, sh, rw, tid);
-  epilogue<NRB, true, true, false, kPhValue>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
-  __syncthreads();
-  epilogue<NRB, true, true, false, kPhValue>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
+  // value columns: each block's bf16 values into this workgroup's tile for that block (the
+  // apply workgroups write out)
+  epilogue<NRB, true, true, true, kPhValue>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
+  epilogue<NRB, true, true, true, kPhValue>(a, red[1], kp[1], sh, 1, w, rw, tid, smem);
 }
 
 template <int NLO, int NHI>
@@ -1640,6 +1646,10 @@ __global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
   static_assert(stage_bytes(NHI) <= NHI * 16384, "output staging exceeds the reduction buffer");
   const int G = a.G, w = blockIdx.x;
+  if (w >= G) {
+    apply_wg(a, smem, w - G);
+    return;
+  }
   const Rows rw = rows_of(w, a.N, G);
   if constexpr (NLO == NHI) {
     tb2_blocks<NLO>(a, smem, sh, w, rw);
@@ -1780,12 +1790,14 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   StreamArgs arg = a;
   arg.G = G;
   arg.n_apply = 0;
+  arg.n_atb = 0;
   if (FUSED && wide && (a.w8 || a.M <= kTB)) {
     // the one-token-block fused kernel: two apply workgroups per value workgroup, whose slots
     // (5 x 32 words each) fit in the token block's gate-slot region (G x 4 x 64 words)
     const int V = value_groups(a.N, a.dim, G);
     if (V < 1 || 2 * V * 160 > G * 256) return hipErrorInvalidValue;
     arg.n_apply = 2 * V;
+    arg.n_atb = 1;
   }
   void* params[] = {&arg};
   const size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
@@ -1846,14 +1858,15 @@ size_t stream_tb_stride(int grid) {
   return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 16;
 }
 
-// One token block of the fused forward also needs the value tiles behind its block (cleared
-// again by the apply workgroups); the larger of the two layouts, so that the size never
-// decreases with M.
+// The fused forward of one or two token blocks also needs the blocks' value tiles behind their
+// control words (cleared again by the apply workgroups); the larger of the two layouts, so that
+// the size never decreases with M.
 size_t stream_workspace_bytes(int64_t M, int N, int dim, int grid) {
   const int64_t n_tb = (M + kTB - 1) / kTB;
   const size_t blocks = size_t(n_tb) * stream_tb_stride(grid);
-  const size_t one = stream_tb_stride(grid) + size_t(value_groups(N, dim, grid)) * kVTile;
-  return 256 + (blocks > one ? blocks : one);
+  const int64_t n_atb = n_tb < 2 ? 1 : 2;
+  const size_t tiled = size_t(n_atb) * (stream_tb_stride(grid) + size_t(value_groups(N, dim, grid)) * kVTile);
+  return 256 + (blocks > tiled ? blocks : tiled);
 }
 
 hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t stream) {
@@ -1863,30 +1876,36 @@ hipError_t launch_kv_proj_stream(const StreamArgs& a, int num_cus, hipStream_t s
 // The two-token-block kernel (65..128 tokens): bf16 weights of at most 2^31 - 1 bytes (copied
 // through a buffer resource); 64-feature chunks inside one table column (head_dim a multiple of
 // 64) and 32-feature groups inside one scale block; one or two row-block counts per workgroup,
-// at most seven; its LDS within the CU's.
-bool stream_tb2_ok(int K, int N, int n_cols, int head_dim, int scale_block, int num_cus) {
+// at most seven; its LDS within the CU's; the apply workgroups' slots within each token
+// block's gate-slot region.
+bool stream_tb2_ok(int K, int N, int dim, int n_cols, int head_dim, int scale_block, int num_cus) {
   const int G = stream_grid(N, num_cus);
   const int lo = min_blocks(N, G), hi = max_blocks(N, G);
+  const int V = value_groups(N, dim, G);
   return (K / 4) % kC2 == 0 && head_dim % kC2 == 0 && scale_block % 32 == 0 && lo >= 1 && hi <= 7 &&
-         hi <= lo + 1 && tb2_lds(hi, n_cols) <= 163840 && int64_t(N) * K * 2 <= 0x7FFFFFFF;
+         hi <= lo + 1 && tb2_lds(hi, n_cols) <= 163840 && int64_t(N) * K * 2 <= 0x7FFFFFFF &&
+         V >= 1 && 2 * V * 160 <= G * 256;
 }
 
 hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
   if (a.M <= kTB || a.M > 2 * kTB || a.w8 || a.n_rows > 0x7FFFFFFF ||
-      !stream_tb2_ok(a.K, a.N, a.n_cols, a.head_dim, a.scale_block, num_cus))
+      !stream_tb2_ok(a.K, a.N, a.dim, a.n_cols, a.head_dim, a.scale_block, num_cus))
     return hipErrorInvalidValue;
   const int G = stream_grid(a.N, num_cus);
   a.ws_hdr = static_cast<uint32_t*>(workspace);
   a.tb_stride = stream_tb_stride(G);
   a.G = G;
-  a.n_apply = 0;
+  // two apply workgroups per value workgroup and token block, their slots (5 x 32 words each)
+  // in the block's gate-slot region (G x 4 x 64 words)
+  a.n_atb = 2;
+  a.n_apply = 4 * value_groups(a.N, a.dim, G);
   void* fn = pick_tb2(min_blocks(a.N, G), max_blocks(a.N, G));
   if (fn == nullptr) return hipErrorInvalidValue;
   const size_t lds = size_t(tb2_lds(max_blocks(a.N, G), a.n_cols));
   const hipError_t e = allow_lds(fn, lds);
   if (e != hipSuccess) return e;
   void* params[] = {&a};
-  return hipLaunchKernel(fn, dim3(G), dim3(256), params, lds, stream);
+  return hipLaunchKernel(fn, dim3(G + a.n_apply), dim3(256), params, lds, stream);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {

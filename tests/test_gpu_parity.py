@@ -468,7 +468,9 @@ def test_workspace_sizes_never_decrease_with_token_count():
 def test_binding_workspace_shared_by_two_layouts():
     say("[gpu] the binding's workspace across layouts: a tiled call (staging at the end) "
         "then three streamed token blocks of another layout (control words over that staging)")
-    a, b = E8M0_TILED, STREAM_ONLY
+    # (five token blocks: their control words reach past the tiled call's control part, which
+    # holds the streaming schedules' words up to 128 tokens, value tiles included)
+    a, b = E8M0_TILED, synth.small_variant(STREAM_ONLY, name="dim320_b2_t150", T=150)
     assert (eg.engram_forward_workspace_bytes(layout(b), b.B, b.T) >
             eg.engram_forward_workspace_bytes(layout(a), a.B, a.T) - eg.engram_forward_staging_bytes(layout(a), a.B, a.T))
     da, db = synth.device_inputs(a), synth.device_inputs(b)
