@@ -1288,8 +1288,6 @@ __host__ __device__ constexpr int tb2_lds(int nrb, int n_cols) {
              ? 8 * nrb * kW2Slot + 4 * kTok2 + 2 * kTB * n_cols * 4
              : nrb * 16384;
 }
-template <int NRB>
-constexpr int kT2Copies = 2 * NRB + 12;  // per wave and chunk: weights, codes, scales
 
 // Weight copy h of row block i: rows 8 h .. 8 h + 7, lane l at 16 l: row 8 h + l / 8, position
 // l % 8, holding the 16-byte part (l % 8) ^ (row & 7) of the row's 128 chunk bytes.  The copies
@@ -1324,8 +1322,15 @@ __device__ __forceinline__ void tb2_copy_w(char* slot, __amdgpu_buffer_rsrc_t wr
 // This wave's 128 tokens at features f .. f + 63 (inside one column): copy k holds tokens
 // 16 k .. 16 k + 15, four lanes each, part p of token t at position p ^ ((t >> 2) & 3); then the
 // scales of features f .. f + 31 and f + 32 .. f + 63 of every token (the fp32 scale, or the
-// aligned dword that holds the E8M0 byte) at 8192 + 512 s + 4 t.
-__device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, const int32_t* s_ids, int f, int lane) {
+// aligned dword that holds the E8M0 byte) at 8192 + 512 s + 4 t.  NS = 1 where both halves of
+// every chunk share their scale word (fp32 scales per a multiple of 64 features; E8M0 scales,
+// whose dwords hold four 32-feature groups): one gather of 64 rows' words fewer per 64 tokens.
+// Then, with `fresh` false (the chunk's scale words are those already in the buffer), the scale
+// copies are replaced by as many reads of one word into the unused second area, which keeps the
+// number of copies per chunk, and with it the wait counts, fixed.
+template <int NS>
+__device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, const int32_t* s_ids, int f, int lane,
+                                             bool fresh = true) {
   const int j = f / a.head_dim;
   const int cc = f - j * a.head_dim;
   int rid[10];
@@ -1342,8 +1347,14 @@ __device__ __forceinline__ void tb2_copy_tok(char* tbuf, const StreamArgs& a, co
   }
   const int nb = a.head_dim / a.scale_block;
   const int sbyte = a.scale_e8m0 ? 1 : 4;
+  if (NS == 1 && !fresh) {
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+    for (int k = 0; k < 2; ++k)
+      __builtin_amdgcn_global_load_lds(a.scales, (lds_ptr_t)(tbuf + 8192 + 512 + k * 256), 4, 0, 0);
+    return;
+  }
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int64_t rr = rid[8 + k] >= 0 ? rid[8 + k] : 0;
@@ -1361,6 +1372,7 @@ struct Tok2Raw {
   uint32_t keep[2][4];
 };
 
+template <int NS>
 __device__ __forceinline__ void tb2_read_tok(Tok2Raw& r, const char* my_tok, const int32_t* s_ids, int j,
                                              int n_cols, int lane) {
 #pragma unroll
@@ -1374,7 +1386,7 @@ __device__ __forceinline__ void tb2_read_tok(Tok2Raw& r, const char* my_tok, con
         const int p = 2 * s + (lane >> 5);
         r.code[s][b][t] = *reinterpret_cast<const u32x2*>(my_tok + tok * 64 + 16 * (p ^ ((tok >> 2) & 3)) +
                                                           8 * ((lane >> 4) & 1));
-        r.sw[s][b][t] = *reinterpret_cast<const uint32_t*>(my_tok + 8192 + s * 512 + 4 * tok);
+        r.sw[s][b][t] = *reinterpret_cast<const uint32_t*>(my_tok + 8192 + (NS == 2 ? s : 0) * 512 + 4 * tok);
       }
     }
 }
@@ -1394,7 +1406,7 @@ __device__ __forceinline__ void tb2_dequant(u32x4 (&bt)[2][2][4], const Tok2Raw&
 // 2's rows right after it is read.  Per chunk the wave first reads and dequantises its token
 // operands (which frees its token buffer for chunk c + 1's copies), then multiplies row block
 // by row block.
-template <int NRB, bool E8>
+template <int NRB, bool E8, int NS>
 __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamArgs& a, const int32_t* s_ids,
                                          char* smem, const Rows& rw, int lane, int wv) {
   // (the wave index as a scalar: the copies' LDS addresses and the chunks' feature offsets are
@@ -1411,17 +1423,20 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
   Tb2WOff wo;
   tb2_woff(wo, a, rw, lane);
   // copy order: chunk 0's weights, its tokens, chunk 1's weights; then each chunk c issues chunk
-  // c + 1's tokens and one weight copy per row block (chunk c + 2's).  A chunk's tokens are then
-  // always followed by exactly one chunk's weight copies (2 NRB) until they are read, and a row
-  // block's copy by the rest of its chunk's, two chunks' tokens, one chunk's weights and as many
-  // weight copies as blocks already read: 4 NRB + 22 copies.
+  // c + 1's tokens (kTok copies) and one weight copy per row block (chunk c + 2's).  A chunk's
+  // tokens are then always followed by exactly one chunk's weight copies (2 NRB) until they are
+  // read, and a row block's copy by the rest of its chunk's, two chunks' tokens, one chunk's
+  // weights and as many weight copies as blocks already read: 4 NRB - 2 + 2 kTok copies.
+  constexpr int kTok = 8 + 2 * NS;
+  // features one scale word covers (NS = 1): a block of fp32 scales, four of E8M0 bytes
+  const int span = E8 ? 4 * a.scale_block : a.scale_block;
   const bool two = nch > 1;
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
     tb2_copy_w(my_slots + i * kW2Slot, wsrc, tb2_wo(wo, i, 0), tb2_wo(wo, i, 1), 2 * feat(0));
     asm volatile("" ::: "memory");
   }
-  tb2_copy_tok(my_tok, a, s_ids, feat(0), lane);
+  tb2_copy_tok<NS>(my_tok, a, s_ids, feat(0), lane);
   asm volatile("" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NRB; ++i) {
@@ -1429,7 +1444,7 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
     else tb2_copy_w(my_slots + (NRB + i) * kW2Slot, wsrc, wo.dummy[0], wo.dummy[1], 0);
     asm volatile("" ::: "memory");
   }
-  constexpr int kInFlight = 4 * NRB + 22;
+  constexpr int kInFlight = 4 * NRB - 2 + 2 * kTok;
   static_assert(kInFlight <= 63, "vmcnt range");
   const int wr = lane & 15;
   // one chunk; the stage is a template argument so that the two stages' slot addresses are
@@ -1446,13 +1461,15 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
     u32x4 bt[2][2][4];
     {
       Tok2Raw raw;
-      tb2_read_tok(raw, my_tok, s_ids, fc / a.head_dim, a.n_cols, lane);
+      tb2_read_tok<NS>(raw, my_tok, s_ids, fc / a.head_dim, a.n_cols, lane);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
       const int cc = fc % a.head_dim;
 #pragma unroll
       for (int g = 0; g < 16; ++g) tb2_dequant<E8>(bt, raw, g, cc, a.scale_block);
     }
-    tb2_copy_tok(my_tok, a, s_ids, fn, lane);
+    // (chunk c + 1 reads chunk c's scale words when both lie in one word's span of one column)
+    const bool fresh = fn / a.head_dim != fc / a.head_dim || (fn % a.head_dim) / span != (fc % a.head_dim) / span;
+    tb2_copy_tok<NS>(my_tok, a, s_ids, fn, lane, fresh);
     asm volatile("" ::: "memory");
     // row block i + 1's fragments are read while block i's MFMAs run (its copy is waited for
     // after the same refills as block i's would be: the count does not change)
@@ -1592,8 +1609,10 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[b][i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (a.scale_e8m0) tb2_loop<NRB, true>(acc, a, s_ids, smem, rw, lane, wv);
-  else tb2_loop<NRB, false>(acc, a, s_ids, smem, rw, lane, wv);
+  // (E8M0 scale dwords hold four 32-feature groups: both halves of a 64-feature chunk in one)
+  if (a.scale_e8m0) tb2_loop<NRB, true, 1>(acc, a, s_ids, smem, rw, lane, wv);
+  else if (a.scale_block % 64 == 0) tb2_loop<NRB, false, 1>(acc, a, s_ids, smem, rw, lane, wv);
+  else tb2_loop<NRB, false, 2>(acc, a, s_ids, smem, rw, lane, wv);
   __syncthreads();
   // Both token blocks' K-partial reductions and key partial sums first (block 0's stores in
   // flight under block 1's reduction), counted in with one drain and one round of atomics; then
