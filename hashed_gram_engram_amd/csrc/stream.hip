@@ -1272,12 +1272,13 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
 // The fused forward of 65..128 tokens in one pass over the weights, the one-block kernel's
 // layout kept (one workgroup per CU over its row blocks, four waves each on a K quarter, every
 // wave streaming its own weight rows, no barrier in the K loop) with two 64-token blocks per
-// wave: chunks of 64 features, so that a wave's weight slots (NRB x 2 KB) and its tokens' codes
-// (128 tokens x 64 bytes, and their scales) fit the LDS together.  Per chunk a wave issues the
-// next chunk's token copies, then each row block's copy for the next chunk right after reading
-// it (24 copies in flight when a block is read, as in the one-block kernel), and multiplies
-// NRB x 2 x 8 MFMAs.  Afterwards each token block goes through the K-partial reduction and the
-// epilogue of the several-token-block schedule (value workgroups wait for their gates).
+// wave: chunks of 64 features, so that a wave's two stages of weight slots (2 x NRB x 2 KB) and
+// its tokens' codes (128 tokens x 64 bytes, and their scales) fit the LDS together.  Per chunk a
+// wave reads and dequantises its token operands, issues the next chunk's token copies, then
+// refills each row block's slot with the rows two chunks ahead right after reading it, and
+// multiplies NRB x 2 x 8 MFMAs.  Afterwards both token blocks go through the K-partial
+// reduction and the key hand-off together; the value workgroups leave bf16 tiles for the apply
+// workgroups, as in the one-block kernel.
 constexpr int kC2 = 64;                 // features per chunk
 constexpr int kW2Slot = 16 * kC2 * 2;   // LDS slot of one row block (2 KB)
 constexpr int kTok2 = 2 * kTB * kC2 + 4 * 256;  // per wave: 128 tokens' codes, 2 x 128 scales
