@@ -579,23 +579,22 @@ __device__ __forceinline__ void reduce_k(f32x4 (&red)[NRB], f32x4 (&acc)[NRB][4]
                                          int wv) {
   if constexpr (ONE_ROUND) {
     // (LDS-only barriers: the wide loop's copies have all landed, and the epilogue inputs loaded
-    // just before stay in flight under the exchange; __syncthreads would wait for them)
+    // just before stay in flight under the exchange; __syncthreads would wait for them.  The
+    // wide kernels instantiate their blocks per row-block count, so cnt == NRB here: every
+    // fragment is exchanged without a branch, and the reads are issued together.)
     lds_barrier();
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
-      if (i < cnt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) X[((i * 4 + wv) * 4 + t) * 64 + lane] = acc[i][t];
+      for (int t = 0; t < 4; ++t) X[((i * 4 + wv) * 4 + t) * 64 + lane] = acc[i][t];
     lds_barrier();
+    f32x4 p[NRB][4];
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
-      if (i < cnt) {
-        f32x4 s = X[((i * 4 + 0) * 4 + wv) * 64 + lane];
-        s += X[((i * 4 + 1) * 4 + wv) * 64 + lane];
-        s += X[((i * 4 + 2) * 4 + wv) * 64 + lane];
-        s += X[((i * 4 + 3) * 4 + wv) * 64 + lane];
-        red[i] = s;
-      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p[i][q] = X[((i * 4 + q) * 4 + wv) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) red[i] = ((p[i][0] + p[i][1]) + p[i][2]) + p[i][3];
     lds_barrier();  // X overlaps the epilogue's shared words
     return;
   }
