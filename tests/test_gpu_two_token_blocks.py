@@ -6,7 +6,9 @@ in both blocks and the output written over x; a small layout where every workgro
 block (dim 320) and one where 16 workgroups own two and the rest one (dim 832: 1040 groups of
 four rows over 256 workgroups), each with a workspace of exactly the reported size followed by
 guard bytes, every token checked, control words left zero, and the in-place result identical;
-and one workspace shared in turn with the tiled and one-block schedules of the decode layout.
+fp32 scales per 32, 64 and 256 features at the decode layout (the scale gathers per chunk: two,
+one, or one kept across a column's chunks); and one workspace shared in turn with the tiled and
+one-block schedules of the decode layout.
 """
 import numpy as np
 import pytest
@@ -52,6 +54,24 @@ def test_forward_two_token_blocks_small_layouts(dim, T):
     torch.cuda.synchronize()
     assert torch.equal(x2, out)
     assert int(torch.count_nonzero(buf[:need]).item()) == 0
+
+
+@pytest.mark.parametrize("sb", [32, 64, 256])
+def test_forward_two_token_blocks_scale_widths(sb):
+    """fp32 scales per 32 features (two scale gathers per chunk), per 64 (one, a fresh word every
+    chunk) and per 256 (one word for the four chunks of a column, kept across them), at 100
+    tokens of the decode layout, every token checked."""
+    w = synth.small_variant(DECODE, name=f"decode_dims_sb{sb}_t100", B=1, T=100, scale_block=sb,
+                            hash_dist="zipf", mask_false_frac=0.1, seed=DECODE.seed + 730 + sb)
+    say(f"[gpu] forward {w.name}: two token blocks, fp32 scales per {sb} features")
+    d = synth.device_inputs(w)
+    out = forward(w, d)
+    torch.cuda.synchronize()
+    sel = np.arange(w.M)
+    got = u16(out).reshape(w.M, w.hc, w.dim)
+    del d, out
+    torch.cuda.empty_cache()
+    say("   ", check_out(w, sel, got, oracle_for(w, sel)))
 
 
 def test_forward_two_token_blocks_decode_bad_ids_in_place():
