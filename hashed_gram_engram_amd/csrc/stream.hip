@@ -357,9 +357,9 @@ __device__ __forceinline__ u32x4 wide_operand(const WideTok& tk, int t, int s) {
 // hash id names a table row.
 constexpr int kTokBuf = kTokBuf_;
 
-template <bool SCALES = true>
+template <bool SCALES = true, typename IdT = int64_t>
 __device__ __forceinline__ void wide_copy_tok(char* tbuf, uint32_t (&keep)[4], const StreamArgs& a,
-                                              const int64_t* s_ids, int f_chunk, int lane) {
+                                              const IdT* s_ids, int f_chunk, int lane) {
   const int j = f_chunk / a.head_dim;
   const int cc0 = f_chunk - j * a.head_dim;
   const int nb = a.head_dim / a.scale_block;
@@ -564,6 +564,117 @@ __device__ __forceinline__ void wide_loop(f32x4 (&acc)[NRB][4], const StreamArgs
     }
   }
   // the refill copies after the last chunk land before the slots are reused
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// The one-token-block decode loop with one more weight slot.  Where every workgroup's rows end
+// in a block of at most four rows (100 rows: six full blocks and four rows), that block keeps
+// only its four rows (a 1 KB slot, one copy per chunk), and the hash ids are staged as 32-bit
+// values; the LDS this frees holds a second slot for row block 0, which is then copied two
+// chunks ahead: a wave keeps NRB x 4 KB of rows in flight instead of (NRB - 1) x 4 KB and four
+// rows.  Wave layout: slots of blocks 0 .. NRB - 2 (4 KB each), the last block's 1 KB slot,
+// block 0's second slot (chunks c with c odd).
+__host__ __device__ constexpr int deep_wave_bytes(int nrb) { return (nrb - 1) * kWBlk + 1024 + kWBlk; }
+__host__ __device__ constexpr int deep_ids_off(int nrb) { return 4 * deep_wave_bytes(nrb) + 4 * kTokBuf_; }
+__host__ __device__ constexpr int deep_lds_bytes(int nrb, int n_cols) {
+  return deep_ids_off(nrb) + kTB * n_cols * 4 > nrb * 16384 ? deep_ids_off(nrb) + kTB * n_cols * 4 : nrb * 16384;
+}
+
+// The last row block's copy: its rows 0..3 (past the workgroup's last row: the last row), lane
+// l at 16 l: row l / 16, part (l % 16) ^ row, as the first copy of a full block.  Not live:
+// rows 0..3 at feature 0 (cache resident).
+__device__ __forceinline__ void deep_copy_last(char* slot, const StreamArgs& a, const Rows& rw, int nrb, int f_chunk,
+                                               bool live, int lane) {
+  const int rr = lane >> 4;
+  const int rbase = live ? rw.r0 + 16 * (nrb - 1) : 0;
+  const int rlast = live ? rw.r1 - 1 : 3;
+  const int r = rbase + rr;
+  const size_t row = size_t(r < rlast ? r : rlast);
+  const size_t fbase = live ? size_t(f_chunk) : 0;
+  __builtin_amdgcn_global_load_lds((const void*)(a.wkv + row * a.K + fbase + 8 * ((lane & 15) ^ rr)),
+                                   (lds_ptr_t)slot, 16, 0, 2);
+}
+
+template <int NRB>
+__device__ __forceinline__ void deep_loop(f32x4 (&acc)[NRB][4], const StreamArgs& a, const int32_t* s_ids,
+                                          char* smem, const Rows& rw, int lane, int wv) {
+  static_assert(NRB >= 2, "a full block and the last one");
+  const int q0 = wv * (a.K >> 2);
+  const int nch = (a.K >> 2) / 128;
+  const int rot = int((5u * blockIdx.x) % uint32_t(nch));
+  auto feat = [&](int c) { return q0 + 128 * ((c + rot) % nch); };
+  char* const base = smem + wv * deep_wave_bytes(NRB);
+  char* const last_slot = base + (NRB - 1) * kWBlk;
+  char* const b0_second = last_slot + 1024;
+  char* const my_tok = smem + 4 * deep_wave_bytes(NRB) + wv * kTokBuf;
+  uint32_t keep[4];
+  // Copy order: chunk 0's tokens, block 0 of chunks 0 and 1, blocks 1 .. NRB - 1 of chunk 0; then
+  // per chunk c: chunk c + 1's tokens (T copies), block 0 of chunk c + 2 (4), blocks 1 .. NRB - 2
+  // of chunk c + 1 (4 each), the last block of chunk c + 1 (1).  So when a chunk's tokens are
+  // waited for, only the next chunk's block 0 and this chunk's blocks 1 .. NRB - 1 may follow
+  // them: 4 (NRB - 1) + 1; that wait also covers this chunk's block 0 (copied before them).
+  // Block i in 1 .. NRB - 2 is followed by the rest of its chunk's blocks, 4 (NRB - 2 - i) + 1,
+  // then the next tokens, T, block 0 two chunks ahead, 4, and blocks 1 .. i - 1 of the next
+  // chunk, 4 (i - 1): 4 (NRB - 2) + 1 + T in all; the last block by T + 4 (NRB - 1).
+  constexpr int T = kTokLoads<true, false>;
+  constexpr int kTokWait = 4 * (NRB - 1) + 1;
+  constexpr int kMidWait = 4 * (NRB - 2) + 1 + T;
+  constexpr int kLastWait = T + 4 * (NRB - 1);
+  static_assert(kMidWait <= 63 && kLastWait <= 63, "vmcnt range");
+  wide_copy_tok<true, int32_t>(my_tok, keep, a, s_ids, feat(0), lane);
+  asm volatile("" ::: "memory");
+  wide_copy_w(base, a, rw, 0, feat(0), true, lane);
+  asm volatile("" ::: "memory");
+  wide_copy_w(b0_second, a, rw, 0, feat(nch > 1 ? 1 : 0), nch > 1, lane);
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int i = 1; i < NRB - 1; ++i) {
+    wide_copy_w(base + i * kWBlk, a, rw, i, feat(0), true, lane);
+    asm volatile("" ::: "memory");
+  }
+  deep_copy_last(last_slot, a, rw, NRB, feat(0), true, lane);
+  asm volatile("" ::: "memory");
+  const int fl = (lane & 15) * 256;  // this lane's fragment row in a full slot
+  const int lr = (lane & 15) < 3 ? (lane & 15) : 3;  // ... and in the last block's slot
+  for (int c = 0; c < nch; ++c) {
+    const bool live = c + 1 < nch, live2 = c + 2 < nch;
+    const int fc = feat(c);
+    const int fn = feat(live ? c + 1 : c);
+    const int fnn = feat(live2 ? c + 2 : c);
+    u32x4 bt[4][4];
+    // the token copies of chunk c (and block 0 of chunk c) have landed
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTokWait) : "memory");
+    const int cc_cur = fc % a.head_dim + 32 * (lane >> 4);
+    const uint32_t e8m0_shift = uint32_t((cc_cur / a.scale_block) & 3) * 8u;
+    wide_tok_operands(bt, my_tok, keep, lane, a.scale_e8m0, e8m0_shift);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the buffer is read before its refill
+    wide_copy_tok<true, int32_t>(my_tok, keep, a, s_ids, fn, lane);
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      const bool last = i == NRB - 1;
+      char* slot = i == 0 ? ((c & 1) ? b0_second : base) : (last ? last_slot : base + i * kWBlk);
+      if (i > 0) {
+        if (last) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLastWait) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kMidWait) : "memory");
+      }
+      u32x4 wf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        wf[s] = last ? *reinterpret_cast<const u32x4*>(slot + lr * 256 + 16 * ((4 * (lane >> 4) + s) ^ lr))
+                     : *reinterpret_cast<const u32x4*>(slot + fl + 16 * ((4 * (lane >> 4) + s) ^ (lane & 15)));
+      // the slot is read (into registers) before its next copy is issued
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (i == 0) wide_copy_w(slot, a, rw, 0, fnn, live2, lane);
+      else if (last) deep_copy_last(slot, a, rw, NRB, fn, live, lane);
+      else wide_copy_w(slot, a, rw, i, fn, live, lane);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[s], bt[s][t], acc[i][t]);
+      asm volatile("" ::: "memory");
+    }
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
@@ -1040,12 +1151,15 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
 }
 
 // One 64-token block: stage the hash ids, run the K loop, reduce, finish.
-template <int NRB, bool WIDE, int U, bool FUSED, bool W8 = false, bool MX = false, bool APPLY = false>
+template <int NRB, bool WIDE, int U, bool FUSED, bool W8 = false, bool MX = false, bool APPLY = false,
+          bool DEEP = false>
 __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Shared& sh, int64_t tb, int w,
                                             const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t m0 = tb * kTB;
   int64_t* const s_ids = reinterpret_cast<int64_t*>(smem + (WIDE ? wide_lds_bytes(NRB, FUSED, W8) : kRedBytes));
+  // the deep decode loop stages the ids as 32-bit values behind its own layout
+  int32_t* const s_ids32 = reinterpret_cast<int32_t*>(smem + deep_ids_off(NRB));
   // MXFP8 weights: the table of the workgroup's weight scales behind the staged ids, loaded with
   // the first token block (with the hash ids' loads in flight, in the fused kernel)
   char* const stable = reinterpret_cast<char*>(s_ids) + (FUSED ? kTB * a.n_cols * 8 : 0);
@@ -1081,7 +1195,10 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
           if (w == 0 && a.err_count != nullptr) atomicAdd(a.err_count, 1);
           r = -1;
         }
-        if (i < n_ids) s_ids[i] = r;
+        if (i < n_ids) {
+          if constexpr (DEEP) s_ids32[i] = int32_t(r);
+          else s_ids[i] = r;
+        }
       }
     }
     // (the scale table's copies of every wave have landed before the barrier)
@@ -1094,13 +1211,15 @@ __device__ __forceinline__ void token_block(const StreamArgs& a, char* smem, Sha
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, stable, ttable, m0, rw, lane, wv);
+  if constexpr (DEEP) deep_loop<NRB>(acc, a, s_ids32, smem, rw, lane, wv);
+  else if constexpr (WIDE) wide_loop<NRB, FUSED, W8, MX>(acc, a, s_ids, smem, stable, ttable, m0, rw, lane, wv);
   else narrow_loop<NRB, U, FUSED>(acc, a, s_ids, m0, rw, lane, wv);
   // the key columns' epilogue inputs are loaded now, so that their latency hides under the
   // K-partial reduction (loaded before the K loop they slow it down: registers)
   if constexpr (FUSED) prefetch_key<NRB>(kp, a, rw, m0, tid);
   f32x4 red[NRB];
-  static_assert(!WIDE || stage_bytes(NRB) <= wide_lds_bytes(NRB, FUSED, W8), "output staging exceeds the LDS");
+  static_assert(!WIDE || DEEP || stage_bytes(NRB) <= wide_lds_bytes(NRB, FUSED, W8), "output staging exceeds the LDS");
+  static_assert(!DEEP || (APPLY && FUSED && !W8), "the deep loop: fused, bf16 weights, apply workgroups");
   reduce_k<NRB, WIDE>(red, acc, reinterpret_cast<f32x4*>(smem), rw.nblk, lane, wv);
   epilogue<NRB, FUSED, WIDE, APPLY>(a, red, kp, sh, tb, w, rw, tid, smem);
   __syncthreads();
@@ -1234,7 +1353,7 @@ __device__ __forceinline__ void apply_wg(const StreamArgs& a, char* smem, int ap
 // ONE_TB: the call has a single token block.  Without a loop over token blocks the compiler
 // has nothing to hoist above the hash-id loads; with one it computes every loop-invariant
 // address of the K loop and the epilogue first, about 3 us before the first memory access.
-template <int NLO, int NHI, bool FUSED, bool ONE_TB, bool W8, bool MX = false>
+template <int NLO, int NHI, bool FUSED, bool ONE_TB, bool W8, bool MX = false, bool DEEP = false>
 __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   // the epilogue's shared words live behind the reduction buffer, in LDS the K loop no longer uses
@@ -1248,7 +1367,10 @@ __global__ __launch_bounds__(256, 1) void k_stream_wide(StreamArgs a) {
   }
   const Rows rw = rows_of(w, a.N, G);
   if constexpr (ONE_TB) {
-    if constexpr (NLO == NHI) {
+    if constexpr (DEEP) {
+      static_assert(NLO == NHI, "the deep loop: one row-block count");
+      token_block<NLO, true, 1, true, false, false, true, true>(a, smem, sh, 0, w, rw);
+    } else if constexpr (NLO == NHI) {
       token_block<NLO, true, 1, FUSED, W8, MX, FUSED>(a, smem, sh, 0, w, rw);
     } else {
       if (rw.nblk == NLO) token_block<NLO, true, 1, FUSED, W8, MX, FUSED>(a, smem, sh, 0, w, rw);
@@ -1704,6 +1826,23 @@ void* pick_wide_n(bool same, bool one_tb) {
                 : reinterpret_cast<void*>(&k_stream_wide<NLO, NLO + 1, FUSED, false, W8>);
 }
 
+// The deep decode loop: one row-block count NRB, the last block four rows.
+template <int NRB>
+void* pick_deep_n() {
+  return reinterpret_cast<void*>(&k_stream_wide<NRB, NRB, true, true, false, false, true>);
+}
+void* pick_deep(int nrb) {
+  switch (nrb) {
+    case 2: return pick_deep_n<2>();
+    case 3: return pick_deep_n<3>();
+    case 4: return pick_deep_n<4>();
+    case 5: return pick_deep_n<5>();
+    case 6: return pick_deep_n<6>();
+    case 7: return pick_deep_n<7>();
+    default: return nullptr;
+  }
+}
+
 template <bool FUSED, bool W8, bool MX = false>
 void* pick_wide(int nlo, int nhi, bool one_tb) {
   const bool same = nlo == nhi;
@@ -1787,7 +1926,7 @@ template <bool FUSED>
 hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
   void* fn = nullptr;
   const bool wide = use_wide(a, G, FUSED);
-  bool mx = false;
+  bool mx = false, deep = false;
   if (a.w8) {
     // MXFP8 weights: the wide loop only; the fused kernel takes one token block
     if (!wide || (FUSED && a.M > kTB)) return hipErrorInvalidValue;
@@ -1797,6 +1936,13 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
     else fn = pick_wide<FUSED, true>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
   } else if (wide) {
     fn = pick_wide<FUSED, false>(min_blocks(a.N, G), max_blocks(a.N, G), a.M <= kTB);
+    // one token block where every workgroup's rows end in a four-row block: the deep loop
+    const int rows = stream_rows_per_group(a.N, G), nrb = max_blocks(a.N, G);
+    if (FUSED && a.M <= kTB && (a.N / 4) % G == 0 && rows % 16 == 4 && nrb >= 2 && a.n_rows <= 0x7FFFFFFF &&
+        size_t(deep_lds_bytes(nrb, a.n_cols)) <= 163840 && pick_deep(nrb) != nullptr) {
+      fn = pick_deep(nrb);
+      deep = true;
+    }
   } else {
     const int per_wg = max_blocks(a.N, G);
     const int nstep = (a.K / 4) / 32;
@@ -1819,7 +1965,11 @@ hipError_t launch_stream_impl(const StreamArgs& a, int G, hipStream_t stream) {
     arg.n_atb = 1;
   }
   void* params[] = {&arg};
-  const size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
+  size_t lds = stream_lds(a.N, a.K, a.n_cols, a.head_dim, a.scale_block, G, FUSED, wide, a.w8 != 0, mx);
+  if (deep) {
+    lds = size_t(deep_lds_bytes(max_blocks(a.N, G), a.n_cols));
+    if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
+  }
   const hipError_t e = allow_lds(fn, lds);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(fn, dim3(G + arg.n_apply), dim3(256), params, lds, stream);
