@@ -76,9 +76,18 @@ bool tb2_layout(const engram_layout* l, int cus) {
          stream_tb2_ok(int(K_of(l)), N, l->dim, l->n_cols, l->head_dim, l->scale_block, cus);
 }
 bool use_tb2(const engram_layout* l, int64_t M, int cus) { return M > 64 && M <= 128 && tb2_layout(l, cus); }
+// The layout admits the four-token-block kernel (bf16 weights, every workgroup the same number
+// of row blocks, workgroups spanning at most two streams), which then takes every forward of
+// 129..256 tokens from rows gathered into the staging area.
+bool tb4_layout(const engram_layout* l, int cus) {
+  const int N = int(N_of(l));
+  return !wkv_mxfp8(l) && stream_rows_per_group(N, stream_grid(N, cus)) <= l->dim &&
+         stream_tb4_ok(int(K_of(l)), N, l->dim, cus);
+}
+bool use_tb4(const engram_layout* l, int64_t M, int cus) { return M > 128 && M <= 256 && tb4_layout(l, cus); }
 // the tiled schedule for the whole forward
 bool use_tiled_fused(const engram_layout* l, int64_t M, int cus) {
-  return use_tiled(l, M, true) && !use_tb2(l, M, cus);
+  return use_tiled(l, M, true) && !use_tb2(l, M, cus) && !use_tb4(l, M, cus);
 }
 
 // The fused weight-streaming kernel reads MXFP8 weights itself for one token block; every other
@@ -98,10 +107,11 @@ bool forward_w8_native(const engram_layout* l, int64_t M, int cus) {
 // call leaves behind never sit where a later call expects zeros.
 size_t forward_control(const engram_layout* l, int64_t M, int cus) {
   const int N = int(N_of(l));
-  // token counts the streaming schedules take: up to the tiled threshold (128 tokens where the
-  // two-token-block kernel fits the layout), or all of them when the layout has no tiled schedule
+  // token counts the streaming schedules take: up to the tiled threshold (256 tokens where the
+  // four-token-block kernel fits the layout, 128 where the two-token-block one does), or all of
+  // them when the layout has no tiled schedule
   const bool tiled_layout = tiled_shape_ok(N, int(K_of(l)), l->dim, true);
-  const int64_t cap = tb2_layout(l, cus) ? 128 : kTiledMinTokensFused - 1;
+  const int64_t cap = tb4_layout(l, cus) ? 256 : tb2_layout(l, cus) ? 128 : kTiledMinTokensFused - 1;
   const int64_t Ms = tiled_layout && M > cap ? cap : M;
   size_t c = stream_workspace_bytes(Ms, N, l->dim, stream_grid(N, cus));
   if (use_tiled_fused(l, M, cus)) {
@@ -124,6 +134,8 @@ bool forward_tiled_mx(const engram_layout* l, int64_t M) {
 // kernel up to 64 tokens, the fp8 tiled kernel above, both with an MXFP8 table; with fp32 table
 // scales only the former).
 size_t forward_staging_tiled(const engram_layout* l, int64_t M, int cus) {
+  // the four-token-block kernel's tokens: bf16, M rounded up to 16 (its operand order)
+  if (use_tb4(l, M, cus)) return (size_t((M + 15) & ~int64_t(15)) * size_t(K_of(l)) * 2 + 255) & ~size_t(255);
   if (!use_tiled_fused(l, M, cus)) return 0;
   const size_t b = forward_tiled_mx(l, M) ? tiled_staging_bytes_mx(M, int(K_of(l)), int(N_of(l)))
                                           : tiled_staging_bytes(M, int(K_of(l)), int(N_of(l)));
@@ -540,9 +552,23 @@ engram_status engram_forward(const engram_layout* l, const uint16_t* x, const in
   a.clamp = l->clamp;
   a.inv_sqrt_dim = float(1.0 / sqrt(double(l->dim)));
   a.spin_budget = g_spin_budget.load(std::memory_order_relaxed);
-  const hipError_t e = use_tb2(l, M, di.cus)
-                          ? launch_forward_tb2(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream))
-                          : launch_forward_stream(a, workspace, di.cus, reinterpret_cast<hipStream_t>(stream));
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (use_tb4(l, M, di.cus)) {
+    // the rows gathered and dequantised into the staging area (in the MFMA operand order), then
+    // one pass over the weights
+    uint16_t* emb = reinterpret_cast<uint16_t*>(stg_start);
+    GatherArgs g{table, scales, hash_ids, M * l->n_cols, l->head_dim, l->scale_block,
+                 l->scale_format == ENGRAM_SCALE_E8M0, l->n_rows, emb, err_count, l->n_cols,
+                 ((M + 15) & ~int64_t(15)) * l->n_cols};
+    e = launch_gather_dequant(g, hs);
+    a.emb = emb;
+    if (e == hipSuccess) e = launch_forward_tb4(a, workspace, di.cus, hs);
+  } else if (use_tb2(l, M, di.cus)) {
+    e = launch_forward_tb2(a, workspace, di.cus, hs);
+  } else {
+    e = launch_forward_stream(a, workspace, di.cus, hs);
+  }
   return e == hipSuccess ? ENGRAM_OK : ENGRAM_E_HIP;
 }
 

@@ -15,15 +15,29 @@ __global__ __launch_bounds__(256) void k_gather_dequant(GatherArgs a) {
   const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t pair = gid / chunks;  // flat (token, column) index m * n_cols + j
   const int ch = int(gid - pair * chunks);
-  if (pair >= a.n_pairs) return;
-  const int64_t r = a.hash_ids[pair];
+  const bool fill = a.frag_cols > 0 && pair >= a.n_pairs;  // a zero row past the last token
+  if (pair >= a.n_pairs && !(fill && pair < a.n_fill)) return;
+  const int64_t r = fill ? -1 : a.hash_ids[pair];
   u32x4 o0 = {0u, 0u, 0u, 0u}, o1 = {0u, 0u, 0u, 0u};
-  if (r >= 0 && r < a.n_rows) {
+  if (fill) {
+  } else if (r >= 0 && r < a.n_rows) {
     const u32x4 c = *reinterpret_cast<const u32x4*>(a.table + r * a.head_dim + ch * 16);
     const float s = load_scale(a.scales, r * nb + (ch * 16) / a.scale_block, a.scale_e8m0);
     dequant16(c, s, o0, o1);
   } else if (ch == 0 && a.err_count != nullptr) {
     atomicAdd(a.err_count, 1);
+  }
+  if (a.frag_cols > 0) {
+    // features f .. f + 15 of token m: two 8-feature pieces, each lane (m % 16) + 16 q of the
+    // 1 KB block (m / 16, f / 32), q = (f / 8) % 4
+    const int64_t m = pair / a.frag_cols;
+    const int64_t f = (pair - m * a.frag_cols) * a.head_dim + ch * 16;
+    const int64_t k32 = int64_t(a.frag_cols) * a.head_dim / 32;
+    u32x4* const blk = reinterpret_cast<u32x4*>(a.emb) + ((m >> 4) * k32 + (f >> 5)) * 64 + (m & 15);
+    const int q = int(f >> 3) & 3;
+    blk[16 * q] = o0;
+    blk[16 * (q + 1)] = o1;
+    return;
   }
   u32x4* dst = reinterpret_cast<u32x4*>(a.emb + pair * a.head_dim + ch * 16);
   dst[0] = o0;
@@ -194,7 +208,8 @@ hipError_t launch_expand_mxfp8(const uint8_t* codes, const uint8_t* scales, int6
 }
 
 hipError_t launch_gather_dequant(const GatherArgs& a, hipStream_t stream) {
-  const int64_t threads = a.n_pairs * (a.head_dim >> 4);
+  const int64_t pairs = a.frag_cols > 0 && a.n_fill > a.n_pairs ? a.n_fill : a.n_pairs;
+  const int64_t threads = pairs * (a.head_dim >> 4);
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL(k_gather_dequant, dim3(unsigned(blocks)), dim3(256), 0, stream, a);
   return hipGetLastError();

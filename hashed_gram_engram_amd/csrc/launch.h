@@ -18,6 +18,11 @@ struct GatherArgs {
   int64_t n_rows;
   uint16_t* emb;
   int32_t* err_count;
+  // frag_cols > 0: emb in the 16 x 16 x 32 MFMA operand order of a table of frag_cols columns
+  // (1 KB per 16 tokens x 32 features: lane l's 16 bytes, token l % 16, features 8 (l / 16) ..),
+  // and the rows of the pairs n_pairs .. n_fill - 1 written as zeros
+  int frag_cols;
+  int64_t n_fill;
 };
 
 struct GateArgs {
@@ -105,6 +110,11 @@ hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hip
 // 65..128 tokens in one pass over bf16 weights (workspace as the streaming kernel's, two blocks)
 bool stream_tb2_ok(int K, int N, int dim, int n_cols, int head_dim, int scale_block, int num_cus);
 hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
+// 129..256 tokens in one pass over bf16 weights, from tokens gathered into a.emb beforehand
+// (bf16 in the MFMA operand order, GatherArgs::frag_cols; workspace as the streaming kernel's, up
+// to four blocks)
+bool stream_tb4_ok(int K, int N, int dim, int num_cus);
+hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStream_t stream);
 // Whether the weight-streaming kernels take MXFP8 weights for this shape (the wide K loop:
 // K / 4 a multiple of 128, 1..7 row blocks per workgroup; fused: head_dim a multiple of 128 and
 // scale_block of 32).  The fused kernel takes them for one token block (M <= 64).

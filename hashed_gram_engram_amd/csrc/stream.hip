@@ -736,6 +736,7 @@ struct Shared {
   float red[4][kTB][3];
   int last[2];
   int last2[2][2];  // the two-token-block kernel: last-arriver marks per (token block, stream slot)
+  int last4[4][2];  // ... and the four-token-block kernel's
 };
 
 // The gate of token t from the four quarter sums in sh.red[q][t] (|h|^2, |key|^2, h q k key),
@@ -1800,6 +1801,257 @@ __global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------ four token blocks
+// The fused forward of 129..256 tokens in one pass over the weights, from the tokens gathered
+// and dequantised beforehand (bf16, in the MFMA's operand order, in the staging area).  One workgroup per CU over
+// its NRB row blocks, eight waves in two roles.  Waves 4..7 copy the workgroup's weight rows
+// into a ring of D stages of 64 features (NRB 2 KB slots each, the two-token-block kernel's
+// slot layout) and wait only for their own copies; waves 0..3 each multiply one 64-token block
+// over all of K, their token fragments loaded from the staging area (an L2-resident 3 MB at 256
+// tokens) straight into registers kTb4Tok stages ahead.  A wave's memory counter thus covers
+// one kind of access: the copies keep D - 1 stages (NRB x 2 KB each) in flight, independently
+// of the token loads.  One workgroup barrier per stage: the copy waves reach it once the stage
+// has landed, the multiplying waves once they have read the stage before it, whose slot the
+// copies issued after the barrier refill.  Then the copy waves leave (a barrier waits only for
+// the waves still running), and the four blocks' sums take the two-token-block kernel's
+// hand-off: key partial sums stored, counted in with one round of atomics, the last arrivers'
+// gates, the value workgroups' bf16 tiles for the apply workgroups.
+constexpr int kTb4Tok = 2;  // stages of token fragments in flight per multiplying wave
+__host__ __device__ constexpr int tb4_ring(int nrb) { return 163840 / (nrb * kW2Slot) < 12 ? 163840 / (nrb * kW2Slot) : 12; }
+// after the loop: the four blocks' sums (NRB x 16 KB) behind the epilogue's shared words, where
+// they stay while the epilogue runs
+constexpr int kTb4X = (kRedBytes + int(sizeof(Shared)) + 4095) & ~4095;
+__host__ __device__ constexpr int tb4_lds(int nrb) {
+  return tb4_ring(nrb) * nrb * kW2Slot > kTb4X + nrb * 16384 ? tb4_ring(nrb) * nrb * kW2Slot : kTb4X + nrb * 16384;
+}
+
+// Copy wave PI: the stage's copies j = PI, PI + 4, .. below 2 NRB (row block j / 2, rows 8 (j %
+// 2) .. + 7: NP of them), through a buffer resource on wkv as in the two-token-block kernel.  Stages
+// past the last one copy cache-resident rows at feature 0 into the free slot instead, so that
+// the count of copies per stage, and with it the wait before each barrier, stays fixed.
+template <int NRB, int PI>
+__device__ __forceinline__ void tb4_produce(const StreamArgs& a, char* smem, const Rows& rw, int lane, int nst,
+                                            int rot) {
+  constexpr int D = tb4_ring(NRB);
+  constexpr int kStage = NRB * kW2Slot;
+  constexpr int NP = (2 * NRB - PI + 3) / 4;
+  static_assert(D >= 3 && (D - 1) * NP <= 63, "copies in flight within the counter's range");
+  const __amdgpu_buffer_rsrc_t wsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.wkv), (short)0, a.N * a.K * 2, 0x00020000);
+  Tb2WOff wo;
+  tb2_woff(wo, a, rw, lane);
+  // (the copy index is a constant in every copy, so that each offset stays in a register)
+  auto issue = [&](int c, char* slot) {
+    const bool live = c < nst;
+    const int soff = live ? 2 * kC2 * ((c + rot) % nst) : 0;
+#pragma unroll
+    for (int k = 0; k < NP; ++k) {
+      const int j = PI + 4 * k, i = j >> 1, h = j & 1;
+      const uint32_t o = live ? tb2_wo(wo, i, h) : wo.dummy[h];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(slot + i * kW2Slot + h * 1024), 16, o, soff, 0, 2);
+    }
+    asm volatile("" ::: "memory");
+  };
+#pragma unroll 1
+  for (int c = 0; c < D - 1; ++c) issue(c, smem + c * kStage);
+  char* nslot = smem + (D - 1) * kStage;  // the slot of stage c + D - 1
+#pragma unroll 1
+  for (int c = 0; c < nst; ++c) {
+    // stage c has landed once only the D - 2 stages after it remain
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((D - 2) * NP) : "memory");
+    issue(c + D - 1, nslot);
+    nslot = nslot + kStage == smem + D * kStage ? smem : nslot + kStage;
+  }
+  // every copy has landed before the multiplying waves reuse the LDS
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Multiplying wave cb: token block cb over all of K, stage by stage from the ring.  The tokens
+// are staged in the MFMA's operand order (1 KB per 16 tokens x 32 features, lane l's 16 bytes at
+// 16 l: token l % 16, features 8 (l / 16) ..), so that every load reads 1 KB in one run; the rows
+// past the last token up to a multiple of 16 are staged as zeros, the sub-blocks after them read
+// as zeros through the buffer resource's range.
+template <int NRB>
+__device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][4], const StreamArgs& a, const char* smem, int lane,
+                                            int cb, int nst, int rot) {
+  constexpr int D = tb4_ring(NRB);
+  constexpr int kStage = NRB * kW2Slot;
+  constexpr int P = kTb4Tok;
+  const __amdgpu_buffer_rsrc_t tsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(a.emb), (short)0, int((a.M + 15) & ~int64_t(15)) * a.K * 2, 0x00020000);
+  // sub-block t's 1 KB blocks: (4 cb + t) x K / 32 + k32
+  uint32_t vo[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) vo[t] = uint32_t(4 * cb + t) * uint32_t(a.K / 32) * 1024u + 16u * uint32_t(lane);
+  u32x4 tk[P][2][4];
+  auto load = [&](u32x4 (&dst)[2][4], int c) {
+    const uint32_t fb = 2048u * uint32_t((c < nst ? c + rot : rot) % nst);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dst[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tsrc, vo[t] + fb + 1024u * s, 0, 0));
+  };
+  // (in stage order, as the loop issues them: otherwise the loads pending at the top of the loop
+  // differ in order between its entry and its back edge, and the compiler waits for all of them)
+#pragma unroll
+  for (int r = 0; r < P; ++r) {
+    load(tk[r], r);
+    asm volatile("" ::: "memory");
+  }
+  const int wr = lane & 15;
+  const char* slot = smem;
+  auto stage = [&](int c, auto reg_tag) {
+    constexpr int r = decltype(reg_tag)::value;
+    // stage c has landed; this wave's reads of stage c - 1 are done
+    lds_barrier();
+    // row block i + 1's fragments are read while block i's MFMAs run
+    u32x4 wf[2][2];
+    auto read_wf = [&](u32x4 (&f)[2], int i) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        f[s] = *reinterpret_cast<const u32x4*>(slot + i * kW2Slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
+    };
+    read_wf(wf[0], 0);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      if (i + 1 < NRB) read_wf(wf[(i + 1) & 1], i + 1);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[i & 1][s], tk[r][s][t], acc[i][t]);
+    }
+    load(tk[r], c + P);
+    slot = slot + kStage == smem + D * kStage ? smem : slot + kStage;
+  };
+  // (nst is even, so that every pass through the loop takes both halves: with a branch around
+  // the second half the compiler would wait for every token load at the top of the loop)
+  static_assert(P == 2, "the stage body is unrolled by two");
+  for (int c = 0; c < nst; c += 2) {
+    stage(c, std::integral_constant<int, 0>{});
+    stage(c + 1, std::integral_constant<int, 1>{});
+  }
+  // the copy waves' last copies have landed
+  lds_barrier();
+}
+
+template <int NRB>
+__device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw,
+                                           f32x4 (&acc)[NRB][4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n_tb = int((a.M + kTB - 1) / kTB);
+  // wave c holds all of K for token block c; read back, wave wv holds token sub-block wv of a
+  // block, as after the K-partial reduction of the other kernels
+  f32x4* const X = reinterpret_cast<f32x4*>(smem + kTb4X);
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) X[((wv * NRB + i) * 4 + t) * 64 + lane] = acc[i][t];
+  lds_barrier();
+  auto red_of = [&](f32x4 (&r)[NRB], int b) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) r[i] = X[((b * NRB + i) * 4 + wv) * 64 + lane];
+  };
+  // the key columns' partial sums of every block (the next block's inputs loaded under the
+  // current block's stores)
+  KeyPre<NRB> kp[2];
+  prefetch_key<NRB>(kp[0], a, rw, 0, tid);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b < n_tb) {
+      if (b + 1 < n_tb) prefetch_key<NRB>(kp[(b + 1) & 1], a, rw, int64_t(b + 1) * kTB, tid);
+      f32x4 red[NRB];
+      red_of(red, b);
+      epilogue<NRB, true, true, false, kPhStore>(a, red, kp[b & 1], sh, b, w, rw, tid, smem);
+    }
+  }
+  // counted in for every block with one drain and one round of atomics
+  {
+    const int seg_lo = rw.r0 / a.dim, seg_hi = (rw.r1 - 1) / a.dim;
+    drain_memory_ops();
+    __syncthreads();
+    if (tid == 0) {
+      const int Q = a.N >> 2, G = a.G;
+      uint32_t old[4][2];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int s = seg_lo + sl;
+          old[b][sl] = b < n_tb && s <= seg_hi && s < 4 ? atomic_add_relaxed(counter_of(a, b, s), 1u) : 0u;
+        }
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) {
+          const int s = seg_lo + sl;
+          const int s3 = s < 4 ? s : 3;
+          const int wf = owner_of_row(s3 * a.dim, Q, G), wl = owner_of_row((s3 + 1) * a.dim - 1, Q, G);
+          sh.last4[b][sl] = b < n_tb && s <= seg_hi && s < 4 && old[b][sl] == uint32_t(wl - wf) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+  }
+  // the last arrivers' gates, block by block
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b < n_tb && (sh.last4[b][0] | sh.last4[b][1]) != 0) {
+      if (tid == 0) {
+        sh.last[0] = sh.last4[b][0];
+        sh.last[1] = sh.last4[b][1];
+      }
+      __syncthreads();
+      f32x4 red[NRB];
+      red_of(red, b);
+      epilogue<NRB, true, true, true, kPhGates>(a, red, kp[0], sh, b, w, rw, tid, smem);
+      __syncthreads();
+    }
+  }
+  // the value columns: each block's bf16 values into this workgroup's tile for that block
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (b < n_tb) {
+      f32x4 red[NRB];
+      red_of(red, b);
+      epilogue<NRB, true, true, true, kPhValue>(a, red, kp[0], sh, b, w, rw, tid, smem);
+    }
+  }
+}
+
+template <int NRB>
+__global__ __launch_bounds__(512, 1) void k_stream_tb4(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
+  const int G = a.G, w = blockIdx.x;
+  // (the wave index as a scalar: a role is taken by whole waves, and the copies' LDS addresses
+  // and feature offsets are scalars)
+  const int wv = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & 63;
+  if (w >= G) {
+    // apply workgroups: four waves, as in the other fused kernels; the rest leave at once
+    if (wv < 4) apply_wg(a, smem, w - G);
+    return;
+  }
+  const Rows rw = rows_of(w, a.N, G);
+  const int nst = a.K / kC2;
+  const int rot = int((5u * uint32_t(w)) % uint32_t(nst));
+  if (wv >= 4) {
+    const int p = wv - 4;
+    if (p == 0) tb4_produce<NRB, 0>(a, smem, rw, lane, nst, rot);
+    else if (p == 1) tb4_produce<NRB, 1>(a, smem, rw, lane, nst, rot);
+    else if (p == 2) tb4_produce<NRB, 2>(a, smem, rw, lane, nst, rot);
+    else tb4_produce<NRB, 3>(a, smem, rw, lane, nst, rot);
+    return;
+  }
+  f32x4 acc[NRB][4];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  tb4_consume<NRB>(acc, a, smem, lane, wv, nst, rot);
+  tb4_blocks<NRB>(a, smem, sh, w, rw, acc);
+}
+
 template <bool FUSED, int NRB>
 void* pick_narrow(int nstep) {
   if (nstep % 3 == 0) return reinterpret_cast<void*>(&k_stream_narrow<NRB, 3, FUSED>);
@@ -2027,13 +2279,13 @@ size_t stream_tb_stride(int grid) {
   return size_t(256) * 4 + size_t(grid) * 4 * kTB * 4 + size_t(grid) * 2 * kTB * 16;
 }
 
-// The fused forward of one or two token blocks also needs the blocks' value tiles behind their
+// The fused forward of one to four token blocks also needs the blocks' value tiles behind their
 // control words (cleared again by the apply workgroups); the larger of the two layouts, so that
 // the size never decreases with M.
 size_t stream_workspace_bytes(int64_t M, int N, int dim, int grid) {
   const int64_t n_tb = (M + kTB - 1) / kTB;
   const size_t blocks = size_t(n_tb) * stream_tb_stride(grid);
-  const int64_t n_atb = n_tb < 2 ? 1 : 2;
+  const int64_t n_atb = n_tb < 4 ? (n_tb < 1 ? 1 : n_tb) : 4;
   const size_t tiled = size_t(n_atb) * (stream_tb_stride(grid) + size_t(value_groups(N, dim, grid)) * kVTile);
   return 256 + (blocks > tiled ? blocks : tiled);
 }
@@ -2075,6 +2327,48 @@ hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStr
   if (e != hipSuccess) return e;
   void* params[] = {&a};
   return hipLaunchKernel(fn, dim3(G + a.n_apply), dim3(256), params, lds, stream);
+}
+
+// The four-token-block kernel (129..256 tokens from staged bf16 rows): every workgroup owns the
+// same number of row blocks, at most seven; an even number of 64-feature stages; bf16 weights and staged tokens of
+// at most 2^31 - 1 bytes each (read through buffer resources); the apply workgroups' slots within
+// each token block's gate-slot region.
+bool stream_tb4_ok(int K, int N, int dim, int num_cus) {
+  const int G = stream_grid(N, num_cus);
+  const int lo = min_blocks(N, G), hi = max_blocks(N, G);
+  const int V = value_groups(N, dim, G);
+  return (N / 4) % G == 0 && K % (2 * kC2) == 0 && lo == hi && hi >= 1 && hi <= 7 && tb4_lds(hi) <= 163840 &&
+         int64_t(N) * K * 2 <= 0x7FFFFFFF && int64_t(4 * kTB) * K * 2 <= 0x7FFFFFFF && V >= 1 &&
+         2 * V * 160 <= G * 256;
+}
+
+hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
+  if (a.M <= 2 * kTB || a.M > 4 * kTB || a.w8 || a.emb == nullptr || !stream_tb4_ok(a.K, a.N, a.dim, num_cus))
+    return hipErrorInvalidValue;
+  const int G = stream_grid(a.N, num_cus);
+  a.ws_hdr = static_cast<uint32_t*>(workspace);
+  a.tb_stride = stream_tb_stride(G);
+  a.G = G;
+  // two apply workgroups per value workgroup and token block
+  a.n_atb = int((a.M + kTB - 1) / kTB);
+  a.n_apply = 2 * a.n_atb * value_groups(a.N, a.dim, G);
+  void* fn = nullptr;
+  switch (max_blocks(a.N, G)) {
+    case 1: fn = reinterpret_cast<void*>(&k_stream_tb4<1>); break;
+    case 2: fn = reinterpret_cast<void*>(&k_stream_tb4<2>); break;
+    case 3: fn = reinterpret_cast<void*>(&k_stream_tb4<3>); break;
+    case 4: fn = reinterpret_cast<void*>(&k_stream_tb4<4>); break;
+    case 5: fn = reinterpret_cast<void*>(&k_stream_tb4<5>); break;
+    case 6: fn = reinterpret_cast<void*>(&k_stream_tb4<6>); break;
+    case 7: fn = reinterpret_cast<void*>(&k_stream_tb4<7>); break;
+    default: return hipErrorInvalidValue;
+  }
+  size_t lds = size_t(tb4_lds(max_blocks(a.N, G)));
+  if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
+  const hipError_t e = allow_lds(fn, lds);
+  if (e != hipSuccess) return e;
+  void* params[] = {&a};
+  return hipLaunchKernel(fn, dim3(G + a.n_apply), dim3(512), params, lds, stream);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {

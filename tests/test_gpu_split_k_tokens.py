@@ -1,14 +1,13 @@
-"""Split K in the tiled schedule, against the CPU oracle: with at most 128 tiles of 256 x 256 every
-tile is computed by two workgroups, each over half of K (the second adds the first one's fp32
-partial tile); with more tiles, the tiles of a last, partial round of the grid (tiles mod the
-CU count, when at most 128) are split the same way.
+"""Token counts above one token block against the CPU oracle, on the schedules that take them.
 
-The decode layout at 129..256 tokens: 256 (one full tile row), 193 (a last 64-token block of one
-token), 150; skewed ids, closed tokens, outlier streams, out-of-range ids, in-place output.  The
-same checks at 65 and 128 tokens, which the two-token-block weight-streaming kernel takes on this
-layout.  Tiny dims at 13,300 tokens: 260 tiles, the last 4 (value tiles of the last four token
-blocks, the ragged one among them) split, every token checked.  Every result is also checked
-for run-to-run identity, control words left zero and no timed-out wait.
+The decode layout at 129..256 tokens: 256, 193 (a last 64-token block of one token), 150, which the
+four-token-block weight-streaming kernel takes on this layout; skewed ids, closed tokens, outlier
+streams, out-of-range ids, in-place output.  The same checks at 65 and 128 tokens (the
+two-token-block kernel).  Split K in the tiled schedule at tiny dims and 13,300 tokens: 260 tiles
+of 256 x 256, the last 4 (tiles mod the CU count; value tiles of the last four token blocks, the
+ragged one among them) computed by two workgroups each over half of K (the second adds the
+first one's fp32 partial tile), every token checked.  Every result is also checked for
+run-to-run identity, control words left zero and no timed-out wait.
 """
 import numpy as np
 import pytest
