@@ -52,6 +52,7 @@ def algorithmic_flops(w) -> int:
 
 TILED_MIN_TOKENS = 65  # the whole forward switches from weight streaming to 256 x 256 tiles here,
 TB2_MAX_TOKENS = 128   # except up to here with bf16 weights (the two-token-block streaming kernel)
+TB4_MAX_TOKENS = 256   # and up to here where the layout admits the four-token-block kernel
 
 
 def fp8_mfma(w) -> bool:
@@ -59,12 +60,29 @@ def fp8_mfma(w) -> bool:
     return w.wkv_format == "mxfp8" and w.scale_format == "e8m0" and w.scale_block % 32 == 0
 
 
+def tb4_layout(w, cus: int = 256) -> bool:
+    """Whether the library's four-token-block kernel takes this layout (bf16 weights, every
+    workgroup of the weight-streaming grid owning the same whole number of at most seven 16-row
+    blocks, K a multiple of 128), as the library decides it on a GPU of `cus` compute units."""
+    N = (w.hc + 1) * w.dim
+    q = N // 4
+    G = min(cus, q)
+    blocks = lambda g: (4 * ((q + g - 1) // g) + 15) // 16
+    while blocks(G) > 8:
+        G += 1
+    rows = 4 * ((q + G - 1) // G)
+    return (w.wkv_format != "mxfp8" and q % G == 0 and w.K % 128 == 0 and rows <= w.dim and 1 <= blocks(G) <= 7)
+
+
 def kernel_of(w):
     """(profile name, sources) of the kernels that engram_forward runs for this workload: the
-    fused weight-streaming kernel for small token counts; for large ones the row gather into the
-    staging area followed by the fused tiled kernel (timed together: one forward)."""
+    fused weight-streaming kernels for up to 256 tokens (above 128 the row gather into the
+    staging area first, timed with it as one forward); for more, the row gather followed by the
+    fused tiled kernel (one forward)."""
     if TILED_MIN_TOKENS <= w.M <= TB2_MAX_TOKENS and w.wkv_format != "mxfp8":
         return "k_stream_tb2", ("stream.hip", "common.h")
+    if TB2_MAX_TOKENS < w.M <= TB4_MAX_TOKENS and tb4_layout(w):
+        return "k_stream_tb4", ("stream.hip", "gather_gate.hip", "common.h")
     if w.M >= TILED_MIN_TOKENS:
         return ("k_tiled_mx_fused" if fp8_mfma(w) else "k_tiled_fused"), ("tiled.hip", "gather_gate.hip", "common.h")
     return "k_stream_wide_fused", ("stream.hip", "common.h")
@@ -73,7 +91,8 @@ def kernel_of(w):
 KERNEL_LABEL = {"k_tiled_fused": "k_gather_dequant + k_tiled<true> (one forward)",
                 "k_tiled_mx_fused": "k_gather_mx + k_tiled<true, true> (fp8 operands; one forward)",
                 "k_stream_wide_fused": "k_stream_wide<.., true>",
-                "k_stream_tb2": "k_stream_tb2 (two token blocks per pass over wkv)"}
+                "k_stream_tb2": "k_stream_tb2 (two token blocks per pass over wkv)",
+                "k_stream_tb4": "k_gather_dequant + k_stream_tb4 (four token blocks per pass over wkv; one forward)"}
 
 
 def kernel_label(w) -> str:

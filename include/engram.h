@@ -88,9 +88,10 @@ engram_status engram_param_counts(const engram_layout* layout, int64_t out[3]);
 
 /* Bytes of workspace engram_forward needs for B x T tokens on the current device (0 on an
  * invalid layout).  The workspace holds control words at its start (counters, gate slots,
- * partial sums and, for up to two 64-token blocks, the bf16 value tiles that the weight-streaming
- * kernels hand to their apply workgroups) and, for token counts where the tiled schedule runs, a staging area for the
- * dequantised rows in its last engram_forward_staging_bytes() bytes.  It must be zero-filled
+ * partial sums and, for up to four 64-token blocks, the bf16 value tiles that the weight-streaming
+ * kernels hand to their apply workgroups) and, for token counts where the tiled schedule or the
+ * four-token-block streaming kernel runs, a staging area for the dequantised rows in its last
+ * engram_forward_staging_bytes() bytes.  It must be zero-filled
  * before its first use.  Every call leaves all control words zero again; the staging area's
  * contents are unspecified after a call.  So one workspace serves any number of calls with one
  * layout and any B x T it is large enough for, on one stream without clearing, provided every

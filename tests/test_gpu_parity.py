@@ -466,11 +466,11 @@ def test_workspace_sizes_never_decrease_with_token_count():
 
 
 def test_binding_workspace_shared_by_two_layouts():
-    say("[gpu] the binding's workspace across layouts: a tiled call (staging at the end) "
-        "then three streamed token blocks of another layout (control words over that staging)")
-    # (five token blocks: their control words reach past the tiled call's control part, which
-    # holds the streaming schedules' words up to 128 tokens, value tiles included)
-    a, b = E8M0_TILED, synth.small_variant(STREAM_ONLY, name="dim320_b2_t150", T=150)
+    say("[gpu] the binding's workspace across layouts: a four-token-block call (staged rows at the "
+        "end) then streamed token blocks of another layout (control words over that staging)")
+    # (five token blocks: their control words reach past the first call's control part, which
+    # holds the streaming schedules' words up to 256 tokens, value tiles included)
+    a, b = E8M0_TB4, synth.small_variant(STREAM_ONLY, name="dim320_b2_t150", T=150)
     assert (eg.engram_forward_workspace_bytes(layout(b), b.B, b.T) >
             eg.engram_forward_workspace_bytes(layout(a), a.B, a.T) - eg.engram_forward_staging_bytes(layout(a), a.B, a.T))
     da, db = synth.device_inputs(a), synth.device_inputs(b)
@@ -487,8 +487,8 @@ def test_binding_workspace_shared_by_two_layouts():
 
 # ---------------------------------------------------------------------------- E8M0 scales
 # MXFP8 tables (E8M0 block scales): the decode layout with one scale per 32 features (the
-# pages' format; weight streaming, the two-token-block kernel at 100 tokens and the tiled
-# schedule at 150), one per 64 features (a scale's byte position in its dword changes from chunk
+# pages' format; weight streaming, the two-token-block kernel at 100 tokens and the
+# four-token-block kernel at 150), one per 64 features (a scale's byte position in its dword changes from chunk
 # to chunk; also at 100 tokens), and tiny dims with 16 features per scale (the narrow streaming
 # loop).  Exponents 120..124 (scales 2^-7 .. 2^-3, the
 # magnitude of the fp32 workloads' scales); the gather test covers all 256 exponents.
@@ -501,7 +501,7 @@ E8M0_TB2 = synth.small_variant(E8M0_DECODE, name="decode_dims_e8m0_t100", B=1, T
                                seed=DECODE.seed + 402)
 E8M0_TB2_64 = synth.small_variant(E8M0_DECODE64, name="decode_dims_e8m0_sb64_t100", B=1, T=100,
                                   seed=DECODE.seed + 404)
-E8M0_TILED = synth.small_variant(E8M0_DECODE, name="decode_dims_e8m0_t150", B=1, T=150,
+E8M0_TB4 = synth.small_variant(E8M0_DECODE, name="decode_dims_e8m0_t150", B=1, T=150,
                                  seed=DECODE.seed + 405)
 E8M0_TINY = synth.small_variant(TINY, name="tiny_e8m0_sb16", scale_block=16, scale_format="e8m0",
                                 seed=TINY.seed + 403)
@@ -538,7 +538,7 @@ def test_device_fill_e8m0_matches_host_generator():
     assert np.array_equal(d["scales"].cpu().numpy(), w.scales_rows(np.arange(w.n_rows)))
 
 
-@pytest.mark.parametrize("w", [E8M0_DECODE, E8M0_DECODE64, E8M0_TB2, E8M0_TB2_64, E8M0_TILED, E8M0_TINY],
+@pytest.mark.parametrize("w", [E8M0_DECODE, E8M0_DECODE64, E8M0_TB2, E8M0_TB2_64, E8M0_TB4, E8M0_TINY],
                          ids=lambda w: w.name)
 def test_forward_e8m0(w):
     say(f"[gpu] forward with E8M0 scales: {w.name} (B={w.B} T={w.T}, scale_block {w.scale_block})")

@@ -4,9 +4,9 @@ The host sets a tiny wait bound (engram_set_spin_budget), so the fused schedules
 while every kernel still runs to its end; engram_forward_check must then report
 ENGRAM_E_TIMEOUT and leave the workspace zero-filled, and the next call with the default bound
 must give the same bits as a call before the time-outs.  Covered: the weight-streaming schedule
-(gates handed to the apply workgroups), the two-token-block kernel at 100 tokens (gates of two
-blocks handed to the value workgroups) and the tiled schedule with split K at 150 tokens
-(partial tiles and gates handed between workgroups)."""
+(gates handed to the apply workgroups), the two-token-block kernel at 100 tokens and the
+four-token-block kernel at 150 tokens (gates and value tiles of two and three blocks handed to
+the apply workgroups), and the tiled schedule at 300 tokens (gates handed between tiles)."""
 import numpy as np
 import pytest
 
@@ -19,7 +19,8 @@ from gpu_common import eg, forward, layout, say  # noqa: E402
 DECODE = synth.workloads()["decode_b64"]
 CASES = [synth.small_variant(DECODE, name="decode_dims_b64", B=64, T=1),
          synth.small_variant(DECODE, name="decode_dims_b1_t100", B=1, T=100, seed=DECODE.seed + 300),
-         synth.small_variant(DECODE, name="decode_dims_b1_t150", B=1, T=150, seed=DECODE.seed + 301)]
+         synth.small_variant(DECODE, name="decode_dims_b1_t150", B=1, T=150, seed=DECODE.seed + 301),
+         synth.small_variant(DECODE, name="decode_dims_b1_t300", B=1, T=300, seed=DECODE.seed + 302)]
 
 
 @pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)

@@ -7,8 +7,8 @@ block (dim 320) and one where 16 workgroups own two and the rest one (dim 832: 1
 four rows over 256 workgroups), each with a workspace of exactly the reported size followed by
 guard bytes, every token checked, control words left zero, and the in-place result identical;
 fp32 scales per 32, 64 and 256 features at the decode layout (the scale gathers per chunk: two,
-one, or one kept across a column's chunks); and one workspace shared in turn with the tiled and
-one-block schedules of the decode layout.
+one, or one kept across a column's chunks); and one workspace shared in turn with the
+four-token-block and one-block schedules of the decode layout.
 """
 import numpy as np
 import pytest
@@ -104,8 +104,8 @@ def test_forward_two_token_blocks_decode_bad_ids_in_place():
 
 
 def test_workspace_shared_with_the_other_decode_schedules():
-    """One workspace for 150 tokens (tiled, split K: staging behind the control words), 100 (two
-    token blocks) and 64 (one token block, apply workgroups) of the decode layout, twice in turn:
+    """One workspace for 150 tokens (four token blocks: staged rows behind the control words), 100
+    (two token blocks) and 64 (one token block) of the decode layout, twice in turn:
     every control word zero after each call, every result equal to a call on a fresh workspace."""
     w150 = synth.small_variant(DECODE, name="decode_dims_b150", B=150, T=1, seed=DECODE.seed + 720)
     say("[gpu] one workspace for the tiled, two-block and one-block schedules at the decode layout")
