@@ -756,6 +756,7 @@ __device__ __forceinline__ float gate_from_quarters(const StreamArgs& a, const S
 // its own: store the key columns' partial sums; count the workgroup in (last-arriver marks); the
 // last arrivers' gates; the value columns.
 constexpr int kPhStore = 1, kPhCount = 2, kPhGates = 4, kPhValue = 8, kPhAll = 15;
+constexpr int kPhNoMark = 16;  // value tiles stored, ready marks left to the caller
 
 // Inputs of the key columns' partial sums, loaded before the K-partial reduction: per row block,
 // the lane's 4 features of x (token 16 wv + lane % 16, its stream) and the fp32 products q * k of
@@ -786,6 +787,26 @@ __device__ __forceinline__ void prefetch_key(KeyPre<NRB>& kp, const StreamArgs& 
     const f32x4 q4 = *reinterpret_cast<const f32x4*>(a.q_weight + s * a.dim + d);
     const f32x4 k4 = *reinterpret_cast<const f32x4*>(a.k_weight + s * a.dim + d);
     kp.wq[i] = f32x4{q4.x * k4.x, q4.y * k4.y, q4.z * k4.z, q4.w * k4.w};
+  }
+}
+
+// The same for another token block whose products q * k are those of `same` (loaded before).
+template <int NRB>
+__device__ __forceinline__ void prefetch_key_x(KeyPre<NRB>& kp, const StreamArgs& a, const Rows& rw, int64_t m0,
+                                               int tid, const KeyPre<NRB>& same) {
+  const int lane = tid & 63, wv = tid >> 6;
+  const int64_t m = m0 + 16 * wv + (lane & 15);
+  const int64_t mm = m < a.M ? m : a.M - 1;
+  const int seg_lo = rw.r0 / a.dim;
+  const int nb1 = (seg_lo + 1) * a.dim;
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+    int n = rw.r0 + 16 * i + 4 * (lane >> 4);
+    n = n < rw.r1 ? n : rw.r1 - 4;
+    const int s0 = n < nb1 ? seg_lo : seg_lo + 1;
+    const int s = s0 < 4 ? s0 : 3;
+    kp.x[i] = *reinterpret_cast<const u32x2*>(a.x + (mm * 4 + s) * a.dim + (n - s0 * a.dim));
+    kp.wq[i] = same.wq[i];
   }
 }
 
@@ -1032,9 +1053,11 @@ __device__ __forceinline__ void epilogue(const StreamArgs& a, f32x4 (&red)[NRB],
                 u32x2{pack_bf16x2(red[i].x, red[i].y), pack_bf16x2(red[i].z, red[i].w)}, wsr,
                 row + 2 * uint32_t(n - cv_lo + shift), 0, kCpolSc1);
         }
-        drain_memory_ops();
-        __syncthreads();
-        if (tid < 2) store_relaxed(apply_slot(a, tb, 2 * j + tid, 4), 0x80000000u);
+        if constexpr ((PH & kPhNoMark) == 0) {
+          drain_memory_ops();
+          __syncthreads();
+          if (tid < 2) store_relaxed(apply_slot(a, tb, 2 * j + tid, 4), 0x80000000u);
+        }
       }
       return;
     }
@@ -1631,11 +1654,13 @@ __device__ __forceinline__ void tb2_loop(f32x4 (&acc)[2][NRB][4], const StreamAr
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// The last arrivers' part for both token blocks: for each stream slot this workgroup closed in
-// either block, the partial sums of every contributor of both blocks are loaded in one round
+// The last arrivers' part for token blocks bb and bb + 1 (flags last[0], last[1]), with
+// barriers that order only the LDS (the slot stores and partial-sum clears need not complete
+// before the next block's): for each stream slot this workgroup closed in either block, the partial sums of every contributor of both blocks are loaded in one round
 // (in order, as in the one-block epilogue), then each block's gates go to the slots of its apply
 // workgroups and its counter and partial sums are cleared.
-__device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const Rows& rw, int tid) {
+__device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const Rows& rw, int tid, int bb,
+                                          const int (*last)[2]) {
   const int Q = a.N >> 2, G = a.G;
   const int seg_lo = rw.r0 / a.dim;
   const __amdgpu_buffer_rsrc_t wsr = coherent_rsrc(a.ws_hdr);
@@ -1643,14 +1668,14 @@ __device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const
   const int napb = a.n_apply / a.n_atb;
 #pragma unroll 1
   for (int sl = 0; sl < 2; ++sl) {
-    const bool L0 = sh.last2[0][sl] != 0, L1 = sh.last2[1][sl] != 0;
+    const bool L0 = last[0][sl] != 0, L1 = last[1][sl] != 0;
     if (!L0 && !L1) continue;
     const int s = seg_lo + sl;
     const int wf = owner_of_row(s * a.dim, Q, G), wl = owner_of_row((s + 1) * a.dim - 1, Q, G);
     const int nW = wl - wf + 1;
     const int wb0 = wf + (nW * q) / 4, wb1 = wf + (nW * (q + 1)) / 4;
     const int sl_f = row_begin(wf, Q, G) < s * a.dim ? 1 : 0;
-    auto poff = [&](int b, int w2) { return partial_off(a, b, w2, w2 == wf ? sl_f : 0) + t * 16; };
+    auto poff = [&](int b, int w2) { return partial_off(a, bb + b, w2, w2 == wf ? sl_f : 0) + t * 16; };
     float r[2][3] = {{0.f, 0.f, 0.f}, {0.f, 0.f, 0.f}};
     for (int base = wb0; base < wb1; base += 16) {
       f32x4 v[2][16];
@@ -1673,18 +1698,18 @@ __device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const
 #pragma unroll 1
     for (int b = 0; b < 2; ++b) {
       if (!(b == 0 ? L0 : L1)) continue;
-      __syncthreads();  // sh.red is free again
+      lds_barrier();  // sh.red is free again
       sh.red[q][t][0] = r[b][0];
       sh.red[q][t][1] = r[b][1];
       sh.red[q][t][2] = r[b][2];
-      __syncthreads();
-      if (q == 0) sh.red[0][t][0] = int64_t(b) * kTB + t < a.M ? gate_from_quarters(a, sh, t) : 0.0f;
-      __syncthreads();
-      if (tid == 0) store_relaxed(counter_of(a, b, s), 0u);
+      lds_barrier();
+      if (q == 0) sh.red[0][t][0] = int64_t(bb + b) * kTB + t < a.M ? gate_from_quarters(a, sh, t) : 0.0f;
+      lds_barrier();
+      if (tid == 0) store_relaxed(counter_of(a, bb + b, s), 0u);
       // apply workgroup ap of the block takes tokens 32 (ap & 1) .. + 31
       for (int i = tid; i < napb * 8; i += 256) {
         const int ap = i >> 3, t4 = 32 * (ap & 1) + 4 * (i & 7);
-        store_coherent4(wsr, ws_off(a, apply_slot(a, b, ap, s) + 4 * (i & 7)),
+        store_coherent4(wsr, ws_off(a, apply_slot(a, bb + b, ap, s) + 4 * (i & 7)),
                         __builtin_bit_cast(f32x4, u32x4{__float_as_uint(sh.red[0][t4][0]) | 0x80000000u,
                                                         __float_as_uint(sh.red[0][t4 + 1][0]) | 0x80000000u,
                                                         __float_as_uint(sh.red[0][t4 + 2][0]) | 0x80000000u,
@@ -1692,7 +1717,7 @@ __device__ __forceinline__ void tb2_gates(const StreamArgs& a, Shared& sh, const
       }
       for (int w2 = wb0; w2 < wb1; ++w2) store_coherent4(wsr, poff(b, w2), f32x4{0.f, 0.f, 0.f, 0.f});
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -1775,7 +1800,7 @@ __device__ __forceinline__ void tb2_blocks(const StreamArgs& a, char* smem, Shar
     }
     __syncthreads();
   }
-  tb2_gates(a, sh, rw, tid);
+  tb2_gates(a, sh, rw, tid, 0, sh.last2);
   // value columns: each block's bf16 values into this workgroup's tile for that block (the
   // apply workgroups write out)
   epilogue<NRB, true, true, true, kPhValue>(a, red[0], kp[0], sh, 0, w, rw, tid, smem);
@@ -1952,17 +1977,19 @@ __device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shar
 #pragma unroll
     for (int i = 0; i < NRB; ++i) r[i] = X[((b * NRB + i) * 4 + wv) * 64 + lane];
   };
-  // the key columns' partial sums of every block (the next block's inputs loaded under the
-  // current block's stores)
-  KeyPre<NRB> kp[2];
+  // the key columns' partial sums of every block (every block's inputs loaded at once: one
+  // memory round trip; the products q k, the same for every block, loaded once)
+  KeyPre<NRB> kp[4];
   prefetch_key<NRB>(kp[0], a, rw, 0, tid);
+#pragma unroll
+  for (int b = 1; b < 4; ++b)
+    if (b < n_tb) prefetch_key_x<NRB>(kp[b], a, rw, int64_t(b) * kTB, tid, kp[0]);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if (b < n_tb) {
-      if (b + 1 < n_tb) prefetch_key<NRB>(kp[(b + 1) & 1], a, rw, int64_t(b + 1) * kTB, tid);
       f32x4 red[NRB];
       red_of(red, b);
-      epilogue<NRB, true, true, false, kPhStore>(a, red, kp[b & 1], sh, b, w, rw, tid, smem);
+      epilogue<NRB, true, true, false, kPhStore>(a, red, kp[b], sh, b, w, rw, tid, smem);
     }
   }
   // counted in for every block with one drain and one round of atomics
@@ -1992,29 +2019,24 @@ __device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shar
     }
     __syncthreads();
   }
-  // the last arrivers' gates, block by block
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (b < n_tb && (sh.last4[b][0] | sh.last4[b][1]) != 0) {
-      if (tid == 0) {
-        sh.last[0] = sh.last4[b][0];
-        sh.last[1] = sh.last4[b][1];
-      }
-      __syncthreads();
-      f32x4 red[NRB];
-      red_of(red, b);
-      epilogue<NRB, true, true, true, kPhGates>(a, red, kp[0], sh, b, w, rw, tid, smem);
-      __syncthreads();
-    }
+  // the last arrivers' gates, two blocks per round (a stream's last arriver is mostly the same
+  // workgroup in every block)
+  tb2_gates(a, sh, rw, tid, 0, sh.last4);
+  tb2_gates(a, sh, rw, tid, 2, sh.last4 + 2);
+  // the value columns: each block's bf16 values into this workgroup's tile for that block (one
+  // copy of the code for every block: it runs once per call, cold in the instruction cache)
+#pragma unroll 1
+  for (int b = 0; b < n_tb; ++b) {
+    f32x4 red[NRB];
+    red_of(red, b);
+    epilogue<NRB, true, true, true, kPhValue | kPhNoMark>(a, red, kp[0], sh, b, w, rw, tid, smem);
   }
-  // the value columns: each block's bf16 values into this workgroup's tile for that block
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if (b < n_tb) {
-      f32x4 red[NRB];
-      red_of(red, b);
-      epilogue<NRB, true, true, true, kPhValue>(a, red, kp[0], sh, b, w, rw, tid, smem);
-    }
+  // every block's tile stored, then their ready marks (one drain for all blocks)
+  if ((rw.r1 - 1) / a.dim == 4) {
+    drain_memory_ops();
+    __syncthreads();
+    const int j = w - owner_of_row(4 * a.dim, a.N >> 2, a.G);
+    if (tid < 2 * n_tb) store_relaxed(apply_slot(a, tid >> 1, 2 * j + (tid & 1), 4), 0x80000000u);
   }
 }
 
