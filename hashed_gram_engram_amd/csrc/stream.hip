@@ -1828,20 +1828,23 @@ __global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
 
 // ------------------------------------------------------------------------------ four token blocks
 // The fused forward of 129..256 tokens in one pass over the weights, from the tokens gathered
-// and dequantised beforehand (bf16, in the MFMA's operand order, in the staging area).  One workgroup per CU over
-// its NRB row blocks, eight waves in two roles.  Waves 4..7 copy the workgroup's weight rows
+// and dequantised beforehand (bf16, in the MFMA's operand order, in the staging area).  One
+// workgroup per CU over its NRB row blocks, twelve waves in two roles.  Waves 8..11 copy the workgroup's weight rows
 // into a ring of D stages of 64 features (NRB 2 KB slots each, the two-token-block kernel's
-// slot layout) and wait only for their own copies; waves 0..3 each multiply one 64-token block
-// over all of K, their token fragments loaded from the staging area (an L2-resident 3 MB at 256
-// tokens) straight into registers kTb4Tok stages ahead.  A wave's memory counter thus covers
+// slot layout) and wait only for their own copies; waves 0..7 each multiply 32 tokens over all
+// of K, their token fragments loaded from the staging area (an L2-resident 3 MB at 256 tokens)
+// straight into registers kTb4Tok stages ahead.  A wave's memory counter thus covers
 // one kind of access: the copies keep D - 1 stages (NRB x 2 KB each) in flight, independently
 // of the token loads.  One workgroup barrier per stage: the copy waves reach it once the stage
 // has landed, the multiplying waves once they have read the stage before it, whose slot the
 // copies issued after the barrier refill.  Then the copy waves leave (a barrier waits only for
-// the waves still running), and the four blocks' sums take the two-token-block kernel's
-// hand-off: key partial sums stored, counted in with one round of atomics, the last arrivers'
+// the waves still running), the sums go through LDS, waves 4..7 leave too, and waves 0..3 take
+// the four blocks through the two-token-block kernel's hand-off: key partial sums stored, counted in with one round of atomics, the last arrivers'
 // gates, the value workgroups' bf16 tiles for the apply workgroups.
 constexpr int kTb4Tok = 2;  // stages of token fragments in flight per multiplying wave
+// 16-token sub-blocks per multiplying wave: 16 / kTb4NT such waves (eight of 32 tokens, two per
+// SIMD, so that one wave's barrier wait and token loads overlap the other's MFMAs)
+constexpr int kTb4NT = 2;
 __host__ __device__ constexpr int tb4_ring(int nrb) { return 163840 / (nrb * kW2Slot) < 12 ? 163840 / (nrb * kW2Slot) : 12; }
 // after the loop: the four blocks' sums (NRB x 16 KB) behind the epilogue's shared words, where
 // they stay while the epilogue runs
@@ -1896,25 +1899,26 @@ __device__ __forceinline__ void tb4_produce(const StreamArgs& a, char* smem, con
 // 16 l: token l % 16, features 8 (l / 16) ..), so that every load reads 1 KB in one run; the rows
 // past the last token up to a multiple of 16 are staged as zeros, the sub-blocks after them read
 // as zeros through the buffer resource's range.
-template <int NRB>
-__device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][4], const StreamArgs& a, const char* smem, int lane,
-                                            int cb, int nst, int rot) {
+template <int NRB, int NT>
+__device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamArgs& a, const char* smem, int lane,
+                                            int cw, int nst, int rot) {
   constexpr int D = tb4_ring(NRB);
   constexpr int kStage = NRB * kW2Slot;
   constexpr int P = kTb4Tok;
   const __amdgpu_buffer_rsrc_t tsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.emb), (short)0, int((a.M + 15) & ~int64_t(15)) * a.K * 2, 0x00020000);
-  // sub-block t's 1 KB blocks: (4 cb + t) x K / 32 + k32
-  uint32_t vo[4];
+  // the wave's sub-block t (16 tokens): group NT cw + t, its 1 KB blocks at (NT cw + t) x K / 32
+  // + k32
+  uint32_t vo[NT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) vo[t] = uint32_t(4 * cb + t) * uint32_t(a.K / 32) * 1024u + 16u * uint32_t(lane);
-  u32x4 tk[P][2][4];
-  auto load = [&](u32x4 (&dst)[2][4], int c) {
+  for (int t = 0; t < NT; ++t) vo[t] = uint32_t(NT * cw + t) * uint32_t(a.K / 32) * 1024u + 16u * uint32_t(lane);
+  u32x4 tk[P][2][NT];
+  auto load = [&](u32x4 (&dst)[2][NT], int c) {
     const uint32_t fb = 2048u * uint32_t((c < nst ? c + rot : rot) % nst);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < NT; ++t)
         dst[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tsrc, vo[t] + fb + 1024u * s, 0, 0));
   };
   // (in stage order, as the loop issues them: otherwise the loads pending at the top of the loop
@@ -1944,7 +1948,7 @@ __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][4], const StreamAr
 #pragma unroll
       for (int s = 0; s < 2; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[i][t] = mfma16x16x32(wf[i & 1][s], tk[r][s][t], acc[i][t]);
+        for (int t = 0; t < NT; ++t) acc[i][t] = mfma16x16x32(wf[i & 1][s], tk[r][s][t], acc[i][t]);
     }
     load(tk[r], c + P);
     slot = slot + kStage == smem + D * kStage ? smem : slot + kStage;
@@ -1960,19 +1964,15 @@ __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][4], const StreamAr
   lds_barrier();
 }
 
+// The multiplying waves' sums after the loop: X[((b NRB + i) 4 + t) 64 + lane] holds row block i
+// of token sub-block t of block b (written by every multiplying wave, then read by waves 0..3:
+// wave wv takes sub-block wv of each block, as after the K-partial reduction of the other
+// kernels).
 template <int NRB>
-__device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw,
-                                           f32x4 (&acc)[NRB][4]) {
+__device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shared& sh, int w, const Rows& rw) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int n_tb = int((a.M + kTB - 1) / kTB);
-  // wave c holds all of K for token block c; read back, wave wv holds token sub-block wv of a
-  // block, as after the K-partial reduction of the other kernels
-  f32x4* const X = reinterpret_cast<f32x4*>(smem + kTb4X);
-#pragma unroll
-  for (int i = 0; i < NRB; ++i)
-#pragma unroll
-    for (int t = 0; t < 4; ++t) X[((wv * NRB + i) * 4 + t) * 64 + lane] = acc[i][t];
-  lds_barrier();
+  const f32x4* const X = reinterpret_cast<const f32x4*>(smem + kTb4X);
   auto red_of = [&](f32x4 (&r)[NRB], int b) {
 #pragma unroll
     for (int i = 0; i < NRB; ++i) r[i] = X[((b * NRB + i) * 4 + wv) * 64 + lane];
@@ -2040,8 +2040,8 @@ __device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shar
   }
 }
 
-template <int NRB>
-__global__ __launch_bounds__(512, 1) void k_stream_tb4(StreamArgs a) {
+template <int NRB, int NT>
+__global__ __launch_bounds__((16 / NT + 4) * 64, 1) void k_stream_tb4(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
   const int G = a.G, w = blockIdx.x;
@@ -2057,21 +2057,37 @@ __global__ __launch_bounds__(512, 1) void k_stream_tb4(StreamArgs a) {
   const Rows rw = rows_of(w, a.N, G);
   const int nst = a.K / kC2;
   const int rot = int((5u * uint32_t(w)) % uint32_t(nst));
-  if (wv >= 4) {
-    const int p = wv - 4;
+  // waves 0 .. NC - 1 multiply (NT sub-blocks of 16 tokens each), the next four copy
+  constexpr int NC = 16 / NT;
+  if (wv >= NC) {
+    const int p = wv - NC;
     if (p == 0) tb4_produce<NRB, 0>(a, smem, rw, lane, nst, rot);
     else if (p == 1) tb4_produce<NRB, 1>(a, smem, rw, lane, nst, rot);
     else if (p == 2) tb4_produce<NRB, 2>(a, smem, rw, lane, nst, rot);
     else tb4_produce<NRB, 3>(a, smem, rw, lane, nst, rot);
     return;
   }
-  f32x4 acc[NRB][4];
+  f32x4 acc[NRB][NT];
 #pragma unroll
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tb4_consume<NRB>(acc, a, smem, lane, wv, nst, rot);
-  tb4_blocks<NRB>(a, smem, sh, w, rw, acc);
+    for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  tb4_consume<NRB, NT>(acc, a, smem, lane, wv, nst, rot);
+  {
+    // the sums through LDS (sub-block g = NT wv + t: block g / 4, sub-block g % 4)
+    f32x4* const X = reinterpret_cast<f32x4*>(smem + kTb4X);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int g = NT * wv + t;
+        X[(((g >> 2) * NRB + i) * 4 + (g & 3)) * 64 + lane] = acc[i][t];
+      }
+    lds_barrier();
+  }
+  // the epilogue takes four waves; the other multiplying waves leave
+  if (wv >= 4) return;
+  tb4_blocks<NRB>(a, smem, sh, w, rw);
 }
 
 template <bool FUSED, int NRB>
@@ -2376,13 +2392,13 @@ hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStr
   a.n_apply = 2 * a.n_atb * value_groups(a.N, a.dim, G);
   void* fn = nullptr;
   switch (max_blocks(a.N, G)) {
-    case 1: fn = reinterpret_cast<void*>(&k_stream_tb4<1>); break;
-    case 2: fn = reinterpret_cast<void*>(&k_stream_tb4<2>); break;
-    case 3: fn = reinterpret_cast<void*>(&k_stream_tb4<3>); break;
-    case 4: fn = reinterpret_cast<void*>(&k_stream_tb4<4>); break;
-    case 5: fn = reinterpret_cast<void*>(&k_stream_tb4<5>); break;
-    case 6: fn = reinterpret_cast<void*>(&k_stream_tb4<6>); break;
-    case 7: fn = reinterpret_cast<void*>(&k_stream_tb4<7>); break;
+    case 1: fn = reinterpret_cast<void*>(&k_stream_tb4<1, kTb4NT>); break;
+    case 2: fn = reinterpret_cast<void*>(&k_stream_tb4<2, kTb4NT>); break;
+    case 3: fn = reinterpret_cast<void*>(&k_stream_tb4<3, kTb4NT>); break;
+    case 4: fn = reinterpret_cast<void*>(&k_stream_tb4<4, kTb4NT>); break;
+    case 5: fn = reinterpret_cast<void*>(&k_stream_tb4<5, kTb4NT>); break;
+    case 6: fn = reinterpret_cast<void*>(&k_stream_tb4<6, kTb4NT>); break;
+    case 7: fn = reinterpret_cast<void*>(&k_stream_tb4<7, kTb4NT>); break;
     default: return hipErrorInvalidValue;
   }
   size_t lds = size_t(tb4_lds(max_blocks(a.N, G)));
@@ -2390,7 +2406,7 @@ hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStr
   const hipError_t e = allow_lds(fn, lds);
   if (e != hipSuccess) return e;
   void* params[] = {&a};
-  return hipLaunchKernel(fn, dim3(G + a.n_apply), dim3(512), params, lds, stream);
+  return hipLaunchKernel(fn, dim3(G + a.n_apply), dim3((16 / kTb4NT + 4) * 64), params, lds, stream);
 }
 
 hipError_t launch_forward_stream(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
