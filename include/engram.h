@@ -104,10 +104,13 @@ size_t engram_forward_workspace_bytes(const engram_layout* layout, int64_t B, in
 /* Bytes at the end of the workspace that engram_forward uses as a staging area for B x T
  * tokens: the dequantised rows (B x T x n_cols x head_dim bf16), room for the fp32 partial
  * tiles of a K loop split over two workgroups (taken for every tile when a call has few tiles,
- * else for the tiles of a last, partial round; a fixed 32 MB per layout), alignment slack; 0 where the fused weight-streaming
- * schedule runs (up to 64 tokens), which keeps the rows on chip.  With MXFP8 weights and an
- * MXFP8 table the rows are staged as fp8 codes plus one E8M0 byte per 32 features (K + K / 32
- * bytes per token); with MXFP8 weights and fp32 table scales above 64 tokens (or on shapes the
+ * else for the tiles of a last, partial round; a fixed 32 MB per layout), alignment slack; 0
+ * where the fused weight-streaming schedules of one or two token blocks run (up to 64 tokens,
+ * and 65..128 with bf16 weights where the layout admits them), which keep the rows on chip.
+ * Where the four-token-block streaming kernel runs (129..256 tokens, bf16 weights, layouts
+ * whose streaming workgroups own equal row counts) only the rows, B x T rounded up to 16.  With
+ * MXFP8 weights and an MXFP8 table the rows are staged as fp8 codes plus one E8M0 byte per 32
+ * features (K + K / 32 bytes per token); with MXFP8 weights and fp32 table scales above 64 tokens (or on shapes the
  * streaming kernel does not take) the weights are expanded to bf16 there as well (N x K x 2
  * bytes).  Included in engram_forward_workspace_bytes(). */
 size_t engram_forward_staging_bytes(const engram_layout* layout, int64_t B, int64_t T);
