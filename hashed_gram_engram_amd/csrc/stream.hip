@@ -1830,8 +1830,8 @@ __global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
 // The fused forward of 129..256 tokens in one pass over the weights, from the tokens gathered
 // and dequantised beforehand (bf16, in the MFMA's operand order, in the staging area).  One
 // workgroup per CU over its NRB row blocks, twelve waves in two roles.  Waves 8..11 copy the workgroup's weight rows
-// into a ring of D stages of 64 features (NRB 2 KB slots each, the two-token-block kernel's
-// slot layout) and wait only for their own copies; waves 0..7 each multiply 32 tokens over all
+// into a ring of D stages of 128 features (NRB 4 KB slots each, the one-block kernel's slot
+// layout: 256 bytes of each row) and wait only for their own copies; waves 0..7 each multiply 32 tokens over all
 // of K, their token fragments loaded from the staging area (an L2-resident 3 MB at 256 tokens)
 // straight into registers kTb4Tok stages ahead.  A wave's memory counter thus covers
 // one kind of access: the copies keep D - 1 stages (NRB x 2 KB each) in flight, independently
@@ -1845,38 +1845,46 @@ constexpr int kTb4Tok = 2;  // stages of token fragments in flight per multiplyi
 // 16-token sub-blocks per multiplying wave: 16 / kTb4NT such waves (eight of 32 tokens, two per
 // SIMD, so that one wave's barrier wait and token loads overlap the other's MFMAs)
 constexpr int kTb4NT = 2;
-__host__ __device__ constexpr int tb4_ring(int nrb) { return 163840 / (nrb * kW2Slot) < 12 ? 163840 / (nrb * kW2Slot) : 12; }
+constexpr int kC4 = 128;  // features per stage: 256 bytes of each weight row
+__host__ __device__ constexpr int tb4_ring(int nrb) { return 163840 / (nrb * kWBlk) < 12 ? 163840 / (nrb * kWBlk) : 12; }
 // after the loop: the four blocks' sums (NRB x 16 KB) behind the epilogue's shared words, where
 // they stay while the epilogue runs
 constexpr int kTb4X = (kRedBytes + int(sizeof(Shared)) + 4095) & ~4095;
 __host__ __device__ constexpr int tb4_lds(int nrb) {
-  return tb4_ring(nrb) * nrb * kW2Slot > kTb4X + nrb * 16384 ? tb4_ring(nrb) * nrb * kW2Slot : kTb4X + nrb * 16384;
+  return tb4_ring(nrb) * nrb * kWBlk > kTb4X + nrb * 16384 ? tb4_ring(nrb) * nrb * kWBlk : kTb4X + nrb * 16384;
 }
 
-// Copy wave PI: the stage's copies j = PI, PI + 4, .. below 2 NRB (row block j / 2, rows 8 (j %
-// 2) .. + 7: NP of them), through a buffer resource on wkv as in the two-token-block kernel.  Stages
-// past the last one copy cache-resident rows at feature 0 into the free slot instead, so that
-// the count of copies per stage, and with it the wait before each barrier, stays fixed.
+// Copy wave PI: rows 4 PI .. 4 PI + 3 of every row block (NRB copies of 4 rows x 256 bytes per
+// stage, through a buffer resource on wkv), lane l at 16 l: row 4 PI + l / 16 of the block,
+// position l % 16 holding the 16-byte part (l % 16) ^ row of the row's 256 stage bytes, as the
+// one-block kernel's slots.  A lane's byte offset of its row in block 0, and in the workgroup's
+// last row (rows past it repeat it), are computed once; the stage's byte offset is a scalar.
+// Stages past the last one copy rows 0..15 at feature 0 (cache resident) into the free slot
+// instead, so that the count of copies per stage, and with it the wait before each barrier,
+// stays fixed.
 template <int NRB, int PI>
 __device__ __forceinline__ void tb4_produce(const StreamArgs& a, char* smem, const Rows& rw, int lane, int nst,
                                             int rot) {
   constexpr int D = tb4_ring(NRB);
-  constexpr int kStage = NRB * kW2Slot;
-  constexpr int NP = (2 * NRB - PI + 3) / 4;
+  constexpr int kStage = NRB * kWBlk;
+  constexpr int NP = NRB;
   static_assert(D >= 3 && (D - 1) * NP <= 63, "copies in flight within the counter's range");
   const __amdgpu_buffer_rsrc_t wsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.wkv), (short)0, a.N * a.K * 2, 0x00020000);
-  Tb2WOff wo;
-  tb2_woff(wo, a, rw, lane);
-  // (the copy index is a constant in every copy, so that each offset stays in a register)
+  const uint32_t rowb = uint32_t(a.K) * 2u;
+  const int rr = 4 * PI + (lane >> 4);  // the lane's row in its block
+  const uint32_t part = 16u * uint32_t((lane & 15) ^ rr);
+  const uint32_t base = uint32_t(rw.r0 + rr) * rowb + part;
+  const uint32_t last = uint32_t(rw.r1 - 1) * rowb + part;
+  const uint32_t dummy = uint32_t(rr) * rowb + part;
   auto issue = [&](int c, char* slot) {
     const bool live = c < nst;
-    const int soff = live ? 2 * kC2 * ((c + rot) % nst) : 0;
+    const int soff = live ? 2 * kC4 * ((c + rot) % nst) : 0;
 #pragma unroll
-    for (int k = 0; k < NP; ++k) {
-      const int j = PI + 4 * k, i = j >> 1, h = j & 1;
-      const uint32_t o = live ? tb2_wo(wo, i, h) : wo.dummy[h];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(slot + i * kW2Slot + h * 1024), 16, o, soff, 0, 2);
+    for (int i = 0; i < NP; ++i) {
+      const uint32_t oi = base + uint32_t(i) * 16u * rowb;
+      const uint32_t o = live ? (oi < last ? oi : last) : dummy;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(slot + i * kWBlk + PI * 1024), 16, o, soff, 0, 2);
     }
     asm volatile("" ::: "memory");
   };
@@ -1903,7 +1911,7 @@ template <int NRB, int NT>
 __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamArgs& a, const char* smem, int lane,
                                             int cw, int nst, int rot) {
   constexpr int D = tb4_ring(NRB);
-  constexpr int kStage = NRB * kW2Slot;
+  constexpr int kStage = NRB * kWBlk;
   constexpr int P = kTb4Tok;
   const __amdgpu_buffer_rsrc_t tsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.emb), (short)0, int((a.M + 15) & ~int64_t(15)) * a.K * 2, 0x00020000);
@@ -1912,11 +1920,11 @@ __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamA
   uint32_t vo[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) vo[t] = uint32_t(NT * cw + t) * uint32_t(a.K / 32) * 1024u + 16u * uint32_t(lane);
-  u32x4 tk[P][2][NT];
-  auto load = [&](u32x4 (&dst)[2][NT], int c) {
-    const uint32_t fb = 2048u * uint32_t((c < nst ? c + rot : rot) % nst);
+  u32x4 tk[P][4][NT];
+  auto load = [&](u32x4 (&dst)[4][NT], int c) {
+    const uint32_t fb = 4096u * uint32_t((c < nst ? c + rot : rot) % nst);
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
         dst[s][t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(tsrc, vo[t] + fb + 1024u * s, 0, 0));
@@ -1934,19 +1942,20 @@ __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamA
     constexpr int r = decltype(reg_tag)::value;
     // stage c has landed; this wave's reads of stage c - 1 are done
     lds_barrier();
-    // row block i + 1's fragments are read while block i's MFMAs run
-    u32x4 wf[2][2];
-    auto read_wf = [&](u32x4 (&f)[2], int i) {
+    // row block i + 1's fragments are read while block i's MFMAs run (K step s, lane group g:
+    // part 4 s + g of the row, at position (4 s + g) ^ row)
+    u32x4 wf[2][4];
+    auto read_wf = [&](u32x4 (&f)[4], int i) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        f[s] = *reinterpret_cast<const u32x4*>(slot + i * kW2Slot + wr * 128 + 16 * ((4 * s + (lane >> 4)) ^ (wr & 7)));
+      for (int s = 0; s < 4; ++s)
+        f[s] = *reinterpret_cast<const u32x4*>(slot + i * kWBlk + wr * 256 + 16 * ((4 * s + (lane >> 4)) ^ wr));
     };
     read_wf(wf[0], 0);
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
       if (i + 1 < NRB) read_wf(wf[(i + 1) & 1], i + 1);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[i][t] = mfma16x16x32(wf[i & 1][s], tk[r][s][t], acc[i][t]);
     }
@@ -2055,7 +2064,7 @@ __global__ __launch_bounds__((16 / NT + 4) * 64, 1) void k_stream_tb4(StreamArgs
     return;
   }
   const Rows rw = rows_of(w, a.N, G);
-  const int nst = a.K / kC2;
+  const int nst = a.K / kC4;
   const int rot = int((5u * uint32_t(w)) % uint32_t(nst));
   // waves 0 .. NC - 1 multiply (NT sub-blocks of 16 tokens each), the next four copy
   constexpr int NC = 16 / NT;
@@ -2368,14 +2377,14 @@ hipError_t launch_forward_tb2(StreamArgs a, void* workspace, int num_cus, hipStr
 }
 
 // The four-token-block kernel (129..256 tokens from staged bf16 rows): every workgroup owns the
-// same number of row blocks, at most seven; an even number of 64-feature stages; bf16 weights and staged tokens of
+// same number of row blocks, at most seven; an even number of 128-feature stages; bf16 weights and staged tokens of
 // at most 2^31 - 1 bytes each (read through buffer resources); the apply workgroups' slots within
 // each token block's gate-slot region.
 bool stream_tb4_ok(int K, int N, int dim, int num_cus) {
   const int G = stream_grid(N, num_cus);
   const int lo = min_blocks(N, G), hi = max_blocks(N, G);
   const int V = value_groups(N, dim, G);
-  return (N / 4) % G == 0 && K % (2 * kC2) == 0 && lo == hi && hi >= 1 && hi <= 7 && tb4_lds(hi) <= 163840 &&
+  return (N / 4) % G == 0 && K % (2 * kC4) == 0 && lo == hi && hi >= 1 && hi <= 7 && tb4_lds(hi) <= 163840 &&
          int64_t(N) * K * 2 <= 0x7FFFFFFF && int64_t(4 * kTB) * K * 2 <= 0x7FFFFFFF && V >= 1 &&
          2 * V * 160 <= G * 256;
 }
