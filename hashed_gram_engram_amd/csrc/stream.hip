@@ -1846,12 +1846,18 @@ constexpr int kTb4Tok = 2;  // stages of token fragments in flight per multiplyi
 // SIMD, so that one wave's barrier wait and token loads overlap the other's MFMAs)
 constexpr int kTb4NT = 2;
 constexpr int kC4 = 128;  // features per stage: 256 bytes of each weight row
-__host__ __device__ constexpr int tb4_ring(int nrb) { return 163840 / (nrb * kWBlk) < 12 ? 163840 / (nrb * kWBlk) : 12; }
+// A stage: NRB 4 KB slots, or with TRIM (every workgroup's last row block holds four rows) the
+// last one a 1 KB slot of its four rows.
+__host__ __device__ constexpr int tb4_stage(int nrb, bool trim) { return trim ? (nrb - 1) * kWBlk + 1024 : nrb * kWBlk; }
+__host__ __device__ constexpr int tb4_ring(int nrb, bool trim = false) {
+  return 163840 / tb4_stage(nrb, trim) < 12 ? 163840 / tb4_stage(nrb, trim) : 12;
+}
 // after the loop: the four blocks' sums (NRB x 16 KB) behind the epilogue's shared words, where
 // they stay while the epilogue runs
 constexpr int kTb4X = (kRedBytes + int(sizeof(Shared)) + 4095) & ~4095;
-__host__ __device__ constexpr int tb4_lds(int nrb) {
-  return tb4_ring(nrb) * nrb * kWBlk > kTb4X + nrb * 16384 ? tb4_ring(nrb) * nrb * kWBlk : kTb4X + nrb * 16384;
+__host__ __device__ constexpr int tb4_lds(int nrb, bool trim = false) {
+  return tb4_ring(nrb, trim) * tb4_stage(nrb, trim) > kTb4X + nrb * 16384 ? tb4_ring(nrb, trim) * tb4_stage(nrb, trim)
+                                                                         : kTb4X + nrb * 16384;
 }
 
 // Copy wave PI: rows 4 PI .. 4 PI + 3 of every row block (NRB copies of 4 rows x 256 bytes per
@@ -1861,13 +1867,14 @@ __host__ __device__ constexpr int tb4_lds(int nrb) {
 // last row (rows past it repeat it), are computed once; the stage's byte offset is a scalar.
 // Stages past the last one copy rows 0..15 at feature 0 (cache resident) into the free slot
 // instead, so that the count of copies per stage, and with it the wait before each barrier,
-// stays fixed.
-template <int NRB, int PI>
+// stays fixed.  With TRIM the last block's slot holds only its four rows (copy wave 0's).
+template <int NRB, int PI, bool TRIM>
 __device__ __forceinline__ void tb4_produce(const StreamArgs& a, char* smem, const Rows& rw, int lane, int nst,
                                             int rot) {
-  constexpr int D = tb4_ring(NRB);
-  constexpr int kStage = NRB * kWBlk;
-  constexpr int NP = NRB;
+  constexpr int D = tb4_ring(NRB, TRIM);
+  constexpr int kStage = tb4_stage(NRB, TRIM);
+  // (with TRIM only copy wave 0 has rows in the last block)
+  constexpr int NP = TRIM && PI > 0 ? NRB - 1 : NRB;
   static_assert(D >= 3 && (D - 1) * NP <= 63, "copies in flight within the counter's range");
   const __amdgpu_buffer_rsrc_t wsrc =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.wkv), (short)0, a.N * a.K * 2, 0x00020000);
@@ -1907,11 +1914,11 @@ __device__ __forceinline__ void tb4_produce(const StreamArgs& a, char* smem, con
 // 16 l: token l % 16, features 8 (l / 16) ..), so that every load reads 1 KB in one run; the rows
 // past the last token up to a multiple of 16 are staged as zeros, the sub-blocks after them read
 // as zeros through the buffer resource's range.
-template <int NRB, int NT>
+template <int NRB, int NT, bool TRIM>
 __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamArgs& a, const char* smem, int lane,
                                             int cw, int nst, int rot) {
-  constexpr int D = tb4_ring(NRB);
-  constexpr int kStage = NRB * kWBlk;
+  constexpr int D = tb4_ring(NRB, TRIM);
+  constexpr int kStage = tb4_stage(NRB, TRIM);
   constexpr int P = kTb4Tok;
   const __amdgpu_buffer_rsrc_t tsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(a.emb), (short)0, int((a.M + 15) & ~int64_t(15)) * a.K * 2, 0x00020000);
@@ -1944,11 +1951,13 @@ __device__ __forceinline__ void tb4_consume(f32x4 (&acc)[NRB][NT], const StreamA
     lds_barrier();
     // row block i + 1's fragments are read while block i's MFMAs run (K step s, lane group g:
     // part 4 s + g of the row, at position (4 s + g) ^ row)
+    // (with TRIM the last block's lanes of rows 4..15 read row 3: their sums are never used)
     u32x4 wf[2][4];
     auto read_wf = [&](u32x4 (&f)[4], int i) {
+      const int lr = TRIM && i == NRB - 1 ? (wr < 3 ? wr : 3) : wr;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        f[s] = *reinterpret_cast<const u32x4*>(slot + i * kWBlk + wr * 256 + 16 * ((4 * s + (lane >> 4)) ^ wr));
+        f[s] = *reinterpret_cast<const u32x4*>(slot + i * kWBlk + lr * 256 + 16 * ((4 * s + (lane >> 4)) ^ lr));
     };
     read_wf(wf[0], 0);
 #pragma unroll
@@ -2049,7 +2058,7 @@ __device__ __forceinline__ void tb4_blocks(const StreamArgs& a, char* smem, Shar
   }
 }
 
-template <int NRB, int NT>
+template <int NRB, int NT, bool TRIM>
 __global__ __launch_bounds__((16 / NT + 4) * 64, 1) void k_stream_tb4(StreamArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   Shared& sh = *reinterpret_cast<Shared*>(smem + kRedBytes);
@@ -2070,10 +2079,10 @@ __global__ __launch_bounds__((16 / NT + 4) * 64, 1) void k_stream_tb4(StreamArgs
   constexpr int NC = 16 / NT;
   if (wv >= NC) {
     const int p = wv - NC;
-    if (p == 0) tb4_produce<NRB, 0>(a, smem, rw, lane, nst, rot);
-    else if (p == 1) tb4_produce<NRB, 1>(a, smem, rw, lane, nst, rot);
-    else if (p == 2) tb4_produce<NRB, 2>(a, smem, rw, lane, nst, rot);
-    else tb4_produce<NRB, 3>(a, smem, rw, lane, nst, rot);
+    if (p == 0) tb4_produce<NRB, 0, TRIM>(a, smem, rw, lane, nst, rot);
+    else if (p == 1) tb4_produce<NRB, 1, TRIM>(a, smem, rw, lane, nst, rot);
+    else if (p == 2) tb4_produce<NRB, 2, TRIM>(a, smem, rw, lane, nst, rot);
+    else tb4_produce<NRB, 3, TRIM>(a, smem, rw, lane, nst, rot);
     return;
   }
   f32x4 acc[NRB][NT];
@@ -2081,7 +2090,7 @@ __global__ __launch_bounds__((16 / NT + 4) * 64, 1) void k_stream_tb4(StreamArgs
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[i][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  tb4_consume<NRB, NT>(acc, a, smem, lane, wv, nst, rot);
+  tb4_consume<NRB, NT, TRIM>(acc, a, smem, lane, wv, nst, rot);
   {
     // the sums through LDS (sub-block g = NT wv + t: block g / 4, sub-block g % 4)
     f32x4* const X = reinterpret_cast<f32x4*>(smem + kTb4X);
@@ -2384,9 +2393,24 @@ bool stream_tb4_ok(int K, int N, int dim, int num_cus) {
   const int G = stream_grid(N, num_cus);
   const int lo = min_blocks(N, G), hi = max_blocks(N, G);
   const int V = value_groups(N, dim, G);
-  return (N / 4) % G == 0 && K % (2 * kC4) == 0 && lo == hi && hi >= 1 && hi <= 7 && tb4_lds(hi) <= 163840 &&
+  const bool trim = hi >= 2 && stream_rows_per_group(N, G) % 16 == 4;
+  return (N / 4) % G == 0 && K % (2 * kC4) == 0 && lo == hi && hi >= 1 && hi <= 7 && tb4_lds(hi, trim) <= 163840 &&
          int64_t(N) * K * 2 <= 0x7FFFFFFF && int64_t(4 * kTB) * K * 2 <= 0x7FFFFFFF && V >= 1 &&
          2 * V * 160 <= G * 256;
+}
+
+template <bool TRIM>
+void* pick_tb4(int nrb) {
+  switch (nrb) {
+    case 1: return TRIM ? nullptr : reinterpret_cast<void*>(&k_stream_tb4<1, kTb4NT, false>);
+    case 2: return reinterpret_cast<void*>(&k_stream_tb4<2, kTb4NT, TRIM>);
+    case 3: return reinterpret_cast<void*>(&k_stream_tb4<3, kTb4NT, TRIM>);
+    case 4: return reinterpret_cast<void*>(&k_stream_tb4<4, kTb4NT, TRIM>);
+    case 5: return reinterpret_cast<void*>(&k_stream_tb4<5, kTb4NT, TRIM>);
+    case 6: return reinterpret_cast<void*>(&k_stream_tb4<6, kTb4NT, TRIM>);
+    case 7: return reinterpret_cast<void*>(&k_stream_tb4<7, kTb4NT, TRIM>);
+    default: return nullptr;
+  }
 }
 
 hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStream_t stream) {
@@ -2399,18 +2423,12 @@ hipError_t launch_forward_tb4(StreamArgs a, void* workspace, int num_cus, hipStr
   // two apply workgroups per value workgroup and token block
   a.n_atb = int((a.M + kTB - 1) / kTB);
   a.n_apply = 2 * a.n_atb * value_groups(a.N, a.dim, G);
-  void* fn = nullptr;
-  switch (max_blocks(a.N, G)) {
-    case 1: fn = reinterpret_cast<void*>(&k_stream_tb4<1, kTb4NT>); break;
-    case 2: fn = reinterpret_cast<void*>(&k_stream_tb4<2, kTb4NT>); break;
-    case 3: fn = reinterpret_cast<void*>(&k_stream_tb4<3, kTb4NT>); break;
-    case 4: fn = reinterpret_cast<void*>(&k_stream_tb4<4, kTb4NT>); break;
-    case 5: fn = reinterpret_cast<void*>(&k_stream_tb4<5, kTb4NT>); break;
-    case 6: fn = reinterpret_cast<void*>(&k_stream_tb4<6, kTb4NT>); break;
-    case 7: fn = reinterpret_cast<void*>(&k_stream_tb4<7, kTb4NT>); break;
-    default: return hipErrorInvalidValue;
-  }
-  size_t lds = size_t(tb4_lds(max_blocks(a.N, G)));
+  // the last row block of four rows (every workgroup alike): its slot trimmed to them
+  const int nrb = max_blocks(a.N, G);
+  const bool trim = nrb >= 2 && stream_rows_per_group(a.N, G) % 16 == 4;
+  void* fn = trim ? pick_tb4<true>(nrb) : pick_tb4<false>(nrb);
+  if (fn == nullptr) return hipErrorInvalidValue;
+  size_t lds = size_t(tb4_lds(nrb, trim));
   if (lds < kRedBytes + sizeof(Shared)) lds = kRedBytes + sizeof(Shared);
   const hipError_t e = allow_lds(fn, lds);
   if (e != hipSuccess) return e;

@@ -1,13 +1,14 @@
 """The four-token-block weight-streaming forward (129..256 tokens, bf16 weights) against the CPU
 oracle: the rows are gathered into the staging area, then every workgroup reads its wkv rows once
-for all token blocks (copy waves filling a ring of weight stages, one multiplying wave per 64-token
-block).
+for all token blocks (copy waves filling a ring of weight stages, eight multiplying waves of 32
+tokens each).
 
 The decode layout at 129 (a last block of one token), 200 (out-of-range ids in three blocks, the
 output written over x) and 256 tokens, each with a workspace of exactly the reported size followed
 by guard bytes, every token checked, control words left zero and a bitwise-identical rerun; E8M0
-table scales at 160 tokens; layouts of two row blocks per workgroup (dim 1024: 20 rows) with four
-and eight table columns (eight and sixteen 64-feature stages).
+table scales at 160 tokens; layouts of two row blocks per workgroup (dim 1024: 20 rows, the
+last block's slot trimmed to its four rows) with four and eight table columns (four and eight
+128-feature stages), and of three (dim 2048: 40 rows, every slot full size).
 """
 import numpy as np
 import pytest
@@ -99,13 +100,15 @@ def test_forward_four_token_blocks_e8m0_scales():
     say("   ", check_out(w, sel, got, oracle_for(w, sel)))
 
 
-@pytest.mark.parametrize("nc,T", [(4, 140), (8, 256)])
-def test_forward_four_token_blocks_two_row_blocks(nc, T):
-    w = synth.small_variant(TINY, name=f"dim1024_cols{nc}_b1_t{T}", B=1, T=T, dim=1024, n_cols=nc,
+@pytest.mark.parametrize("dim,nc,T", [(1024, 4, 140), (1024, 8, 256), (2048, 8, 200)])
+def test_forward_four_token_blocks_small_layouts(dim, nc, T):
+    """dim 1024: 20 rows per workgroup (a full row block and one of four rows, whose slot holds
+    only them); dim 2048: 40 rows (two full blocks and one of eight: every slot full size)."""
+    w = synth.small_variant(TINY, name=f"dim{dim}_cols{nc}_b1_t{T}", B=1, T=T, dim=dim, n_cols=nc,
                             head_dim=128, scale_block=32, primes=synth.primes_from(1009, nc), hash_dist="zipf",
                             mask_false_frac=0.1, masked_positions=(), outlier_frac=0.05,
-                            seed=TINY.seed + 830 + nc + T)
-    say(f"[gpu] forward {w.name}: four token blocks, two row blocks per workgroup")
+                            seed=TINY.seed + 830 + nc + T + dim)
+    say(f"[gpu] forward {w.name}: four token blocks, small layout")
     d = synth.device_inputs(w)
     out, _, err = run_checked(w, d)
     assert err == 0
