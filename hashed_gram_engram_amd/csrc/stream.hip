@@ -1829,18 +1829,19 @@ __global__ __launch_bounds__(256, 1) void k_stream_tb2(StreamArgs a) {
 // ------------------------------------------------------------------------------ four token blocks
 // The fused forward of 129..256 tokens in one pass over the weights, from the tokens gathered
 // and dequantised beforehand (bf16, in the MFMA's operand order, in the staging area).  One
-// workgroup per CU over its NRB row blocks, twelve waves in two roles.  Waves 8..11 copy the workgroup's weight rows
-// into a ring of D stages of 128 features (NRB 4 KB slots each, the one-block kernel's slot
-// layout: 256 bytes of each row) and wait only for their own copies; waves 0..7 each multiply 32 tokens over all
-// of K, their token fragments loaded from the staging area (an L2-resident 3 MB at 256 tokens)
-// straight into registers kTb4Tok stages ahead.  A wave's memory counter thus covers
-// one kind of access: the copies keep D - 1 stages (NRB x 2 KB each) in flight, independently
-// of the token loads.  One workgroup barrier per stage: the copy waves reach it once the stage
-// has landed, the multiplying waves once they have read the stage before it, whose slot the
-// copies issued after the barrier refill.  Then the copy waves leave (a barrier waits only for
-// the waves still running), the sums go through LDS, waves 4..7 leave too, and waves 0..3 take
-// the four blocks through the two-token-block kernel's hand-off: key partial sums stored, counted in with one round of atomics, the last arrivers'
-// gates, the value workgroups' bf16 tiles for the apply workgroups.
+// workgroup per CU over its NRB row blocks, twelve waves in two roles.  Waves 8..11 copy the
+// workgroup's weight rows into a ring of D stages of 128 features (NRB 4 KB slots each, the
+// one-block kernel's slot layout: 256 bytes of each row) and wait only for their own copies;
+// waves 0..7 each multiply 32 tokens over all of K, their token fragments loaded from the staging
+// area (an L2-resident 3 MB at 256 tokens) straight into registers kTb4Tok stages ahead.  A
+// wave's memory counter thus covers one kind of access: the copies keep D - 1 stages (up to NRB x
+// 4 KB each) in flight, independently of the token loads.  One workgroup barrier per stage: the
+// copy waves reach it once the stage has landed, the multiplying waves once they have read the
+// stage before it, whose slot the copies issued after the barrier refill.  Then the copy waves
+// leave (a barrier waits only for the waves still running), the sums go through LDS, waves 4..7
+// leave too, and waves 0..3 take the four blocks through the two-token-block kernel's hand-off:
+// key partial sums stored, counted in with one round of atomics, the last arrivers' gates, the
+// value workgroups' bf16 tiles for the apply workgroups.
 constexpr int kTb4Tok = 2;  // stages of token fragments in flight per multiplying wave
 // 16-token sub-blocks per multiplying wave: 16 / kTb4NT such waves (eight of 32 tokens, two per
 // SIMD, so that one wave's barrier wait and token loads overlap the other's MFMAs)
