@@ -1,6 +1,7 @@
 """The benchmark's roofline accounting (CPU): algorithmic bytes and flops of the forward and of the
 split path's entry points, against the per-token and per-call figures derived by hand from the
-layer sizes (every input read once, every output written once), and the one-GPU guard."""
+layer sizes (every input read once, every output written once), the kernel whose profile each
+token count's roofline names, and the one-GPU guard."""
 import os
 import subprocess
 import sys
@@ -64,3 +65,22 @@ def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=300)
     assert p.returncode == 2 and "one GPU" in p.stderr
+
+
+def test_kernel_of_token_ranges_at_the_decode_layout():
+    """The profile each workload's roofline names follows the library's schedule choice: one
+    token block streams, 65..128 tokens take the two-token-block kernel, 129..256 the
+    four-token-block kernel (bf16 weights, every workgroup owning 100 rows), more the tiled one;
+    MXFP8 weights never take the several-block streaming kernels."""
+    dec = synth.get("decode_b64")
+    cases = [(1, "k_stream_wide_fused"), (64, "k_stream_wide_fused"), (65, "k_stream_tb2"),
+             (128, "k_stream_tb2"), (129, "k_stream_tb4"), (256, "k_stream_tb4"), (257, "k_tiled_fused")]
+    for m, name in cases:
+        assert bench.kernel_of(synth.small_variant(dec, B=m, T=1))[0] == name, m
+    assert bench.tb4_layout(dec)
+    assert not bench.tb4_layout(synth.small_variant(dec, wkv_format="mxfp8"))
+    # 1600 wkv rows over 256 workgroups: 4 or 8 rows each, not one row count for all
+    assert not bench.tb4_layout(synth.small_variant(dec, dim=320, n_cols=4, head_dim=128))
+    assert bench.kernel_of(synth.small_variant(dec, B=200, T=1, wkv_format="mxfp8"))[0] != "k_stream_tb4"
+    # the profile names the sources whose hash it was taken at
+    assert bench.kernel_of(synth.small_variant(dec, B=256, T=1))[1] == ("stream.hip", "gather_gate.hip", "common.h")
